@@ -1,0 +1,192 @@
+/*
+ * specverify.h -- C ABI of the MI355X (gfx950) library for batched lossless
+ * speculative-sampling verification and the first-order Markov-head draft.
+ *
+ * The method (sources cited by page title and section):
+ *  - DART reading note (zhongzhuzhou.org, "DART：把草稿并行生成之后，还要补上
+ *    哪些依赖？"), sec. 2.3, eq. (3)-(4): accept a draft token x with
+ *    probability min(1, q(x)/p(x)); on rejection draw from the residual
+ *    [q - p]_+ / R, R = sum_v [q - p]_+ = 1 - sum_v min(p, q); no residual is
+ *    needed when R = 0; at temperature 0 verification compares with the
+ *    target argmax.
+ *  - DSpark paper guide (personal-site-bgy.pages.dev), "speculative decoding
+ *    basics": gamma drafts verified in one target pass, strict left-to-right
+ *    prefix survival, one bonus token from the target when every draft passes;
+ *    "confidence head": the analytic acceptance rate c* = 1 - 1/2 ||p - q||_1;
+ *    "scheduler": a verify length l_r per request, verify batch sum(1 + l_r);
+ *    "Markov head": p_k(v | x_0, x_<k) = softmax(U_k(v) + W1[x_{k-1}] W2(v)),
+ *    W1 in R^{V x r}, W2 in R^{r x V}, r = 256, x_0 the anchor token.
+ *  - Speculative-decoding survey (zhifeiding.github.io), sec. 1.2-1.3 and
+ *    2.1: one corrected token at the first rejection, tau = N + 1 tokens per
+ *    cycle, greedy verification as a position-wise argmax comparison.
+ *
+ * Notation: q = target distribution, p = draft distribution, both softmaxes
+ * of logits divided by the request's temperature T (T = 0: greedy).
+ *
+ * Conventions for every entry point:
+ *  - Every array pointer is a DEVICE pointer owned by the caller.  The library
+ *    never allocates, frees or synchronises (except spec_get_device_status),
+ *    and enqueues its work on `stream` (a hipStream_t passed as void*; NULL is
+ *    the null stream).  Calls return once the work is enqueued.
+ *  - Arrays are dense and row-major with the last dimension contiguous; logit
+ *    rows are fp32 or bf16 (spec_dtype).
+ *  - Host-checkable faults (null required pointer, negative size, unknown
+ *    dtype, workspace too small or not 256-byte aligned, unsupported shape)
+ *    return a negative spec_status before anything is enqueued.  A failed
+ *    kernel launch returns SPEC_EHIP.
+ *  - Data faults are found on the device, per request: l_r outside [0, gamma],
+ *    T negative / NaN / infinite / outside [1e-30, 1e30] when nonzero, a draft
+ *    token outside [0, V), a uniform outside [0, 1), a NaN or +inf logit, or a
+ *    logit row that is entirely -inf.  Such a request gets num_accepted = -1,
+ *    tokens -1 and NaN floats, and SPEC_DEV_BAD_REQUEST is set in the
+ *    workspace's status word.  Other requests are unaffected.  -inf logits
+ *    (masked ids) are valid.
+ *  - A workspace is a device buffer of at least the queried size, 256-byte
+ *    aligned, initialised once with spec_workspace_init before its first use.
+ *    The library keeps it consistent afterwards.  Calls that share a
+ *    workspace must be ordered (same stream, or synchronised); calls with
+ *    distinct workspaces may run concurrently.
+ */
+#ifndef SPECVERIFY_H
+#define SPECVERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { SPEC_F32 = 0, SPEC_BF16 = 1 } spec_dtype;
+
+typedef enum {
+    SPEC_OK = 0,
+    SPEC_EINVAL = -1,        /* null required pointer or negative size            */
+    SPEC_EDTYPE = -2,        /* dtype not supported for this argument            */
+    SPEC_EWORKSPACE = -3,    /* workspace null, too small or misaligned          */
+    SPEC_EHIP = -4,          /* a HIP runtime call or kernel launch failed       */
+    SPEC_EUNSUPPORTED = -5   /* shape outside the supported range                */
+} spec_status;
+
+/* Bits of the device status word kept in the workspace. */
+#define SPEC_DEV_BAD_REQUEST 0x1u   /* a request had invalid data (see above)      */
+#define SPEC_DEV_SPIN_TIMEOUT 0x2u  /* a cross-workgroup wait gave up; the outputs
+                                       of that call are undefined                  */
+
+/* Largest vocabulary the kernels accept. */
+#define SPEC_MAX_VOCAB 2097152
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int spec_version(void);
+
+/* Human-readable name of a spec_status value (static string). */
+const char *spec_status_string(int status);
+
+/* Workspace bytes for spec_verify_batch at these sizes (0 if the sizes are
+ * negative or unsupported).  The same buffer may serve every entry point as
+ * long as it is large enough for each call. */
+size_t spec_verify_workspace_bytes(int R, int gamma, int V);
+
+/* Zero-fills a workspace (one small kernel on `stream`).  Call once on a new
+ * buffer, or to recover a buffer after SPEC_DEV_SPIN_TIMEOUT. */
+int spec_workspace_init(void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Batched verification (DART note eq. (3)-(4); DSpark guide "basics",
+ * "confidence head", "scheduler"; survey sec. 1.3).
+ *
+ * For request r with l = verify_len[r], T = temperature[r], x_{i+1} =
+ * draft_tokens[r][i]:
+ *   T > 0:  for i < l: accept_i <=> q_i(x) >= p_i(x) or u_accept[r][i] <
+ *           q_i(x)/p_i(x).  A_r = number of leading accepts.  If A_r < l the
+ *           next token is an inverse-CDF draw (ascending token id, first id
+ *           whose running sum exceeds u * total) from [q_A - p_A]_+ with
+ *           u_sample[r][A_r] (from q_A if that residual mass is exactly 0);
+ *           otherwise from q_l (target row l) with u_sample[r][l].
+ *   T = 0:  g_i = argmax of target row i (lowest id on ties); accept_i <=>
+ *           x == g_i; the next token is g_{A_r}.  Uniforms are not read.
+ * Rows read: target rows 0..l, draft rows 0..l-1; other rows are never read.
+ *
+ *   target_logits  [R][gamma+1][V]  t_dtype   row i <-> draft position i+1,
+ *                                             row gamma the bonus row
+ *   draft_logits   [R][gamma][V]    d_dtype   (may be NULL when gamma == 0)
+ *   draft_tokens   [R][gamma]   int32         (may be NULL when gamma == 0)
+ *   verify_len     [R]          int32         0 <= l_r <= gamma
+ *   temperature    [R]          fp32          T >= 0
+ *   u_accept       [R][gamma]   fp32 in [0,1) (may be NULL when gamma == 0)
+ *   u_sample       [R][gamma+1] fp32 in [0,1)
+ *   out_tokens       [R][gamma+1] int32: x_1..x_A, then the drawn token, then -1
+ *   out_num_accepted [R]          int32: A_r (tokens committed = A_r + 1)
+ *   out_cstar        [R][gamma]   fp32, nullable: c*_i = sum_v min(p_i, q_i) for
+ *                                 i < l_r (T = 0: [argmax draft == g_i]), NaN beyond
+ *   out_resid_mass   [R][gamma]   fp32, nullable: sum_v [q_i - p_i]_+ (T = 0:
+ *                                 1 - c*_i), NaN beyond l_r
+ *   out_logq         [R][gamma+1] fp32, nullable: natural log of q_j at the
+ *                                 committed token j <= A_r (0 at T = 0), NaN beyond
+ * Sizes: R >= 0, gamma >= 0, 1 <= V <= SPEC_MAX_VOCAB.  R == 0 enqueues nothing.
+ */
+int spec_verify_batch(const void *target_logits, int t_dtype,
+                      const void *draft_logits, int d_dtype,
+                      const int32_t *draft_tokens, const int32_t *verify_len,
+                      const float *temperature, const float *u_accept, const float *u_sample,
+                      int R, int gamma, int V,
+                      int32_t *out_tokens, int32_t *out_num_accepted,
+                      float *out_cstar, float *out_resid_mass, float *out_logq,
+                      void *workspace, size_t workspace_bytes, void *stream);
+
+/* Workspace bytes for spec_tv_accept_rate. */
+size_t spec_tv_workspace_bytes(int N, int V);
+
+/*
+ * Analytic acceptance rate of N independent row pairs (DSpark guide,
+ * "confidence head": c* = 1 - 1/2 ||p - q||_1; DART note eq. (3)).
+ *   draft_logits, target_logits  [N][V]  dtype
+ *   temperature                  [N]     fp32 (T = 0: c* = [argmax p == argmax q])
+ *   out_cstar                    [N]     fp32 = sum_v min(p, q)
+ *   out_resid_mass               [N]     fp32, nullable = sum_v [q - p]_+
+ * Invalid rows (data faults as above) give NaN and set SPEC_DEV_BAD_REQUEST.
+ */
+int spec_tv_accept_rate(const void *draft_logits, const void *target_logits, int dtype,
+                        const float *temperature, int N, int V,
+                        float *out_cstar, float *out_resid_mass,
+                        void *workspace, size_t workspace_bytes, void *stream);
+
+/* Workspace bytes for spec_markov_draft_sample. */
+size_t spec_markov_workspace_bytes(int R, int gamma, int V, int rank);
+
+/*
+ * First-order Markov-head draft (DSpark guide, "Markov head"), serial over
+ * k = 1..gamma for every request r, with x_0 = anchor[r]:
+ *   l_k(v) = fp32( U[r][k-1][v] + sum_j W1[x_{k-1}][j] W2[j][v] )
+ *   x_k    = inverse-CDF draw (ascending id) from softmax(l_k / T_r) with
+ *            u_draft[r][k-1]; argmax of l_k (lowest id) at T_r = 0.
+ * The stored fp32 logits are the draft distribution that verification must
+ * compare against (pass out_draft_logits as draft_logits, d_dtype SPEC_F32).
+ *   U              [R][gamma][V]  u_dtype (fp32 or bf16)
+ *   W1             [V][rank]      w_dtype (bf16)
+ *   W2             [rank][V]      w_dtype (bf16)
+ *   anchor         [R]            int32 in [0, V)
+ *   temperature    [R]            fp32
+ *   u_draft        [R][gamma]     fp32 in [0,1)
+ *   out_draft_tokens [R][gamma]   int32 (-1 for an invalid request)
+ *   out_draft_logits [R][gamma][V] fp32
+ * Sizes: R >= 0, gamma >= 0, 1 <= V <= SPEC_MAX_VOCAB, rank == 256.
+ */
+int spec_markov_draft_sample(const void *U, int u_dtype,
+                             const void *W1, const void *W2, int w_dtype,
+                             const int32_t *anchor, const float *temperature,
+                             const float *u_draft,
+                             int R, int gamma, int V, int rank,
+                             int32_t *out_draft_tokens, float *out_draft_logits,
+                             void *workspace, size_t workspace_bytes, void *stream);
+
+/* Synchronises `stream`, copies the workspace's device status word (the OR
+ * of SPEC_DEV_* bits raised since the last clear) to *host_bits, and clears
+ * it when `clear` is nonzero. */
+int spec_get_device_status(void *workspace, uint32_t *host_bits, int clear, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPECVERIFY_H */

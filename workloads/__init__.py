@@ -1,0 +1,321 @@
+"""Seeded synthetic workloads for the verification and Markov-draft paths.
+
+This module only draws random inputs.  It holds none of the method's
+arithmetic (no softmax, no accept test, no inverse-CDF draw): the oracle and
+the HIP library both consume what it produces, and neither imports the other.
+
+Random numbers come from numpy's Philox counter-based generator
+(``numpy.random.Philox``), one independent key per (seed, stream id):
+
+  stream 0  draft tokens (Gumbel-max draws from the draft logits)
+  stream 1  u_accept   [R, gamma]       uniforms for the accept tests
+  stream 2  u_sample   [R, gamma + 1]   uniforms for the residual / bonus draw
+  stream 3  u_draft    [R, gamma]       uniforms for the Markov-head draft
+  stream 4  target logits
+  stream 5  draft-logit noise
+  stream 6  per-request parameters (verify lengths, noise scales, anchors)
+  stream 7  Markov tables W1, W2 and base logits U
+
+Uniforms are fp32 values (w >> 8) * 2**-24 of 32-bit Philox words: exact in
+fp32 and always in [0, 1).
+
+bf16 tensors are carried as ``numpy.uint16`` bit patterns (round to nearest
+even from fp32); fp32 tensors as ``numpy.float32``.
+
+The five named workloads follow the shapes, value distributions and
+structure of the pages' settings (gamma = 7 for DSpark's block, gamma = 8 for
+DART's default draft length, Qwen3- and DeepSeek-scale vocabularies, batch 1
+to 256, suffix decay of acceptance across positions).  The pages evaluate on
+public benchmark suites that are not used here: these synthetic inputs stand
+in for them.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional
+
+import numpy as np
+
+STREAM_DRAFT_TOKENS = 0
+STREAM_U_ACCEPT = 1
+STREAM_U_SAMPLE = 2
+STREAM_U_DRAFT = 3
+STREAM_TARGET = 4
+STREAM_NOISE = 5
+STREAM_PARAMS = 6
+STREAM_MARKOV = 7
+
+
+def rng(seed: int, stream: int) -> np.random.Generator:
+    """Philox generator keyed by (seed, stream)."""
+    return np.random.Generator(np.random.Philox(key=[int(seed), int(stream)]))
+
+
+def uniforms(gen: np.random.Generator, shape) -> np.ndarray:
+    """fp32 uniforms in [0, 1): top 24 bits of a 32-bit word times 2**-24."""
+    w = gen.integers(0, 2**32, size=shape, dtype=np.uint32)
+    return ((w >> np.uint32(8)).astype(np.float32) * np.float32(2.0**-24)).astype(np.float32)
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round fp32 to bf16 (nearest, ties to even); returns uint16 bit patterns."""
+    b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    out = b >> np.uint32(16)
+    out &= np.uint32(1)
+    out += np.uint32(0x7FFF)
+    out += b
+    out >>= np.uint32(16)
+    return out.astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Exact widening of bf16 bit patterns to fp32."""
+    return (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def as_f32(x: np.ndarray) -> np.ndarray:
+    """fp32 values of a logit array (uint16 = bf16 bits, float32 as is)."""
+    if x.dtype == np.uint16:
+        return bf16_bits_to_f32(x)
+    return np.asarray(x, dtype=np.float32)
+
+
+def _store(x: np.ndarray, dtype: str) -> np.ndarray:
+    if dtype == "bf16":
+        return f32_to_bf16_bits(x)
+    if dtype == "f32":
+        return np.ascontiguousarray(x, dtype=np.float32)
+    raise ValueError(dtype)
+
+
+def gumbel_max_tokens(zd: np.ndarray, temperature: np.ndarray, seed: int) -> np.ndarray:
+    """Draft tokens x_{i+1} drawn from softmax(zd[r, i] / T_r) by the Gumbel-max
+    construction (argmax of z/T + Gumbel noise); argmax of zd at T = 0.  This is
+    how a draft model hands its samples to verification; it is not the
+    verifier's own inverse-CDF rule."""
+    R, G, V = zd.shape
+    gen = rng(seed, STREAM_DRAFT_TOKENS)
+    out = np.empty((R, G), dtype=np.int32)
+    for r in range(R):
+        z = as_f32(zd[r]).astype(np.float64)
+        T = float(temperature[r])
+        if T == 0.0:
+            out[r] = np.argmax(z, axis=1)
+            continue
+        w = gen.integers(1, 2**32, size=(G, V), dtype=np.uint64).astype(np.float64) * 2.0**-32
+        out[r] = np.argmax(z / T - np.log(-np.log(w)), axis=1)
+    return out
+
+
+@dataclasses.dataclass
+class VerifyCase:
+    """Inputs of one batched verification call (shapes follow the C ABI)."""
+
+    name: str
+    target: np.ndarray          # [R, gamma+1, V] uint16 (bf16) or float32
+    draft: np.ndarray           # [R, gamma, V]   uint16 (bf16) or float32
+    draft_tokens: np.ndarray    # [R, gamma] int32
+    verify_len: np.ndarray      # [R] int32
+    temperature: np.ndarray     # [R] float32
+    u_accept: np.ndarray        # [R, gamma] float32
+    u_sample: np.ndarray        # [R, gamma+1] float32
+    seed: int = 0
+
+    @property
+    def R(self) -> int:
+        return int(self.target.shape[0])
+
+    @property
+    def gamma(self) -> int:
+        return int(self.draft.shape[1])
+
+    @property
+    def V(self) -> int:
+        return int(self.target.shape[2])
+
+    def subset(self, rows) -> "VerifyCase":
+        rows = np.asarray(rows)
+        return VerifyCase(self.name + "[sub]", self.target[rows], self.draft[rows],
+                          self.draft_tokens[rows], self.verify_len[rows],
+                          self.temperature[rows], self.u_accept[rows], self.u_sample[rows],
+                          self.seed)
+
+
+@dataclasses.dataclass
+class MarkovCase:
+    """Inputs of one Markov-head draft call plus the target for verification."""
+
+    name: str
+    U: np.ndarray               # [R, gamma, V] base draft logits
+    W1: np.ndarray              # [V, rank]
+    W2: np.ndarray              # [rank, V]
+    anchor: np.ndarray          # [R] int32
+    temperature: np.ndarray     # [R] float32
+    u_draft: np.ndarray         # [R, gamma] float32
+    target: np.ndarray          # [R, gamma+1, V]
+    verify_len: np.ndarray      # [R] int32
+    u_accept: np.ndarray        # [R, gamma]
+    u_sample: np.ndarray        # [R, gamma+1]
+    seed: int = 0
+
+    @property
+    def R(self) -> int:
+        return int(self.U.shape[0])
+
+    @property
+    def gamma(self) -> int:
+        return int(self.U.shape[1])
+
+    @property
+    def V(self) -> int:
+        return int(self.U.shape[2])
+
+    @property
+    def rank(self) -> int:
+        return int(self.W1.shape[1])
+
+
+def _uniform_streams(seed: int, R: int, gamma: int):
+    return (uniforms(rng(seed, STREAM_U_ACCEPT), (R, gamma)),
+            uniforms(rng(seed, STREAM_U_SAMPLE), (R, gamma + 1)))
+
+
+def make_verify_case(R: int, gamma: int, V: int, dtype: str = "bf16", seed: int = 0,
+                     target_std: float = 3.0, noise_std=1.0,
+                     verify_len=None, temperature=1.0, draft_dtype: Optional[str] = None,
+                     planted_boost: float = 0.0, name: str = "custom") -> VerifyCase:
+    """Generic case: target ~ N(0, target_std^2) (optionally one planted id per
+    target row raised by `planted_boost`), draft = target + N(0, sigma^2) with
+    sigma per position (array of length gamma), per request (array of length R)
+    or scalar; verify lengths and temperatures scalar or per request."""
+    draft_dtype = draft_dtype or dtype
+    gt = rng(seed, STREAM_TARGET)
+    z = gt.standard_normal((R, gamma + 1, V), dtype=np.float32)
+    z *= np.float32(target_std)
+    if planted_boost:
+        ids = rng(seed, STREAM_PARAMS).integers(0, V, size=(R, gamma + 1))
+        rr, ii = np.meshgrid(np.arange(R), np.arange(gamma + 1), indexing="ij")
+        z[rr, ii, ids] += np.float32(planted_boost)
+    target = _store(z, dtype)
+    del z
+    zt = as_f32(target)[:, :gamma, :]
+    sig = np.asarray(noise_std, dtype=np.float32)
+    if sig.ndim == 0:
+        sig = np.full((R, gamma), float(sig), dtype=np.float32)
+    elif sig.shape == (gamma,):
+        sig = np.broadcast_to(sig[None, :], (R, gamma))
+    elif sig.shape == (R,):
+        sig = np.broadcast_to(sig[:, None], (R, gamma))
+    gn = rng(seed, STREAM_NOISE)
+    noise = gn.standard_normal((R, gamma, V), dtype=np.float32)
+    noise *= sig[:, :, None].astype(np.float32)
+    noise += zt
+    draft = _store(noise, draft_dtype)
+    del noise, zt
+    if verify_len is None:
+        verify_len = gamma
+    vl = np.asarray(verify_len, dtype=np.int32)
+    if vl.ndim == 0:
+        vl = np.full((R,), int(vl), dtype=np.int32)
+    T = np.asarray(temperature, dtype=np.float32)
+    if T.ndim == 0:
+        T = np.full((R,), float(T), dtype=np.float32)
+    tokens = gumbel_max_tokens(draft, T, seed)
+    ua, us = _uniform_streams(seed, R, gamma)
+    return VerifyCase(name, target, draft, tokens, vl.astype(np.int32), T.astype(np.float32),
+                      ua, us, seed)
+
+
+# ---------------------------------------------------------------------------
+# the five named workloads
+# ---------------------------------------------------------------------------
+
+def tiny_chain(temperature: float = 1.0, seed: int = 1) -> VerifyCase:
+    """R=1, gamma=4 (+1 bonus row), V=32, fp32 target ~ N(0, 2^2), draft =
+    target + N(0, 1), l = 4; run at T = 1 and T = 0."""
+    return make_verify_case(1, 4, 32, "f32", seed, target_std=2.0, noise_std=1.0,
+                            verify_len=4, temperature=temperature,
+                            name=f"tiny_chain_T{temperature:g}")
+
+
+def single_user(seed: int = 2) -> VerifyCase:
+    """R=1, gamma=8, V=151936, fp32 target ~ N(0, 3^2) with one planted
+    dominant id per row (+8), draft = target + N(0, 1.5^2), l = 8, T = 1."""
+    return make_verify_case(1, 8, 151936, "f32", seed, target_std=3.0, noise_std=1.5,
+                            verify_len=8, temperature=1.0, planted_boost=8.0,
+                            name="single_user")
+
+
+def batched(seed: int = 3, R: int = 64, gamma: int = 7, V: int = 151936) -> VerifyCase:
+    """R=64, gamma=7, V=151936, bf16 target ~ N(0, 3^2); draft noise sigma
+    rising linearly 0.5 -> 2.5 across positions (suffix decay); l_r uniform on
+    0..7; T = 1."""
+    sig = (0.5 + 2.0 * np.arange(gamma) / max(gamma - 1, 1)).astype(np.float32)
+    vl = rng(seed, STREAM_PARAMS).integers(0, gamma + 1, size=R).astype(np.int32)
+    return make_verify_case(R, gamma, V, "bf16", seed, target_std=3.0, noise_std=sig,
+                            verify_len=vl, temperature=1.0, name="batched")
+
+
+def truncated_geometric(gen: np.random.Generator, p: float, kmax: int, size: int) -> np.ndarray:
+    """Draws on 0..kmax with P(k) proportional to p (1-p)^k."""
+    k = np.arange(kmax + 1)
+    w = p * (1.0 - p) ** k
+    return gen.choice(k, size=size, p=w / w.sum()).astype(np.int32)
+
+
+def high_load_mixed(seed: int = 5, R: int = 256, gamma: int = 7, V: int = 129280) -> VerifyCase:
+    """R=256, gamma=7, V=129280, bf16 target ~ N(0, 3^2); per-request noise
+    sigma ~ U[0.5, 3]; l_r truncated geometric(0.3) on 0..7; even requests at
+    T = 0 (greedy), odd requests at T = 1."""
+    gp = rng(seed, STREAM_PARAMS)
+    vl = truncated_geometric(gp, 0.3, gamma, R)
+    sig = gp.uniform(0.5, 3.0, size=R).astype(np.float32)
+    T = np.where(np.arange(R) % 2 == 0, 0.0, 1.0).astype(np.float32)
+    return make_verify_case(R, gamma, V, "bf16", seed, target_std=3.0, noise_std=sig,
+                            verify_len=vl, temperature=T, name="high_load_mixed")
+
+
+def dspark_markov(seed: int = 4, R: int = 64, gamma: int = 7, V: int = 129280,
+                  rank: int = 256, temperature: float = 1.0) -> MarkovCase:
+    """R=64, gamma=7, V=129280: bf16 base draft logits U_k ~ N(0, 2^2); W1
+    [V, 256] and W2 [256, V] bf16 ~ N(0, 0.02^2); anchor uniform over V; target
+    rows 0..gamma-1 = U_k + N(0, 1), target row gamma a fresh N(0, 2^2) +
+    N(0, 1); l = gamma; T = 1."""
+    gm = rng(seed, STREAM_MARKOV)
+    U32 = gm.standard_normal((R, gamma, V), dtype=np.float32) * np.float32(2.0)
+    W1 = f32_to_bf16_bits(gm.standard_normal((V, rank), dtype=np.float32) * np.float32(0.02))
+    W2 = f32_to_bf16_bits(gm.standard_normal((rank, V), dtype=np.float32) * np.float32(0.02))
+    U = f32_to_bf16_bits(U32)
+    del U32
+    gp = rng(seed, STREAM_PARAMS)
+    anchor = gp.integers(0, V, size=R).astype(np.int32)
+    gt = rng(seed, STREAM_TARGET)
+    extra = gt.standard_normal((R, 1, V), dtype=np.float32) * np.float32(2.0)
+    base = np.concatenate([bf16_bits_to_f32(U), extra], axis=1)
+    del extra
+    base += rng(seed, STREAM_NOISE).standard_normal((R, gamma + 1, V), dtype=np.float32)
+    target = f32_to_bf16_bits(base)
+    del base
+    T = np.full((R,), float(temperature), dtype=np.float32)
+    ud = uniforms(rng(seed, STREAM_U_DRAFT), (R, gamma))
+    ua, us = _uniform_streams(seed, R, gamma)
+    return MarkovCase("dspark_markov", U, W1, W2, anchor, T, ud, target,
+                      np.full((R,), gamma, dtype=np.int32), ua, us, seed)
+
+
+# name -> (builder, description) for the parity tests and the benchmark
+WORKLOADS = {
+    "tiny_chain": tiny_chain,
+    "single_user": single_user,
+    "batched": batched,
+    "dspark_markov": dspark_markov,
+    "high_load_mixed": high_load_mixed,
+}
+
+
+def algorithmic_bytes(verify_len: np.ndarray, V: int, t_elt: int, d_elt: int) -> int:
+    """Bytes the method must move for one verification call: every verified
+    draft row and target row, read once, plus the bonus target row."""
+    vl = np.asarray(verify_len, dtype=np.int64)
+    vl = vl[(vl >= 0)]
+    return int(((vl * (t_elt + d_elt)).sum() + vl.size * t_elt) * V)
