@@ -1,0 +1,249 @@
+"""Benchmark of batched speculative-sampling verification on one MI355X.
+
+A step is one spec_verify_batch call over the batched workload (R = 64
+requests, gamma = 7, V = 151936, bf16 logits, verify lengths uniform on 0..7,
+T = 1): every row of the hot path (softmax statistics, c*, accept tests,
+prefix survival, residual / bonus draw, commit) runs in that one launch.
+
+Inputs are generated once (seeded), uploaded, and replicated into enough
+device copies that consecutive steps never find their logits in the 256 MB
+Infinity Cache: each step reads a copy untouched for at least 512 MB of other
+traffic, so the timed region streams from HBM.
+
+Prints one JSON line:
+  value      verified draft positions per second (sum of l_r per call / time)
+  roofline   algorithmic bytes (every verified draft row and target row plus
+             the bonus row, read once) / average kernel time, against 8 TB/s
+  cpu_baseline  the fp64 oracle on the host (one thread) over the same batch
+
+--workload dspark measures the Markov-head draft (R = 64, gamma = 7,
+V = 129280, rank 256) instead, as an extra line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = ("verified draft positions/sec and achieved HBM GB/s (% of peak), "
+          "R=64 γ=7 V=151936")
+HBM_PEAK_GBS = 8000.0
+MALL_BYTES = 256 << 20
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "lossless_verification_sampling_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel_key: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources; None otherwise."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = t.get(kernel_key)
+    if not e or e.get("source_hash") != source_hash():
+        return None
+    return e.get("bytes_per_launch")
+
+
+def to_device(x, dev):
+    import torch
+    x = np.ascontiguousarray(x)
+    if x.dtype == np.uint16:
+        return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
+    return torch.from_numpy(x).to(dev)
+
+
+def cpu_baseline(case, min_seconds: float):
+    import oracle
+    passes, t0 = 0, time.perf_counter()
+    while True:
+        oracle.verify_case(case)
+        passes += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds:
+            break
+    positions = int(case.verify_len.sum()) * passes
+    return {"value": positions / dt, "unit": "positions/s", "cores": 1, "kind": "oracle",
+            "sample": f"the full {case.R}-request batch, {passes} pass(es), {dt:.1f} s, "
+                      f"fp64 C oracle on one host thread"}
+
+
+def bench_verify(args):
+    import torch
+    import lossless_verification_sampling_amd as sv
+    import workloads
+
+    dev = torch.device("cuda:0")
+    case = workloads.batched(seed=args.seed)
+    R, G1, V = case.target.shape
+    gamma = G1 - 1
+    sum_l = int(case.verify_len.sum())
+    alg_bytes = workloads.algorithmic_bytes(case.verify_len, V, 2, 2)
+    touched = alg_bytes
+    ncopy = args.copies or max(2, int(np.ceil(2 * MALL_BYTES / touched)) + 1)
+    tgt0 = to_device(case.target, dev)
+    drf0 = to_device(case.draft, dev)
+    tgts = [tgt0] + [tgt0.clone() for _ in range(ncopy - 1)]
+    drfs = [drf0] + [drf0.clone() for _ in range(ncopy - 1)]
+    tok = to_device(case.draft_tokens, dev)
+    vl = to_device(case.verify_len, dev)
+    T = to_device(case.temperature, dev)
+    ua = to_device(case.u_accept, dev)
+    us = to_device(case.u_sample, dev)
+    ws = sv.Workspace(dev, sv.spec_verify_workspace_bytes(R, gamma, V))
+    out = dict(tokens=torch.empty((R, G1), dtype=torch.int32, device=dev),
+               num_accepted=torch.empty((R,), dtype=torch.int32, device=dev),
+               cstar=torch.empty((R, gamma), dtype=torch.float32, device=dev),
+               resid_mass=torch.empty((R, gamma), dtype=torch.float32, device=dev),
+               logq=torch.empty((R, G1), dtype=torch.float32, device=dev))
+
+    def step(k):
+        sv.spec_verify_batch(tgts[k % ncopy], drfs[k % ncopy], tok, vl, T, ua, us, out=out,
+                             workspace=ws)
+
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+    if sv.spec_get_device_status(ws, clear=True):
+        raise RuntimeError("device status bits set during warm-up")
+    stream = torch.cuda.current_stream(dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        ev[k][0].record(stream)
+        step(args.warmup + k)
+        ev[k][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_ms = np.array([a.elapsed_time(b) for a, b in ev])
+    bits = sv.spec_get_device_status(ws, clear=True)
+    if bits:
+        raise RuntimeError(f"device status bits {bits:#x} during the timed steps")
+    avg_kernel_s = float(kern_ms.mean()) / 1e3
+    ms_per_step = wall / args.steps * 1e3
+    achieved = alg_bytes / avg_kernel_s / 1e9
+    traffic = measured_traffic("verify_batched")
+    result = {
+        "metric": METRIC,
+        "value": sum_l / (ms_per_step / 1e3),
+        "unit": "positions/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "batched", "R": R, "gamma": gamma, "V": V, "logits": "bf16",
+                   "sum_verify_len": sum_l, "temperature": 1.0, "seed": args.seed,
+                   "input_copies": ncopy, "parallelism": "none (one GPU)"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "algorithmic_bytes_per_launch": alg_bytes,
+                     "kernel_ms_mean": float(kern_ms.mean()),
+                     "kernel_ms_p10": float(np.percentile(kern_ms, 10)),
+                     "kernel_ms_p90": float(np.percentile(kern_ms, 90)),
+                     "kernel": "verify_kernel (bf16, bf16)"},
+        "kernel_positions_per_s": sum_l / avg_kernel_s,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
+    return result
+
+
+def bench_dspark(args):
+    import torch
+    import lossless_verification_sampling_amd as sv
+    import workloads
+
+    dev = torch.device("cuda:0")
+    mk = workloads.dspark_markov(seed=args.seed + 1)
+    R, gamma, V, rank = mk.R, mk.gamma, mk.V, mk.rank
+    U = to_device(mk.U, dev)
+    W1 = to_device(mk.W1, dev)
+    W2 = to_device(mk.W2, dev)
+    anc = to_device(mk.anchor, dev)
+    T = to_device(mk.temperature, dev)
+    ud = to_device(mk.u_draft, dev)
+    tok = torch.empty((R, gamma), dtype=torch.int32, device=dev)
+    lg = torch.empty((R, gamma, V), dtype=torch.float32, device=dev)
+    ws = sv.Workspace(dev, sv.spec_markov_workspace_bytes(R, gamma, V, rank))
+    for _ in range(args.warmup):
+        sv.spec_markov_draft_sample(U, W1, W2, anc, T, ud, out_tokens=tok, out_logits=lg,
+                                    workspace=ws)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        ev[k][0].record(stream)
+        sv.spec_markov_draft_sample(U, W1, W2, anc, T, ud, out_tokens=tok, out_logits=lg,
+                                    workspace=ws)
+        ev[k][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = np.array([a.elapsed_time(b) for a, b in ev])
+    flops = 2.0 * R * rank * V * gamma
+    per_step_bytes = (R * V * 2 + rank * V * 2 + R * V * 4) * gamma
+    return {
+        "metric": "Markov-head draft: drafted tokens/sec",
+        "value": R * gamma / (wall / args.steps),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": wall / args.steps * 1e3,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16-mfma/f32", "data": "synthetic",
+        "config": {"workload": "dspark_markov", "R": R, "gamma": gamma, "V": V, "rank": rank},
+        "roofline": {"bound": "hbm", "achieved": per_step_bytes / (ms.mean() / 1e3) / 1e9,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": per_step_bytes / (ms.mean() / 1e3) / 1e9 / HBM_PEAK_GBS,
+                     "traffic": None, "algorithmic_bytes_per_call": per_step_bytes,
+                     "mfma_tflops": flops / (ms.mean() / 1e3) / 1e12},
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--seed", type=int, default=3)
+    ap.add_argument("--copies", type=int, default=0, help="input copies rotated (0 = auto)")
+    ap.add_argument("--workload", choices=["batched", "dspark"], default="batched")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(requests shard across GPUs with no exchange; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+    res = bench_verify(args) if args.workload == "batched" else bench_dspark(args)
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

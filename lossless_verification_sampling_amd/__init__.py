@@ -1,0 +1,325 @@
+"""Python binding of libspecverify (batched lossless speculative-sampling
+verification and the Markov-head draft on MI355X).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in include/specverify.h.  The functions keep
+the C names.  Tensors must be contiguous CUDA (HIP) tensors on one device;
+logits are torch.float32 or torch.bfloat16.  Work is enqueued on the current
+torch stream and nothing synchronises except spec_get_device_status.
+
+The library must have been built (``python -m
+lossless_verification_sampling_amd._build`` or ``__graft_entry__.build()``);
+importing this module without it raises, there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libspecverify.so")
+
+SPEC_F32, SPEC_BF16 = 0, 1
+SPEC_OK = 0
+SPEC_DEV_BAD_REQUEST = 0x1
+SPEC_DEV_SPIN_TIMEOUT = 0x2
+SPEC_MAX_VOCAB = 2097152
+
+EXPORTED = (
+    "spec_version",
+    "spec_status_string",
+    "spec_verify_workspace_bytes",
+    "spec_workspace_init",
+    "spec_verify_batch",
+    "spec_tv_workspace_bytes",
+    "spec_tv_accept_rate",
+    "spec_markov_workspace_bytes",
+    "spec_markov_draft_sample",
+    "spec_get_device_status",
+)
+
+
+class SpecError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {spec_status_string(status)} ({status})")
+        self.status = status
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build the HIP library first "
+                          "(python -m lossless_verification_sampling_amd._build)")
+    lib = ctypes.CDLL(LIB_PATH)
+    p, i, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    lib.spec_version.restype = i
+    lib.spec_version.argtypes = []
+    lib.spec_status_string.restype = ctypes.c_char_p
+    lib.spec_status_string.argtypes = [i]
+    lib.spec_verify_workspace_bytes.restype = sz
+    lib.spec_verify_workspace_bytes.argtypes = [i, i, i]
+    lib.spec_tv_workspace_bytes.restype = sz
+    lib.spec_tv_workspace_bytes.argtypes = [i, i]
+    lib.spec_markov_workspace_bytes.restype = sz
+    lib.spec_markov_workspace_bytes.argtypes = [i, i, i, i]
+    lib.spec_workspace_init.restype = i
+    lib.spec_workspace_init.argtypes = [p, sz, p]
+    lib.spec_verify_batch.restype = i
+    lib.spec_verify_batch.argtypes = [p, i, p, i, p, p, p, p, p, i, i, i, p, p, p, p, p, p, sz, p]
+    lib.spec_tv_accept_rate.restype = i
+    lib.spec_tv_accept_rate.argtypes = [p, p, i, p, i, i, p, p, p, sz, p]
+    lib.spec_markov_draft_sample.restype = i
+    lib.spec_markov_draft_sample.argtypes = [p, i, p, p, i, p, p, p, i, i, i, i, p, p, p, sz, p]
+    lib.spec_get_device_status.restype = i
+    lib.spec_get_device_status.argtypes = [p, ctypes.POINTER(ctypes.c_uint32), i, p]
+    return lib
+
+
+_lib = _load()
+
+
+def library() -> ctypes.CDLL:
+    return _lib
+
+
+def spec_version() -> int:
+    return int(_lib.spec_version())
+
+
+def spec_status_string(status: int) -> str:
+    return _lib.spec_status_string(int(status)).decode()
+
+
+def spec_verify_workspace_bytes(R: int, gamma: int, V: int) -> int:
+    return int(_lib.spec_verify_workspace_bytes(R, gamma, V))
+
+
+def spec_tv_workspace_bytes(N: int, V: int) -> int:
+    return int(_lib.spec_tv_workspace_bytes(N, V))
+
+
+def spec_markov_workspace_bytes(R: int, gamma: int, V: int, rank: int) -> int:
+    return int(_lib.spec_markov_workspace_bytes(R, gamma, V, rank))
+
+
+# ---------------------------------------------------------------------------
+# marshalling helpers
+# ---------------------------------------------------------------------------
+
+def _stream_ptr(stream: Optional[torch.cuda.Stream], device) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return s.cuda_stream
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return SPEC_F32
+    if t.dtype == torch.bfloat16:
+        return SPEC_BF16
+    raise TypeError(f"logits must be float32 or bfloat16, got {t.dtype}")
+
+
+def _check(t: Optional[torch.Tensor], name: str, dtype=None, shape=None, device=None):
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _raise(status: int, what: str):
+    if status != SPEC_OK:
+        raise SpecError(status, what)
+
+
+class Workspace:
+    """A device buffer for the library's cross-workgroup exchange, initialised
+    once with spec_workspace_init and grown on demand.  Calls that share a
+    workspace must be stream-ordered."""
+
+    def __init__(self, device=None, nbytes: int = 0):
+        self.device = torch.device(device if device is not None else "cuda")
+        self.buf: Optional[torch.Tensor] = None
+        if nbytes:
+            self.ensure(nbytes)
+
+    def ensure(self, nbytes: int, stream=None) -> torch.Tensor:
+        if self.buf is None or self.buf.numel() < nbytes:
+            n = max(int(nbytes), 1 << 16)
+            n = (n + 255) // 256 * 256
+            self.buf = torch.empty(n, dtype=torch.uint8, device=self.device)
+            _raise(_lib.spec_workspace_init(_ptr(self.buf), n, _stream_ptr(stream, self.device)),
+                   "spec_workspace_init")
+        return self.buf
+
+    @property
+    def nbytes(self) -> int:
+        return 0 if self.buf is None else self.buf.numel()
+
+
+_default_ws = {}
+
+
+def default_workspace(device) -> Workspace:
+    device = torch.device(device)
+    key = (device.type, device.index if device.index is not None else torch.cuda.current_device())
+    ws = _default_ws.get(key)
+    if ws is None:
+        ws = Workspace(torch.device("cuda", key[1]))
+        _default_ws[key] = ws
+    return ws
+
+
+def spec_workspace_init(workspace: Workspace, stream=None) -> None:
+    buf = workspace.buf
+    if buf is None:
+        return
+    _raise(_lib.spec_workspace_init(_ptr(buf), buf.numel(), _stream_ptr(stream, buf.device)),
+           "spec_workspace_init")
+
+
+def spec_get_device_status(workspace: Workspace, clear: bool = True, stream=None) -> int:
+    """Synchronises the stream and returns the OR of SPEC_DEV_* bits."""
+    bits = ctypes.c_uint32(0)
+    buf = workspace.buf
+    if buf is None:
+        return 0
+    _raise(_lib.spec_get_device_status(_ptr(buf), ctypes.byref(bits), int(clear),
+                                       _stream_ptr(stream, buf.device)),
+           "spec_get_device_status")
+    return int(bits.value)
+
+
+# ---------------------------------------------------------------------------
+# entry points
+# ---------------------------------------------------------------------------
+
+def spec_verify_batch(target_logits: torch.Tensor, draft_logits: Optional[torch.Tensor],
+                      draft_tokens: Optional[torch.Tensor], verify_len: torch.Tensor,
+                      temperature: torch.Tensor, u_accept: Optional[torch.Tensor],
+                      u_sample: torch.Tensor, *, out: Optional[dict] = None,
+                      want_cstar: bool = True, want_resid: bool = True, want_logq: bool = True,
+                      workspace: Optional[Workspace] = None, stream=None) -> dict:
+    """Batched verification.  target_logits [R, gamma+1, V], draft_logits
+    [R, gamma, V] (float32 / bfloat16), draft_tokens [R, gamma] int32,
+    verify_len [R] int32, temperature [R] float32, u_accept [R, gamma] and
+    u_sample [R, gamma+1] float32.  Returns dict(tokens, num_accepted, cstar,
+    resid_mass, logq); `out` may supply preallocated output tensors."""
+    R, G1, V = target_logits.shape
+    gamma = G1 - 1
+    dev = target_logits.device
+    _check(target_logits, "target_logits", device=dev)
+    _check(draft_logits, "draft_logits", shape=(R, gamma, V), device=dev)
+    _check(draft_tokens, "draft_tokens", torch.int32, (R, gamma), dev)
+    _check(verify_len, "verify_len", torch.int32, (R,), dev)
+    _check(temperature, "temperature", torch.float32, (R,), dev)
+    _check(u_accept, "u_accept", torch.float32, (R, gamma), dev)
+    _check(u_sample, "u_sample", torch.float32, (R, G1), dev)
+    if out is None:
+        out = {}
+    o_tok = out.get("tokens")
+    if o_tok is None:
+        o_tok = torch.empty((R, G1), dtype=torch.int32, device=dev)
+    o_n = out.get("num_accepted")
+    if o_n is None:
+        o_n = torch.empty((R,), dtype=torch.int32, device=dev)
+    o_cs = out.get("cstar")
+    if o_cs is None and want_cstar:
+        o_cs = torch.empty((R, gamma), dtype=torch.float32, device=dev)
+    o_rs = out.get("resid_mass")
+    if o_rs is None and want_resid:
+        o_rs = torch.empty((R, gamma), dtype=torch.float32, device=dev)
+    o_lq = out.get("logq")
+    if o_lq is None and want_logq:
+        o_lq = torch.empty((R, G1), dtype=torch.float32, device=dev)
+    _check(o_tok, "out tokens", torch.int32, (R, G1), dev)
+    _check(o_n, "out num_accepted", torch.int32, (R,), dev)
+    _check(o_cs, "out cstar", torch.float32, (R, gamma), dev)
+    _check(o_rs, "out resid_mass", torch.float32, (R, gamma), dev)
+    _check(o_lq, "out logq", torch.float32, (R, G1), dev)
+    ws = workspace or default_workspace(dev)
+    need = spec_verify_workspace_bytes(R, gamma, V)
+    if need == 0:
+        raise SpecError(-5, "spec_verify_workspace_bytes")
+    buf = ws.ensure(need, stream)
+    d_dtype = _dtype(draft_logits) if draft_logits is not None else SPEC_F32
+    st = _lib.spec_verify_batch(_ptr(target_logits), _dtype(target_logits), _ptr(draft_logits),
+                                d_dtype, _ptr(draft_tokens), _ptr(verify_len), _ptr(temperature),
+                                _ptr(u_accept), _ptr(u_sample), R, gamma, V, _ptr(o_tok),
+                                _ptr(o_n), _ptr(o_cs), _ptr(o_rs), _ptr(o_lq), _ptr(buf),
+                                buf.numel(), _stream_ptr(stream, dev))
+    _raise(st, "spec_verify_batch")
+    return dict(tokens=o_tok, num_accepted=o_n, cstar=o_cs, resid_mass=o_rs, logq=o_lq)
+
+
+def spec_tv_accept_rate(draft_logits: torch.Tensor, target_logits: torch.Tensor,
+                        temperature: torch.Tensor, *, want_resid: bool = True,
+                        workspace: Optional[Workspace] = None, stream=None):
+    """c* and Res of N row pairs [N, V]; returns (cstar [N], resid_mass [N] or None)."""
+    N, V = target_logits.shape
+    dev = target_logits.device
+    _check(target_logits, "target_logits", device=dev)
+    _check(draft_logits, "draft_logits", target_logits.dtype, (N, V), dev)
+    _check(temperature, "temperature", torch.float32, (N,), dev)
+    cs = torch.empty((N,), dtype=torch.float32, device=dev)
+    rs = torch.empty((N,), dtype=torch.float32, device=dev) if want_resid else None
+    ws = workspace or default_workspace(dev)
+    need = spec_tv_workspace_bytes(N, V)
+    if need == 0:
+        raise SpecError(-5, "spec_tv_workspace_bytes")
+    buf = ws.ensure(need, stream)
+    st = _lib.spec_tv_accept_rate(_ptr(draft_logits), _ptr(target_logits), _dtype(target_logits),
+                                  _ptr(temperature), N, V, _ptr(cs), _ptr(rs), _ptr(buf),
+                                  buf.numel(), _stream_ptr(stream, dev))
+    _raise(st, "spec_tv_accept_rate")
+    return cs, rs
+
+
+def spec_markov_draft_sample(U: torch.Tensor, W1: torch.Tensor, W2: torch.Tensor,
+                             anchor: torch.Tensor, temperature: torch.Tensor,
+                             u_draft: torch.Tensor, *, out_tokens: Optional[torch.Tensor] = None,
+                             out_logits: Optional[torch.Tensor] = None,
+                             workspace: Optional[Workspace] = None, stream=None):
+    """Markov-head draft.  U [R, gamma, V] (float32 / bfloat16), W1 [V, rank],
+    W2 [rank, V] bfloat16, anchor [R] int32, temperature [R], u_draft
+    [R, gamma] float32.  Returns (tokens [R, gamma] int32, logits [R, gamma, V]
+    float32)."""
+    R, gamma, V = U.shape
+    rank = W1.shape[1]
+    dev = U.device
+    _check(U, "U", device=dev)
+    _check(W1, "W1", torch.bfloat16, (V, rank), dev)
+    _check(W2, "W2", torch.bfloat16, (rank, V), dev)
+    _check(anchor, "anchor", torch.int32, (R,), dev)
+    _check(temperature, "temperature", torch.float32, (R,), dev)
+    _check(u_draft, "u_draft", torch.float32, (R, gamma), dev)
+    tok = out_tokens if out_tokens is not None else torch.empty((R, gamma), dtype=torch.int32,
+                                                                 device=dev)
+    lg = out_logits if out_logits is not None else torch.empty((R, gamma, V),
+                                                                dtype=torch.float32, device=dev)
+    _check(tok, "out_tokens", torch.int32, (R, gamma), dev)
+    _check(lg, "out_logits", torch.float32, (R, gamma, V), dev)
+    ws = workspace or default_workspace(dev)
+    need = spec_markov_workspace_bytes(R, gamma, V, rank)
+    if need == 0:
+        raise SpecError(-5, "spec_markov_workspace_bytes")
+    buf = ws.ensure(need, stream)
+    st = _lib.spec_markov_draft_sample(_ptr(U), _dtype(U), _ptr(W1), _ptr(W2), SPEC_BF16,
+                                       _ptr(anchor), _ptr(temperature), _ptr(u_draft), R, gamma,
+                                       V, rank, _ptr(tok), _ptr(lg), _ptr(buf), buf.numel(),
+                                       _stream_ptr(stream, dev))
+    _raise(st, "spec_markov_draft_sample")
+    return tok, lg

@@ -1,0 +1,301 @@
+// common.h -- device helpers shared by the library's kernels (internal).
+//
+// The verification kernels hand data to each other only through kernel
+// boundaries (chunk statistics -> pair sums -> finalisers), so they need no
+// cross-workgroup synchronisation inside a launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "specverify.h"
+
+namespace sv {
+
+constexpr int kBlock = 256;               // threads per workgroup (4 wave64s)
+constexpr int kWaves = kBlock / 64;
+constexpr int kMaxGamma = 64;             // per-request rows kept in LDS by finalisers
+constexpr uint32_t kSpinLimit = 1u << 20; // polls before a wait gives up
+constexpr int kMaxChunks = 4096;          // chunks per row
+constexpr double kLog2e = 1.4426950408889634;
+constexpr double kLn2 = 0.6931471805599453;
+
+// Workspace control block (offset 0, 256 bytes).
+struct Control {
+    uint32_t epoch;      // launches completed on this workspace
+    uint32_t status;     // SPEC_DEV_* bits
+    uint32_t closed;     // requests closed in the running call
+    uint32_t pad[61];
+};
+static_assert(sizeof(Control) == 256, "control block size");
+
+__device__ __forceinline__ uint32_t atomic_load_u32(const uint32_t *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void atomic_store_u32(uint32_t *p, uint32_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t atomic_add_u32(uint32_t *p, uint32_t v) {
+    return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void atomic_or_u32(uint32_t *p, uint32_t v) {
+    __hip_atomic_fetch_or(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Launch tag: never 0, so a zero-initialised workspace holds no valid word.
+__device__ __forceinline__ uint32_t launch_tag(uint32_t epoch) { return epoch | 0x80000000u; }
+
+__device__ __forceinline__ void publish(uint64_t *slot, uint32_t tag, uint32_t payload) {
+    __hip_atomic_store(slot, ((uint64_t)tag << 32) | payload, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void publish_f(uint64_t *slot, uint32_t tag, float v) {
+    publish(slot, tag, __float_as_uint(v));
+}
+
+// Spins until the word carries `tag`; returns its payload.  On timeout raises
+// SPEC_DEV_SPIN_TIMEOUT and returns 0.  Out of line: it is the cold path of
+// every exchange and would otherwise be inlined at each call site.
+__device__ __noinline__ uint32_t await_word(const uint64_t *slot, uint32_t tag, Control *ctl) {
+    for (uint32_t it = 0; it < kSpinLimit; ++it) {
+        uint64_t v = __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if ((uint32_t)(v >> 32) == tag) return (uint32_t)v;
+        __builtin_amdgcn_s_sleep(2);
+    }
+    atomic_or_u32(&ctl->status, SPEC_DEV_SPIN_TIMEOUT);
+    return 0u;
+}
+__device__ __forceinline__ float await_f(const uint64_t *slot, uint32_t tag, Control *ctl) {
+    return __uint_as_float(await_word(slot, tag, ctl));
+}
+
+// Loads n (<= 4) consecutive published words in parallel, then waits for any
+// that do not carry `tag` yet.
+__device__ inline void await_n(const uint64_t *w, int n, uint32_t tag, Control *ctl,
+                               uint32_t *out) {
+    uint64_t v[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        if (q < n) v[q] = __hip_atomic_load(w + q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        if (q < n)
+            out[q] = ((uint32_t)(v[q] >> 32) == tag) ? (uint32_t)v[q] : await_word(w + q, tag, ctl);
+}
+
+
+// Adds one to a launch-tagged counter (tag in the high word, count in the low
+// word) and returns the count after the add.  A word carrying another launch's
+// tag (or zero) counts as 0, so the counter needs no reset between launches
+// and stale workspace contents cannot corrupt it.
+__device__ inline uint32_t tagged_increment(uint64_t *w, uint32_t tag) {
+    uint64_t old = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (;;) {
+        const uint32_t cnt = ((uint32_t)(old >> 32) == tag) ? (uint32_t)old : 0u;
+        const uint64_t nw = ((uint64_t)tag << 32) | (uint64_t)(cnt + 1u);
+        if (__hip_atomic_compare_exchange_strong(w, &old, nw, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT))
+            return cnt + 1u;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// element conversion
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+template <typename T> struct EltBytes;
+template <> struct EltBytes<float> { static constexpr int value = 4; };
+template <> struct EltBytes<uint16_t> { static constexpr int value = 2; };
+
+// Loads EPV consecutive logits starting at element e of `row` (e a multiple of
+// EPV; EPV * sizeof(T) <= 16) as fp32.
+template <typename T, int EPV> struct VecLoad;
+
+template <int EPV> struct VecLoad<float, EPV> {
+    __device__ __forceinline__ static void run(const float *row, long e, float *out) {
+        if constexpr (EPV == 4) {
+            float4 v = *reinterpret_cast<const float4 *>(row + e);
+            out[0] = v.x; out[1] = v.y; out[2] = v.z; out[3] = v.w;
+        } else if constexpr (EPV == 2) {
+            float2 v = *reinterpret_cast<const float2 *>(row + e);
+            out[0] = v.x; out[1] = v.y;
+        } else {
+            static_assert(EPV == 1, "fp32 vector width");
+            out[0] = row[e];
+        }
+    }
+};
+
+template <int EPV> struct VecLoad<uint16_t, EPV> {
+    __device__ __forceinline__ static void run(const uint16_t *row, long e, float *out) {
+        if constexpr (EPV == 8) {
+            uint4 v = *reinterpret_cast<const uint4 *>(row + e);
+            out[0] = bf16_lo(v.x); out[1] = bf16_hi(v.x);
+            out[2] = bf16_lo(v.y); out[3] = bf16_hi(v.y);
+            out[4] = bf16_lo(v.z); out[5] = bf16_hi(v.z);
+            out[6] = bf16_lo(v.w); out[7] = bf16_hi(v.w);
+        } else if constexpr (EPV == 4) {
+            uint2 v = *reinterpret_cast<const uint2 *>(row + e);
+            out[0] = bf16_lo(v.x); out[1] = bf16_hi(v.x);
+            out[2] = bf16_lo(v.y); out[3] = bf16_hi(v.y);
+        } else if constexpr (EPV == 2) {
+            uint32_t v = *reinterpret_cast<const uint32_t *>(row + e);
+            out[0] = bf16_lo(v); out[1] = bf16_hi(v);
+        } else {
+            static_assert(EPV == 1, "bf16 vector width");
+            out[0] = __uint_as_float(((uint32_t)row[e]) << 16);
+        }
+    }
+};
+
+template <typename T>
+__device__ __forceinline__ float load_one(const T *row, long e) {
+    float v;
+    VecLoad<T, 1>::run(row, e, &v);
+    return v;
+}
+
+// ---------------------------------------------------------------------------
+// wave / block reductions (fixed association order: every lane and every
+// workgroup running the same code on the same values gets the same bits)
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+__device__ __forceinline__ double wave_sum(double v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+__device__ __forceinline__ int wave_max_i(int v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o, 64));
+    return v;
+}
+__device__ __forceinline__ int wave_min_i(int v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o, 64));
+    return v;
+}
+// (value, index): larger value wins, equal values -> smaller index.
+__device__ __forceinline__ void argmax_combine(float &v, int &i, float v2, int i2) {
+    if (v2 > v || (v2 == v && i2 < i)) {
+        v = v2;
+        i = i2;
+    }
+}
+__device__ __forceinline__ void wave_argmax(float &v, int &i) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        float v2 = __shfl_xor(v, o, 64);
+        int i2 = __shfl_xor(i, o, 64);
+        argmax_combine(v, i, v2, i2);
+    }
+}
+
+struct BlockScratch {
+    float f[2][kWaves];
+    double d[2][kWaves];
+    int i[2][kWaves];
+};
+
+// Block-wide max of two values; all threads receive the results.
+__device__ inline void block_max2(float &a, float &b, BlockScratch &s) {
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    a = wave_max(a);
+    b = wave_max(b);
+    __syncthreads();
+    if (lane == 0) {
+        s.f[0][w] = a;
+        s.f[1][w] = b;
+    }
+    __syncthreads();
+    a = fmaxf(fmaxf(s.f[0][0], s.f[0][1]), fmaxf(s.f[0][2], s.f[0][3]));
+    b = fmaxf(fmaxf(s.f[1][0], s.f[1][1]), fmaxf(s.f[1][2], s.f[1][3]));
+}
+
+// Block-wide fp64 sum of two values; all threads receive the results.
+__device__ inline void block_sum2(double &a, double &b, BlockScratch &s) {
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    a = wave_sum(a);
+    b = wave_sum(b);
+    __syncthreads();
+    if (lane == 0) {
+        s.d[0][w] = a;
+        s.d[1][w] = b;
+    }
+    __syncthreads();
+    a = (s.d[0][0] + s.d[0][1]) + (s.d[0][2] + s.d[0][3]);
+    b = (s.d[1][0] + s.d[1][1]) + (s.d[1][2] + s.d[1][3]);
+}
+
+__device__ inline int block_max_i(int a, BlockScratch &s) {
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    a = wave_max_i(a);
+    __syncthreads();
+    if (lane == 0) s.i[0][w] = a;
+    __syncthreads();
+    return max(max(s.i[0][0], s.i[0][1]), max(s.i[0][2], s.i[0][3]));
+}
+
+__device__ inline int block_min_i(int a, BlockScratch &s) {
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    a = wave_min_i(a);
+    __syncthreads();
+    if (lane == 0) s.i[0][w] = a;
+    __syncthreads();
+    return min(min(s.i[0][0], s.i[0][1]), min(s.i[0][2], s.i[0][3]));
+}
+
+// Block-wide argmax of two (value, index) pairs.
+__device__ inline void block_argmax2(float &va, int &ia, float &vb, int &ib, BlockScratch &s) {
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    wave_argmax(va, ia);
+    wave_argmax(vb, ib);
+    __syncthreads();
+    if (lane == 0) {
+        s.f[0][w] = va; s.i[0][w] = ia;
+        s.f[1][w] = vb; s.i[1][w] = ib;
+    }
+    __syncthreads();
+    va = s.f[0][0]; ia = s.i[0][0];
+    vb = s.f[1][0]; ib = s.i[1][0];
+#pragma unroll
+    for (int k = 1; k < kWaves; ++k) {
+        argmax_combine(va, ia, s.f[0][k], s.i[0][k]);
+        argmax_combine(vb, ib, s.f[1][k], s.i[1][k]);
+    }
+}
+
+// Block-wide exclusive prefix sum (fp64) in thread order; *total gets the sum.
+// Any thread t may use excl_t + v_t as its inclusive value: callers locate a
+// target by "the first thread whose excl + v exceeds it", which is robust to
+// the last-bit differences between association orders.
+__device__ inline double block_exclusive_scan(double v, double *total, BlockScratch &s) {
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    double incl = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        double n = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += n;
+    }
+    double excl = __shfl_up(incl, 1, 64);
+    if (lane == 0) excl = 0.0;
+    __syncthreads();
+    if (lane == 63) s.d[0][w] = incl;
+    __syncthreads();
+    double base = 0.0;
+    for (int k = 0; k < w; ++k) base += s.d[0][k];
+    double tot = 0.0;
+    for (int k = 0; k < kWaves; ++k) tot += s.d[0][k];
+    *total = tot;
+    return base + excl;
+}
+
+}  // namespace sv

@@ -1,0 +1,144 @@
+"""The C-ABI library on the host (no GPU needed): it loads, exports every
+function include/specverify.h declares, and rejects bad arguments before
+enqueuing anything."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "specverify.h")
+LIB = os.path.join(ROOT, "lossless_verification_sampling_amd", "libspecverify.so")
+
+SPEC_OK, SPEC_EINVAL, SPEC_EDTYPE, SPEC_EWORKSPACE, SPEC_EHIP, SPEC_EUNSUPPORTED = 0, -1, -2, -3, -4, -5
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(spec_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    assert os.path.exists(LIB), "build the library first (__graft_entry__.build())"
+    return ctypes.CDLL(LIB)
+
+
+def test_exports_every_declared_function(lib):
+    names = declared_functions()
+    assert len(names) >= 10, names
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in specverify.h but not exported"
+
+
+def test_python_binding_names_match_header():
+    import lossless_verification_sampling_amd as sv
+    assert sorted(sv.EXPORTED) == declared_functions()
+    for n in sv.EXPORTED:
+        assert callable(getattr(sv, n))
+
+
+def test_status_strings_and_version(lib):
+    lib.spec_status_string.restype = ctypes.c_char_p
+    for s in (SPEC_OK, SPEC_EINVAL, SPEC_EDTYPE, SPEC_EWORKSPACE, SPEC_EHIP, SPEC_EUNSUPPORTED):
+        assert lib.spec_status_string(s).startswith(b"SPEC_")
+    assert lib.spec_version() >= 100
+
+
+def test_workspace_sizes(lib):
+    f = lib.spec_verify_workspace_bytes
+    f.restype = ctypes.c_size_t
+    assert f(64, 7, 151936) > 0 and f(64, 7, 151936) % 256 == 0
+    assert f(-1, 7, 100) == 0 and f(1, -1, 100) == 0 and f(1, 1, 0) == 0
+    assert f(1, 65, 100) == 0                      # gamma above the supported maximum
+    assert f(1, 1, 2097152) > 0 and f(1, 1, 2097153) == 0
+    assert f(256, 7, 129280) >= f(64, 7, 129280)
+    g = lib.spec_tv_workspace_bytes
+    g.restype = ctypes.c_size_t
+    assert g(10, 1000) > 0 and g(-1, 10) == 0
+    m = lib.spec_markov_workspace_bytes
+    m.restype = ctypes.c_size_t
+    assert m(64, 7, 129280, 256) > 0 and m(64, 7, 129280, 128) == 0
+
+
+def _verify(lib, **kw):
+    p = ctypes.c_void_p
+    fake = p(0x1000)
+    args = dict(target=fake, t_dtype=1, draft=fake, d_dtype=1, tokens=fake, vlen=fake, temp=fake,
+                ua=fake, us=fake, R=4, gamma=3, V=100, out_tok=fake, out_n=fake, cs=None,
+                rs=None, lq=None, ws=p(0x10000), ws_bytes=1 << 30, stream=None)
+    args.update(kw)
+    f = lib.spec_verify_batch
+    f.restype = ctypes.c_int
+    f.argtypes = [p, ctypes.c_int, p, ctypes.c_int, p, p, p, p, p, ctypes.c_int, ctypes.c_int,
+                  ctypes.c_int, p, p, p, p, p, p, ctypes.c_size_t, p]
+    return f(args["target"], args["t_dtype"], args["draft"], args["d_dtype"], args["tokens"],
+             args["vlen"], args["temp"], args["ua"], args["us"], args["R"], args["gamma"],
+             args["V"], args["out_tok"], args["out_n"], args["cs"], args["rs"], args["lq"],
+             args["ws"], args["ws_bytes"], args["stream"])
+
+
+def test_verify_argument_validation(lib):
+    """Every case below must be rejected on the host before any HIP call."""
+    assert _verify(lib, R=-1) == SPEC_EINVAL
+    assert _verify(lib, V=0) == SPEC_EINVAL
+    assert _verify(lib, gamma=-2) == SPEC_EINVAL
+    assert _verify(lib, t_dtype=7) == SPEC_EDTYPE
+    assert _verify(lib, d_dtype=-1) == SPEC_EDTYPE
+    assert _verify(lib, gamma=65) == SPEC_EUNSUPPORTED
+    assert _verify(lib, V=2097153) == SPEC_EUNSUPPORTED
+    assert _verify(lib, target=None) == SPEC_EINVAL
+    assert _verify(lib, us=None) == SPEC_EINVAL
+    assert _verify(lib, out_n=None) == SPEC_EINVAL
+    assert _verify(lib, draft=None) == SPEC_EINVAL
+    assert _verify(lib, tokens=None) == SPEC_EINVAL
+    assert _verify(lib, ws=None) == SPEC_EWORKSPACE
+    assert _verify(lib, ws=ctypes.c_void_p(0x10010)) == SPEC_EWORKSPACE   # misaligned
+    assert _verify(lib, ws_bytes=256) == SPEC_EWORKSPACE                  # too small
+    assert _verify(lib, R=0) == SPEC_OK                                   # nothing to do
+
+
+def test_markov_and_tv_argument_validation(lib):
+    p = ctypes.c_void_p
+    fake = p(0x1000)
+    m = lib.spec_markov_draft_sample
+    m.restype = ctypes.c_int
+    m.argtypes = [p, ctypes.c_int, p, p, ctypes.c_int, p, p, p, ctypes.c_int, ctypes.c_int,
+                  ctypes.c_int, ctypes.c_int, p, p, p, ctypes.c_size_t, p]
+
+    def mk(**kw):
+        a = dict(U=fake, ud=1, W1=fake, W2=fake, wd=1, anchor=fake, temp=fake, u=fake, R=2,
+                 gamma=3, V=100, rank=256, tok=fake, lg=fake, ws=p(0x10000), wsb=1 << 30)
+        a.update(kw)
+        return m(a["U"], a["ud"], a["W1"], a["W2"], a["wd"], a["anchor"], a["temp"], a["u"],
+                 a["R"], a["gamma"], a["V"], a["rank"], a["tok"], a["lg"], a["ws"], a["wsb"],
+                 None)
+
+    assert mk(rank=128) == SPEC_EUNSUPPORTED
+    assert mk(wd=0) == SPEC_EDTYPE
+    assert mk(ud=5) == SPEC_EDTYPE
+    assert mk(R=-1) == SPEC_EINVAL
+    assert mk(U=None) == SPEC_EINVAL
+    assert mk(W1=p(0x1002)) == SPEC_EINVAL          # W1 must be 16-byte aligned
+    assert mk(ws=None) == SPEC_EWORKSPACE
+    assert mk(wsb=100) == SPEC_EWORKSPACE
+    assert mk(R=0) == SPEC_OK and mk(gamma=0) == SPEC_OK
+
+    t = lib.spec_tv_accept_rate
+    t.restype = ctypes.c_int
+    t.argtypes = [p, p, ctypes.c_int, p, ctypes.c_int, ctypes.c_int, p, p, p, ctypes.c_size_t, p]
+    assert t(fake, fake, 3, fake, 4, 100, fake, None, p(0x10000), 1 << 30, None) == SPEC_EDTYPE
+    assert t(None, fake, 0, fake, 4, 100, fake, None, p(0x10000), 1 << 30, None) == SPEC_EINVAL
+    assert t(fake, fake, 0, fake, 4, 100, fake, None, None, 1 << 30, None) == SPEC_EWORKSPACE
+    assert t(fake, fake, 0, fake, 0, 100, fake, None, None, 0, None) == SPEC_OK
+
+
+def test_workspace_init_validation(lib):
+    f = lib.spec_workspace_init
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    assert f(None, 1024, None) == SPEC_EWORKSPACE
+    assert f(ctypes.c_void_p(0x10010), 1024, None) == SPEC_EWORKSPACE
+    assert f(ctypes.c_void_p(0x10000), 16, None) == SPEC_EWORKSPACE

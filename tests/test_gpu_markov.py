@@ -1,0 +1,110 @@
+"""GPU parity of spec_markov_draft_sample against the oracle, and the DSpark
+workload end to end (Markov-head draft, then verification of its fp32 draft
+logits against the bf16 target)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_util import compare_verify, run_verify, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def sv():
+    import lossless_verification_sampling_amd as m
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return m
+
+
+@pytest.fixture(scope="module")
+def dev(sv):
+    return torch.device("cuda:0")
+
+
+def run_markov(sv, mk, dev):
+    tok, lg = sv.spec_markov_draft_sample(to_device(mk.U, dev), to_device(mk.W1, dev),
+                                          to_device(mk.W2, dev), to_device(mk.anchor, dev),
+                                          to_device(mk.temperature, dev),
+                                          to_device(mk.u_draft, dev))
+    torch.cuda.synchronize()
+    return tok.cpu().numpy(), lg.cpu().numpy()
+
+
+def compare_markov(mk, tok, lg, ref, rows=None):
+    """Tokens bit-exact up to the oracle's first near tie.  Logits: the oracle
+    rounds U + b once from the exact b; the GPU rounds the MFMA sum b to fp32
+    first (error below 1e-7 |b| + fp32 accumulation), then U + b.  So the
+    two differ by at most one ulp of l plus 1e-7 absolute (|b| < 0.1 here);
+    the bound is absolute because U + b can cancel."""
+    rows = range(mk.R) if rows is None else rows
+    ties = 0
+    for i, r in enumerate(rows):
+        rt = ref["tokens"][i]
+        if rt[0] < 0:
+            assert (tok[r] == -1).all(), r
+            continue
+        ft = int(ref["first_tie"][i])
+        upto = mk.gamma if ft < 0 else ft
+        ties += ft >= 0
+        assert np.array_equal(tok[r, :upto], rt[:upto]), (r, tok[r], rt, ft)
+        # logits of the steps whose conditioning token agreed
+        steps = upto + 1 if ft >= 0 else mk.gamma
+        g = lg[r, :steps].astype(np.float64)
+        o = ref["logits"][i, :steps].astype(np.float64)
+        ulp = np.spacing(np.abs(ref["logits"][i, :steps])).astype(np.float64)
+        err = np.abs(g - o)
+        bad = err > ulp + 1e-7
+        assert not bad.any(), (r, int(bad.sum()), float(err.max()), g[bad][:4], o[bad][:4])
+    return ties
+
+
+@pytest.mark.parametrize("R,gamma,V,T", [
+    (3, 4, 1000, 1.0),
+    (2, 3, 1001, 0.7),      # ragged V (scalar W2 staging)
+    (70, 2, 2048, 1.0),     # two MFMA row blocks
+    (4, 3, 4096, 0.0),      # greedy
+    (1, 7, 129280, 1.0),
+])
+def test_markov_small(sv, dev, R, gamma, V, T):
+    print(f"[markov] R={R} gamma={gamma} V={V} T={T}", flush=True)
+    mk = workloads.dspark_markov(seed=R + V, R=R, gamma=gamma, V=V, temperature=T)
+    tok, lg = run_markov(sv, mk, dev)
+    ref = oracle.markov_draft(mk.U, mk.W1, mk.W2, mk.anchor, mk.temperature, mk.u_draft)
+    ties = compare_markov(mk, tok, lg, ref)
+    print(f"[markov] near ties: {ties}", flush=True)
+
+
+def test_markov_invalid(sv, dev):
+    mk = workloads.dspark_markov(seed=3, R=4, gamma=3, V=777)
+    mk.anchor[1] = 777            # out of range
+    mk.temperature[2] = -1.0      # invalid temperature
+    tok, _ = run_markov(sv, mk, dev)
+    ref = oracle.markov_draft(mk.U, mk.W1, mk.W2, mk.anchor, mk.temperature, mk.u_draft)
+    assert (tok[1] == -1).all() and (tok[2] == -1).all()
+    compare_markov(mk, tok, np.zeros((4, 3, 777), np.float32) + ref["logits"], ref)
+
+
+def test_dspark_full_end_to_end(sv, dev):
+    """R=64, gamma=7, V=129280: GPU Markov draft (oracle on sampled requests),
+    then GPU verification of the GPU's fp32 draft logits against the bf16
+    target, checked against the oracle fed the same draft logits and tokens."""
+    mk = workloads.dspark_markov()
+    print(f"[dspark] R={mk.R} gamma={mk.gamma} V={mk.V}", flush=True)
+    tok, lg = run_markov(sv, mk, dev)
+    rows = [0, 17, 63]
+    sub = oracle.markov_draft(mk.U[rows], mk.W1, mk.W2, mk.anchor[rows], mk.temperature[rows],
+                              mk.u_draft[rows])
+    ties = compare_markov(mk, tok, lg, sub, rows)
+    print(f"[dspark] draft near ties on sampled rows: {ties}", flush=True)
+    assert (tok >= 0).all() and (tok < mk.V).all()
+    case = workloads.VerifyCase("dspark_verify", mk.target, lg, tok.astype(np.int32),
+                                mk.verify_len, mk.temperature, mk.u_accept, mk.u_sample)
+    gpu = run_verify(sv, case, dev)
+    ref = oracle.verify_case(case)
+    st = compare_verify(case, gpu, ref, rtol=2e-3)
+    print(f"[dspark] verify exact={st['exact']} near_ties={st['near_ties']} "
+          f"max_rel c*={st['max_rel_cstar']:.2e}", flush=True)
+    assert st["exact"] + st["near_ties"] == mk.R

@@ -1,0 +1,256 @@
+"""GPU parity of spec_verify_batch and spec_tv_accept_rate against the oracle
+(called through the C ABI via the binding).  The named workloads run at their
+full sizes; small cases span several chunks and a ragged tail; edge cases cover
+empty, degenerate and invalid inputs."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import oracle_pins
+import workloads
+from gpu_util import compare_verify, run_verify, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def sv():
+    import lossless_verification_sampling_amd as m
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return m
+
+
+@pytest.fixture(scope="module")
+def dev(sv):
+    return torch.device("cuda:0")
+
+
+def _report(name, stats):
+    print(f"[{name}] exact={stats['exact']} near_ties={stats['near_ties']} "
+          f"(matched anyway {stats['near_ties_matched']}) invalid={stats['invalid']} "
+          f"max_rel c*={stats['max_rel_cstar']:.2e} res={stats['max_rel_resid']:.2e} "
+          f"(abs {stats['max_abs_resid']:.1e}) logq={stats['max_rel_logq']:.2e}", flush=True)
+
+
+def _check(sv, dev, case, name, workspace=None, rtol=None):
+    print(f"[{name}] R={case.R} gamma={case.gamma} V={case.V} "
+          f"dtypes={case.target.dtype},{case.draft.dtype}", flush=True)
+    gpu = run_verify(sv, case, dev, workspace)
+    ref = oracle.verify_case(case)
+    stats = compare_verify(case, gpu, ref, rtol)
+    _report(name, stats)
+    return gpu, ref, stats
+
+
+# ---------------------------------------------------------------------------
+# the named workloads at full size
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("T", [1.0, 0.0])
+def test_tiny_chain(sv, dev, T):
+    _check(sv, dev, workloads.tiny_chain(temperature=T), f"tiny_chain_T{T}")
+
+
+def test_single_user_full(sv, dev):
+    gpu, ref, st = _check(sv, dev, workloads.single_user(), "single_user")
+    assert st["exact"] + st["near_ties"] == 1
+
+
+def test_batched_full(sv, dev):
+    case = workloads.batched()
+    gpu, ref, st = _check(sv, dev, case, "batched")
+    assert st["exact"] + st["near_ties"] == case.R
+
+
+def test_high_load_mixed_full(sv, dev):
+    case = workloads.high_load_mixed()
+    gpu, ref, st = _check(sv, dev, case, "high_load_mixed")
+    assert st["exact"] + st["near_ties"] == case.R
+    # greedy requests are exact by construction
+    greedy = case.temperature == 0
+    assert (ref["first_tie"][greedy] < 0).all()
+
+
+# ---------------------------------------------------------------------------
+# small cases: several chunks, ragged tails, dtypes, temperatures
+# ---------------------------------------------------------------------------
+
+SMALL = [
+    # R, gamma, V, t_dtype, d_dtype
+    (5, 4, 1000, "bf16", "bf16"),
+    (3, 7, 70001, "bf16", "bf16"),     # odd V: scalar-load path, ragged chunk
+    (4, 3, 65536, "f32", "f32"),
+    (6, 5, 9000, "bf16", "f32"),       # mixed dtypes (Markov-draft verify layout)
+    (6, 5, 9000, "f32", "bf16"),
+    (2, 8, 151936, "bf16", "bf16"),
+    (9, 2, 17, "f32", "f32"),          # V smaller than one vector group
+    (1, 1, 1, "f32", "f32"),           # single-token vocabulary
+]
+
+
+@pytest.mark.parametrize("shape", SMALL, ids=lambda s: "R%d_g%d_V%d_%s_%s" % s)
+def test_small_shapes(sv, dev, shape):
+    R, gamma, V, tdt, ddt = shape
+    gen = np.random.default_rng(R * 1000 + V)
+    vl = gen.integers(0, gamma + 1, R).astype(np.int32)
+    vl[0] = gamma
+    T = np.array([1.0, 0.0, 0.6, 1.7, 1.0, 0.05][:R] * (R // 6 + 1), np.float32)[:R]
+    case = workloads.make_verify_case(R, gamma, V, tdt, seed=V + R, draft_dtype=ddt,
+                                      target_std=2.5, noise_std=1.0, verify_len=vl,
+                                      temperature=T)
+    _check(sv, dev, case, f"small_{R}_{gamma}_{V}_{tdt}_{ddt}")
+
+
+def test_gamma_zero(sv, dev):
+    """gamma = 0: each request commits one token drawn from target row 0."""
+    case = workloads.make_verify_case(7, 0, 5000, "bf16", seed=4, verify_len=0,
+                                      temperature=[1.0, 0.0, 1.0, 0.5, 2.0, 0.0, 1.0])
+    _check(sv, dev, case, "gamma0")
+
+
+def test_verify_len_extremes(sv, dev):
+    for l in (0, 6):
+        case = workloads.make_verify_case(8, 6, 20000, "bf16", seed=10 + l, verify_len=l,
+                                          temperature=1.0)
+        _check(sv, dev, case, f"all_l{l}")
+
+
+def test_max_gamma(sv, dev):
+    case = workloads.make_verify_case(2, 64, 3000, "bf16", seed=64, noise_std=0.05,
+                                      verify_len=[64, 40], temperature=1.0)
+    _check(sv, dev, case, "gamma64")
+
+
+def test_identical_and_disjoint_rows(sv, dev):
+    case = workloads.make_verify_case(6, 4, 4096, "f32", seed=8, verify_len=4, temperature=1.0)
+    case.draft[:3] = case.target[:3, :4]                 # p == q: every draft accepted
+    case.draft[3:, :, 1::2] = -np.inf                    # disjoint supports: draft on
+    case.target[3:, :, 0::2] = -np.inf                   # even ids, target on odd ids
+    case.draft_tokens[3:] = 2 * (case.draft_tokens[3:] // 2)
+    gpu, ref, _ = _check(sv, dev, case, "identical_disjoint")
+    assert (gpu["num_accepted"][:3] == 4).all()
+    assert np.allclose(gpu["cstar"][:3], 1.0, atol=1e-6)
+    assert np.allclose(gpu["resid_mass"][:3], 0.0, atol=1e-6)
+    assert (gpu["num_accepted"][3:] == 0).all() and (gpu["tokens"][3:, 0] % 2 == 1).all()
+    assert np.allclose(gpu["cstar"][3:], 0.0, atol=1e-6)
+
+
+def test_small_and_large_temperature(sv, dev):
+    case = workloads.make_verify_case(4, 3, 8192, "bf16", seed=12, verify_len=3,
+                                      temperature=[0.01, 0.2, 5.0, 50.0])
+    _check(sv, dev, case, "temperatures")
+
+
+def test_invalid_requests(sv, dev):
+    """Invalid inputs flag only their own request (num_accepted -1, tokens -1,
+    NaN floats) and raise the device status bit."""
+    from lossless_verification_sampling_amd import (SPEC_DEV_BAD_REQUEST, Workspace,
+                                                    spec_get_device_status)
+    R = 10
+    case = workloads.make_verify_case(R, 3, 2048, "f32", seed=5, verify_len=3, temperature=1.0)
+    case.verify_len[1] = 4              # l > gamma
+    case.draft_tokens[2, 1] = 2048      # token out of range
+    case.target[3, 2, 7] = np.nan       # NaN logit
+    case.draft[4, 0, 9] = np.inf        # +inf logit
+    case.temperature[5] = -1.0          # negative temperature
+    case.u_accept[6, 0] = 1.0           # uniform out of range
+    case.target[7, 1] = -np.inf         # a row of only -inf
+    case.temperature[8] = 0.0
+    case.target[8, 0, 3] = np.nan       # NaN at T = 0
+    ws = Workspace(dev)
+    gpu, ref, st = _check(sv, dev, case, "invalid", workspace=ws)
+    assert st["invalid"] == 8 and gpu["num_accepted"][0] >= 0 and gpu["num_accepted"][9] >= 0
+    bits = spec_get_device_status(ws, clear=True)
+    assert bits & SPEC_DEV_BAD_REQUEST
+    assert spec_get_device_status(ws, clear=True) == 0
+
+
+def test_masked_ids_are_valid(sv, dev):
+    case = workloads.make_verify_case(4, 3, 5000, "bf16", seed=6, verify_len=3, temperature=1.0)
+    ninf = workloads.f32_to_bf16_bits(np.array([-np.inf], np.float32))[0]
+    case.target[:, :, 4000:] = ninf     # padded vocabulary tail
+    case.draft[:, :, 4000:] = ninf
+    case.draft_tokens[:] = np.minimum(case.draft_tokens, 3999)
+    gpu, _, st = _check(sv, dev, case, "masked")
+    assert st["invalid"] == 0 and (gpu["tokens"] < 4000).all()
+
+
+# ---------------------------------------------------------------------------
+# exact law on the GPU: the committed token follows q exactly
+# ---------------------------------------------------------------------------
+
+def test_exact_grid_law_on_gpu(sv, dev):
+    """The oracle's exact-enumeration pin, replayed through the GPU: over every
+    draft token and an 840-point grid of both uniforms the law of the first
+    committed token equals q0 exactly (DART note eq. (3)-(4))."""
+    from fractions import Fraction
+    den, p0, q0, q1 = oracle_pins.EXACT_CASES[0]
+    V, n_grid = 4, oracle_pins.GRID_FOR_DEN[den]
+    g = (np.arange(n_grid, dtype=np.float64) + 0.5) / n_grid
+    ua, us = np.meshgrid(g, g, indexing="ij")
+    xs = [x for x in range(V) if p0[x] > 0]
+    n = ua.size
+    R = n * len(xs)
+    target = np.empty((R, 2, V), np.float32)
+    target[:, 0] = oracle_pins._logits_from_probs(np.array(q0) / den)
+    target[:, 1] = oracle_pins._logits_from_probs(np.array(q1) / den)
+    draft = np.empty((R, 1, V), np.float32)
+    draft[:, 0] = oracle_pins._logits_from_probs(np.array(p0) / den)
+    case = workloads.VerifyCase("grid", target, draft,
+                                np.repeat(np.array(xs, np.int32), n)[:, None],
+                                np.ones(R, np.int32), np.ones(R, np.float32),
+                                np.tile(ua.ravel(), len(xs)).astype(np.float32)[:, None],
+                                np.stack([np.tile(us.ravel(), len(xs))] * 2, 1).astype(np.float32))
+    gpu = run_verify(sv, case, dev)
+    tok0 = gpu["tokens"][:, 0].reshape(len(xs), n)
+    law = [Fraction(0)] * V
+    for k, x in enumerate(xs):
+        for v in range(V):
+            law[v] += Fraction(p0[x], den) / n * int((tok0[k] == v).sum())
+    assert law == [Fraction(a, den) for a in q0], law
+
+
+# ---------------------------------------------------------------------------
+# determinism, workspace reuse, and the standalone c* entry point
+# ---------------------------------------------------------------------------
+
+def test_run_twice_bit_identical(sv, dev):
+    case = workloads.make_verify_case(16, 7, 151936, "bf16", seed=77,
+                                      noise_std=np.linspace(0.5, 2.5, 7),
+                                      verify_len=np.arange(16) % 8, temperature=1.0)
+    a = run_verify(sv, case, dev)
+    b = run_verify(sv, case, dev)
+    for k in a:
+        if a[k] is not None:
+            assert np.array_equal(a[k], b[k], equal_nan=True), k
+
+
+def test_workspace_reuse_across_shapes(sv, dev):
+    from lossless_verification_sampling_amd import Workspace
+    ws = Workspace(dev)
+    shapes = [(3, 2, 50000), (40, 7, 4096), (1, 8, 151936), (40, 7, 4096), (2, 1, 33)]
+    for i, (R, gamma, V) in enumerate(shapes):
+        case = workloads.make_verify_case(R, gamma, V, "bf16", seed=200 + i,
+                                          verify_len=np.arange(R) % (gamma + 1),
+                                          temperature=1.0)
+        _check(sv, dev, case, f"reuse_{i}", workspace=ws)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_tv_accept_rate(sv, dev, dtype):
+    N, V = 37, 30011
+    gen = np.random.default_rng(3)
+    zt = (gen.standard_normal((N, V)) * 3).astype(np.float32)
+    zd = (zt + gen.standard_normal((N, V)) * np.linspace(0.05, 3, N)[:, None]).astype(np.float32)
+    zd[0] = zt[0]
+    T = np.array([1.0, 0.0, 0.7, 2.0] * 10, np.float32)[:N]
+    if dtype == "bf16":
+        zt, zd = workloads.f32_to_bf16_bits(zt), workloads.f32_to_bf16_bits(zd)
+    cs, rs = sv.spec_tv_accept_rate(to_device(zd, dev), to_device(zt, dev), to_device(T, dev))
+    torch.cuda.synchronize()
+    ref_c, ref_r = oracle.tv_accept_rate(zd, zt, T)
+    tol = 1e-5 if dtype == "f32" else 2e-3
+    assert np.allclose(cs.cpu().numpy(), ref_c, rtol=tol, atol=1e-6)
+    assert np.allclose(rs.cpu().numpy(), ref_r, rtol=tol, atol=1e-6)
+    assert abs(cs[0].item() - 1.0) < 1e-6
