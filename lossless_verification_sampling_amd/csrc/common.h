@@ -163,25 +163,82 @@ __device__ __forceinline__ float load_one(const T *row, long e) {
 // workgroup running the same code on the same values gets the same bits)
 // ---------------------------------------------------------------------------
 
+// Wave-wide reductions with every one of the 64 lanes active.  Four DPP
+// steps inside each row of 16 lanes (swap neighbours, swap pairs, mirror the
+// half-row, mirror the row) leave every lane of a row holding that row's
+// result; the four row results are read into scalar registers and combined,
+// so the value returned is uniform across the wave.  DPP moves run in the
+// VALU pipeline: no LDS round trip per step, unlike ds_bpermute shuffles.
+constexpr int kDppSwap1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppSwap2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;  // lane i <- lane 7 - i within 8
+constexpr int kDppMirror = 0x140;      // lane i <- lane 15 - i within 16
+
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+    return __builtin_amdgcn_mov_dpp(v, CTRL, 0xf, 0xf, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __int_as_float(dpp_i<CTRL>(__float_as_int(v)));
+}
+template <int CTRL>
+__device__ __forceinline__ double dpp_d(double v) {
+    const long long b = __double_as_longlong(v);
+    const int lo = dpp_i<CTRL>((int)(b & 0xffffffffLL));
+    const int hi = dpp_i<CTRL>((int)(b >> 32));
+    return __longlong_as_double(((long long)hi << 32) | (unsigned)lo);
+}
+__device__ __forceinline__ float readlane_f(float v, int l) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+__device__ __forceinline__ double readlane_d(double v, int l) {
+    const long long b = __double_as_longlong(v);
+    const unsigned lo = (unsigned)__builtin_amdgcn_readlane((int)(b & 0xffffffffLL), l);
+    const int hi = __builtin_amdgcn_readlane((int)(b >> 32), l);
+    return __longlong_as_double(((long long)hi << 32) | lo);
+}
+
+// wave_max propagates NaN (IEEE maximum, one v_maximum3 per step); callers
+// pass lane maxima built with fmaxf, which are never NaN.
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-    return v;
+    v = __builtin_elementwise_maximum(v, dpp_f<kDppSwap1>(v));
+    v = __builtin_elementwise_maximum(v, dpp_f<kDppSwap2>(v));
+    v = __builtin_elementwise_maximum(v, dpp_f<kDppHalfMirror>(v));
+    v = __builtin_elementwise_maximum(v, dpp_f<kDppMirror>(v));
+    return __builtin_elementwise_maximum(
+        __builtin_elementwise_maximum(readlane_f(v, 0), readlane_f(v, 16)),
+        __builtin_elementwise_maximum(readlane_f(v, 32), readlane_f(v, 48)));
 }
 __device__ __forceinline__ double wave_sum(double v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-    return v;
+    v += dpp_d<kDppSwap1>(v);
+    v += dpp_d<kDppSwap2>(v);
+    v += dpp_d<kDppHalfMirror>(v);
+    v += dpp_d<kDppMirror>(v);
+    return (readlane_d(v, 0) + readlane_d(v, 16)) + (readlane_d(v, 32) + readlane_d(v, 48));
+}
+__device__ __forceinline__ float wave_sum_f(float v) {
+    v += dpp_f<kDppSwap1>(v);
+    v += dpp_f<kDppSwap2>(v);
+    v += dpp_f<kDppHalfMirror>(v);
+    v += dpp_f<kDppMirror>(v);
+    return (readlane_f(v, 0) + readlane_f(v, 16)) + (readlane_f(v, 32) + readlane_f(v, 48));
 }
 __device__ __forceinline__ int wave_max_i(int v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o, 64));
-    return v;
+    v = max(v, dpp_i<kDppSwap1>(v));
+    v = max(v, dpp_i<kDppSwap2>(v));
+    v = max(v, dpp_i<kDppHalfMirror>(v));
+    v = max(v, dpp_i<kDppMirror>(v));
+    return max(max(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
+               max(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
 }
 __device__ __forceinline__ int wave_min_i(int v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o, 64));
-    return v;
+    v = min(v, dpp_i<kDppSwap1>(v));
+    v = min(v, dpp_i<kDppSwap2>(v));
+    v = min(v, dpp_i<kDppHalfMirror>(v));
+    v = min(v, dpp_i<kDppMirror>(v));
+    return min(min(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
+               min(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
 }
 // (value, index): larger value wins, equal values -> smaller index.
 __device__ __forceinline__ void argmax_combine(float &v, int &i, float v2, int i2) {
@@ -190,13 +247,24 @@ __device__ __forceinline__ void argmax_combine(float &v, int &i, float v2, int i
         i = i2;
     }
 }
+template <int CTRL>
+__device__ __forceinline__ void argmax_step(float &v, int &i) {
+    const float v2 = dpp_f<CTRL>(v);
+    const int i2 = dpp_i<CTRL>(i);
+    argmax_combine(v, i, v2, i2);
+}
 __device__ __forceinline__ void wave_argmax(float &v, int &i) {
+    argmax_step<kDppSwap1>(v, i);
+    argmax_step<kDppSwap2>(v, i);
+    argmax_step<kDppHalfMirror>(v, i);
+    argmax_step<kDppMirror>(v, i);
+    float bv = readlane_f(v, 0);
+    int bi = __builtin_amdgcn_readlane(i, 0);
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        float v2 = __shfl_xor(v, o, 64);
-        int i2 = __shfl_xor(i, o, 64);
-        argmax_combine(v, i, v2, i2);
-    }
+    for (int l = 16; l < 64; l += 16)
+        argmax_combine(bv, bi, readlane_f(v, l), __builtin_amdgcn_readlane(i, l));
+    v = bv;
+    i = bi;
 }
 
 struct BlockScratch {

@@ -14,7 +14,7 @@
 //  * Speculative-decoding survey (zhifeiding.github.io), sec. 1.3: greedy
 //    verification is a position-wise argmax comparison.
 //
-// Design (three launches per call, each a hand-off through the workspace):
+// Design (four launches per call, each a hand-off through the workspace):
 //  * A "unit" is one position of one request: a (draft row, target row) pair
 //    for positions i < l_r, the bonus target row at i = l_r.  Each unit's rows
 //    are cut into C chunks of 64 N logits; one wave streams one chunk.
@@ -22,12 +22,14 @@
 //    exactly once from HBM, chunk by chunk with the next chunk's 16-byte loads
 //    in flight, and writes each chunk's max and exp-sum
 //    sum 2^((z - m) s), s = log2(e) / T (or its argmax at T = 0).
-//  * Kernel 2 (tv_kernel, same structure) re-reads only the pair rows --
-//    kernel 1 has just streamed them, so they come from the 256 MB Infinity
-//    Cache -- combines the row normalisers from kernel 1's chunk statistics
-//    and reduces sum min(p, q) and sum [q - p]_+ per chunk.
-//  * Kernel 3 (finalize_kernel, one workgroup per request): c*, Res and the
-//    row normalisers (one row per wave), the accept tests on the gathered
+//  * norm_kernel (one wave per unit) combines kernel 1's chunk statistics
+//    into each row's normaliser (max M, Z = sum 2^((z - M) s)), or its argmax
+//    at T = 0.
+//  * Kernel 2 (tv_kernel, same structure as kernel 1) re-reads only the pair
+//    rows -- kernel 1 has just streamed them, so they come from the 256 MB
+//    Infinity Cache -- and reduces sum min(p, q) and sum [q - p]_+ per chunk.
+//  * Kernel 3 (finalize_kernel, one workgroup per request): c* and Res (one
+//    row per wave), the accept tests on the gathered
 //    logits q(x), p(x) in fp64 (one position per lane, prefix survival by
 //    ballot), and the residual or bonus draw as a two-level inverse CDF
 //    (chunk masses, then one re-read chunk scanned in ascending token id).
@@ -41,6 +43,10 @@
 
 
 #include "common.h"
+
+#ifndef SV_RING
+#define SV_RING 2
+#endif
 
 namespace sv {
 
@@ -65,6 +71,15 @@ struct VerifyArgs {
     Control *ctl;
     float4 *st1;             // [units][C] chunk statistics (kernel 1)
     float2 *st2;             // [units][C] sum min / sum res of pair chunks (kernel 2)
+    struct RowNorm *nrm;     // [units] row normalisers (norm_kernel)
+};
+
+// Normalisers of one unit's rows: at T > 0 the maxima and Z = sum 2^((z - M) s)
+// of the target (t) and draft (d) rows; at T = 0 their argmax (-1: invalid).
+struct RowNorm {
+    float Mt, Md;
+    int gt, gd;
+    double Zt, Zd;
 };
 
 constexpr float kInf = __builtin_inff();
@@ -79,21 +94,34 @@ __device__ __forceinline__ bool uniform_ok(float u) { return u >= 0.0f && u < 1.
 // request derives the same value.
 __device__ __forceinline__ float exp2_scale(float T) { return (float)(kLog2e / (double)T); }
 
-// Weight of a chunk whose max is cm and exp-sum cs, relative to the row max M:
-// cs * 2^((cm - M) s), the power in fp32 (relative error ~1e-7, like the
-// fp32 exp-sums themselves), accumulated by callers in fp64.  Shared by every
-// workgroup that combines a row, so all of them obtain identical normalisers.
-__device__ __forceinline__ double chunk_weight(float cm, float cs, float M, float s) {
-    return (cm > -kInf) ? (double)cs * (double)__builtin_amdgcn_exp2f((cm - M) * s) : 0.0;
+// Softmax arithmetic in scaled units.  With s = log2(e) / T a logit z has
+// weight 2^(z s - mu) for any reference mu; the reference cancels in the
+// normalisation, so every stage may pick its own as long as it scales
+// consistently.  A chunk's reference is mu_c = fl(m_c s), its max logit times
+// s rounded once, and an element's exponent is fma(z, s, -mu_c): a single
+// rounding, tiny for the logits near the max that carry the mass.  Rounding
+// is monotone, so the row's reference max_c mu_c is fl(M s).
+
+// Exponent reference of a chunk with scaled max mu: mu itself, or 0 when the
+// chunk holds no finite logit (then -inf gives weight 0, a NaN stays NaN).
+__device__ __forceinline__ float exp_ref(float mu) { return (mu > -kInf) ? mu : 0.0f; }
+
+// 2^(z s - ref) with the exponent from one fused multiply-add.
+__device__ __forceinline__ float exp_w(float z, float s, float ref) {
+    return __builtin_amdgcn_exp2f(__builtin_fmaf(z, s, -ref));
 }
 
-// Probability scale of a chunk: p_v = e_v * scale with e_v = 2^((z_v - cm) s).
-__device__ __forceinline__ float chunk_scale(float cm, float M, float s, double Z) {
-    return (cm > -kInf) ? (float)((double)__builtin_amdgcn_exp2f((cm - M) * s) / Z) : 0.0f;
+// Weight of a chunk with scaled max mu and exp-sum S relative to the row's
+// scaled max muM: S * 2^(mu - muM), the power in fp32 (relative error ~1e-7,
+// like the fp32 exp-sums), accumulated by callers in fp64.  Shared by every
+// stage that combines a row, so all obtain identical normalisers.
+__device__ __forceinline__ double chunk_weight(float mu, float S, float muM) {
+    return (mu > -kInf) ? (double)S * (double)__builtin_amdgcn_exp2f(mu - muM) : 0.0;
 }
 
-__device__ __forceinline__ float exp_rel(float z, float m, float s) {
-    return __builtin_amdgcn_exp2f((z - m) * s);
+// Probability scale of a chunk: p_v = 2^(z_v s - mu) * scale.
+__device__ __forceinline__ float chunk_scale(float mu, float muM, double Z) {
+    return (mu > -kInf) ? (float)((double)__builtin_amdgcn_exp2f(mu - muM) / Z) : 0.0f;
 }
 
 // [q - p]_+ computed as q - min(p, q) with rounded products (no contraction),
@@ -133,7 +161,7 @@ constexpr int kLanes = 64;
 
 struct Item {
     int u, r, i, c, l;
-    float T;
+    float T, s;   // temperature and log2(e) / T
     bool pair;    // the draft row is present (i < l)
 };
 
@@ -152,7 +180,7 @@ struct ItemCursor {
     long base = -64;
     uint64_t mask = 0;
     int lr = 0, li = 0, lc = 0, ll = 0;
-    float lT = 0.0f;
+    float lT = 0.0f, ls = 0.0f;
 
     // pairs_only: yield only pair items at T > 0 (the ones kernel 2 reduces)
     __device__ bool next(const VerifyArgs &a, long work, Item &x, bool pairs_only = false) {
@@ -166,6 +194,7 @@ struct ItemCursor {
                 x.c = __builtin_amdgcn_readlane(lc, k);
                 x.l = __builtin_amdgcn_readlane(ll, k);
                 x.T = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lT), k));
+                x.s = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ls), k));
                 x.u = x.r * a.UG + x.i;
                 x.pair = x.i < x.l;
                 return true;
@@ -183,6 +212,7 @@ struct ItemCursor {
                 ll = a.tv_mode ? 1 : a.vlen[lr];
                 act = temperature_ok(lT) && ll >= 0 && ll <= a.gamma && li <= ll;
                 if (pairs_only) act = act && li < ll && lT != 0.0f;
+                ls = act && lT != 0.0f ? exp2_scale(lT) : 0.0f;
             }
             mask = __ballot(act);
         }
@@ -200,37 +230,48 @@ struct RawChunk {
 
     // Slot j * EPV + q of lane l holds logit c0 + (j * 64 + l) * EPV + q, so
     // each load instruction of the wave reads consecutive 16-byte pieces.
+    // A chunk inside the row (all but the last) loads without bounds checks;
+    // past the row end a vector holds -inf (V % EPV == 0 when EPV > 1).
     __device__ __forceinline__ void load(const T *row, long c0, int V) {
         const int lane = threadIdx.x & 63;
+        if (c0 + (long)kLanes * N <= V) {
 #pragma unroll
-        for (int j = 0; j < N / EPV; ++j) {
-            const long e = c0 + ((long)j * kLanes + lane) * EPV;
-            const bool in = e < V;  // whole vector in or out: V % EPV == 0 here
-            if constexpr (EPV == 1) {
-                w[j] = __float_as_uint(in ? load_one(row, e) : -kInf);
-            } else if constexpr (kPacked) {
-                constexpr int NW = EPV / 2;
-                if constexpr (NW == 4) {
-                    uint4 v = in ? *reinterpret_cast<const uint4 *>(row + e)
-                                 : make_uint4(0xff80ff80u, 0xff80ff80u, 0xff80ff80u, 0xff80ff80u);
-                    w[j * 4 + 0] = v.x; w[j * 4 + 1] = v.y; w[j * 4 + 2] = v.z; w[j * 4 + 3] = v.w;
-                } else if constexpr (NW == 2) {
-                    uint2 v = in ? *reinterpret_cast<const uint2 *>(row + e)
-                                 : make_uint2(0xff80ff80u, 0xff80ff80u);
-                    w[j * 2 + 0] = v.x; w[j * 2 + 1] = v.y;
-                } else {
-                    w[j] = in ? *reinterpret_cast<const uint32_t *>(row + e) : 0xff80ff80u;
-                }
+            for (int j = 0; j < N / EPV; ++j)
+                load_vec(row, c0 + ((long)j * kLanes + lane) * EPV, j, true);
+        } else {
+#pragma unroll
+            for (int j = 0; j < N / EPV; ++j) {
+                const long e = c0 + ((long)j * kLanes + lane) * EPV;
+                load_vec(row, e, j, e < V);
+            }
+        }
+    }
+
+    __device__ __forceinline__ void load_vec(const T *row, long e, int j, bool in) {
+        if constexpr (EPV == 1) {
+            w[j] = __float_as_uint(in ? load_one(row, e) : -kInf);
+        } else if constexpr (kPacked) {
+            constexpr int NW = EPV / 2;
+            if constexpr (NW == 4) {
+                uint4 v = in ? *reinterpret_cast<const uint4 *>(row + e)
+                             : make_uint4(0xff80ff80u, 0xff80ff80u, 0xff80ff80u, 0xff80ff80u);
+                w[j * 4 + 0] = v.x; w[j * 4 + 1] = v.y; w[j * 4 + 2] = v.z; w[j * 4 + 3] = v.w;
+            } else if constexpr (NW == 2) {
+                uint2 v = in ? *reinterpret_cast<const uint2 *>(row + e)
+                             : make_uint2(0xff80ff80u, 0xff80ff80u);
+                w[j * 2 + 0] = v.x; w[j * 2 + 1] = v.y;
             } else {
-                if constexpr (EPV == 4) {
-                    uint4 v = in ? *reinterpret_cast<const uint4 *>(row + e)
-                                 : make_uint4(0xff800000u, 0xff800000u, 0xff800000u, 0xff800000u);
-                    w[j * 4 + 0] = v.x; w[j * 4 + 1] = v.y; w[j * 4 + 2] = v.z; w[j * 4 + 3] = v.w;
-                } else {
-                    uint2 v = in ? *reinterpret_cast<const uint2 *>(row + e)
-                                 : make_uint2(0xff800000u, 0xff800000u);
-                    w[j * 2 + 0] = v.x; w[j * 2 + 1] = v.y;
-                }
+                w[j] = in ? *reinterpret_cast<const uint32_t *>(row + e) : 0xff80ff80u;
+            }
+        } else {
+            if constexpr (EPV == 4) {
+                uint4 v = in ? *reinterpret_cast<const uint4 *>(row + e)
+                             : make_uint4(0xff800000u, 0xff800000u, 0xff800000u, 0xff800000u);
+                w[j * 4 + 0] = v.x; w[j * 4 + 1] = v.y; w[j * 4 + 2] = v.z; w[j * 4 + 3] = v.w;
+            } else {
+                uint2 v = in ? *reinterpret_cast<const uint2 *>(row + e)
+                             : make_uint2(0xff800000u, 0xff800000u);
+                w[j * 2 + 0] = v.x; w[j * 2 + 1] = v.y;
             }
         }
     }
@@ -256,16 +297,15 @@ __device__ __forceinline__ void load_item(const VerifyArgs &a, const Item &x,
 // kernel 1: per-chunk statistics (every needed row, read once from HBM)
 // ---------------------------------------------------------------------------
 
-// Chunk c of unit u (one wave): max m and exp-sum S = sum 2^((z - m) s) of the
-// target row (and of the draft row for pairs) -> st1[u * C + c] =
-// (m_t, S_t, m_d, S_d); at T = 0 the argmax (value, index; index 0xffffffff
-// if a NaN was seen).
-template <typename TT, typename TD, int N, int EPV>
-__device__ __forceinline__ void chunk_stats(const VerifyArgs &a, const Item &x,
-                                            const RawChunk<TT, N, EPV> &rt,
-                                            const RawChunk<TD, N, EPV> &rd) {
+// Chunk c of unit u (one wave): scaled max mu = fl(m s) and exp-sum
+// S = sum 2^(z s - mu) of the target row (and of the draft row for pairs)
+// -> st1[u * C + c] = (mu_t, S_t, mu_d, S_d); at T = 0 the argmax (value,
+// index; index 0xffffffff if a NaN was seen).
+template <bool PAIR, typename TT, typename TD, int N, int EPV>
+__device__ __forceinline__ void chunk_stats_t(const VerifyArgs &a, const Item &x,
+                                              const RawChunk<TT, N, EPV> &rt,
+                                              const RawChunk<TD, N, EPV> &rd) {
     const int lane = threadIdx.x & 63;
-    const bool pair = x.pair;
     float4 *out = a.st1 + (size_t)x.u * a.C + x.c;
     if (x.T == 0.0f) {
         const long c0 = chunk_start<N>(x.c);
@@ -277,71 +317,95 @@ __device__ __forceinline__ void chunk_stats(const VerifyArgs &a, const Item &x,
             const float zt = rt.get(k);
             if (zt != zt) bad |= 1;
             if (zt > bt) { bt = zt; it = e; }
-            if (pair) {
+            if constexpr (PAIR) {
                 const float zd = rd.get(k);
                 if (zd != zd) bad |= 2;
                 if (zd > bd) { bd = zd; id = e; }
             }
         }
         wave_argmax(bt, it);
-        wave_argmax(bd, id);
+        if constexpr (PAIR) wave_argmax(bd, id);
         bad = wave_max_i(bad);
         if (lane == 0)
             *out = make_float4(bt, __uint_as_float((bad & 1) ? 0xffffffffu : (uint32_t)it), bd,
                                __uint_as_float((bad & 2) ? 0xffffffffu : (uint32_t)id));
         return;
     }
-    const float s = exp2_scale(x.T);
+    const float s = x.s;
     float mt = -kInf, md = -kInf;
 #pragma unroll
     for (int k = 0; k < N; ++k) {
         mt = fmaxf(mt, rt.get(k));
-        if (pair) md = fmaxf(md, rd.get(k));
+        if constexpr (PAIR) md = fmaxf(md, rd.get(k));
     }
-    mt = wave_max(mt);
-    md = wave_max(md);
+    const float mut = wave_max(mt) * s;
+    const float mud = PAIR ? wave_max(md) * s : -kInf;
+    const float rt0 = exp_ref(mut), rd0 = exp_ref(mud);
     float et = 0.0f, ed = 0.0f;
 #pragma unroll
     for (int k = 0; k < N; ++k) {
-        const float zt = rt.get(k);
-        // a chunk of -inf (or NaN) has no mass; a NaN must stay visible
-        et += (mt > -kInf) ? exp_rel(zt, mt, s) : ((zt != zt) ? zt : 0.0f);
-        if (pair) {
-            const float zd = rd.get(k);
-            ed += (md > -kInf) ? exp_rel(zd, md, s) : ((zd != zd) ? zd : 0.0f);
-        }
+        et += exp_w(rt.get(k), s, rt0);
+        if constexpr (PAIR) ed += exp_w(rd.get(k), s, rd0);
     }
-    const double st = wave_sum((double)et);
-    const double sd = wave_sum((double)ed);
-    if (lane == 0) *out = make_float4(mt, (float)st, md, (float)sd);
+    const float st = wave_sum_f(et);
+    const float sd = PAIR ? wave_sum_f(ed) : 0.0f;
+    if (lane == 0) *out = make_float4(mut, st, mud, sd);
 }
 
-// Kernel 1, a persistent grid of independent waves: each wave walks its active
-// chunk items in order with the next item's loads in flight while it reduces
-// the current one (two register buffers, the loop unrolled by two).
 template <typename TT, typename TD, int N, int EPV>
-__global__ void __launch_bounds__(kBlock) stats_kernel(VerifyArgs a) {
+__device__ __forceinline__ void chunk_stats(const VerifyArgs &a, const Item &x,
+                                            const RawChunk<TT, N, EPV> &rt,
+                                            const RawChunk<TD, N, EPV> &rd) {
+    if (x.pair) chunk_stats_t<true>(a, x, rt, rd);
+    else chunk_stats_t<false>(a, x, rt, rd);
+}
+
+// Persistent loop of one wave over its items with a ring of kRing register
+// buffers: while the wave reduces item k, the loads of items k+1 .. k+kRing-1
+// are in flight.  Op::apply(a, item, target chunk, draft chunk) is the
+// per-item work.
+constexpr int kRing = SV_RING;
+
+template <typename Op, typename TT, typename TD, int N, int EPV>
+__device__ __forceinline__ void run_items(const VerifyArgs &a, bool pairs_only) {
     const long work = (long)a.R * a.UG * a.C;
     ItemCursor cur;
-    Item x0, x1;
-    if (!cur.next(a, work, x0)) return;
-    RawChunk<TT, N, EPV> t0, t1;
-    RawChunk<TD, N, EPV> d0, d1;
-    load_item(a, x0, t0, d0);
-    for (;;) {
-        const bool has1 = cur.next(a, work, x1);
-        if (!has1) x1 = x0;
-        __asm__ volatile("" ::: "memory");
-        load_item(a, x1, t1, d1);  // prefetch (the last one re-reads)
-        chunk_stats<TT, TD, N, EPV>(a, x0, t0, d0);
-        if (!has1) break;
-        const bool has0 = cur.next(a, work, x0);
-        if (!has0) x0 = x1;
-        __asm__ volatile("" ::: "memory");
-        load_item(a, x0, t0, d0);
-        chunk_stats<TT, TD, N, EPV>(a, x1, t1, d1);
-        if (!has0) break;
+    Item x[kRing];
+    bool has[kRing];
+    RawChunk<TT, N, EPV> t[kRing];
+    RawChunk<TD, N, EPV> d[kRing];
+#pragma unroll
+    for (int k = 0; k < kRing - 1; ++k) {
+        has[k] = cur.next(a, work, x[k], pairs_only);
+        if (has[k]) load_item(a, x[k], t[k], d[k]);
     }
+    has[kRing - 1] = false;
+    for (;;) {
+#pragma unroll
+        for (int k = 0; k < kRing; ++k) {
+            const int pf = (k + kRing - 1) % kRing;
+            has[pf] = has[(pf + kRing - 1) % kRing] && cur.next(a, work, x[pf], pairs_only);
+            __asm__ volatile("" ::: "memory");
+            if (has[pf]) load_item(a, x[pf], t[pf], d[pf]);
+            if (!has[k]) return;
+            Op::apply(a, x[k], t[k], d[k]);
+        }
+    }
+}
+
+struct StatsOp {
+    template <typename TT, typename TD, int N, int EPV>
+    __device__ __forceinline__ static void apply(const VerifyArgs &a, const Item &x,
+                                                 const RawChunk<TT, N, EPV> &rt,
+                                                 const RawChunk<TD, N, EPV> &rd) {
+        chunk_stats<TT, TD, N, EPV>(a, x, rt, rd);
+    }
+};
+
+// Kernel 1, a persistent grid of independent waves.
+template <typename TT, typename TD, int N, int EPV>
+__global__ void __launch_bounds__(kBlock) stats_kernel(VerifyArgs a) {
+    run_items<StatsOp, TT, TD, N, EPV>(a, false);
 }
 
 // ---------------------------------------------------------------------------
@@ -361,9 +425,9 @@ struct FinalState {
 };
 
 // Row normalisers of unit u from kernel 1's chunk statistics, by one wave
-// (lanes over chunks).
-__device__ void wave_row_stats(const VerifyArgs &a, int u, bool pair, float s, float &Mt,
-                               double &Zt, float &Md, double &Zd) {
+// (lanes over chunks): the scaled maxima muM and Z = sum_c S_c 2^(mu_c - muM).
+__device__ void wave_row_stats(const VerifyArgs &a, int u, bool pair, float &Mt, double &Zt,
+                               float &Md, double &Zd) {
     const int lane = threadIdx.x & 63;
     const float4 *st = a.st1 + (size_t)u * a.C;
     float mt = -kInf, md = -kInf;
@@ -377,8 +441,8 @@ __device__ void wave_row_stats(const VerifyArgs &a, int u, bool pair, float s, f
     double zt = 0.0, zd = 0.0;
     for (int c = lane; c < a.C; c += 64) {
         const float4 v = st[c];
-        zt += chunk_weight(v.x, v.y, Mt, s);
-        if (pair) zd += chunk_weight(v.z, v.w, Md, s);
+        zt += chunk_weight(v.x, v.y, Mt);
+        if (pair) zd += chunk_weight(v.z, v.w, Md);
     }
     Zt = wave_sum(zt);
     Zd = wave_sum(zd);
@@ -408,7 +472,8 @@ __device__ void wave_row_argmax(const VerifyArgs &a, int u, bool pair, int &gt, 
     gd = pair ? ((!bad && vd < kInf && id != 0x7fffffff) ? id : -1) : 0;
 }
 
-// Inverse-CDF draw inside chunk c of row j of request r by the workgroup: the
+// Inverse-CDF draw inside chunk c of row j of request r by the workgroup (cmt,
+// cmd: the chunk's exponent references, at, ad: its probability scales): the
 // first logit (ascending id) whose running weight exceeds tsel, with weights
 // q - min(p, q) (resid) or q, computed exactly as kernel 2 computed them.
 // Thread t owns logits [c0 + t P, c0 + (t+1) P), P = 64 N / 256; a block scan
@@ -437,9 +502,9 @@ __device__ int draw_in_chunk(const VerifyArgs &a, int r, int j, int c, bool resi
         }
 #pragma unroll
         for (int q = 0; q < VW; ++q) {
-            const float et = (cmt > -kInf) ? exp_rel(zt[q], cmt, s) : 0.0f;
+            const float et = exp_w(zt[q], s, cmt);
             if (resid) {
-                const float ed = (cmd > -kInf) ? exp_rel(zd[q], cmd, s) : 0.0f;
+                const float ed = exp_w(zd[q], s, cmd);
                 float qv, mn;
                 pq_weights(et, ed, at, ad, qv, mn);
                 w[q] = qv - mn;
@@ -517,8 +582,8 @@ __device__ void finalize(const VerifyArgs &a, const Item &x, BlockScratch &bs, F
 
     if (T == 0.0f) {
         for (int i = wave; i < nrows; i += kWaves) {
-            int gt, gd;
-            wave_row_argmax(a, u0 + i, i < l, gt, gd);
+            const RowNorm nm = a.nrm[u0 + i];
+            const int gt = nm.gt, gd = nm.gd;
             if (lane == 0) {
                 f.gt[i] = gt;
                 if (i < l) f.gd[i] = gd;
@@ -565,9 +630,9 @@ __device__ void finalize(const VerifyArgs &a, const Item &x, BlockScratch &bs, F
     const float s = exp2_scale(T);
     for (int i = wave; i < nrows; i += kWaves) {
         const bool pair = i < l;
-        float Mt, Md;
-        double Zt, Zd;
-        wave_row_stats(a, u0 + i, pair, s, Mt, Zt, Md, Zd);
+        const RowNorm nm = a.nrm[u0 + i];
+        const float Mt = nm.Mt, Md = nm.Md;
+        const double Zt = nm.Zt, Zd = nm.Zd;
         double dm = 0.0, dr = 0.0;
         if (pair) {
             for (int c = lane; c < C; c += 64) {
@@ -614,8 +679,8 @@ __device__ void finalize(const VerifyArgs &a, const Item &x, BlockScratch &bs, F
             if (!bad) {
                 const TT *trow = (const TT *)a.zt + ((long)r * a.tG + lane) * V;
                 const TD *drow = (const TD *)a.zd + ((long)r * a.dG + lane) * V;
-                const double lq = ((double)load_one(trow, xv) - (double)f.Mt[lane]) * (double)s;
-                const double lp = ((double)load_one(drow, xv) - (double)f.Md[lane]) * (double)s;
+                const double lq = (double)load_one(trow, xv) * (double)s - (double)f.Mt[lane];
+                const double lp = (double)load_one(drow, xv) * (double)s - (double)f.Md[lane];
                 const double q = exp2(lq) / f.Zt[lane];
                 const double p = exp2(lp) / f.Zd[lane];
                 acc = q >= p || (double)u < q / p;
@@ -652,7 +717,7 @@ __device__ void finalize(const VerifyArgs &a, const Item &x, BlockScratch &bs, F
             W = 0.0;
             for (int c = lane; c < C; c += 64) {
                 const float4 v = a.st1[(size_t)uj * C + c];
-                W += chunk_weight(v.x, v.y, Mt, s) / Zt;
+                W += chunk_weight(v.x, v.y, Mt) / Zt;
             }
             W = wave_sum(W);
         }
@@ -667,7 +732,7 @@ __device__ void finalize(const VerifyArgs &a, const Item &x, BlockScratch &bs, F
                     wc = (double)a.st2[(size_t)uj * C + c].y;
                 } else {
                     const float4 v = a.st1[(size_t)uj * C + c];
-                    wc = chunk_weight(v.x, v.y, Mt, s) / Zt;
+                    wc = chunk_weight(v.x, v.y, Mt) / Zt;
                 }
             }
             double incl = wc;
@@ -700,15 +765,15 @@ __device__ void finalize(const VerifyArgs &a, const Item &x, BlockScratch &bs, F
     const int csel = f.csel;
     const bool resid = f.resid;
     const float4 cst = a.st1[(size_t)uj * C + csel];
-    const float cmt = cst.x;
-    const float cmd = resid ? cst.z : -kInf;
-    const float at = chunk_scale(cmt, Mt, s, Zt);
-    const float ad = resid ? chunk_scale(cmd, f.Md[j], s, f.Zd[j]) : 0.0f;
+    const float cmt = exp_ref(cst.x);
+    const float cmd = resid ? exp_ref(cst.z) : 0.0f;
+    const float at = chunk_scale(cst.x, Mt, Zt);
+    const float ad = resid ? chunk_scale(cst.z, f.Md[j], f.Zd[j]) : 0.0f;
     float ztok;
     const int token = draw_in_chunk<TT, TD, N, EPV>(a, r, j, csel, resid, s, cmt, cmd, at, ad,
                                                     f.tsel, &ztok, bs, f);
     if (wave == 0) {
-        const float lqj = (float)((((double)ztok - (double)Mt) * (double)s) * kLn2 - log(Zt));
+        const float lqj = (float)(((double)ztok * (double)s - (double)Mt) * kLn2 - log(Zt));
         int32_t *tok = a.out_tok + (size_t)r * (G + 1);
         for (int k = lane; k <= G; k += 64) {
             tok[k] = (k < A) ? a.tokens[(size_t)r * G + k] : (k == A ? token : -1);
@@ -723,77 +788,73 @@ __device__ void finalize(const VerifyArgs &a, const Item &x, BlockScratch &bs, F
     }
 }
 
-// Kernel 2 work for one pair item at T > 0 (one wave): the row normalisers
-// from kernel 1's chunk statistics of the unit, then sum min(p, q) and
-// sum [q - p]_+ over the chunk -> st2[u * C + c].
+// Kernel 2 work for one pair item at T > 0 (one wave): sum min(p, q) and
+// sum [q - p]_+ over the chunk, with the row normalisers of norm_kernel
+// -> st2[u * C + c].
 template <typename TT, typename TD, int N, int EPV>
 __device__ __forceinline__ void chunk_tv(const VerifyArgs &a, const Item &x,
                                          const RawChunk<TT, N, EPV> &rt,
                                          const RawChunk<TD, N, EPV> &rd) {
     const int lane = threadIdx.x & 63;
-    const float s = exp2_scale(x.T);
-    const float4 *st = a.st1 + (size_t)x.u * a.C;
-    float Mt = -kInf, Md = -kInf;
-    for (int c = lane; c < a.C; c += kLanes) {
-        const float4 v = st[c];
-        Mt = fmaxf(Mt, v.x);
-        Md = fmaxf(Md, v.z);
-    }
-    Mt = wave_max(Mt);
-    Md = wave_max(Md);
-    double Zt = 0.0, Zd = 0.0;
-    for (int c = lane; c < a.C; c += kLanes) {
-        const float4 v = st[c];
-        Zt += chunk_weight(v.x, v.y, Mt, s);
-        Zd += chunk_weight(v.z, v.w, Md, s);
-    }
-    Zt = wave_sum(Zt);
-    Zd = wave_sum(Zd);
-    const float4 own = st[x.c];
-    const float at = chunk_scale(own.x, Mt, s, Zt);
-    const float ad = chunk_scale(own.z, Md, s, Zd);
+    const float s = x.s;
+    const RowNorm nm = a.nrm[x.u];
+    const float4 own = a.st1[(size_t)x.u * a.C + x.c];
+    const float at = chunk_scale(own.x, nm.Mt, nm.Zt);
+    const float ad = chunk_scale(own.z, nm.Md, nm.Zd);
+    const float rt0 = exp_ref(own.x), rd0 = exp_ref(own.z);
     float smin = 0.0f, sres = 0.0f;
 #pragma unroll
     for (int k = 0; k < N; ++k) {
-        const float et = (own.x > -kInf) ? exp_rel(rt.get(k), own.x, s) : 0.0f;
-        const float ed = (own.z > -kInf) ? exp_rel(rd.get(k), own.z, s) : 0.0f;
+        const float et = exp_w(rt.get(k), s, rt0);
+        const float ed = exp_w(rd.get(k), s, rd0);
         float q, mn;
         pq_weights(et, ed, at, ad, q, mn);
         smin += mn;
         sres += q - mn;
     }
-    const double dm = wave_sum((double)smin);
-    const double dr = wave_sum((double)sres);
-    if (lane == 0) a.st2[(size_t)x.u * a.C + x.c] = make_float2((float)dm, (float)dr);
+    const float dm = wave_sum_f(smin);
+    const float dr = wave_sum_f(sres);
+    if (lane == 0) a.st2[(size_t)x.u * a.C + x.c] = make_float2(dm, dr);
 }
 
+struct TvOp {
+    template <typename TT, typename TD, int N, int EPV>
+    __device__ __forceinline__ static void apply(const VerifyArgs &a, const Item &x,
+                                                 const RawChunk<TT, N, EPV> &rt,
+                                                 const RawChunk<TD, N, EPV> &rd) {
+        chunk_tv<TT, TD, N, EPV>(a, x, rt, rd);
+    }
+};
+
 // Kernel 2, a persistent grid of independent waves over the pair items at
-// T > 0 with the same two-buffer prefetch as kernel 1.  The rows it re-reads
-// were streamed by kernel 1 moments before, so they come from the 256 MB
-// Infinity Cache; the chunk statistics it combines are a few hundred KB.
+// T > 0 with the same load ring as kernel 1.  The rows it re-reads were
+// streamed by kernel 1 moments before, so they come from the 256 MB Infinity
+// Cache.
 template <typename TT, typename TD, int N, int EPV>
 __global__ void __launch_bounds__(kBlock) tv_kernel(VerifyArgs a) {
-    const long work = (long)a.R * a.UG * a.C;
-    ItemCursor cur;
-    Item x0, x1;
-    if (!cur.next(a, work, x0, true)) return;
-    RawChunk<TT, N, EPV> t0, t1;
-    RawChunk<TD, N, EPV> d0, d1;
-    load_item(a, x0, t0, d0);
-    for (;;) {
-        const bool has1 = cur.next(a, work, x1, true);
-        if (!has1) x1 = x0;
-        __asm__ volatile("" ::: "memory");
-        load_item(a, x1, t1, d1);  // prefetch (the last one re-reads)
-        chunk_tv<TT, TD, N, EPV>(a, x0, t0, d0);
-        if (!has1) break;
-        const bool has0 = cur.next(a, work, x0, true);
-        if (!has0) x0 = x1;
-        __asm__ volatile("" ::: "memory");
-        load_item(a, x0, t0, d0);
-        chunk_tv<TT, TD, N, EPV>(a, x1, t1, d1);
-        if (!has0) break;
+    run_items<TvOp, TT, TD, N, EPV>(a, true);
+}
+
+// Row normalisers (T > 0) or argmaxes (T = 0) of every active unit, one wave
+// per unit, from kernel 1's chunk statistics.
+__global__ void __launch_bounds__(kBlock) norm_kernel(VerifyArgs a) {
+    const long u = wave_index();
+    if (u >= (long)a.R * a.UG) return;
+    const int r = (int)(u / a.UG), i = (int)(u % a.UG);
+    const float T = a.temp[r];
+    const int l = a.tv_mode ? 1 : a.vlen[r];
+    if (!(temperature_ok(T) && l >= 0 && l <= a.gamma && i <= l)) return;
+    const bool pair = i < l;
+    RowNorm nm;
+    if (T == 0.0f) {
+        wave_row_argmax(a, (int)u, pair, nm.gt, nm.gd);
+        nm.Mt = nm.Md = 0.0f;
+        nm.Zt = nm.Zd = 0.0;
+    } else {
+        wave_row_stats(a, (int)u, pair, nm.Mt, nm.Zt, nm.Md, nm.Zd);
+        nm.gt = nm.gd = 0;
     }
+    if ((threadIdx.x & 63) == 0) a.nrm[u] = nm;
 }
 
 // Kernel 3: one workgroup per request writes its final outputs (or the
@@ -827,13 +888,13 @@ __global__ void clear_status_kernel(Control *ctl) { atomic_store_u32(&ctl->statu
 
 namespace {
 
-constexpr long kTargetItems = 16384;   // chunk items wanted to keep 8192 waves busy
+constexpr long kTargetItems = 65536;   // chunk items wanted: several per resident wave
 
 struct Plan {
     int N;           // logits per thread per row
     int C;           // chunks per row
     long units;
-    size_t off_st1, off_st2, bytes;
+    size_t off_st1, off_st2, off_nrm, bytes;
 };
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -869,7 +930,8 @@ bool make_plan(long R, long units_per_req, long V, Plan &p) {
     p.units = units;
     p.off_st1 = sizeof(Control);
     p.off_st2 = round_up(p.off_st1 + sizeof(float4) * (size_t)units * chosen_C, 256);
-    p.bytes = round_up(p.off_st2 + sizeof(float2) * (size_t)units * chosen_C, 256);
+    p.off_nrm = round_up(p.off_st2 + sizeof(float2) * (size_t)units * chosen_C, 256);
+    p.bytes = round_up(p.off_nrm + sizeof(RowNorm) * (size_t)units, 256);
     return true;
 }
 
@@ -905,7 +967,8 @@ template <typename TT, typename TD, int N, int EPV>
 int launch_kernels(const VerifyArgs &a, long items, hipStream_t st) {
     const void *k1 = reinterpret_cast<const void *>(&stats_kernel<TT, TD, N, EPV>);
     const void *k2 = reinterpret_cast<const void *>(&tv_kernel<TT, TD, N, EPV>);
-    long g1 = grid_for(k1, items), g2 = grid_for(k2, items);
+    const long wgs = (items + kWaves - 1) / kWaves;  // one item per wave at a time
+    long g1 = grid_for(k1, wgs), g2 = grid_for(k2, wgs);
     if (g1 < 1) g1 = 1;
     if (g2 < 1) g2 = 1;
     static bool said = false;
@@ -915,6 +978,9 @@ int launch_kernels(const VerifyArgs &a, long items, hipStream_t st) {
                 EPV, a.C, items, g1, g2);
     }
     hipLaunchKernelGGL((stats_kernel<TT, TD, N, EPV>), dim3((unsigned)g1), dim3(kBlock), 0, st, a);
+    const long units = (long)a.R * a.UG;
+    hipLaunchKernelGGL(norm_kernel, dim3((unsigned)((units + kWaves - 1) / kWaves)), dim3(kBlock),
+                       0, st, a);
     hipLaunchKernelGGL((tv_kernel<TT, TD, N, EPV>), dim3((unsigned)g2), dim3(kBlock), 0, st, a);
     hipLaunchKernelGGL((finalize_kernel<TT, TD, N, EPV>), dim3((unsigned)a.R), dim3(kBlock), 0, st,
                        a);
@@ -955,6 +1021,7 @@ void bind_workspace(VerifyArgs &a, void *ws, const Plan &p) {
     a.ctl = (Control *)b;
     a.st1 = (float4 *)(b + p.off_st1);
     a.st2 = (float2 *)(b + p.off_st2);
+    a.nrm = (RowNorm *)(b + p.off_nrm);
     a.C = p.C;
 }
 
