@@ -73,8 +73,11 @@ typedef enum {
 #define SPEC_DEV_SPIN_TIMEOUT 0x2u  /* a cross-workgroup wait gave up; the outputs
                                        of that call are undefined                  */
 
-/* Largest vocabulary the kernels accept. */
+/* Largest vocabulary the Markov-draft kernels accept. */
 #define SPEC_MAX_VOCAB 2097152
+/* Largest vocabulary spec_verify_batch and spec_tv_accept_rate accept (a row
+ * is cut into at most 256 chunks of 1024 logits). */
+#define SPEC_MAX_VERIFY_VOCAB 262144
 
 /* Library version, major * 10000 + minor * 100 + patch. */
 int spec_version(void);
@@ -123,7 +126,8 @@ int spec_workspace_init(void *workspace, size_t workspace_bytes, void *stream);
  *                                 1 - c*_i), NaN beyond l_r
  *   out_logq         [R][gamma+1] fp32, nullable: natural log of q_j at the
  *                                 committed token j <= A_r (0 at T = 0), NaN beyond
- * Sizes: R >= 0, gamma >= 0, 1 <= V <= SPEC_MAX_VOCAB.  R == 0 enqueues nothing.
+ * Sizes: R >= 0, 0 <= gamma <= 64, 1 <= V <= SPEC_MAX_VERIFY_VOCAB.  R == 0
+ * enqueues nothing.
  */
 int spec_verify_batch(const void *target_logits, int t_dtype,
                       const void *draft_logits, int d_dtype,

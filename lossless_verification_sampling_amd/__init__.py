@@ -27,6 +27,7 @@ SPEC_OK = 0
 SPEC_DEV_BAD_REQUEST = 0x1
 SPEC_DEV_SPIN_TIMEOUT = 0x2
 SPEC_MAX_VOCAB = 2097152
+SPEC_MAX_VERIFY_VOCAB = 262144
 
 EXPORTED = (
     "spec_version",

@@ -1,8 +1,4 @@
 // common.h -- device helpers shared by the library's kernels (internal).
-//
-// The verification kernels hand data to each other only through kernel
-// boundaries (chunk statistics -> pair sums -> finalisers), so they need no
-// cross-workgroup synchronisation inside a launch.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -14,20 +10,25 @@ namespace sv {
 
 constexpr int kBlock = 256;               // threads per workgroup (4 wave64s)
 constexpr int kWaves = kBlock / 64;
-constexpr int kMaxGamma = 64;             // per-request rows kept in LDS by finalisers
-constexpr uint32_t kSpinLimit = 1u << 20; // polls before a wait gives up
+constexpr int kMaxGamma = 64;             // largest draft length (gamma) accepted
+constexpr uint32_t kSpinLimit = 1u << 20; // polls before a cross-wave wait gives up
 constexpr int kMaxChunks = 4096;          // chunks per row
 constexpr double kLog2e = 1.4426950408889634;
 constexpr double kLn2 = 0.6931471805599453;
 
 // Workspace control block (offset 0, 256 bytes).
 struct Control {
-    uint32_t epoch;      // launches completed on this workspace
+    uint32_t reserved;
     uint32_t status;     // SPEC_DEV_* bits
-    uint32_t closed;     // requests closed in the running call
-    uint32_t pad[61];
+    uint32_t pad[62];
 };
 static_assert(sizeof(Control) == 256, "control block size");
+
+// Host side: records that the first `bytes` of workspace `ws` read zero
+// outside the control block once the work enqueued so far has run (every
+// entry point that writes a workspace calls it; the verification counters
+// rely on it).
+void note_workspace_clean(const void *ws, size_t bytes);
 
 __device__ __forceinline__ uint32_t atomic_load_u32(const uint32_t *p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -40,63 +41,6 @@ __device__ __forceinline__ uint32_t atomic_add_u32(uint32_t *p, uint32_t v) {
 }
 __device__ __forceinline__ void atomic_or_u32(uint32_t *p, uint32_t v) {
     __hip_atomic_fetch_or(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Launch tag: never 0, so a zero-initialised workspace holds no valid word.
-__device__ __forceinline__ uint32_t launch_tag(uint32_t epoch) { return epoch | 0x80000000u; }
-
-__device__ __forceinline__ void publish(uint64_t *slot, uint32_t tag, uint32_t payload) {
-    __hip_atomic_store(slot, ((uint64_t)tag << 32) | payload, __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void publish_f(uint64_t *slot, uint32_t tag, float v) {
-    publish(slot, tag, __float_as_uint(v));
-}
-
-// Spins until the word carries `tag`; returns its payload.  On timeout raises
-// SPEC_DEV_SPIN_TIMEOUT and returns 0.  Out of line: it is the cold path of
-// every exchange and would otherwise be inlined at each call site.
-__device__ __noinline__ uint32_t await_word(const uint64_t *slot, uint32_t tag, Control *ctl) {
-    for (uint32_t it = 0; it < kSpinLimit; ++it) {
-        uint64_t v = __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if ((uint32_t)(v >> 32) == tag) return (uint32_t)v;
-        __builtin_amdgcn_s_sleep(2);
-    }
-    atomic_or_u32(&ctl->status, SPEC_DEV_SPIN_TIMEOUT);
-    return 0u;
-}
-__device__ __forceinline__ float await_f(const uint64_t *slot, uint32_t tag, Control *ctl) {
-    return __uint_as_float(await_word(slot, tag, ctl));
-}
-
-// Loads n (<= 4) consecutive published words in parallel, then waits for any
-// that do not carry `tag` yet.
-__device__ inline void await_n(const uint64_t *w, int n, uint32_t tag, Control *ctl,
-                               uint32_t *out) {
-    uint64_t v[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-        if (q < n) v[q] = __hip_atomic_load(w + q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-        if (q < n)
-            out[q] = ((uint32_t)(v[q] >> 32) == tag) ? (uint32_t)v[q] : await_word(w + q, tag, ctl);
-}
-
-
-// Adds one to a launch-tagged counter (tag in the high word, count in the low
-// word) and returns the count after the add.  A word carrying another launch's
-// tag (or zero) counts as 0, so the counter needs no reset between launches
-// and stale workspace contents cannot corrupt it.
-__device__ inline uint32_t tagged_increment(uint64_t *w, uint32_t tag) {
-    uint64_t old = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    for (;;) {
-        const uint32_t cnt = ((uint32_t)(old >> 32) == tag) ? (uint32_t)old : 0u;
-        const uint64_t nw = ((uint64_t)tag << 32) | (uint64_t)(cnt + 1u);
-        if (__hip_atomic_compare_exchange_strong(w, &old, nw, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                                 __HIP_MEMORY_SCOPE_AGENT))
-            return cnt + 1u;
-    }
 }
 
 // ---------------------------------------------------------------------------

@@ -359,6 +359,7 @@ int spec_markov_draft_sample(const void *U, int u_dtype, const void *W1, const v
     a.tstats = (float2 *)(ws + p.off_stats);
     a.bad = (uint32_t *)(ws + p.off_bad);
     a.ctl = (Control *)ws;
+    note_workspace_clean(workspace, sizeof(Control));
     hipStream_t st = (hipStream_t)stream;
     hipLaunchKernelGGL(markov_clear_kernel, dim3((R + kBlock - 1) / kBlock), dim3(kBlock), 0, st,
                        a.bad, R);

@@ -1,5 +1,5 @@
 // verify.hip -- batched lossless speculative-sampling verification and the
-// analytic acceptance rate on gfx950.
+// analytic acceptance rate on gfx950, in one persistent launch per call.
 //
 // Method (pages cited by title and section):
 //  * DART reading note (zhongzhuzhou.org), sec. 2.3, eq. (3)-(4): a draft token
@@ -14,41 +14,54 @@
 //  * Speculative-decoding survey (zhifeiding.github.io), sec. 1.3: greedy
 //    verification is a position-wise argmax comparison.
 //
-// Design (four launches per call, each a hand-off through the workspace):
-//  * A "unit" is one position of one request: a (draft row, target row) pair
-//    for positions i < l_r, the bonus target row at i = l_r.  Each unit's rows
-//    are cut into C chunks of 64 N logits; one wave streams one chunk.
-//  * Kernel 1 (stats_kernel, a persistent grid) reads every needed row
-//    exactly once from HBM, chunk by chunk with the next chunk's 16-byte loads
-//    in flight, and writes each chunk's max and exp-sum
-//    sum 2^((z - m) s), s = log2(e) / T (or its argmax at T = 0).
-//  * norm_kernel (one wave per unit) combines kernel 1's chunk statistics
-//    into each row's normaliser (max M, Z = sum 2^((z - M) s)), or its argmax
-//    at T = 0.
-//  * Kernel 2 (tv_kernel, same structure as kernel 1) re-reads only the pair
-//    rows -- kernel 1 has just streamed them, so they come from the 256 MB
-//    Infinity Cache -- and reduces sum min(p, q) and sum [q - p]_+ per chunk.
-//  * Kernel 3 (finalize_kernel, one workgroup per request): c* and Res (one
-//    row per wave), the accept tests on the gathered
-//    logits q(x), p(x) in fp64 (one position per lane, prefix survival by
-//    ballot), and the residual or bonus draw as a two-level inverse CDF
-//    (chunk masses, then one re-read chunk scanned in ascending token id).
+// Design.  A "unit" is one position of one request: the (target, draft) row
+// pair of position i < l_r, or the bonus target row i = l_r.  Each unit's rows
+// are cut into C chunks of 64 N logits, and an "item" is one chunk of one
+// unit.  Two persistent launches of independent wave64s walk the items
+// round-robin (item k belongs to wave k mod W):
+//  1. stats_kernel streams every needed row exactly once from HBM with
+//     16-byte loads (two items in flight per wave).  Per item it publishes the
+//     chunk's scaled max mu and weight sum S = sum 2^(z s - mu) per row
+//     (s = log2(e) / T; the argmax at T = 0) and arrives on the unit's
+//     counter.  The wave whose arrival completes a unit ("last arriver")
+//     combines the C chunk words into the rows' normalisers, runs the
+//     position's accept test on the two gathered logits, and for the bonus
+//     unit makes the inverse-CDF draw from q; at T = 0 it settles the unit.
+//  2. tv_kernel re-reads the pair chunks at T > 0 -- kernel 1 has just
+//     streamed them, so they come from the 256 MB Infinity Cache when they
+//     fit -- rebuilds each chunk's weights exactly and publishes sum min(p, q)
+//     and the residual mass.  The unit's last TV arriver sums c* and Res and,
+//     if the position was rejected, makes the residual draw.
+//  3. The wave that finishes a request's last unit (in either kernel) applies
+//     prefix survival to the units' accept bits and writes the outputs.
+// Words passed between waves are 64-bit (launch tag, payload) pairs written
+// and read with agent-scope atomics, so a reader never mistakes a stale word
+// for a current one; counters return to zero when their last arriver is done.
+// A wave only ever waits for words whose stores were issued before the
+// counter arrival that made it the last arriver, so no wait depends on
+// another wave being scheduled; every wait is still bounded and raises
+// SPEC_DEV_SPIN_TIMEOUT rather than spin forever.
 #include <math.h>
 #include <stddef.h>
 #include <stdio.h>
 #include <stdlib.h>
 
+#include <atomic>
 #include <mutex>
 #include <vector>
 
-
 #include "common.h"
 
-#ifndef SV_RING
-#define SV_RING 2
-#endif
-
 namespace sv {
+
+constexpr float kInf = __builtin_inff();
+constexpr int kLanes = 64;
+
+// Per-unit record words (tagged), filled by the unit's last arrivers and read
+// by the request's finaliser.
+enum : int { kRecFlags = 0, kRecLqx = 1, kRecDraw = 2, kRecLqd = 3, kRecCs = 4, kRecRs = 5,
+             kRecWords = 8 };
+constexpr uint32_t kFlagValid = 1u, kFlagAccept = 2u;
 
 struct VerifyArgs {
     const void *zt;          // target logits
@@ -63,128 +76,147 @@ struct VerifyArgs {
     int UG;                  // units per request (gamma + 1, or 1 for row pairs)
     int tG, dG;              // rows per request in the target / draft tensors
     int tv_mode;             // 1: independent row pairs, c* and Res only
+    uint32_t tag;            // this launch's tag (nonzero, top bit set)
     int32_t *out_tok;
     int32_t *out_n;
     float *out_cs;
     float *out_rs;
     float *out_lq;
     Control *ctl;
-    float4 *st1;             // [units][C] chunk statistics (kernel 1)
-    float2 *st2;             // [units][C] sum min / sum res of pair chunks (kernel 2)
-    struct RowNorm *nrm;     // [units] row normalisers (norm_kernel)
+    uint32_t *cnt_r;         // [R] finished units per request
+    uint64_t *st1;           // [units][C][4] chunk stats
+    uint64_t *st2;           // [units][C][2] chunk sum min(p, q), residual mass
+    uint64_t *nrm;           // [units][4] unit normalisers
+    uint64_t *rec;           // [units][kRecWords] unit records
 };
 
-// Normalisers of one unit's rows: at T > 0 the maxima and Z = sum 2^((z - M) s)
-// of the target (t) and draft (d) rows; at T = 0 their argmax (-1: invalid).
-struct RowNorm {
-    float Mt, Md;
-    int gt, gd;
-    double Zt, Zd;
-};
+// ---------------------------------------------------------------------------
+// small helpers
+// ---------------------------------------------------------------------------
 
-constexpr float kInf = __builtin_inff();
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
 __device__ __forceinline__ bool temperature_ok(float T) {
     if (!(T >= 0.0f) || !(T <= 1e30f)) return false;  // NaN, negative, +inf, huge
     return T == 0.0f || T >= 1e-30f;
 }
 __device__ __forceinline__ bool uniform_ok(float u) { return u >= 0.0f && u < 1.0f; }
+__device__ __forceinline__ bool finite_f(float x) { return x - x == 0.0f; }
 
-// exp2 scale of log2(e) / T, rounded to fp32 once; every workgroup of a
-// request derives the same value.
+// exp2 scale log2(e) / T rounded to fp32 once; every wave derives the same value.
 __device__ __forceinline__ float exp2_scale(float T) { return (float)(kLog2e / (double)T); }
 
-// Softmax arithmetic in scaled units.  With s = log2(e) / T a logit z has
-// weight 2^(z s - mu) for any reference mu; the reference cancels in the
-// normalisation, so every stage may pick its own as long as it scales
-// consistently.  A chunk's reference is mu_c = fl(m_c s), its max logit times
-// s rounded once, and an element's exponent is fma(z, s, -mu_c): a single
-// rounding, tiny for the logits near the max that carry the mass.  Rounding
-// is monotone, so the row's reference max_c mu_c is fl(M s).
-
 // Exponent reference of a chunk with scaled max mu: mu itself, or 0 when the
-// chunk holds no finite logit (then -inf gives weight 0, a NaN stays NaN).
+// chunk holds no finite logit (-inf then gives weight 0, a NaN stays NaN).
 __device__ __forceinline__ float exp_ref(float mu) { return (mu > -kInf) ? mu : 0.0f; }
 
-// 2^(z s - ref) with the exponent from one fused multiply-add.
-__device__ __forceinline__ float exp_w(float z, float s, float ref) {
+// 2^(z s - ref), the exponent from one fused multiply-add: a single rounding,
+// tiny for the logits near the chunk max that carry the mass.
+__device__ __forceinline__ float ew(float z, float s, float ref) {
     return __builtin_amdgcn_exp2f(__builtin_fmaf(z, s, -ref));
 }
 
-// Weight of a chunk with scaled max mu and exp-sum S relative to the row's
-// scaled max muM: S * 2^(mu - muM), the power in fp32 (relative error ~1e-7,
-// like the fp32 exp-sums), accumulated by callers in fp64.  Shared by every
-// stage that combines a row, so all obtain identical normalisers.
-__device__ __forceinline__ double chunk_weight(float mu, float S, float muM) {
-    return (mu > -kInf) ? (double)S * (double)__builtin_amdgcn_exp2f(mu - muM) : 0.0;
+// Probability scale of a chunk (p_v = e_v * alpha) from its scaled max mu and
+// the row normalisers (M = max over chunks of mu, Z = sum 2^(z s - M)).
+__device__ __forceinline__ float chunk_alpha(float mu, float M, float Z) {
+    return (mu > -kInf) ? (float)((double)__builtin_amdgcn_exp2f(mu - M) / (double)Z) : 0.0f;
 }
 
-// Probability scale of a chunk: p_v = 2^(z_v s - mu) * scale.
-__device__ __forceinline__ float chunk_scale(float mu, float muM, double Z) {
-    return (mu > -kInf) ? (float)((double)__builtin_amdgcn_exp2f(mu - muM) / Z) : 0.0f;
+// Agent-scope 64-bit words: (tag << 32) | payload.
+__device__ __forceinline__ uint64_t ld_word(const uint64_t *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_word(uint64_t *p, uint32_t tag, uint32_t payload) {
+    __hip_atomic_store(p, ((uint64_t)tag << 32) | payload, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// [q - p]_+ computed as q - min(p, q) with rounded products (no contraction),
-// identical wherever it is evaluated.
-__device__ __forceinline__ void pq_weights(float et, float ed, float at, float ad, float &q,
-                                           float &mn) {
-    q = __fmul_rn(et, at);
-    float p = __fmul_rn(ed, ad);
-    mn = fminf(p, q);
-}
-
-
-__device__ void write_invalid(const VerifyArgs &a, int r) {
-    const float nan = __builtin_nanf("");
-    if (a.tv_mode) {
-        a.out_cs[r] = nan;
-        if (a.out_rs) a.out_rs[r] = nan;
-    } else {
-        for (int j = 0; j <= a.gamma; ++j) {
-            a.out_tok[(size_t)r * (a.gamma + 1) + j] = -1;
-            if (a.out_lq) a.out_lq[(size_t)r * (a.gamma + 1) + j] = nan;
+// Every lane with `act` reads the word at p until it carries `tag`, then
+// returns its payload (0 for inactive lanes).  Called by every active lane of
+// the wave.  The wait is bounded: past kSpinLimit polls, or once any wave of
+// the launch has timed out, it raises SPEC_DEV_SPIN_TIMEOUT and returns.
+__device__ __forceinline__ uint32_t await_lane(const uint64_t *p, bool act, uint32_t tag,
+                                               Control *ctl) {
+    uint64_t v = act ? ld_word(p) : 0;
+    bool stale = act && (uint32_t)(v >> 32) != tag;
+    uint32_t it = 0;
+    while (__ballot(stale)) {
+        if ((++it & 255u) == 0u &&
+            (it > kSpinLimit || (atomic_load_u32(&ctl->status) & SPEC_DEV_SPIN_TIMEOUT))) {
+            if (stale) atomic_or_u32(&ctl->status, SPEC_DEV_SPIN_TIMEOUT);
+            break;
         }
-        for (int i = 0; i < a.gamma; ++i) {
-            if (a.out_cs) a.out_cs[(size_t)r * a.gamma + i] = nan;
-            if (a.out_rs) a.out_rs[(size_t)r * a.gamma + i] = nan;
+        __builtin_amdgcn_s_sleep(2);
+        if (stale) {
+            v = ld_word(p);
+            stale = (uint32_t)(v >> 32) != tag;
         }
-        a.out_n[r] = -1;
     }
-    atomic_or_u32(&a.ctl->status, SPEC_DEV_BAD_REQUEST);
+    return (uint32_t)v;
+}
+
+// Lanes 0..n-1 store words w[lane] at p[lane] (n <= 4).
+__device__ __forceinline__ void publish_n(uint64_t *p, uint32_t tag, int n, uint32_t w0,
+                                          uint32_t w1, uint32_t w2, uint32_t w3) {
+    const int lane = lane_id();
+    if (lane < n) {
+        const uint32_t w = lane == 0 ? w0 : lane == 1 ? w1 : lane == 2 ? w2 : w3;
+        st_word(p + lane, tag, w);
+    }
+}
+
+__device__ __forceinline__ uint32_t rl(uint32_t v, int l) {
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, l);
+}
+__device__ __forceinline__ float rlf(float v, int l) { return readlane_f(v, l); }
+
+// Wave inclusive prefix sum (fp64) in lane order.
+__device__ __forceinline__ double wave_incl_scan(double v) {
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const double n = __shfl_up(v, o, 64);
+        if (lane_id() >= o) v += n;
+    }
+    return v;
 }
 
 // ---------------------------------------------------------------------------
-// chunk items: one wave streams one chunk of kLanes * N logits per row
+// items
 // ---------------------------------------------------------------------------
-
-constexpr int kLanes = 64;
 
 struct Item {
     int u, r, i, c, l;
-    float T, s;   // temperature and log2(e) / T
-    bool pair;    // the draft row is present (i < l)
+    float T, s;   // temperature and log2(e) / T (0 at T = 0)
 };
+__device__ __forceinline__ bool is_pair(const Item &x) { return x.i < x.l; }
+__device__ __forceinline__ bool is_tv(const Item &x) { return x.i < x.l && x.T != 0.0f; }
 
-// Global wave index and wave count of the launch (each wave works alone).
 __device__ __forceinline__ long wave_index() {
     return (long)blockIdx.x * kWaves + (threadIdx.x >> 6);
 }
 __device__ __forceinline__ long wave_count() { return (long)gridDim.x * kWaves; }
 
+// Request r's (T, l) and whether the request is well formed.
+__device__ __forceinline__ bool request_ok(const VerifyArgs &a, int r, float &T, int &l) {
+    T = a.temp[r];
+    l = a.tv_mode ? 1 : a.vlen[r];
+    return temperature_ok(T) && l >= 0 && l <= a.gamma;
+}
+
 // Walks this wave's items wave_index() + k * wave_count() in increasing k and
-// yields the active ones.  The wave decides the activity of 64 candidates at
-// once (lane k holds candidate base + k and its request parameters) and hands
-// them out in order with readlane, so the item loop issues no loads of its
-// own; one round of loads per 64 candidates.
+// yields the active ones (units i <= l_r of well-formed requests).  Lane j
+// judges candidate base + j, so one round of loads serves 64 candidates.
 struct ItemCursor {
-    long base = -64;
+    uint32_t base = 0;       // candidate round: candidates w0 + (base + j) W
     uint64_t mask = 0;
     int lr = 0, li = 0, lc = 0, ll = 0;
     float lT = 0.0f, ls = 0.0f;
+    bool first = true;
 
-    // pairs_only: yield only pair items at T > 0 (the ones kernel 2 reduces)
-    __device__ bool next(const VerifyArgs &a, long work, Item &x, bool pairs_only = false) {
-        const long W = wave_count(), w0 = wave_index();
+    // work < 2^31 (checked by the host), so 32-bit indices suffice.
+    // tv_only: yield only pair items at T > 0 (the TV pass's items).
+    __device__ bool next(const VerifyArgs &a, uint32_t work, Item &x, bool tv_only) {
+        const uint32_t W = (uint32_t)wave_count(), w0 = (uint32_t)wave_index();
         for (;;) {
             if (mask) {
                 const int k = __builtin_ctzll(mask);
@@ -193,87 +225,92 @@ struct ItemCursor {
                 x.i = __builtin_amdgcn_readlane(li, k);
                 x.c = __builtin_amdgcn_readlane(lc, k);
                 x.l = __builtin_amdgcn_readlane(ll, k);
-                x.T = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lT), k));
-                x.s = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ls), k));
+                x.T = rlf(lT, k);
+                x.s = rlf(ls, k);
                 x.u = x.r * a.UG + x.i;
-                x.pair = x.i < x.l;
                 return true;
             }
-            base += 64;
-            if (w0 + base * W >= work) return false;
-            const long it = w0 + (base + (threadIdx.x & 63)) * W;
+            if (!first) base += 64;
+            first = false;
+            // first candidate of this round; rounds past the end stop
+            if ((uint64_t)w0 + (uint64_t)base * W >= work) return false;
+            const uint64_t it64 = (uint64_t)w0 + (uint64_t)(base + (uint32_t)lane_id()) * W;
             bool act = false;
-            if (it < work) {
-                const int u = (int)(it / a.C);
-                lc = (int)(it % a.C);
-                lr = u / a.UG;
-                li = u % a.UG;
-                lT = a.temp[lr];
-                ll = a.tv_mode ? 1 : a.vlen[lr];
-                act = temperature_ok(lT) && ll >= 0 && ll <= a.gamma && li <= ll;
-                if (pairs_only) act = act && li < ll && lT != 0.0f;
-                ls = act && lT != 0.0f ? exp2_scale(lT) : 0.0f;
+            if (it64 < work) {
+                const uint32_t it = (uint32_t)it64;
+                const uint32_t u = it / (uint32_t)a.C;
+                lc = (int)(it - u * (uint32_t)a.C);
+                lr = (int)(u / (uint32_t)a.UG);
+                li = (int)(u - (uint32_t)lr * (uint32_t)a.UG);
+                act = request_ok(a, lr, lT, ll) && li <= ll;
+                if (tv_only) act = act && li < ll && lT != 0.0f;
+                ls = (act && lT != 0.0f) ? exp2_scale(lT) : 0.0f;
             }
             mask = __ballot(act);
         }
     }
 };
 
-// Raw register image of one row chunk, N logits per lane.  With vector loads
-// (EPV > 1) bf16 logits stay packed two per word; on the scalar path every
-// logit is widened to fp32 when loaded.
+// ---------------------------------------------------------------------------
+// chunk registers
+// ---------------------------------------------------------------------------
+
+// Raw register image of one row chunk, N logits per lane.  Slot j * EPV + q of
+// lane l holds logit c0 + (j * 64 + l) * EPV + q, so each load instruction of
+// the wave reads consecutive 16-byte pieces.  bf16 logits stay packed two per
+// word with vector loads; the scalar path (EPV == 1) widens them at load time.
 template <typename T, int N, int EPV>
 struct RawChunk {
     static constexpr bool kPacked = (EPV > 1) && (EltBytes<T>::value == 2);
     static constexpr int kWords = kPacked ? N / 2 : N;
     uint32_t w[kWords];
 
-    // Slot j * EPV + q of lane l holds logit c0 + (j * 64 + l) * EPV + q, so
-    // each load instruction of the wave reads consecutive 16-byte pieces.
-    // A chunk inside the row (all but the last) loads without bounds checks;
-    // past the row end a vector holds -inf (V % EPV == 0 when EPV > 1).
+    // Chunks inside the row load without bounds checks; in the last chunk a
+    // vector past the row end holds -inf (V % EPV == 0 when EPV > 1).
     __device__ __forceinline__ void load(const T *row, long c0, int V) {
-        const int lane = threadIdx.x & 63;
+        const T *base = row + c0;
+        const uint32_t lane = (uint32_t)lane_id();
         if (c0 + (long)kLanes * N <= V) {
 #pragma unroll
-            for (int j = 0; j < N / EPV; ++j)
-                load_vec(row, c0 + ((long)j * kLanes + lane) * EPV, j, true);
+            for (int j = 0; j < N / EPV; ++j) load_vec(base, (j * kLanes + lane) * EPV, j, true);
         } else {
+            const int rem = (int)(V - c0);
 #pragma unroll
             for (int j = 0; j < N / EPV; ++j) {
-                const long e = c0 + ((long)j * kLanes + lane) * EPV;
-                load_vec(row, e, j, e < V);
+                const int e = (int)((j * kLanes + lane) * EPV);
+                load_vec(base, e, j, e < rem);
             }
         }
     }
 
-    __device__ __forceinline__ void load_vec(const T *row, long e, int j, bool in) {
+    __device__ __forceinline__ void load_vec(const T *base, uint32_t e, int j, bool in) {
         if constexpr (EPV == 1) {
-            w[j] = __float_as_uint(in ? load_one(row, e) : -kInf);
+            w[j] = __float_as_uint(in ? load_one(base, (long)e) : -kInf);
         } else if constexpr (kPacked) {
             constexpr int NW = EPV / 2;
             if constexpr (NW == 4) {
-                uint4 v = in ? *reinterpret_cast<const uint4 *>(row + e)
-                             : make_uint4(0xff80ff80u, 0xff80ff80u, 0xff80ff80u, 0xff80ff80u);
+                uint4 v = make_uint4(0xff80ff80u, 0xff80ff80u, 0xff80ff80u, 0xff80ff80u);
+                if (in) v = *reinterpret_cast<const uint4 *>(base + e);
                 w[j * 4 + 0] = v.x; w[j * 4 + 1] = v.y; w[j * 4 + 2] = v.z; w[j * 4 + 3] = v.w;
-            } else if constexpr (NW == 2) {
-                uint2 v = in ? *reinterpret_cast<const uint2 *>(row + e)
-                             : make_uint2(0xff80ff80u, 0xff80ff80u);
-                w[j * 2 + 0] = v.x; w[j * 2 + 1] = v.y;
             } else {
-                w[j] = in ? *reinterpret_cast<const uint32_t *>(row + e) : 0xff80ff80u;
+                static_assert(NW == 2, "bf16 vector width");
+                uint2 v = make_uint2(0xff80ff80u, 0xff80ff80u);
+                if (in) v = *reinterpret_cast<const uint2 *>(base + e);
+                w[j * 2 + 0] = v.x; w[j * 2 + 1] = v.y;
             }
         } else {
-            if constexpr (EPV == 4) {
-                uint4 v = in ? *reinterpret_cast<const uint4 *>(row + e)
-                             : make_uint4(0xff800000u, 0xff800000u, 0xff800000u, 0xff800000u);
-                w[j * 4 + 0] = v.x; w[j * 4 + 1] = v.y; w[j * 4 + 2] = v.z; w[j * 4 + 3] = v.w;
-            } else {
-                uint2 v = in ? *reinterpret_cast<const uint2 *>(row + e)
-                             : make_uint2(0xff800000u, 0xff800000u);
-                w[j * 2 + 0] = v.x; w[j * 2 + 1] = v.y;
-            }
+            static_assert(EPV == 4, "fp32 vector width");
+            uint4 v = make_uint4(0xff800000u, 0xff800000u, 0xff800000u, 0xff800000u);
+            if (in) v = *reinterpret_cast<const uint4 *>(base + e);
+            w[j * 4 + 0] = v.x; w[j * 4 + 1] = v.y; w[j * 4 + 2] = v.z; w[j * 4 + 3] = v.w;
         }
+    }
+
+    // Hides the words' values from the optimiser (no instruction), so that
+    // values widened from them before this point are not reused after it.
+    __device__ __forceinline__ void opaque() {
+#pragma unroll
+        for (int q = 0; q < kWords; ++q) __asm__ volatile("" : "+v"(w[q]));
     }
 
     __device__ __forceinline__ float get(int k) const {
@@ -282,596 +319,834 @@ struct RawChunk {
     }
 };
 
+// Token id of slot k of this lane in the chunk starting at c0.
+template <int EPV>
+__device__ __forceinline__ int slot_id(long c0, int k) {
+    return (int)(c0 + ((long)(k / EPV) * kLanes + lane_id()) * EPV + (k % EPV));
+}
+
+template <typename TT, typename TD, int N>
+struct ChunkGeom {
+    static constexpr int kEB = (EltBytes<TT>::value > EltBytes<TD>::value) ? EltBytes<TT>::value
+                                                                          : EltBytes<TD>::value;
+    static constexpr int kVec = (16 / kEB < N) ? 16 / kEB : N;
+};
+
+template <typename T>
+__device__ __forceinline__ const T *row_ptr(const void *base, int r, int G, int i, int V) {
+    return (const T *)base + ((long)r * G + i) * V;
+}
+
+// ---------------------------------------------------------------------------
+// per-chunk reductions
+// ---------------------------------------------------------------------------
+
+// Sum of the N values of a lane in slot order.  Every sum over a chunk's
+// weights goes through this function, so sums of identical weights are
+// bitwise identical wherever they are taken.
 template <int N>
-__device__ __forceinline__ long chunk_start(int c) { return (long)c * kLanes * N; }
+__device__ __forceinline__ float lane_sum(const float (&v)[N]) {
+    float acc = 0.0f;
+#pragma unroll
+    for (int k = 0; k < N; ++k) acc += v[k];
+    return acc;
+}
+
+// T > 0: scaled chunk max mu = fl(m s), weights e_k = 2^(z_k s - mu) (kept in
+// e) and their wave sum S.
+template <int N, typename RC>
+__device__ __forceinline__ void chunk_exp(const RC &raw, float s, float (&e)[N], float &mu,
+                                          float &S) {
+    float m = -kInf;
+#pragma unroll
+    for (int k = 0; k < N; ++k) m = __builtin_elementwise_maximum(m, raw.get(k));
+    mu = wave_max(m) * s;
+    const float ref = exp_ref(mu);
+    // widen the logits again instead of keeping N widened copies alive
+    RC r2 = raw;
+    r2.opaque();
+#pragma unroll
+    for (int k = 0; k < N; ++k) e[k] = ew(r2.get(k), s, ref);
+    S = wave_sum_f(lane_sum<N>(e));
+}
+
+// T = 0: chunk argmax (value, index; lowest index on ties); bad = a NaN seen.
+template <int N, int EPV, typename RC>
+__device__ __forceinline__ void chunk_argmax(const RC &raw, long c0, float &bv, int &bi,
+                                             int &bad) {
+    bv = -kInf;
+    bi = 0x7fffffff;
+    bad = 0;
+#pragma unroll
+    for (int k = 0; k < N; ++k) {
+        const float z = raw.get(k);
+        if (z != z) bad = 1;
+        if (z > bv) {
+            bv = z;
+            bi = slot_id<EPV>(c0, k);
+        }
+    }
+    wave_argmax(bv, bi);
+    bad = wave_max_i(bad);
+}
+
+// Scaling of a row pair's chunk weights for min(p, q): p_v = e_d alpha_d and
+// q_v = e_t alpha_t are compared as min(e_t kt, e_d kd) in units of `unit`
+// probability.  kt = 1 (unit alpha_t) unless the draft scale exceeds the
+// target's by more than 2^100; then kd = 1 (unit alpha_d).  Both products stay
+// finite because every e is at most 1 (up to one rounding).
+struct PairScale {
+    float kt, kd, unit;
+};
+__device__ __forceinline__ PairScale pair_scale(float at, float ad) {
+    PairScale ps;
+    const double k = (at > 0.0f) ? (double)ad / (double)at : INFINITY;
+    if (k <= 0x1p100) {
+        ps.kt = 1.0f;
+        ps.kd = (float)k;
+        ps.unit = at;
+    } else {
+        ps.kt = (ad > 0.0f) ? (float)((double)at / (double)ad) : 0.0f;
+        ps.kd = 1.0f;
+        ps.unit = ad;
+    }
+    return ps;
+}
+
+// Online combine of chunk statistics (scaled max mu, weight sum S) into a
+// row's normalisers M = max mu and Z = sum S 2^(mu - M).  A NaN or +inf mu
+// (a NaN or +inf logit in the chunk) makes M NaN.
+struct OnlineZ {
+    float m = -kInf;
+    double z = 0.0;
+    int bad = 0;
+    __device__ __forceinline__ void add(float mu, float S) {
+        if (!(mu == mu) || mu == kInf) {
+            bad = 1;
+        } else if (mu > -kInf) {
+            if (mu > m) {
+                z = z * (double)__builtin_amdgcn_exp2f(m - mu) + (double)S;
+                m = mu;
+            } else {
+                z += (double)S * (double)__builtin_amdgcn_exp2f(mu - m);
+            }
+        }
+    }
+    // Wave-wide result (every lane gets it).
+    __device__ __forceinline__ void reduce(float &M, float &Z) const {
+        M = wave_max(m);
+        const double zl = (m > -kInf) ? z * (double)__builtin_amdgcn_exp2f(m - M) : 0.0;
+        Z = (float)wave_sum(zl);
+        if (wave_max_i(bad)) M = __builtin_nanf("");
+    }
+};
+
+// ---------------------------------------------------------------------------
+// output helpers
+// ---------------------------------------------------------------------------
+
+// Invalid-request outputs of request r, written by the whole wave.
+__device__ __forceinline__ void write_invalid(const VerifyArgs &a, int r) {
+    const float nan = __builtin_nanf("");
+    const int lane = lane_id();
+    if (a.tv_mode) {
+        if (lane == 0) {
+            a.out_cs[r] = nan;
+            if (a.out_rs) a.out_rs[r] = nan;
+        }
+    } else {
+        for (int j = lane; j <= a.gamma; j += 64) {
+            a.out_tok[(size_t)r * (a.gamma + 1) + j] = -1;
+            if (a.out_lq) a.out_lq[(size_t)r * (a.gamma + 1) + j] = nan;
+        }
+        for (int i = lane; i < a.gamma; i += 64) {
+            if (a.out_cs) a.out_cs[(size_t)r * a.gamma + i] = nan;
+            if (a.out_rs) a.out_rs[(size_t)r * a.gamma + i] = nan;
+        }
+        if (lane == 0) a.out_n[r] = -1;
+    }
+    if (lane == 0) atomic_or_u32(&a.ctl->status, SPEC_DEV_BAD_REQUEST);
+}
+
+// ---------------------------------------------------------------------------
+// batched waits on tagged words
+// ---------------------------------------------------------------------------
+
+// A unit has at most kCB * 64 chunks, so a lane owns at most kCB of them
+// (chunk c = 64 b + lane) and every per-chunk word of a unit fits in
+// registers: the combines below issue all their loads at once and wait once.
+constexpr int kCB = 4;
+
+// Lane-parallel batch: word k of this lane is p[k] if act[k].  Issues every
+// load, then re-reads only the words that do not carry `tag` yet, until all
+// do (bounded as in await_lane).  out[k] = payload (0 for inactive words).
+template <int K>
+__device__ __forceinline__ void await_batch(const uint64_t *const (&p)[K], const bool (&act)[K],
+                                            uint32_t tag, Control *ctl, uint32_t (&out)[K]) {
+    uint64_t v[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) v[k] = act[k] ? ld_word(p[k]) : ((uint64_t)tag << 32);
+    uint32_t it = 0;
+    for (;;) {
+        bool stale = false;
+#pragma unroll
+        for (int k = 0; k < K; ++k) stale = stale || (uint32_t)(v[k] >> 32) != tag;
+        if (!__ballot(stale)) break;
+        if ((++it & 255u) == 0u &&
+            (it > kSpinLimit || (atomic_load_u32(&ctl->status) & SPEC_DEV_SPIN_TIMEOUT))) {
+            if (stale) atomic_or_u32(&ctl->status, SPEC_DEV_SPIN_TIMEOUT);
+            break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+#pragma unroll
+        for (int k = 0; k < K; ++k)
+            if ((uint32_t)(v[k] >> 32) != tag) v[k] = ld_word(p[k]);
+    }
+#pragma unroll
+    for (int k = 0; k < K; ++k) out[k] = (uint32_t)v[k];
+}
+
+// Chunk words of a unit, for the lane's chunks c = 64 b + lane (b < kCB):
+// w[b][q] = word q of chunk c (q < Q), 0 where c >= C or !want[q].
+template <int Q>
+__device__ __forceinline__ void load_unit_words(const uint64_t *base, int C, const bool (&want)[Q],
+                                                uint32_t tag, Control *ctl,
+                                                uint32_t (&w)[kCB][Q]) {
+    const uint64_t *p[kCB * Q];
+    bool act[kCB * Q];
+    uint32_t o[kCB * Q];
+#pragma unroll
+    for (int b = 0; b < kCB; ++b)
+#pragma unroll
+        for (int q = 0; q < Q; ++q) {
+            const int c = b * 64 + lane_id();
+            p[b * Q + q] = base + (size_t)c * Q + q;
+            act[b * Q + q] = c < C && want[q];
+        }
+    await_batch<kCB * Q>(p, act, tag, ctl, o);
+#pragma unroll
+    for (int b = 0; b < kCB; ++b)
+#pragma unroll
+        for (int q = 0; q < Q; ++q) w[b][q] = o[b * Q + q];
+}
+
+// ---------------------------------------------------------------------------
+// inverse-CDF draw (two levels: chunk masses, then one chunk in id order)
+// ---------------------------------------------------------------------------
+
+// The chunk holding t in the running sum of the chunk masses m[b] (lane's
+// chunks c = 64 b + lane, ascending chunk order, strict >).  Returns the chunk
+// and, in *tin, t minus the mass before it; if t is at or past the total
+// (rounding), the last chunk with mass and *tin = +inf.
+__device__ __forceinline__ int select_chunk(int C, double t, const double (&m)[kCB], double *tin) {
+    const int lane = lane_id();
+    double run = 0.0;
+    int clast = -1;
+#pragma unroll
+    for (int b = 0; b < kCB; ++b) {
+        const int c = b * 64 + lane;
+        const double wc = (c < C) ? m[b] : 0.0;
+        const double incl = wave_incl_scan(wc);
+        const double excl = run + incl - wc;
+        const uint64_t hit = __ballot(c < C && excl + wc > t);
+        const uint64_t pos = __ballot(c < C && wc > 0.0);
+        if (pos) clast = b * 64 + 63 - __builtin_clzll(pos);
+        if (hit) {
+            const int k = __builtin_ctzll(hit);
+            *tin = __shfl(t - excl, k, 64);
+            return b * 64 + k;
+        }
+        run += __shfl(incl, 63, 64);
+    }
+    *tin = INFINITY;
+    return clast >= 0 ? clast : 0;
+}
+
+// Word q of chunk c from the lane-strided registers w (uniform result).
+template <int Q>
+__device__ __forceinline__ uint32_t chunk_word(const uint32_t (&w)[kCB][Q], int c, int q) {
+    uint32_t v = 0;
+#pragma unroll
+    for (int b = 0; b < kCB; ++b)
+        if ((c >> 6) == b) v = rl(w[b][q], c & 63);
+    return v;
+}
+
+// Draw inside chunk c0 of a row: the first id (ascending) whose running weight
+// exceeds tin.  wfn(e, out) gives the EPV weights of ids e..e+EPV-1 (0 past
+// the row end).  Scans the chunk one vector row (64 lanes x EPV ids) at a
+// time.  Clamps to the chunk's last positive weight; if none, its first id.
+template <int N, int EPV, typename WFn>
+__device__ __forceinline__ int draw_in_chunk(long c0, double tin, WFn wfn) {
+    const int lane = lane_id();
+    double run = 0.0;
+    int lastpos = -1;
+#pragma unroll 1
+    for (int j = 0; j < N / EPV; ++j) {
+        const long e = c0 + ((long)j * kLanes + lane) * EPV;
+        float w[EPV];
+        wfn(e, w);
+        double tot = 0.0;
+        int lp = -1;
+#pragma unroll
+        for (int q = 0; q < EPV; ++q) {
+            tot += (double)w[q];
+            if (w[q] > 0.0f) lp = (int)e + q;
+        }
+        lastpos = max(lastpos, wave_max_i(lp));
+        const double incl = wave_incl_scan(tot);
+        const double excl = run + incl - tot;
+        const uint64_t hit = __ballot(tot > 0.0 && excl + tot > tin);
+        if (hit) {
+            const int k = __builtin_ctzll(hit);
+            int tok = -1;
+            if (lane == k) {
+                double cum = excl;
+#pragma unroll
+                for (int q = 0; q < EPV; ++q) {
+                    cum += (double)w[q];
+                    if (tok < 0 && cum > tin) tok = (int)e + q;
+                }
+                if (tok < 0) tok = lp;  // rounding: last positive id of this lane
+            }
+            return __builtin_amdgcn_readlane(tok, k);
+        }
+        run += __shfl(incl, 63, 64);
+    }
+    return lastpos >= 0 ? lastpos : (int)c0;
+}
+
+// Loads EPV logits of a row at ids e.. as fp32 (-inf past the row end).
+template <typename T, int EPV>
+__device__ __forceinline__ void load_ids(const T *row, long e, int V, float (&z)[EPV]) {
+    if (e < V) {
+        VecLoad<T, EPV>::run(row, e, z);
+    } else {
+#pragma unroll
+        for (int q = 0; q < EPV; ++q) z[q] = -kInf;
+    }
+}
+
+// Draw from q of a target row (T > 0), its chunk words w (mu_t, S_t in q = 0,
+// 1) and normalisers (M, Z) in hand.  Returns the token; *ztok its logit.
+template <typename TT, int N, int EPV, int Q>
+__device__ __forceinline__ int draw_from_q(const VerifyArgs &a, const TT *trow,
+                                           const uint32_t (&w)[kCB][Q], float s, float M, float Z,
+                                           float uu, float *ztok) {
+    const int C = a.C;
+    double m[kCB];
+    double W = 0.0;
+#pragma unroll
+    for (int b = 0; b < kCB; ++b) {
+        const int c = b * 64 + lane_id();
+        m[b] = (c < C) ? (double)chunk_alpha(__uint_as_float(w[b][0]), M, Z) *
+                             (double)__uint_as_float(w[b][1])
+                       : 0.0;
+        W += m[b];
+    }
+    W = wave_sum(W);
+    double tin;
+    const int cs = select_chunk(C, (double)uu * W, m, &tin);
+    const float mu = __uint_as_float(chunk_word<Q>(w, cs, 0));
+    const float al = chunk_alpha(mu, M, Z);
+    const float ref = exp_ref(mu);
+    const long c0 = (long)cs * kLanes * N;
+    const double te = (al > 0.0f) ? tin / (double)al : INFINITY;
+    const int tok = draw_in_chunk<N, EPV>(c0, te, [&](long e, float (&wv)[EPV]) {
+        float z[EPV];
+        load_ids<TT, EPV>(trow, e, a.V, z);
+#pragma unroll
+        for (int q = 0; q < EPV; ++q) wv[q] = ew(z[q], s, ref);
+    });
+    *ztok = load_one(trow, tok);
+    return tok;
+}
+
+// ---------------------------------------------------------------------------
+// request finaliser
+// ---------------------------------------------------------------------------
+
+// Prefix survival over the unit records of request r and the final outputs.
+// Run by the wave that finished the request's last unit.  Units 0..l sit on
+// lanes i = 64 b + lane, b < 2 (l <= kMaxGamma = 64).
+__device__ __forceinline__ void finalize_request(const VerifyArgs &a, int r, int l) {
+    const int lane = lane_id();
+    const int G = a.gamma;
+    const float nan = __builtin_nanf("");
+    const uint64_t *rec0 = a.rec + (size_t)r * a.UG * kRecWords;
+    constexpr int kQ = 6;  // flags, lqx, draw, lqd, c*, Res
+    const uint64_t *p[2 * kQ];
+    bool act[2 * kQ];
+    uint32_t w[2 * kQ];
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int q = 0; q < kQ; ++q) {
+            const int i = b * 64 + lane;
+            p[b * kQ + q] = rec0 + (size_t)i * kRecWords + q;
+            // c* and Res exist for positions only, log q(x) is read below A only
+            act[b * kQ + q] = i <= l && ((q != kRecCs && q != kRecRs && q != kRecLqx) || i < l);
+        }
+    await_batch<2 * kQ>(p, act, a.tag, a.ctl, w);
+    const bool bad0 = lane <= l && !(w[kRecFlags] & kFlagValid);
+    const bool bad1 = 64 + lane <= l && !(w[kQ + kRecFlags] & kFlagValid);
+    if (__ballot(bad0 || bad1)) {
+        write_invalid(a, r);
+    } else {
+        const uint64_t accm = __ballot(lane < l && (w[kRecFlags] & kFlagAccept));
+        int A = (~accm == 0) ? 64 : __builtin_ctzll(~accm);
+        if (A > l) A = l;
+        const int bA = A >> 6, lA = A & 63;
+        const int draw = (int)rl(bA ? w[kQ + kRecDraw] : w[kRecDraw], lA);
+        const float lqd = __uint_as_float(rl(bA ? w[kQ + kRecLqd] : w[kRecLqd], lA));
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            const int k = b * 64 + lane;
+            if (k > G) continue;
+            const int32_t t = (k < A) ? a.tokens[(size_t)r * G + k] : (k == A ? draw : -1);
+            a.out_tok[(size_t)r * (G + 1) + k] = t;
+            if (a.out_lq)
+                a.out_lq[(size_t)r * (G + 1) + k] =
+                    (k < A) ? __uint_as_float(w[b * kQ + kRecLqx]) : (k == A ? lqd : nan);
+            if (k < G) {
+                if (a.out_cs)
+                    a.out_cs[(size_t)r * G + k] = (k < l) ? __uint_as_float(w[b * kQ + kRecCs]) : nan;
+                if (a.out_rs)
+                    a.out_rs[(size_t)r * G + k] = (k < l) ? __uint_as_float(w[b * kQ + kRecRs]) : nan;
+            }
+        }
+        if (lane == 0) a.out_n[r] = A;
+    }
+    if (lane == 0) atomic_store_u32(&a.cnt_r[r], 0u);
+}
+
+// Marks unit x finished; the request's last unit finalises it.
+__device__ __forceinline__ void unit_done(const VerifyArgs &a, const Item &x) {
+    uint32_t old = 0;
+    if (lane_id() == 0) old = atomic_add_u32(&a.cnt_r[x.r], 1u);
+    if (rl(old, 0) == (uint32_t)x.l) finalize_request(a, x.r, x.l);
+}
+
+// ---------------------------------------------------------------------------
+// unit combines (run by the wave whose arrival completed the unit)
+// ---------------------------------------------------------------------------
+
+// All C chunk statistics of unit x are published: row normalisers (published
+// first, for the TV items), then the unit's accept test or bonus draw.
+template <typename TT, typename TD, int N, int EPV>
+__device__ __forceinline__ void stats_combine(const VerifyArgs &a, const Item &x) {
+    const int lane = lane_id();
+    const int C = a.C, G = a.gamma;
+    const bool pair = is_pair(x);
+    uint64_t *nrm = a.nrm + (size_t)x.u * 4;
+    uint64_t *rec = a.rec + (size_t)x.u * kRecWords;
+    const float nan = __builtin_nanf("");
+    // the position's draft token and uniforms, loaded early
+    int xtok = 0;
+    float uacc = 0.0f, usm = 0.0f;
+    if (!a.tv_mode) {
+        if (pair) xtok = a.tokens[(size_t)x.r * G + x.i];
+        if (pair) uacc = a.ua[(size_t)x.r * G + x.i];
+        usm = a.us[(size_t)x.r * (G + 1) + x.i];
+    }
+    uint32_t w[kCB][4];
+    const bool want[4] = {true, true, pair, pair};
+    load_unit_words<4>(a.st1 + (size_t)x.u * C * 4, C, want, a.tag, a.ctl, w);
+
+    if (x.T == 0.0f) {
+        float vt = -kInf, vd = -kInf;
+        int it = 0x7fffffff, id = 0x7fffffff, bad = 0;
+#pragma unroll
+        for (int b = 0; b < kCB; ++b) {
+            if (b * 64 + lane < C) {
+                if (w[b][1] == 0xffffffffu) bad = 1;
+                else argmax_combine(vt, it, __uint_as_float(w[b][0]), (int)w[b][1]);
+                if (pair) {
+                    if (w[b][3] == 0xffffffffu) bad = 1;
+                    else argmax_combine(vd, id, __uint_as_float(w[b][2]), (int)w[b][3]);
+                }
+            }
+        }
+        wave_argmax(vt, it);
+        wave_argmax(vd, id);
+        bad = wave_max_i(bad);
+        const int gt = (!bad && vt > -kInf && vt < kInf && it != 0x7fffffff) ? it : -1;
+        const int gd = pair ? ((!bad && vd > -kInf && vd < kInf && id != 0x7fffffff) ? id : -1) : 0;
+        bool valid = gt >= 0 && gd >= 0;
+        if (a.tv_mode) {
+            if (!valid) {
+                write_invalid(a, x.r);
+            } else if (lane == 0) {
+                const float cv = (gt == gd) ? 1.0f : 0.0f;
+                a.out_cs[x.r] = cv;
+                if (a.out_rs) a.out_rs[x.r] = 1.0f - cv;
+            }
+            return;
+        }
+        bool acc = false;
+        if (pair) {
+            valid = valid && xtok >= 0 && xtok < a.V;
+            acc = xtok == gt;
+        }
+        const float cv = (gt == gd) ? 1.0f : 0.0f;
+        const uint32_t fl = (valid ? kFlagValid : 0u) | (acc ? kFlagAccept : 0u);
+        publish_n(rec, a.tag, 4, fl, __float_as_uint(0.0f), (uint32_t)gt, __float_as_uint(0.0f));
+        publish_n(rec + 4, a.tag, 2, __float_as_uint(pair ? cv : nan),
+                  __float_as_uint(pair ? 1.0f - cv : nan), 0u, 0u);
+        unit_done(a, x);
+        return;
+    }
+
+    // T > 0: per-lane online combine of (mu, S) over the lane's chunks, then
+    // across the wave: M = max mu, Z = sum S 2^(mu - M).
+    OnlineZ ot, od;
+#pragma unroll
+    for (int b = 0; b < kCB; ++b) {
+        if (b * 64 + lane < C) {
+            ot.add(__uint_as_float(w[b][0]), __uint_as_float(w[b][1]));
+            if (pair) od.add(__uint_as_float(w[b][2]), __uint_as_float(w[b][3]));
+        }
+    }
+    float Mt, Zt, Md = 0.0f, Zd = 1.0f;
+    ot.reduce(Mt, Zt);
+    if (pair) od.reduce(Md, Zd);
+    publish_n(nrm, a.tag, 4, __float_as_uint(Mt), __float_as_uint(Zt), __float_as_uint(Md),
+              __float_as_uint(Zd));
+
+    bool valid = finite_f(Mt) && Zt > 0.0f && finite_f(Zt);
+    if (pair) valid = valid && finite_f(Md) && Zd > 0.0f && finite_f(Zd);
+    if (a.tv_mode) {
+        publish_n(rec, a.tag, 1, valid ? kFlagValid : 0u, 0u, 0u, 0u);
+        return;
+    }
+    const float s = x.s;
+    const TT *trow = row_ptr<TT>(a.zt, x.r, a.tG, x.i, a.V);
+    if (pair) {
+        valid = valid && xtok >= 0 && xtok < a.V && uniform_ok(uacc) && uniform_ok(usm);
+        bool acc = false;
+        float lqx = nan;
+        if (valid) {
+            const float zx = load_one(trow, xtok);
+            const float dx = load_one(row_ptr<TD>(a.zd, x.r, a.dG, x.i, a.V), xtok);
+            const double lq2 = (double)zx * (double)s - (double)Mt;
+            const double lp2 = (double)dx * (double)s - (double)Md;
+            const double q = exp2(lq2) / (double)Zt;
+            const double p = exp2(lp2) / (double)Zd;
+            acc = q >= p || (double)uacc < q / p;
+            lqx = (float)(lq2 * kLn2 - log((double)Zt));
+        }
+        const uint32_t fl = (valid ? kFlagValid : 0u) | (acc ? kFlagAccept : 0u);
+        publish_n(rec, a.tag, 2, fl, __float_as_uint(lqx), 0u, 0u);
+        return;  // c*, Res and any residual draw come from the TV combine
+    }
+    // bonus unit: the draw from q of target row l
+    valid = valid && uniform_ok(usm);
+    int tok = -1;
+    float lqd = nan;
+    if (valid) {
+        float ztok;
+        tok = draw_from_q<TT, N, EPV, 4>(a, trow, w, s, Mt, Zt, usm, &ztok);
+        lqd = (float)(((double)ztok * (double)s - (double)Mt) * kLn2 - log((double)Zt));
+    }
+    publish_n(rec, a.tag, 4, valid ? kFlagValid : 0u, 0u, (uint32_t)tok, __float_as_uint(lqd));
+    unit_done(a, x);
+}
+
+// All C TV partials of pair unit x (T > 0) are published: c*, Res, and the
+// residual draw if the position was rejected.
+template <typename TT, typename TD, int N, int EPV>
+__device__ __forceinline__ void tv_combine(const VerifyArgs &a, const Item &x) {
+    const int lane = lane_id();
+    const int C = a.C, G = a.gamma;
+    uint64_t *rec = a.rec + (size_t)x.u * kRecWords;
+    float usm = 0.0f;
+    if (!a.tv_mode) usm = a.us[(size_t)x.r * (G + 1) + x.i];
+    // the unit's TV words, its record flags and its normalisers in one batch
+    uint32_t v2[kCB][2];
+    {
+        const uint64_t *p[2 * kCB + 2];
+        bool act[2 * kCB + 2];
+        uint32_t o[2 * kCB + 2];
+#pragma unroll
+        for (int b = 0; b < kCB; ++b)
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const int c = b * 64 + lane;
+                p[b * 2 + q] = a.st2 + ((size_t)x.u * C + c) * 2 + q;
+                act[b * 2 + q] = c < C;
+            }
+        p[2 * kCB] = rec + kRecFlags;
+        act[2 * kCB] = lane == 0;
+        p[2 * kCB + 1] = a.nrm + (size_t)x.u * 4 + (lane & 3);
+        act[2 * kCB + 1] = lane < 4;
+        await_batch<2 * kCB + 2>(p, act, a.tag, a.ctl, o);
+#pragma unroll
+        for (int b = 0; b < kCB; ++b) {
+            v2[b][0] = o[b * 2];
+            v2[b][1] = o[b * 2 + 1];
+        }
+        const uint32_t fl = rl(o[2 * kCB], 0);
+        const float Mt = __uint_as_float(rl(o[2 * kCB + 1], 0));
+        const float Zt = __uint_as_float(rl(o[2 * kCB + 1], 1));
+        const float Md = __uint_as_float(rl(o[2 * kCB + 1], 2));
+        const float Zd = __uint_as_float(rl(o[2 * kCB + 1], 3));
+        double cs = 0.0, rs = 0.0;
+#pragma unroll
+        for (int b = 0; b < kCB; ++b) {
+            cs += (double)__uint_as_float(v2[b][0]);
+            rs += (double)__uint_as_float(v2[b][1]);
+        }
+        cs = wave_sum(cs);
+        rs = wave_sum(rs);
+        const bool valid = fl & kFlagValid;
+        if (a.tv_mode) {
+            if (!valid) {
+                write_invalid(a, x.r);
+            } else if (lane == 0) {
+                a.out_cs[x.r] = (float)cs;
+                if (a.out_rs) a.out_rs[x.r] = (float)rs;
+            }
+            return;
+        }
+        int tok = -1;
+        float lqd = __builtin_nanf("");
+        if (valid && !(fl & kFlagAccept)) {
+            const float s = x.s;
+            const TT *trow = row_ptr<TT>(a.zt, x.r, a.tG, x.i, a.V);
+            const TD *drow = row_ptr<TD>(a.zd, x.r, a.dG, x.i, a.V);
+            float ztok = 0.0f;
+            if (rs > 0.0) {
+                // residual [q - p]_+: chunk masses, then one chunk in id order
+                double m[kCB];
+#pragma unroll
+                for (int b = 0; b < kCB; ++b) m[b] = (double)__uint_as_float(v2[b][1]);
+                double tin;
+                const int csel = select_chunk(C, (double)usm * rs, m, &tin);
+                const uint32_t s4 = await_lane(a.st1 + ((size_t)x.u * C + csel) * 4 + (lane & 3),
+                                               lane < 4, a.tag, a.ctl);
+                const float mut = __uint_as_float(rl(s4, 0)), mud = __uint_as_float(rl(s4, 2));
+                const PairScale ps =
+                    pair_scale(chunk_alpha(mut, Mt, Zt), chunk_alpha(mud, Md, Zd));
+                const float reft = exp_ref(mut), refd = exp_ref(mud);
+                const long c0 = (long)csel * kLanes * N;
+                const double te = (ps.unit > 0.0f) ? tin / (double)ps.unit : INFINITY;
+                tok = draw_in_chunk<N, EPV>(c0, te, [&](long e, float (&wv)[EPV]) {
+                    float zt[EPV], zd[EPV];
+                    load_ids<TT, EPV>(trow, e, a.V, zt);
+                    load_ids<TD, EPV>(drow, e, a.V, zd);
+#pragma unroll
+                    for (int q = 0; q < EPV; ++q) {
+                        const float et = ew(zt[q], s, reft) * ps.kt;
+                        const float mn = __builtin_elementwise_minimum(et, ew(zd[q], s, refd) * ps.kd);
+                        wv[q] = et - mn;
+                    }
+                });
+                ztok = load_one(trow, tok);
+            } else {
+                // no residual mass (rounding): draw from q of the same row
+                uint32_t w4[kCB][4];
+                const bool want4[4] = {true, true, false, false};
+                load_unit_words<4>(a.st1 + (size_t)x.u * C * 4, C, want4, a.tag, a.ctl, w4);
+                tok = draw_from_q<TT, N, EPV, 4>(a, trow, w4, s, Mt, Zt, usm, &ztok);
+            }
+            lqd = (float)(((double)ztok * (double)s - (double)Mt) * kLn2 - log((double)Zt));
+        }
+        publish_n(rec + kRecDraw, a.tag, 4, (uint32_t)tok, __float_as_uint(lqd),
+                  __float_as_uint((float)cs), __float_as_uint((float)rs));
+    }
+    unit_done(a, x);
+}
+
+// ---------------------------------------------------------------------------
+// the two persistent kernels
+// ---------------------------------------------------------------------------
 
 template <typename TT, typename TD, int N, int EPV>
 __device__ __forceinline__ void load_item(const VerifyArgs &a, const Item &x,
                                           RawChunk<TT, N, EPV> &rt, RawChunk<TD, N, EPV> &rd) {
-    const long c0 = chunk_start<N>(x.c);
-    rt.load((const TT *)a.zt + ((long)x.r * a.tG + x.i) * a.V, c0, a.V);
-    if (x.pair) rd.load((const TD *)a.zd + ((long)x.r * a.dG + x.i) * a.V, c0, a.V);
+    const long c0 = (long)x.c * kLanes * N;
+    rt.load(row_ptr<TT>(a.zt, x.r, a.tG, x.i, a.V), c0, a.V);
+    if (is_pair(x)) rd.load(row_ptr<TD>(a.zd, x.r, a.dG, x.i, a.V), c0, a.V);
 }
 
-// ---------------------------------------------------------------------------
-// kernel 1: per-chunk statistics (every needed row, read once from HBM)
-// ---------------------------------------------------------------------------
-
-// Chunk c of unit u (one wave): scaled max mu = fl(m s) and exp-sum
-// S = sum 2^(z s - mu) of the target row (and of the draft row for pairs)
-// -> st1[u * C + c] = (mu_t, S_t, mu_d, S_d); at T = 0 the argmax (value,
-// index; index 0xffffffff if a NaN was seen).
-template <bool PAIR, typename TT, typename TD, int N, int EPV>
-__device__ __forceinline__ void chunk_stats_t(const VerifyArgs &a, const Item &x,
-                                              const RawChunk<TT, N, EPV> &rt,
-                                              const RawChunk<TD, N, EPV> &rd) {
-    const int lane = threadIdx.x & 63;
-    float4 *out = a.st1 + (size_t)x.u * a.C + x.c;
+// Stats of item x: the chunk words (mu, S) per row, or the argmax words at
+// T = 0, published for the unit's combine and the TV pass.
+template <int N, int EPV, typename RT, typename RD>
+__device__ __forceinline__ void stats_item(const VerifyArgs &a, const Item &x, const RT &rt,
+                                           const RD &rd) {
+    const long c0 = (long)x.c * kLanes * N;
+    uint32_t w0, w1, w2 = 0, w3 = 0;
     if (x.T == 0.0f) {
-        const long c0 = chunk_start<N>(x.c);
-        float bt = -kInf, bd = -kInf;
-        int it = 0x7fffffff, id = 0x7fffffff, bad = 0;
+        float bv;
+        int bi, bad;
+        chunk_argmax<N, EPV>(rt, c0, bv, bi, bad);
+        w0 = __float_as_uint(bv);
+        w1 = bad ? 0xffffffffu : (uint32_t)bi;
+        if (is_pair(x)) {
+            chunk_argmax<N, EPV>(rd, c0, bv, bi, bad);
+            w2 = __float_as_uint(bv);
+            w3 = bad ? 0xffffffffu : (uint32_t)bi;
+        }
+    } else {
+        float e[N], mu, S;
+        chunk_exp<N>(rt, x.s, e, mu, S);
+        w0 = __float_as_uint(mu);
+        w1 = __float_as_uint(S);
+        if (is_pair(x)) {
+            chunk_exp<N>(rd, x.s, e, mu, S);
+            w2 = __float_as_uint(mu);
+            w3 = __float_as_uint(S);
+        }
+    }
+    publish_n(a.st1 + ((size_t)x.u * a.C + x.c) * 4, a.tag, 4, w0, w1, w2, w3);
+}
+
+// Item of unit u with chunk 0 (for the per-unit kernels); false if the unit
+// is not active (request malformed, or i > l_r).
+__device__ __forceinline__ bool unit_item(const VerifyArgs &a, long u, Item &x) {
+    if (u >= (long)a.R * a.UG) return false;
+    x.u = (int)u;
+    x.r = (int)(u / a.UG);
+    x.i = (int)(u % a.UG);
+    x.c = 0;
+    if (!request_ok(a, x.r, x.T, x.l) || x.i > x.l) return false;
+    x.s = x.T != 0.0f ? exp2_scale(x.T) : 0.0f;
+    return true;
+}
+
+// Kernel 1: every needed row streamed once from HBM, two items in flight per
+// wave; per item the chunk words.  Malformed requests get their outputs here.
+template <typename TT, typename TD, int N, int EPV>
+__global__ void __launch_bounds__(kBlock, 4) stats_kernel(VerifyArgs a) {
+    for (long r = wave_index(); r < a.R; r += wave_count()) {
+        float T;
+        int l;
+        if (!request_ok(a, (int)r, T, l)) write_invalid(a, (int)r);
+    }
+    const uint32_t work = (uint32_t)a.R * (uint32_t)a.UG * (uint32_t)a.C;
+    ItemCursor cur;
+    Item x0, x1;
+    RawChunk<TT, N, EPV> rt0, rt1;
+    RawChunk<TD, N, EPV> rd0, rd1;
+    bool h0 = cur.next(a, work, x0, false);
+    if (h0) load_item(a, x0, rt0, rd0);
+    bool h1 = h0 && cur.next(a, work, x1, false);
+    if (h1) load_item(a, x1, rt1, rd1);
+    while (h0) {
+        stats_item<N, EPV>(a, x0, rt0, rd0);
+        h0 = h1 && cur.next(a, work, x0, false);
+        if (h0) load_item(a, x0, rt0, rd0);
+        if (!h1) break;
+        stats_item<N, EPV>(a, x1, rt1, rd1);
+        h1 = h0 && cur.next(a, work, x1, false);
+        if (h1) load_item(a, x1, rt1, rd1);
+    }
+}
+
+// Kernel 2: one wave per active unit combines kernel 1's chunk words
+// (normalisers, accept test, bonus draw; everything at T = 0).
+template <typename TT, typename TD, int N, int EPV>
+__global__ void __launch_bounds__(kBlock) norm_kernel(VerifyArgs a) {
+    Item x;
+    if (unit_item(a, wave_index(), x)) stats_combine<TT, TD, N, EPV>(a, x);
+}
+
+// TV of pair item x at T > 0 (chunk re-read, from the Infinity Cache when the
+// rows fit there): with the chunk's words and the unit's normalisers from
+// kernel 1, the weights e = 2^(z s - mu) are rebuilt exactly as kernel 1 made
+// them, and sum min(p, q) and the residual mass of the chunk are published.
+template <int N, typename RT, typename RD>
+__device__ __forceinline__ void tv_item(const VerifyArgs &a, const Item &x, const RT &rt,
+                                        const RD &rd, uint32_t w8) {
+    // lanes 0..3: the chunk's words (mu_t, S_t, mu_d, S_d); 4..7: normalisers
+    const float mut = __uint_as_float(rl(w8, 0)), St = __uint_as_float(rl(w8, 1));
+    const float mud = __uint_as_float(rl(w8, 2));
+    const float Mt = __uint_as_float(rl(w8, 4)), Zt = __uint_as_float(rl(w8, 5));
+    const float Md = __uint_as_float(rl(w8, 6)), Zd = __uint_as_float(rl(w8, 7));
+    const float s = x.s;
+    const PairScale ps = pair_scale(chunk_alpha(mut, Mt, Zt), chunk_alpha(mud, Md, Zd));
+    const float reft = exp_ref(mut), refd = exp_ref(mud);
+    // min(p, q) in units of ps.unit, summed in the same slot order as the
+    // chunk's weight sum in kernel 1, so a chunk with q <= p everywhere has a
+    // residual of exactly 0
+    float acc = 0.0f, ssum;
+    if (ps.kt == 1.0f) {
+#pragma unroll
+        for (int k = 0; k < N; ++k)
+            acc += __builtin_elementwise_minimum(ew(rt.get(k), s, reft),
+                                                 ew(rd.get(k), s, refd) * ps.kd);
+        ssum = St;
+    } else {
+        float et[N];
 #pragma unroll
         for (int k = 0; k < N; ++k) {
-            const int e = (int)(c0 + ((long)(k / EPV) * kLanes + lane) * EPV + (k % EPV));
-            const float zt = rt.get(k);
-            if (zt != zt) bad |= 1;
-            if (zt > bt) { bt = zt; it = e; }
-            if constexpr (PAIR) {
-                const float zd = rd.get(k);
-                if (zd != zd) bad |= 2;
-                if (zd > bd) { bd = zd; id = e; }
-            }
+            et[k] = ew(rt.get(k), s, reft) * ps.kt;
+            acc += __builtin_elementwise_minimum(et[k], ew(rd.get(k), s, refd));
         }
-        wave_argmax(bt, it);
-        if constexpr (PAIR) wave_argmax(bd, id);
-        bad = wave_max_i(bad);
-        if (lane == 0)
-            *out = make_float4(bt, __uint_as_float((bad & 1) ? 0xffffffffu : (uint32_t)it), bd,
-                               __uint_as_float((bad & 2) ? 0xffffffffu : (uint32_t)id));
-        return;
+        ssum = wave_sum_f(lane_sum<N>(et));
     }
-    const float s = x.s;
-    float mt = -kInf, md = -kInf;
-#pragma unroll
-    for (int k = 0; k < N; ++k) {
-        mt = fmaxf(mt, rt.get(k));
-        if constexpr (PAIR) md = fmaxf(md, rd.get(k));
-    }
-    const float mut = wave_max(mt) * s;
-    const float mud = PAIR ? wave_max(md) * s : -kInf;
-    const float rt0 = exp_ref(mut), rd0 = exp_ref(mud);
-    float et = 0.0f, ed = 0.0f;
-#pragma unroll
-    for (int k = 0; k < N; ++k) {
-        et += exp_w(rt.get(k), s, rt0);
-        if constexpr (PAIR) ed += exp_w(rd.get(k), s, rd0);
-    }
-    const float st = wave_sum_f(et);
-    const float sd = PAIR ? wave_sum_f(ed) : 0.0f;
-    if (lane == 0) *out = make_float4(mut, st, mud, sd);
+    const float smin = wave_sum_f(acc);
+    const double cmin = (double)ps.unit * (double)smin;
+    const double cres = fmax((double)ps.unit * ((double)ssum - (double)smin), 0.0);
+    publish_n(a.st2 + ((size_t)x.u * a.C + x.c) * 2, a.tag, 2, __float_as_uint((float)cmin),
+              __float_as_uint((float)cres), 0u, 0u);
 }
 
+// Issues the loads of pair item x: its chunk of both rows, and (lanes 0..7)
+// the chunk's words and the unit's normalisers.
 template <typename TT, typename TD, int N, int EPV>
-__device__ __forceinline__ void chunk_stats(const VerifyArgs &a, const Item &x,
-                                            const RawChunk<TT, N, EPV> &rt,
-                                            const RawChunk<TD, N, EPV> &rd) {
-    if (x.pair) chunk_stats_t<true>(a, x, rt, rd);
-    else chunk_stats_t<false>(a, x, rt, rd);
+__device__ __forceinline__ uint64_t load_tv_item(const VerifyArgs &a, const Item &x,
+                                                 RawChunk<TT, N, EPV> &rt,
+                                                 RawChunk<TD, N, EPV> &rd) {
+    const int lane = lane_id();
+    const uint64_t *p = (lane < 4) ? a.st1 + ((size_t)x.u * a.C + x.c) * 4 + lane
+                                   : a.nrm + (size_t)x.u * 4 + (lane & 3);
+    const uint64_t w = (lane < 8) ? ld_word(p) : 0;
+    load_item(a, x, rt, rd);
+    return w;
 }
 
-// Persistent loop of one wave over its items with a ring of kRing register
-// buffers: while the wave reduces item k, the loads of items k+1 .. k+kRing-1
-// are in flight.  Op::apply(a, item, target chunk, draft chunk) is the
-// per-item work.
-constexpr int kRing = SV_RING;
-
-template <typename Op, typename TT, typename TD, int N, int EPV>
-__device__ __forceinline__ void run_items(const VerifyArgs &a, bool pairs_only) {
-    const long work = (long)a.R * a.UG * a.C;
+// Kernel 3: the TV pass over the pair items at T > 0, two items in flight
+// per wave.
+template <typename TT, typename TD, int N, int EPV>
+__global__ void __launch_bounds__(kBlock, 4) tv_kernel(VerifyArgs a) {
+    const int lane = lane_id();
+    const uint32_t work = (uint32_t)a.R * (uint32_t)a.UG * (uint32_t)a.C;
     ItemCursor cur;
-    Item x[kRing];
-    bool has[kRing];
-    RawChunk<TT, N, EPV> t[kRing];
-    RawChunk<TD, N, EPV> d[kRing];
-#pragma unroll
-    for (int k = 0; k < kRing - 1; ++k) {
-        has[k] = cur.next(a, work, x[k], pairs_only);
-        if (has[k]) load_item(a, x[k], t[k], d[k]);
-    }
-    has[kRing - 1] = false;
-    for (;;) {
-#pragma unroll
-        for (int k = 0; k < kRing; ++k) {
-            const int pf = (k + kRing - 1) % kRing;
-            has[pf] = has[(pf + kRing - 1) % kRing] && cur.next(a, work, x[pf], pairs_only);
-            __asm__ volatile("" ::: "memory");
-            if (has[pf]) load_item(a, x[pf], t[pf], d[pf]);
-            if (!has[k]) return;
-            Op::apply(a, x[k], t[k], d[k]);
-        }
-    }
-}
-
-struct StatsOp {
-    template <typename TT, typename TD, int N, int EPV>
-    __device__ __forceinline__ static void apply(const VerifyArgs &a, const Item &x,
-                                                 const RawChunk<TT, N, EPV> &rt,
-                                                 const RawChunk<TD, N, EPV> &rd) {
-        chunk_stats<TT, TD, N, EPV>(a, x, rt, rd);
-    }
-};
-
-// Kernel 1, a persistent grid of independent waves.
-template <typename TT, typename TD, int N, int EPV>
-__global__ void __launch_bounds__(kBlock) stats_kernel(VerifyArgs a) {
-    run_items<StatsOp, TT, TD, N, EPV>(a, false);
-}
-
-// ---------------------------------------------------------------------------
-// kernel 2: sum min(p, q) and sum [q - p]_+ per chunk, then the finalisers
-// ---------------------------------------------------------------------------
-
-struct FinalState {
-    float Mt[kMaxGamma + 1], Md[kMaxGamma];
-    double Zt[kMaxGamma + 1], Zd[kMaxGamma];
-    double cs[kMaxGamma], rs[kMaxGamma];
-    int gt[kMaxGamma + 1], gd[kMaxGamma];
-    int rowok[kMaxGamma + 1];
-    float lq[kMaxGamma + 1];
-    int A, ok, csel, resid, token;
-    double tsel;
-    float ztok;
-};
-
-// Row normalisers of unit u from kernel 1's chunk statistics, by one wave
-// (lanes over chunks): the scaled maxima muM and Z = sum_c S_c 2^(mu_c - muM).
-__device__ void wave_row_stats(const VerifyArgs &a, int u, bool pair, float &Mt, double &Zt,
-                               float &Md, double &Zd) {
-    const int lane = threadIdx.x & 63;
-    const float4 *st = a.st1 + (size_t)u * a.C;
-    float mt = -kInf, md = -kInf;
-    for (int c = lane; c < a.C; c += 64) {
-        const float4 v = st[c];
-        mt = fmaxf(mt, v.x);
-        if (pair) md = fmaxf(md, v.z);
-    }
-    Mt = wave_max(mt);
-    Md = wave_max(md);
-    double zt = 0.0, zd = 0.0;
-    for (int c = lane; c < a.C; c += 64) {
-        const float4 v = st[c];
-        zt += chunk_weight(v.x, v.y, Mt);
-        if (pair) zd += chunk_weight(v.z, v.w, Md);
-    }
-    Zt = wave_sum(zt);
-    Zd = wave_sum(zd);
-}
-
-// Argmax of a row (and of its draft row) from kernel 1's words (T = 0), by one
-// wave; -1 for an invalid row.
-__device__ void wave_row_argmax(const VerifyArgs &a, int u, bool pair, int &gt, int &gd) {
-    const int lane = threadIdx.x & 63;
-    const float4 *st = a.st1 + (size_t)u * a.C;
-    float vt = -kInf, vd = -kInf;
-    int it = 0x7fffffff, id = 0x7fffffff, bad = 0;
-    for (int c = lane; c < a.C; c += 64) {
-        const float4 v = st[c];
-        const uint32_t ti = __float_as_uint(v.y), di = __float_as_uint(v.w);
-        if (ti == 0xffffffffu) bad = 1;
-        else argmax_combine(vt, it, v.x, (int)ti);
-        if (pair) {
-            if (di == 0xffffffffu) bad = 1;
-            else argmax_combine(vd, id, v.z, (int)di);
-        }
-    }
-    wave_argmax(vt, it);
-    wave_argmax(vd, id);
-    bad = wave_max_i(bad);
-    gt = (!bad && vt < kInf && it != 0x7fffffff) ? it : -1;
-    gd = pair ? ((!bad && vd < kInf && id != 0x7fffffff) ? id : -1) : 0;
-}
-
-// Inverse-CDF draw inside chunk c of row j of request r by the workgroup (cmt,
-// cmd: the chunk's exponent references, at, ad: its probability scales): the
-// first logit (ascending id) whose running weight exceeds tsel, with weights
-// q - min(p, q) (resid) or q, computed exactly as kernel 2 computed them.
-// Thread t owns logits [c0 + t P, c0 + (t+1) P), P = 64 N / 256; a block scan
-// finds the owner, which walks its logits again.  Clamps to the chunk's last
-// positive weight.
-template <typename TT, typename TD, int N, int EPV>
-__device__ int draw_in_chunk(const VerifyArgs &a, int r, int j, int c, bool resid, float s,
-                             float cmt, float cmd, float at, float ad, double tsel, float *ztok,
-                             BlockScratch &bs, FinalState &f) {
-    constexpr int PER = kLanes * N / kBlock;          // logits per thread
-    constexpr int VW = (EPV < PER) ? EPV : PER;       // vector width of its loads
-    const int tid = threadIdx.x;
-    const int V = a.V;
-    const long c0 = chunk_start<N>(c);
-    const long e0 = c0 + (long)tid * PER;
-    const TT *trow = (const TT *)a.zt + ((long)r * a.tG + j) * V;
-    const TD *drow = resid ? (const TD *)a.zd + ((long)r * a.dG + j) * V : nullptr;
-    auto weights = [&](long e, float *w, float *zo) {
-        float zt[VW], zd[VW];
-        if (e < V) {
-            VecLoad<TT, VW>::run(trow, e, zt);
-            if (resid) VecLoad<TD, VW>::run(drow, e, zd);
-        } else {
-#pragma unroll
-            for (int q = 0; q < VW; ++q) zt[q] = zd[q] = -kInf;
-        }
-#pragma unroll
-        for (int q = 0; q < VW; ++q) {
-            const float et = exp_w(zt[q], s, cmt);
-            if (resid) {
-                const float ed = exp_w(zd[q], s, cmd);
-                float qv, mn;
-                pq_weights(et, ed, at, ad, qv, mn);
-                w[q] = qv - mn;
-            } else {
-                w[q] = __fmul_rn(et, at);
-            }
-            zo[q] = zt[q];
-        }
+    Item x0, x1;
+    uint64_t w0 = 0, w1 = 0;
+    RawChunk<TT, N, EPV> rt0, rt1;
+    RawChunk<TD, N, EPV> rd0, rd1;
+    bool h0 = cur.next(a, work, x0, true);
+    if (h0) w0 = load_tv_item(a, x0, rt0, rd0);
+    bool h1 = h0 && cur.next(a, work, x1, true);
+    if (h1) w1 = load_tv_item(a, x1, rt1, rd1);
+    // kernels 1 and 2 wrote the words before this launch: a stale tag could
+    // only come from an earlier call, so the wait never spins
+    auto words = [&](const Item &it, uint64_t w) -> uint32_t {
+        if (!__ballot(lane < 8 && (uint32_t)(w >> 32) != a.tag)) return (uint32_t)w;
+        const uint64_t *p = (lane < 4) ? a.st1 + ((size_t)it.u * a.C + it.c) * 4 + lane
+                                       : a.nrm + (size_t)it.u * 4 + (lane & 3);
+        return await_lane(p, lane < 8, a.tag, a.ctl);
     };
-    double tot = 0.0;
-    int lastpos = -1;
-#pragma unroll
-    for (int k = 0; k < PER; k += VW) {
-        float w[VW], z[VW];
-        weights(e0 + k, w, z);
-#pragma unroll
-        for (int q = 0; q < VW; ++q) {
-            tot += (double)w[q];
-            if (w[q] > 0.0f) lastpos = k + q;
-        }
+    while (h0) {
+        tv_item<N>(a, x0, rt0, rd0, words(x0, w0));
+        h0 = h1 && cur.next(a, work, x0, true);
+        if (h0) w0 = load_tv_item(a, x0, rt0, rd0);
+        if (!h1) break;
+        tv_item<N>(a, x1, rt1, rd1, words(x1, w1));
+        h1 = h0 && cur.next(a, work, x1, true);
+        if (h1) w1 = load_tv_item(a, x1, rt1, rd1);
     }
-    double all;
-    const double excl = block_exclusive_scan(tot, &all, bs);
-    const int owner = block_min_i((tot > 0.0 && excl + tot > tsel) ? tid : 0x7fffffff, bs);
-    if (owner == 0x7fffffff) {
-        // tsel at or past the chunk's total (rounding): last positive weight;
-        // if every fp32 weight underflowed, the chunk's first logit
-        const int last = block_max_i(lastpos >= 0 ? (int)(e0 + lastpos) : -1, bs);
-        const int tok = last >= 0 ? last : (int)c0;
-        *ztok = load_one(trow, tok);
-        return tok;
-    }
-    if (tid == owner) {
-        double cum = excl;
-        int tok = -1;
-        float zz = 0.0f;
-        for (int k = 0; k < PER && tok < 0; k += VW) {
-            float w[VW], z[VW];
-            weights(e0 + k, w, z);
-#pragma unroll
-            for (int q = 0; q < VW; ++q) {
-                cum += (double)w[q];
-                if (tok < 0 && cum > tsel) {
-                    tok = (int)(e0 + k + q);
-                    zz = z[q];
-                }
-            }
-        }
-        if (tok < 0) {  // tot > 0, so lastpos >= 0
-            tok = (int)(e0 + lastpos);
-            zz = load_one(trow, tok);
-        }
-        f.token = tok;
-        f.ztok = zz;
-    }
-    __syncthreads();
-    *ztok = f.ztok;
-    return f.token;
 }
 
-// Final outputs of request r: accept tests, prefix survival, the residual or
-// bonus draw and the commit (or c* / Res for independent row pairs).  Every
-// input it reads was written by kernels 1 and 2 before this launch.
+// Kernel 4: one wave per pair unit at T > 0 sums its TV words into c* and
+// Res and makes the residual draw if the position was rejected; the wave that
+// finishes a request's last unit writes the request's outputs.
 template <typename TT, typename TD, int N, int EPV>
-__device__ void finalize(const VerifyArgs &a, const Item &x, BlockScratch &bs, FinalState &f) {
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int G = a.gamma, V = a.V, C = a.C, r = x.r, l = x.l;
-    const float T = x.T;
-    const float nan = __builtin_nanf("");
-    const int nrows = a.tv_mode ? 1 : l + 1;
-    const int npairs = a.tv_mode ? 1 : l;
-    const int u0 = r * a.UG;
-    if (tid == 0) f.ok = 1;
-    __syncthreads();
-
-    if (T == 0.0f) {
-        for (int i = wave; i < nrows; i += kWaves) {
-            const RowNorm nm = a.nrm[u0 + i];
-            const int gt = nm.gt, gd = nm.gd;
-            if (lane == 0) {
-                f.gt[i] = gt;
-                if (i < l) f.gd[i] = gd;
-                if (gt < 0 || (i < l && gd < 0)) f.ok = 0;
-            }
-        }
-        __syncthreads();
-        if (wave != 0) return;
-        if (!f.ok) { if (lane == 0) write_invalid(a, r); return; }
-        if (a.tv_mode) {
-            if (lane == 0) {
-                const float cv = (f.gt[0] == f.gd[0]) ? 1.0f : 0.0f;
-                a.out_cs[r] = cv;
-                if (a.out_rs) a.out_rs[r] = 1.0f - cv;
-            }
-            return;
-        }
-        bool bad = false, acc = false;
-        if (lane < l) {
-            const int xv = a.tokens[(size_t)r * G + lane];
-            bad = xv < 0 || xv >= V;
-            acc = !bad && xv == f.gt[lane];
-        }
-        const uint64_t badm = __ballot(bad), accm = __ballot(acc);
-        if (badm) { if (lane == 0) write_invalid(a, r); return; }
-        int A = (~accm == 0) ? 64 : __builtin_ctzll(~accm);
-        if (A > l) A = l;
-        const int gA = f.gt[A];
-        int32_t *tok = a.out_tok + (size_t)r * (G + 1);
-        for (int k = lane; k <= G; k += 64) {
-            tok[k] = (k < A) ? a.tokens[(size_t)r * G + k] : (k == A ? gA : -1);
-            if (a.out_lq) a.out_lq[(size_t)r * (G + 1) + k] = (k <= A) ? 0.0f : nan;
-        }
-        for (int i = lane; i < G; i += 64) {
-            const float cv = (i < l) ? ((f.gt[i] == f.gd[i]) ? 1.0f : 0.0f) : nan;
-            if (a.out_cs) a.out_cs[(size_t)r * G + i] = cv;
-            if (a.out_rs) a.out_rs[(size_t)r * G + i] = (i < l) ? 1.0f - cv : nan;
-        }
-        if (lane == 0) a.out_n[r] = A;
-        return;
-    }
-
-    // ---- T > 0: row normalisers and c* / Res, one row per wave -------------
-    const float s = exp2_scale(T);
-    for (int i = wave; i < nrows; i += kWaves) {
-        const bool pair = i < l;
-        const RowNorm nm = a.nrm[u0 + i];
-        const float Mt = nm.Mt, Md = nm.Md;
-        const double Zt = nm.Zt, Zd = nm.Zd;
-        double dm = 0.0, dr = 0.0;
-        if (pair) {
-            for (int c = lane; c < C; c += 64) {
-                const float2 w = a.st2[(size_t)(u0 + i) * C + c];
-                dm += (double)w.x;
-                dr += (double)w.y;
-            }
-            dm = wave_sum(dm);
-            dr = wave_sum(dr);
-        }
-        if (lane == 0) {
-            f.Mt[i] = Mt;
-            f.Zt[i] = Zt;
-            bool ok = (Mt > -kInf) && (Mt < kInf) && (Zt > 0.0) && (Zt < 1e300);
-            if (pair) {
-                f.Md[i] = Md;
-                f.Zd[i] = Zd;
-                f.cs[i] = dm;
-                f.rs[i] = dr;
-                ok = ok && (Md > -kInf) && (Md < kInf) && (Zd > 0.0) && (Zd < 1e300);
-            }
-            if (!ok) f.ok = 0;
-        }
-    }
-    __syncthreads();
-    if (a.tv_mode) {
-        if (tid == 0) {
-            if (!f.ok) { write_invalid(a, r); return; }
-            a.out_cs[r] = (float)f.cs[0];
-            if (a.out_rs) a.out_rs[r] = (float)f.rs[0];
-        }
-        return;
-    }
-
-    // ---- accept tests (lane i tests position i), prefix survival by ballot --
-    if (wave == 0) {
-        bool bad = !f.ok, acc = false;
-        for (int j2 = lane; j2 <= l; j2 += 64)
-            bad = bad || !uniform_ok(a.us[(size_t)r * (G + 1) + j2]);
-        if (lane < l) {
-            const int xv = a.tokens[(size_t)r * G + lane];
-            const float u = a.ua[(size_t)r * G + lane];
-            bad = bad || xv < 0 || xv >= V || !uniform_ok(u);
-            if (!bad) {
-                const TT *trow = (const TT *)a.zt + ((long)r * a.tG + lane) * V;
-                const TD *drow = (const TD *)a.zd + ((long)r * a.dG + lane) * V;
-                const double lq = (double)load_one(trow, xv) * (double)s - (double)f.Mt[lane];
-                const double lp = (double)load_one(drow, xv) * (double)s - (double)f.Md[lane];
-                const double q = exp2(lq) / f.Zt[lane];
-                const double p = exp2(lp) / f.Zd[lane];
-                acc = q >= p || (double)u < q / p;
-                f.lq[lane] = (float)(lq * kLn2 - log(f.Zt[lane]));
-            }
-        }
-        const uint64_t badm = __ballot(bad), accm = __ballot(acc);
-        if (lane == 0) {
-            const int A = (~accm == 0) ? 64 : __builtin_ctzll(~accm);
-            f.A = A > l ? l : A;
-            f.ok = badm == 0;
-        }
-    }
-    __syncthreads();
-    if (!f.ok) {
-        if (tid == 0) write_invalid(a, r);
-        return;
-    }
-    const int A = f.A, j = A;
-    const int uj = u0 + j;
-    const float Mt = f.Mt[j];
-    const double Zt = f.Zt[j];
-
-    // ---- chunk masses of the final draw and the chunk holding u * W --------
-    if (wave == 0) {
-        bool resid = A < l;
-        double W = 0.0;
-        if (resid) {
-            for (int c = lane; c < C; c += 64) W += (double)a.st2[(size_t)uj * C + c].y;
-            W = wave_sum(W);
-            if (!(W > 0.0)) resid = false;  // no residual mass (rounding): draw from q
-        }
-        if (!resid) {
-            W = 0.0;
-            for (int c = lane; c < C; c += 64) {
-                const float4 v = a.st1[(size_t)uj * C + c];
-                W += chunk_weight(v.x, v.y, Mt) / Zt;
-            }
-            W = wave_sum(W);
-        }
-        const double t = (double)a.us[(size_t)r * (G + 1) + j] * W;
-        int csel = -1, clast = -1;
-        double tsel = 0.0, run = 0.0;
-        for (int cb = 0; cb < C && csel < 0; cb += 64) {
-            const int c = cb + lane;
-            double wc = 0.0;
-            if (c < C) {
-                if (resid) {
-                    wc = (double)a.st2[(size_t)uj * C + c].y;
-                } else {
-                    const float4 v = a.st1[(size_t)uj * C + c];
-                    wc = chunk_weight(v.x, v.y, Mt) / Zt;
-                }
-            }
-            double incl = wc;
-#pragma unroll
-            for (int o = 1; o < 64; o <<= 1) {
-                const double nb = __shfl_up(incl, o, 64);
-                if (lane >= o) incl += nb;
-            }
-            const double excl = run + incl - wc;
-            const uint64_t hit = __ballot(c < C && excl + wc > t);
-            const uint64_t pos = __ballot(c < C && wc > 0.0);
-            if (pos) clast = cb + 63 - __builtin_clzll(pos);
-            if (hit) {
-                csel = cb + __builtin_ctzll(hit);
-                tsel = __shfl(t - excl, csel - cb, 64);
-            }
-            run += __shfl(incl, 63, 64);
-        }
-        if (csel < 0) {  // t at or past the total (rounding): last chunk with mass
-            csel = clast >= 0 ? clast : 0;
-            tsel = INFINITY;
-        }
-        if (lane == 0) {
-            f.csel = csel;
-            f.tsel = tsel;
-            f.resid = resid;
-        }
-    }
-    __syncthreads();
-    const int csel = f.csel;
-    const bool resid = f.resid;
-    const float4 cst = a.st1[(size_t)uj * C + csel];
-    const float cmt = exp_ref(cst.x);
-    const float cmd = resid ? exp_ref(cst.z) : 0.0f;
-    const float at = chunk_scale(cst.x, Mt, Zt);
-    const float ad = resid ? chunk_scale(cst.z, f.Md[j], f.Zd[j]) : 0.0f;
-    float ztok;
-    const int token = draw_in_chunk<TT, TD, N, EPV>(a, r, j, csel, resid, s, cmt, cmd, at, ad,
-                                                    f.tsel, &ztok, bs, f);
-    if (wave == 0) {
-        const float lqj = (float)(((double)ztok * (double)s - (double)Mt) * kLn2 - log(Zt));
-        int32_t *tok = a.out_tok + (size_t)r * (G + 1);
-        for (int k = lane; k <= G; k += 64) {
-            tok[k] = (k < A) ? a.tokens[(size_t)r * G + k] : (k == A ? token : -1);
-            if (a.out_lq)
-                a.out_lq[(size_t)r * (G + 1) + k] = (k < A) ? f.lq[k] : (k == A ? lqj : nan);
-        }
-        for (int i = lane; i < G; i += 64) {
-            if (a.out_cs) a.out_cs[(size_t)r * G + i] = (i < l) ? (float)f.cs[i] : nan;
-            if (a.out_rs) a.out_rs[(size_t)r * G + i] = (i < l) ? (float)f.rs[i] : nan;
-        }
-        if (lane == 0) a.out_n[r] = A;
-    }
-}
-
-// Kernel 2 work for one pair item at T > 0 (one wave): sum min(p, q) and
-// sum [q - p]_+ over the chunk, with the row normalisers of norm_kernel
-// -> st2[u * C + c].
-template <typename TT, typename TD, int N, int EPV>
-__device__ __forceinline__ void chunk_tv(const VerifyArgs &a, const Item &x,
-                                         const RawChunk<TT, N, EPV> &rt,
-                                         const RawChunk<TD, N, EPV> &rd) {
-    const int lane = threadIdx.x & 63;
-    const float s = x.s;
-    const RowNorm nm = a.nrm[x.u];
-    const float4 own = a.st1[(size_t)x.u * a.C + x.c];
-    const float at = chunk_scale(own.x, nm.Mt, nm.Zt);
-    const float ad = chunk_scale(own.z, nm.Md, nm.Zd);
-    const float rt0 = exp_ref(own.x), rd0 = exp_ref(own.z);
-    float smin = 0.0f, sres = 0.0f;
-#pragma unroll
-    for (int k = 0; k < N; ++k) {
-        const float et = exp_w(rt.get(k), s, rt0);
-        const float ed = exp_w(rd.get(k), s, rd0);
-        float q, mn;
-        pq_weights(et, ed, at, ad, q, mn);
-        smin += mn;
-        sres += q - mn;
-    }
-    const float dm = wave_sum_f(smin);
-    const float dr = wave_sum_f(sres);
-    if (lane == 0) a.st2[(size_t)x.u * a.C + x.c] = make_float2(dm, dr);
-}
-
-struct TvOp {
-    template <typename TT, typename TD, int N, int EPV>
-    __device__ __forceinline__ static void apply(const VerifyArgs &a, const Item &x,
-                                                 const RawChunk<TT, N, EPV> &rt,
-                                                 const RawChunk<TD, N, EPV> &rd) {
-        chunk_tv<TT, TD, N, EPV>(a, x, rt, rd);
-    }
-};
-
-// Kernel 2, a persistent grid of independent waves over the pair items at
-// T > 0 with the same load ring as kernel 1.  The rows it re-reads were
-// streamed by kernel 1 moments before, so they come from the 256 MB Infinity
-// Cache.
-template <typename TT, typename TD, int N, int EPV>
-__global__ void __launch_bounds__(kBlock) tv_kernel(VerifyArgs a) {
-    run_items<TvOp, TT, TD, N, EPV>(a, true);
-}
-
-// Row normalisers (T > 0) or argmaxes (T = 0) of every active unit, one wave
-// per unit, from kernel 1's chunk statistics.
-__global__ void __launch_bounds__(kBlock) norm_kernel(VerifyArgs a) {
-    const long u = wave_index();
-    if (u >= (long)a.R * a.UG) return;
-    const int r = (int)(u / a.UG), i = (int)(u % a.UG);
-    const float T = a.temp[r];
-    const int l = a.tv_mode ? 1 : a.vlen[r];
-    if (!(temperature_ok(T) && l >= 0 && l <= a.gamma && i <= l)) return;
-    const bool pair = i < l;
-    RowNorm nm;
-    if (T == 0.0f) {
-        wave_row_argmax(a, (int)u, pair, nm.gt, nm.gd);
-        nm.Mt = nm.Md = 0.0f;
-        nm.Zt = nm.Zd = 0.0;
-    } else {
-        wave_row_stats(a, (int)u, pair, nm.Mt, nm.Zt, nm.Md, nm.Zd);
-        nm.gt = nm.gd = 0;
-    }
-    if ((threadIdx.x & 63) == 0) a.nrm[u] = nm;
-}
-
-// Kernel 3: one workgroup per request writes its final outputs (or the
-// invalid-request outputs).
-template <typename TT, typename TD, int N, int EPV>
-__global__ void __launch_bounds__(kBlock) finalize_kernel(VerifyArgs a) {
-    __shared__ BlockScratch bs;
-    __shared__ FinalState f;
+__global__ void __launch_bounds__(kBlock) tv_combine_kernel(VerifyArgs a) {
     Item x;
-    x.r = blockIdx.x;
-    x.T = a.temp[x.r];
-    x.l = a.tv_mode ? 1 : a.vlen[x.r];
-    if (!(temperature_ok(x.T) && x.l >= 0 && x.l <= a.gamma)) {
-        if (threadIdx.x == 0) write_invalid(a, x.r);
-        return;
-    }
-    finalize<TT, TD, N, EPV>(a, x, bs, f);
+    if (unit_item(a, wave_index(), x) && is_tv(x)) tv_combine<TT, TD, N, EPV>(a, x);
 }
 
 __global__ void zero_fill_kernel(uint32_t *p, size_t n_words) {
@@ -888,141 +1163,177 @@ __global__ void clear_status_kernel(Control *ctl) { atomic_store_u32(&ctl->statu
 
 namespace {
 
-constexpr long kTargetItems = 65536;   // chunk items wanted: several per resident wave
-
 struct Plan {
-    int N;           // logits per thread per row
+    int N;           // logits per lane per row
     int C;           // chunks per row
     long units;
-    size_t off_st1, off_st2, off_nrm, bytes;
+    // counters first (they must read zero at launch), then tagged words
+    size_t off_cr, off_data, off_st1, off_st2, off_nrm, off_rec, bytes;
 };
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-int forced_n() {
-    static int v = -1;
-    if (v < 0) {
-        const char *e = getenv("SPECVERIFY_CHUNK_N");
-        v = e ? atoi(e) : 0;
-        if (v != 4 && v != 8 && v != 16 && v != 32) v = 0;
-    }
-    return v;
+// kN logits per lane and row: the weights of both rows then stay in registers
+// at four waves per SIMD.
+constexpr int kN = 16;
+
+bool make_plan(long R, long units_per_req, long V, Plan &p) {
+    const int N = kN;
+    const long C = (V + (long)kLanes * N - 1) / ((long)kLanes * N);
+    if (C > kCB * 64) return false;  // the combines hold a unit's chunk words in registers
+    const long units = R * units_per_req;
+    if (units * C > 0x7fffffffL) return false;
+    p.N = N;
+    p.C = (int)C;
+    p.units = units;
+    p.off_cr = sizeof(Control);
+    p.off_data = round_up(p.off_cr + 4 * (size_t)R, 256);
+    p.off_st1 = p.off_data;
+    p.off_st2 = round_up(p.off_st1 + 32 * (size_t)units * C, 256);
+    p.off_nrm = round_up(p.off_st2 + 16 * (size_t)units * C, 256);
+    p.off_rec = round_up(p.off_nrm + 32 * (size_t)units, 256);
+    p.bytes = round_up(p.off_rec + 8 * kRecWords * (size_t)units, 256);
+    return true;
 }
 
-// Largest per-thread chunk that still gives enough workgroups; the smallest
-// one otherwise.  Returns false if V needs more than kMaxChunks chunks.
-bool make_plan(long R, long units_per_req, long V, Plan &p) {
-    static const int kN[] = {32, 16, 8, 4};
-    const long units = R * units_per_req;
-    int chosen = -1, chosen_C = 0;
-    for (int N : kN) {
-        const long C = (V + (long)kLanes * N - 1) / ((long)kLanes * N);
-        if (C > kMaxChunks) continue;
-        chosen = N;
-        chosen_C = (int)C;
-        if (forced_n() == N) break;
-        if (!forced_n() && units * C >= kTargetItems) break;
-    }
-    if (chosen < 0) return false;
-    if (units * (long)chosen_C > 0x7fffffffL) return false;
-    p.N = chosen;
-    p.C = chosen_C;
-    p.units = units;
-    p.off_st1 = sizeof(Control);
-    p.off_st2 = round_up(p.off_st1 + sizeof(float4) * (size_t)units * chosen_C, 256);
-    p.off_nrm = round_up(p.off_st2 + sizeof(float2) * (size_t)units * chosen_C, 256);
-    p.bytes = round_up(p.off_nrm + sizeof(RowNorm) * (size_t)units, 256);
-    return true;
+// Host-side record of how much of each workspace is known to read zero
+// outside the control block: the whole buffer after spec_workspace_init; the
+// counter area of the last call after it (its counters end at zero, the
+// tagged words after them hold data).  A call whose counters reach past that
+// prefix first clears the difference on its stream.
+struct CleanPrefix {
+    uintptr_t ws;
+    size_t bytes;
+};
+std::mutex g_clean_mu;
+std::vector<CleanPrefix> g_clean;
+
+size_t clean_prefix(const void *ws) {
+    std::lock_guard<std::mutex> lock(g_clean_mu);
+    for (const CleanPrefix &c : g_clean)
+        if (c.ws == (uintptr_t)ws) return c.bytes;
+    return sizeof(Control);
+}
+}  // namespace
+
+void note_workspace_clean(const void *ws, size_t bytes) {
+    std::lock_guard<std::mutex> lock(g_clean_mu);
+    for (CleanPrefix &c : g_clean)
+        if (c.ws == (uintptr_t)ws) {
+            c.bytes = bytes;
+            return;
+        }
+    g_clean.push_back(CleanPrefix{(uintptr_t)ws, bytes});
+}
+
+namespace {
+
+size_t plan_bytes(long R, long upr, long V) {
+    Plan p;
+    return make_plan(R, upr, V, p) ? p.bytes : 0;
 }
 
 bool dtype_ok(int d) { return d == SPEC_F32 || d == SPEC_BF16; }
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
-// Workgroups of a persistent grid: the kernel's resident capacity on the
-// current device (cached per kernel and device), at most `items`.
-long grid_for(const void *kernel, long items) {
+// Resident workgroups of a kernel on the current device (cached).
+long resident_blocks(const void *kernel) {
     struct Entry { const void *k; int dev; long cap; };
     static std::mutex mu;
     static std::vector<Entry> cache;
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return items;
-    long cap = 0;
-    {
-        std::lock_guard<std::mutex> lock(mu);
-        for (const Entry &e : cache)
-            if (e.k == kernel && e.dev == dev) cap = e.cap;
-        if (cap == 0) {
-            int nb = 0, ncu = 0;
-            if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kernel, kBlock, 0) != hipSuccess ||
-                hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-                return items;
-            cap = (long)(nb > 0 ? nb : 1) * (ncu > 0 ? ncu : 1);
-            cache.push_back(Entry{kernel, dev, cap});
-        }
-    }
-    return items < cap ? items : cap;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    std::lock_guard<std::mutex> lock(mu);
+    for (const Entry &e : cache)
+        if (e.k == kernel && e.dev == dev) return e.cap;
+    int nb = 0, ncu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kernel, kBlock, 0) != hipSuccess ||
+        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return 0;
+    const long cap = (long)nb * ncu;
+    cache.push_back(Entry{kernel, dev, cap});
+    return cap;
+}
+
+uint32_t next_tag() {
+    static std::atomic<uint32_t> counter{0};
+    return (counter.fetch_add(1u) + 1u) | 0x80000000u;
+}
+
+// Persistent grid of kernel k: its resident capacity, at most one wave per item.
+long persistent_grid(const void *k, long items) {
+    const long cap = resident_blocks(k);
+    const long want = (items + kWaves - 1) / kWaves;
+    if (cap <= 0) return want > 0 ? want : 1;
+    const long g = want < cap ? want : cap;
+    return g > 0 ? g : 1;
 }
 
 template <typename TT, typename TD, int N, int EPV>
-int launch_kernels(const VerifyArgs &a, long items, hipStream_t st) {
+int launch_kernels(VerifyArgs a, hipStream_t st) {
     const void *k1 = reinterpret_cast<const void *>(&stats_kernel<TT, TD, N, EPV>);
-    const void *k2 = reinterpret_cast<const void *>(&tv_kernel<TT, TD, N, EPV>);
-    const long wgs = (items + kWaves - 1) / kWaves;  // one item per wave at a time
-    long g1 = grid_for(k1, wgs), g2 = grid_for(k2, wgs);
-    if (g1 < 1) g1 = 1;
-    if (g2 < 1) g2 = 1;
+    const void *k3 = reinterpret_cast<const void *>(&tv_kernel<TT, TD, N, EPV>);
+    const long items = (long)a.R * a.UG * a.C;
+    const long units = (long)a.R * a.UG;
+    const long g1 = persistent_grid(k1, items), g3 = persistent_grid(k3, items);
+    const long gu = (units + kWaves - 1) / kWaves;
+    a.tag = next_tag();  // one tag for every launch of the call
     static bool said = false;
     if (!said && getenv("SPECVERIFY_VERBOSE")) {
         said = true;
         fprintf(stderr, "[specverify] verify N=%d EPV=%d C=%d items=%ld grids %ld / %ld\n", N,
-                EPV, a.C, items, g1, g2);
+                EPV, a.C, items, g1, g3);
     }
     hipLaunchKernelGGL((stats_kernel<TT, TD, N, EPV>), dim3((unsigned)g1), dim3(kBlock), 0, st, a);
-    const long units = (long)a.R * a.UG;
-    hipLaunchKernelGGL(norm_kernel, dim3((unsigned)((units + kWaves - 1) / kWaves)), dim3(kBlock),
-                       0, st, a);
-    hipLaunchKernelGGL((tv_kernel<TT, TD, N, EPV>), dim3((unsigned)g2), dim3(kBlock), 0, st, a);
-    hipLaunchKernelGGL((finalize_kernel<TT, TD, N, EPV>), dim3((unsigned)a.R), dim3(kBlock), 0, st,
-                       a);
+    hipLaunchKernelGGL((norm_kernel<TT, TD, N, EPV>), dim3((unsigned)gu), dim3(kBlock), 0, st, a);
+    hipLaunchKernelGGL((tv_kernel<TT, TD, N, EPV>), dim3((unsigned)g3), dim3(kBlock), 0, st, a);
+    hipLaunchKernelGGL((tv_combine_kernel<TT, TD, N, EPV>), dim3((unsigned)gu), dim3(kBlock), 0,
+                       st, a);
     return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_EHIP;
 }
 
 template <typename TT, typename TD, int N>
-int launch_n(const VerifyArgs &a, bool vec, long items, hipStream_t st) {
-    constexpr int eb = (EltBytes<TT>::value > EltBytes<TD>::value) ? EltBytes<TT>::value
-                                                                   : EltBytes<TD>::value;
-    constexpr int ev = (16 / eb < N) ? 16 / eb : N;
-    return vec ? launch_kernels<TT, TD, N, ev>(a, items, st)
-               : launch_kernels<TT, TD, N, 1>(a, items, st);
+int launch_n(const VerifyArgs &a, bool vec, hipStream_t st) {
+    constexpr int ev = ChunkGeom<TT, TD, N>::kVec;
+    return vec ? launch_kernels<TT, TD, N, ev>(a, st) : launch_kernels<TT, TD, N, 1>(a, st);
 }
 
 template <typename TT, typename TD>
-int launch_types(const VerifyArgs &a, int N, bool vec, long items, hipStream_t st) {
-    switch (N) {
-        case 32: return launch_n<TT, TD, 32>(a, vec, items, st);
-        case 16: return launch_n<TT, TD, 16>(a, vec, items, st);
-        case 8: return launch_n<TT, TD, 8>(a, vec, items, st);
-        case 4: return launch_n<TT, TD, 4>(a, vec, items, st);
-    }
+int launch_types(const VerifyArgs &a, int N, bool vec, hipStream_t st) {
+    if (N == kN) return launch_n<TT, TD, kN>(a, vec, st);
     return SPEC_EUNSUPPORTED;
 }
 
-int launch(const VerifyArgs &a, int tdt, int ddt, int N, bool vec, long items, hipStream_t st) {
-    if (tdt == SPEC_BF16 && ddt == SPEC_BF16)
-        return launch_types<uint16_t, uint16_t>(a, N, vec, items, st);
-    if (tdt == SPEC_F32 && ddt == SPEC_F32) return launch_types<float, float>(a, N, vec, items, st);
-    if (tdt == SPEC_BF16 && ddt == SPEC_F32)
-        return launch_types<uint16_t, float>(a, N, vec, items, st);
-    return launch_types<float, uint16_t>(a, N, vec, items, st);
+int launch(const VerifyArgs &a, int tdt, int ddt, int N, bool vec, hipStream_t st) {
+    if (tdt == SPEC_BF16 && ddt == SPEC_BF16) return launch_types<uint16_t, uint16_t>(a, N, vec, st);
+    if (tdt == SPEC_F32 && ddt == SPEC_F32) return launch_types<float, float>(a, N, vec, st);
+    if (tdt == SPEC_BF16 && ddt == SPEC_F32) return launch_types<uint16_t, float>(a, N, vec, st);
+    return launch_types<float, uint16_t>(a, N, vec, st);
 }
 
 void bind_workspace(VerifyArgs &a, void *ws, const Plan &p) {
     char *b = (char *)ws;
     a.ctl = (Control *)b;
-    a.st1 = (float4 *)(b + p.off_st1);
-    a.st2 = (float2 *)(b + p.off_st2);
-    a.nrm = (RowNorm *)(b + p.off_nrm);
+    a.cnt_r = (uint32_t *)(b + p.off_cr);
+    a.st1 = (uint64_t *)(b + p.off_st1);
+    a.st2 = (uint64_t *)(b + p.off_st2);
+    a.nrm = (uint64_t *)(b + p.off_nrm);
+    a.rec = (uint64_t *)(b + p.off_rec);
     a.C = p.C;
+}
+
+// Makes the plan's counters read zero at launch (see CleanPrefix).
+int prepare_counters(void *ws, const Plan &p, hipStream_t st) {
+    const size_t have = clean_prefix(ws);
+    if (have < p.off_data) {
+        const size_t words = (p.off_data - have) / 4;
+        const size_t blocks = (words + kBlock - 1) / kBlock;
+        hipLaunchKernelGGL(zero_fill_kernel, dim3((unsigned)(blocks < 4096 ? blocks : 4096)),
+                           dim3(kBlock), 0, st, (uint32_t *)((char *)ws + have), words);
+        if (hipGetLastError() != hipSuccess) return SPEC_EHIP;
+    }
+    note_workspace_clean(ws, p.off_data);
+    return SPEC_OK;
 }
 
 }  // namespace
@@ -1032,7 +1343,7 @@ using namespace sv;
 
 extern "C" {
 
-int spec_version(void) { return 100; }
+int spec_version(void) { return 200; }
 
 const char *spec_status_string(int status) {
     switch (status) {
@@ -1047,17 +1358,13 @@ const char *spec_status_string(int status) {
 }
 
 size_t spec_verify_workspace_bytes(int R, int gamma, int V) {
-    if (R < 0 || gamma < 0 || gamma > kMaxGamma || V < 1 || V > SPEC_MAX_VOCAB) return 0;
-    Plan p;
-    if (!make_plan(R > 0 ? R : 1, gamma + 1, V, p)) return 0;
-    return p.bytes;
+    if (R < 0 || gamma < 0 || gamma > kMaxGamma || V < 1 || V > SPEC_MAX_VERIFY_VOCAB) return 0;
+    return plan_bytes(R > 0 ? R : 1, gamma + 1, V);
 }
 
 size_t spec_tv_workspace_bytes(int N, int V) {
-    if (N < 0 || V < 1 || V > SPEC_MAX_VOCAB) return 0;
-    Plan p;
-    if (!make_plan(N > 0 ? N : 1, 1, V, p)) return 0;
-    return p.bytes;
+    if (N < 0 || V < 1 || V > SPEC_MAX_VERIFY_VOCAB) return 0;
+    return plan_bytes(N > 0 ? N : 1, 1, V);
 }
 
 int spec_workspace_init(void *workspace, size_t workspace_bytes, void *stream) {
@@ -1067,7 +1374,9 @@ int spec_workspace_init(void *workspace, size_t workspace_bytes, void *stream) {
     const size_t blocks = (words + kBlock - 1) / kBlock;
     hipLaunchKernelGGL(zero_fill_kernel, dim3((unsigned)(blocks < 4096 ? blocks : 4096)),
                        dim3(kBlock), 0, (hipStream_t)stream, (uint32_t *)workspace, words);
-    return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_EHIP;
+    if (hipGetLastError() != hipSuccess) return SPEC_EHIP;
+    note_workspace_clean(workspace, words * 4);
+    return SPEC_OK;
 }
 
 int spec_get_device_status(void *workspace, uint32_t *host_bits, int clear, void *stream) {
@@ -1093,7 +1402,7 @@ int spec_verify_batch(const void *target_logits, int t_dtype, const void *draft_
                       size_t workspace_bytes, void *stream) {
     if (R < 0 || gamma < 0 || V < 1) return SPEC_EINVAL;
     if (!dtype_ok(t_dtype) || !dtype_ok(d_dtype)) return SPEC_EDTYPE;
-    if (gamma > kMaxGamma || V > SPEC_MAX_VOCAB) return SPEC_EUNSUPPORTED;
+    if (gamma > kMaxGamma || V > SPEC_MAX_VERIFY_VOCAB) return SPEC_EUNSUPPORTED;
     if (R == 0) return SPEC_OK;
     if (!target_logits || !verify_len || !temperature || !u_sample || !out_tokens ||
         !out_num_accepted)
@@ -1124,9 +1433,12 @@ int spec_verify_batch(const void *target_logits, int t_dtype, const void *draft_
     a.out_rs = out_resid_mass;
     a.out_lq = out_logq;
     bind_workspace(a, workspace, p);
+    if (const int rc = prepare_counters(workspace, p, (hipStream_t)stream)) return rc;
     const bool vec = (V % 8 == 0) && aligned16(target_logits) &&
                      (gamma == 0 || aligned16(draft_logits));
-    return launch(a, t_dtype, d_dtype, p.N, vec, p.units * p.C, (hipStream_t)stream);
+    // with gamma == 0 no draft row exists; the draft type only shapes the plan
+    const int ddt = gamma > 0 ? d_dtype : t_dtype;
+    return launch(a, t_dtype, ddt, p.N, vec, (hipStream_t)stream);
 }
 
 int spec_tv_accept_rate(const void *draft_logits, const void *target_logits, int dtype,
@@ -1135,7 +1447,7 @@ int spec_tv_accept_rate(const void *draft_logits, const void *target_logits, int
                         void *stream) {
     if (N < 0 || V < 1) return SPEC_EINVAL;
     if (!dtype_ok(dtype)) return SPEC_EDTYPE;
-    if (V > SPEC_MAX_VOCAB) return SPEC_EUNSUPPORTED;
+    if (V > SPEC_MAX_VERIFY_VOCAB) return SPEC_EUNSUPPORTED;
     if (N == 0) return SPEC_OK;
     if (!draft_logits || !target_logits || !temperature || !out_cstar) return SPEC_EINVAL;
     Plan p;
@@ -1156,8 +1468,9 @@ int spec_tv_accept_rate(const void *draft_logits, const void *target_logits, int
     a.out_cs = out_cstar;
     a.out_rs = out_resid_mass;
     bind_workspace(a, workspace, p);
+    if (const int rc = prepare_counters(workspace, p, (hipStream_t)stream)) return rc;
     const bool vec = (V % 8 == 0) && aligned16(target_logits) && aligned16(draft_logits);
-    return launch(a, dtype, dtype, p.N, vec, p.units * p.C, (hipStream_t)stream);
+    return launch(a, dtype, dtype, p.N, vec, (hipStream_t)stream);
 }
 
 }  // extern "C"

@@ -53,7 +53,7 @@ def test_workspace_sizes(lib):
     assert f(64, 7, 151936) > 0 and f(64, 7, 151936) % 256 == 0
     assert f(-1, 7, 100) == 0 and f(1, -1, 100) == 0 and f(1, 1, 0) == 0
     assert f(1, 65, 100) == 0                      # gamma above the supported maximum
-    assert f(1, 1, 2097152) > 0 and f(1, 1, 2097153) == 0
+    assert f(1, 1, 262144) > 0 and f(1, 1, 262145) == 0
     assert f(256, 7, 129280) >= f(64, 7, 129280)
     g = lib.spec_tv_workspace_bytes
     g.restype = ctypes.c_size_t
