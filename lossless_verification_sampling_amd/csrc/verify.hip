@@ -56,6 +56,8 @@ namespace sv {
 
 constexpr float kInf = __builtin_inff();
 constexpr int kLanes = 64;
+// waves per SIMD the streaming kernels are compiled for (their registers fit)
+constexpr int kStreamWaves = 5;
 
 // Per-unit record words (tagged), filled by the unit's last arrivers and read
 // by the request's finaliser.
@@ -77,6 +79,7 @@ struct VerifyArgs {
     int tG, dG;              // rows per request in the target / draft tensors
     int tv_mode;             // 1: independent row pairs, c* and Res only
     uint32_t tag;            // this launch's tag (nonzero, top bit set)
+    int compact;             // streaming kernels walk a unit table in LDS (else all candidates)
     int32_t *out_tok;
     int32_t *out_n;
     float *out_cs;
@@ -191,8 +194,12 @@ struct Item {
 __device__ __forceinline__ bool is_pair(const Item &x) { return x.i < x.l; }
 __device__ __forceinline__ bool is_tv(const Item &x) { return x.i < x.l && x.T != 0.0f; }
 
+// The wave's index in the grid, made explicitly wave-uniform (the compiler
+// cannot tell that threadIdx.x / 64 is the same in every lane of a wave), so
+// that everything derived from it stays in scalar registers and branches.
 __device__ __forceinline__ long wave_index() {
-    return (long)blockIdx.x * kWaves + (threadIdx.x >> 6);
+    const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    return (long)blockIdx.x * kWaves + w;
 }
 __device__ __forceinline__ long wave_count() { return (long)gridDim.x * kWaves; }
 
@@ -251,6 +258,143 @@ struct ItemCursor {
     }
 };
 
+// Invalid-request outputs of request r, written by one thread.
+__device__ __forceinline__ void write_invalid_thread(const VerifyArgs &a, int r) {
+    const float nan = __builtin_nanf("");
+    if (a.tv_mode) {
+        a.out_cs[r] = nan;
+        if (a.out_rs) a.out_rs[r] = nan;
+    } else {
+        for (int j = 0; j <= a.gamma; ++j) {
+            a.out_tok[(size_t)r * (a.gamma + 1) + j] = -1;
+            if (a.out_lq) a.out_lq[(size_t)r * (a.gamma + 1) + j] = nan;
+        }
+        for (int i = 0; i < a.gamma; ++i) {
+            if (a.out_cs) a.out_cs[(size_t)r * a.gamma + i] = nan;
+            if (a.out_rs) a.out_rs[(size_t)r * a.gamma + i] = nan;
+        }
+        a.out_n[r] = -1;
+    }
+    atomic_or_u32(&a.ctl->status, SPEC_DEV_BAD_REQUEST);
+}
+
+// Work list of the streaming kernels when the unit table fits in LDS: every
+// workgroup lists the active units (request-major) in shared memory at launch,
+// and item k (unit k / C, chunk k % C) belongs to wave k mod W.  Only active
+// items are enumerated, so every wave gets the same number of items (+-1).
+// Shared layout: req[3 R] = (T, s, l) per request, then units[] = r << 7 | i.
+struct UnitTable {
+    const uint32_t *req;
+    const uint32_t *units;
+    uint32_t items;  // active units * C
+};
+
+// Units of one request in the table: positions 0..l (the TV pass: the pairs
+// 0..l-1 at T > 0), never more than the request's UG unit slots (row pairs
+// have no bonus unit).
+__device__ __forceinline__ int table_units(const VerifyArgs &a, bool ok, float T, int l,
+                                           bool tv_only) {
+    if (!ok) return 0;
+    const int n = tv_only ? (T != 0.0f ? l : 0) : l + 1;
+    return n < a.UG ? n : a.UG;
+}
+
+// Builds the table in shared memory `lds` (all threads of the block).  tv_only
+// lists the pair units at T > 0 only.
+__device__ __forceinline__ UnitTable build_unit_table(const VerifyArgs &a, uint32_t *lds,
+                                                      bool tv_only) {
+    __shared__ uint32_t wsum[kWaves];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    uint32_t *req = lds;
+    uint32_t *units = lds + 3 * a.R;
+    // thread t owns requests [t K, t K + K)
+    const int K = (a.R + kBlock - 1) / kBlock;
+    const int r0 = tid * K, r1 = min(r0 + K, a.R);
+    uint32_t own = 0;
+    for (int r = r0; r < r1; ++r) {
+        float T;
+        int l;
+        const bool ok = request_ok(a, r, T, l);
+        // the stats pass's first workgroup writes the outputs of malformed
+        // requests (their units are never visited)
+        if (!ok && !tv_only && blockIdx.x == 0) write_invalid_thread(a, r);
+        req[3 * r + 0] = __float_as_uint(T);
+        req[3 * r + 1] = __float_as_uint(ok && T != 0.0f ? exp2_scale(T) : 0.0f);
+        req[3 * r + 2] = (uint32_t)l;
+        own += (uint32_t)table_units(a, ok, T, l, tv_only);
+    }
+    // block exclusive scan of the per-thread unit counts
+    uint32_t incl = own;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t n = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += n;
+    }
+    if (lane == 63) wsum[wave] = incl;
+    __syncthreads();
+    uint32_t base = 0, total = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+        if (w < wave) base += wsum[w];
+        total += wsum[w];
+    }
+    uint32_t pos = base + incl - own;
+    for (int r = r0; r < r1; ++r) {
+        const int l = (int)req[3 * r + 2];
+        const float T = __uint_as_float(req[3 * r]);
+        const bool ok = temperature_ok(T) && l >= 0 && l <= a.gamma;
+        const int n = table_units(a, ok, T, l, tv_only);
+        for (int i = 0; i < n; ++i) units[pos++] = ((uint32_t)r << 7) | (uint32_t)i;
+    }
+    __syncthreads();
+    UnitTable t;
+    t.req = req;
+    t.units = units;
+    t.items = total * (uint32_t)a.C;
+    return t;
+}
+
+struct CompactCursor {
+    uint32_t k;
+    __device__ bool next(const VerifyArgs &a, const UnitTable &t, Item &x) {
+        if (k >= t.items) return false;
+        const uint32_t U = k / (uint32_t)a.C;
+        x.c = (int)(k - U * (uint32_t)a.C);
+        k += (uint32_t)wave_count();
+        const uint32_t e = __builtin_amdgcn_readfirstlane(t.units[U]);
+        x.r = (int)(e >> 7);
+        x.i = (int)(e & 127u);
+        x.T = __uint_as_float(__builtin_amdgcn_readfirstlane(t.req[3 * x.r]));
+        x.s = __uint_as_float(__builtin_amdgcn_readfirstlane(t.req[3 * x.r + 1]));
+        x.l = (int)__builtin_amdgcn_readfirstlane(t.req[3 * x.r + 2]);
+        x.u = x.r * a.UG + x.i;
+        return true;
+    }
+};
+
+// Either cursor behind one interface.
+struct Walker {
+    bool compact;
+    UnitTable t;
+    CompactCursor cc;
+    ItemCursor ic;
+    uint32_t work;
+    bool tv_only;
+    __device__ bool next(const VerifyArgs &a, Item &x) {
+        return compact ? cc.next(a, t, x) : ic.next(a, work, x, tv_only);
+    }
+};
+
+__device__ __forceinline__ Walker make_walker(const VerifyArgs &a, uint32_t *lds, bool tv_only) {
+    Walker w;
+    w.compact = a.compact != 0;
+    w.tv_only = tv_only;
+    w.work = (uint32_t)a.R * (uint32_t)a.UG * (uint32_t)a.C;
+    w.cc.k = (uint32_t)wave_index();
+    if (w.compact) w.t = build_unit_table(a, lds, tv_only);
+    return w;
+}
+
 // ---------------------------------------------------------------------------
 // chunk registers
 // ---------------------------------------------------------------------------
@@ -265,52 +409,56 @@ struct RawChunk {
     static constexpr int kWords = kPacked ? N / 2 : N;
     uint32_t w[kWords];
 
-    // Chunks inside the row load without bounds checks; in the last chunk a
-    // vector past the row end holds -inf (V % EPV == 0 when EPV > 1).
+    int rem;  // ids of the chunk inside the row (64 N except in the last chunk)
+
+    // Issues the chunk's loads unconditionally, in one basic block, so that
+    // the compiler can wait for exactly these loads later: a vector past the
+    // row end re-reads the chunk's first vector (inside the row) and is turned
+    // into -inf by fix() (V % EPV == 0 when EPV > 1).
     __device__ __forceinline__ void load(const T *row, long c0, int V) {
         const T *base = row + c0;
         const uint32_t lane = (uint32_t)lane_id();
-        if (c0 + (long)kLanes * N <= V) {
+        const long left = (long)V - c0;
+        rem = left < (long)kLanes * N ? (int)left : kLanes * N;
 #pragma unroll
-            for (int j = 0; j < N / EPV; ++j) load_vec(base, (j * kLanes + lane) * EPV, j, true);
-        } else {
-            const int rem = (int)(V - c0);
-#pragma unroll
-            for (int j = 0; j < N / EPV; ++j) {
-                const int e = (int)((j * kLanes + lane) * EPV);
-                load_vec(base, e, j, e < rem);
-            }
+        for (int j = 0; j < N / EPV; ++j) {
+            const uint32_t e = (j * kLanes + lane) * EPV;
+            load_vec(base, (int)e < rem ? e : 0u, j);
         }
     }
 
-    __device__ __forceinline__ void load_vec(const T *base, uint32_t e, int j, bool in) {
+    // Marks the vectors past the row end -inf; call before using the words.
+    __device__ __forceinline__ void fix() {
+        if (rem == kLanes * N) return;
+        const uint32_t lane = (uint32_t)lane_id();
+#pragma unroll
+        for (int j = 0; j < N / EPV; ++j) {
+            const bool out = (int)((j * kLanes + lane) * EPV) >= rem;
+            constexpr int WPV = kWords / (N / EPV);  // words per vector
+#pragma unroll
+            for (int q = 0; q < WPV; ++q)
+                if (out) w[j * WPV + q] = kPacked ? 0xff80ff80u : 0xff800000u;
+        }
+    }
+
+    __device__ __forceinline__ void load_vec(const T *base, uint32_t e, int j) {
         if constexpr (EPV == 1) {
-            w[j] = __float_as_uint(in ? load_one(base, (long)e) : -kInf);
+            w[j] = __float_as_uint(load_one(base, (long)e));
         } else if constexpr (kPacked) {
             constexpr int NW = EPV / 2;
             if constexpr (NW == 4) {
-                uint4 v = make_uint4(0xff80ff80u, 0xff80ff80u, 0xff80ff80u, 0xff80ff80u);
-                if (in) v = *reinterpret_cast<const uint4 *>(base + e);
+                const uint4 v = *reinterpret_cast<const uint4 *>(base + e);
                 w[j * 4 + 0] = v.x; w[j * 4 + 1] = v.y; w[j * 4 + 2] = v.z; w[j * 4 + 3] = v.w;
             } else {
                 static_assert(NW == 2, "bf16 vector width");
-                uint2 v = make_uint2(0xff80ff80u, 0xff80ff80u);
-                if (in) v = *reinterpret_cast<const uint2 *>(base + e);
+                const uint2 v = *reinterpret_cast<const uint2 *>(base + e);
                 w[j * 2 + 0] = v.x; w[j * 2 + 1] = v.y;
             }
         } else {
             static_assert(EPV == 4, "fp32 vector width");
-            uint4 v = make_uint4(0xff800000u, 0xff800000u, 0xff800000u, 0xff800000u);
-            if (in) v = *reinterpret_cast<const uint4 *>(base + e);
+            const uint4 v = *reinterpret_cast<const uint4 *>(base + e);
             w[j * 4 + 0] = v.x; w[j * 4 + 1] = v.y; w[j * 4 + 2] = v.z; w[j * 4 + 3] = v.w;
         }
-    }
-
-    // Hides the words' values from the optimiser (no instruction), so that
-    // values widened from them before this point are not reused after it.
-    __device__ __forceinline__ void opaque() {
-#pragma unroll
-        for (int q = 0; q < kWords; ++q) __asm__ volatile("" : "+v"(w[q]));
     }
 
     __device__ __forceinline__ float get(int k) const {
@@ -362,11 +510,8 @@ __device__ __forceinline__ void chunk_exp(const RC &raw, float s, float (&e)[N],
     for (int k = 0; k < N; ++k) m = __builtin_elementwise_maximum(m, raw.get(k));
     mu = wave_max(m) * s;
     const float ref = exp_ref(mu);
-    // widen the logits again instead of keeping N widened copies alive
-    RC r2 = raw;
-    r2.opaque();
 #pragma unroll
-    for (int k = 0; k < N; ++k) e[k] = ew(r2.get(k), s, ref);
+    for (int k = 0; k < N; ++k) e[k] = ew(raw.get(k), s, ref);
     S = wave_sum_f(lane_sum<N>(e));
 }
 
@@ -480,12 +625,21 @@ constexpr int kCB = 4;
 // Lane-parallel batch: word k of this lane is p[k] if act[k].  Issues every
 // load, then re-reads only the words that do not carry `tag` yet, until all
 // do (bounded as in await_lane).  out[k] = payload (0 for inactive words).
+// `cached`: the words were written by an earlier launch, so a plain (cached)
+// load sees them; only a stale tag (not expected) falls back to the coherent
+// re-reads.
 template <int K>
 __device__ __forceinline__ void await_batch(const uint64_t *const (&p)[K], const bool (&act)[K],
-                                            uint32_t tag, Control *ctl, uint32_t (&out)[K]) {
+                                            uint32_t tag, Control *ctl, uint32_t (&out)[K],
+                                            bool cached = false) {
     uint64_t v[K];
+    if (cached) {
 #pragma unroll
-    for (int k = 0; k < K; ++k) v[k] = act[k] ? ld_word(p[k]) : ((uint64_t)tag << 32);
+        for (int k = 0; k < K; ++k) v[k] = act[k] ? *p[k] : ((uint64_t)tag << 32);
+    } else {
+#pragma unroll
+        for (int k = 0; k < K; ++k) v[k] = act[k] ? ld_word(p[k]) : ((uint64_t)tag << 32);
+    }
     uint32_t it = 0;
     for (;;) {
         bool stale = false;
@@ -511,7 +665,7 @@ __device__ __forceinline__ void await_batch(const uint64_t *const (&p)[K], const
 template <int Q>
 __device__ __forceinline__ void load_unit_words(const uint64_t *base, int C, const bool (&want)[Q],
                                                 uint32_t tag, Control *ctl,
-                                                uint32_t (&w)[kCB][Q]) {
+                                                uint32_t (&w)[kCB][Q], bool cached = false) {
     const uint64_t *p[kCB * Q];
     bool act[kCB * Q];
     uint32_t o[kCB * Q];
@@ -523,7 +677,7 @@ __device__ __forceinline__ void load_unit_words(const uint64_t *base, int C, con
             p[b * Q + q] = base + (size_t)c * Q + q;
             act[b * Q + q] = c < C && want[q];
         }
-    await_batch<kCB * Q>(p, act, tag, ctl, o);
+    await_batch<kCB * Q>(p, act, tag, ctl, o, cached);
 #pragma unroll
     for (int b = 0; b < kCB; ++b)
 #pragma unroll
@@ -751,7 +905,7 @@ __device__ __forceinline__ void stats_combine(const VerifyArgs &a, const Item &x
     }
     uint32_t w[kCB][4];
     const bool want[4] = {true, true, pair, pair};
-    load_unit_words<4>(a.st1 + (size_t)x.u * C * 4, C, want, a.tag, a.ctl, w);
+    load_unit_words<4>(a.st1 + (size_t)x.u * C * 4, C, want, a.tag, a.ctl, w, true);
 
     if (x.T == 0.0f) {
         float vt = -kInf, vd = -kInf;
@@ -879,7 +1033,7 @@ __device__ __forceinline__ void tv_combine(const VerifyArgs &a, const Item &x) {
         act[2 * kCB] = lane == 0;
         p[2 * kCB + 1] = a.nrm + (size_t)x.u * 4 + (lane & 3);
         act[2 * kCB + 1] = lane < 4;
-        await_batch<2 * kCB + 2>(p, act, a.tag, a.ctl, o);
+        await_batch<2 * kCB + 2>(p, act, a.tag, a.ctl, o, true);
 #pragma unroll
         for (int b = 0; b < kCB; ++b) {
             v2[b][0] = o[b * 2];
@@ -922,8 +1076,11 @@ __device__ __forceinline__ void tv_combine(const VerifyArgs &a, const Item &x) {
                 for (int b = 0; b < kCB; ++b) m[b] = (double)__uint_as_float(v2[b][1]);
                 double tin;
                 const int csel = select_chunk(C, (double)usm * rs, m, &tin);
-                const uint32_t s4 = await_lane(a.st1 + ((size_t)x.u * C + csel) * 4 + (lane & 3),
-                                               lane < 4, a.tag, a.ctl);
+                const uint64_t *const sp[1] = {a.st1 + ((size_t)x.u * C + csel) * 4 + (lane & 3)};
+                const bool sa[1] = {lane < 4};
+                uint32_t so[1];
+                await_batch<1>(sp, sa, a.tag, a.ctl, so, true);
+                const uint32_t s4 = so[0];
                 const float mut = __uint_as_float(rl(s4, 0)), mud = __uint_as_float(rl(s4, 2));
                 const PairScale ps =
                     pair_scale(chunk_alpha(mut, Mt, Zt), chunk_alpha(mud, Md, Zd));
@@ -946,7 +1103,7 @@ __device__ __forceinline__ void tv_combine(const VerifyArgs &a, const Item &x) {
                 // no residual mass (rounding): draw from q of the same row
                 uint32_t w4[kCB][4];
                 const bool want4[4] = {true, true, false, false};
-                load_unit_words<4>(a.st1 + (size_t)x.u * C * 4, C, want4, a.tag, a.ctl, w4);
+                load_unit_words<4>(a.st1 + (size_t)x.u * C * 4, C, want4, a.tag, a.ctl, w4, true);
                 tok = draw_from_q<TT, N, EPV, 4>(a, trow, w4, s, Mt, Zt, usm, &ztok);
             }
             lqd = (float)(((double)ztok * (double)s - (double)Mt) * kLn2 - log((double)Zt));
@@ -961,6 +1118,8 @@ __device__ __forceinline__ void tv_combine(const VerifyArgs &a, const Item &x) {
 // the two persistent kernels
 // ---------------------------------------------------------------------------
 
+// Issues item x's loads: its chunk of the target row and, for a pair, of the
+// draft row.
 template <typename TT, typename TD, int N, int EPV>
 __device__ __forceinline__ void load_item(const VerifyArgs &a, const Item &x,
                                           RawChunk<TT, N, EPV> &rt, RawChunk<TD, N, EPV> &rd) {
@@ -972,9 +1131,10 @@ __device__ __forceinline__ void load_item(const VerifyArgs &a, const Item &x,
 // Stats of item x: the chunk words (mu, S) per row, or the argmax words at
 // T = 0, published for the unit's combine and the TV pass.
 template <int N, int EPV, typename RT, typename RD>
-__device__ __forceinline__ void stats_item(const VerifyArgs &a, const Item &x, const RT &rt,
-                                           const RD &rd) {
+__device__ __forceinline__ void stats_item(const VerifyArgs &a, const Item &x, RT &rt, RD &rd) {
     const long c0 = (long)x.c * kLanes * N;
+    rt.fix();
+    if (is_pair(x)) rd.fix();
     uint32_t w0, w1, w2 = 0, w3 = 0;
     if (x.T == 0.0f) {
         float bv;
@@ -1017,29 +1177,22 @@ __device__ __forceinline__ bool unit_item(const VerifyArgs &a, long u, Item &x) 
 // Kernel 1: every needed row streamed once from HBM, two items in flight per
 // wave; per item the chunk words.  Malformed requests get their outputs here.
 template <typename TT, typename TD, int N, int EPV>
-__global__ void __launch_bounds__(kBlock, 4) stats_kernel(VerifyArgs a) {
-    for (long r = wave_index(); r < a.R; r += wave_count()) {
-        float T;
-        int l;
-        if (!request_ok(a, (int)r, T, l)) write_invalid(a, (int)r);
+__global__ void __launch_bounds__(kBlock, kStreamWaves) stats_kernel(VerifyArgs a) {
+    if (!a.compact) {
+        for (long r = wave_index(); r < a.R; r += wave_count()) {
+            float T;
+            int l;
+            if (!request_ok(a, (int)r, T, l)) write_invalid(a, (int)r);
+        }
     }
-    const uint32_t work = (uint32_t)a.R * (uint32_t)a.UG * (uint32_t)a.C;
-    ItemCursor cur;
-    Item x0, x1;
-    RawChunk<TT, N, EPV> rt0, rt1;
-    RawChunk<TD, N, EPV> rd0, rd1;
-    bool h0 = cur.next(a, work, x0, false);
-    if (h0) load_item(a, x0, rt0, rd0);
-    bool h1 = h0 && cur.next(a, work, x1, false);
-    if (h1) load_item(a, x1, rt1, rd1);
-    while (h0) {
-        stats_item<N, EPV>(a, x0, rt0, rd0);
-        h0 = h1 && cur.next(a, work, x0, false);
-        if (h0) load_item(a, x0, rt0, rd0);
-        if (!h1) break;
-        stats_item<N, EPV>(a, x1, rt1, rd1);
-        h1 = h0 && cur.next(a, work, x1, false);
-        if (h1) load_item(a, x1, rt1, rd1);
+    extern __shared__ uint32_t lds[];
+    Walker cur = make_walker(a, lds, false);
+    Item x;
+    RawChunk<TT, N, EPV> rt;
+    RawChunk<TD, N, EPV> rd;
+    while (cur.next(a, x)) {
+        load_item(a, x, rt, rd);
+        stats_item<N, EPV>(a, x, rt, rd);
     }
 }
 
@@ -1056,8 +1209,10 @@ __global__ void __launch_bounds__(kBlock) norm_kernel(VerifyArgs a) {
 // kernel 1, the weights e = 2^(z s - mu) are rebuilt exactly as kernel 1 made
 // them, and sum min(p, q) and the residual mass of the chunk are published.
 template <int N, typename RT, typename RD>
-__device__ __forceinline__ void tv_item(const VerifyArgs &a, const Item &x, const RT &rt,
-                                        const RD &rd, uint32_t w8) {
+__device__ __forceinline__ void tv_item(const VerifyArgs &a, const Item &x, RT &rt, RD &rd,
+                                        uint32_t w8) {
+    rt.fix();
+    rd.fix();
     // lanes 0..3: the chunk's words (mu_t, S_t, mu_d, S_d); 4..7: normalisers
     const float mut = __uint_as_float(rl(w8, 0)), St = __uint_as_float(rl(w8, 1));
     const float mud = __uint_as_float(rl(w8, 2));
@@ -1101,7 +1256,8 @@ __device__ __forceinline__ uint64_t load_tv_item(const VerifyArgs &a, const Item
     const int lane = lane_id();
     const uint64_t *p = (lane < 4) ? a.st1 + ((size_t)x.u * a.C + x.c) * 4 + lane
                                    : a.nrm + (size_t)x.u * 4 + (lane & 3);
-    const uint64_t w = (lane < 8) ? ld_word(p) : 0;
+    // written by the earlier launches of this call: a plain load sees it
+    const uint64_t w = (lane < 8) ? *p : 0;
     load_item(a, x, rt, rd);
     return w;
 }
@@ -1109,18 +1265,10 @@ __device__ __forceinline__ uint64_t load_tv_item(const VerifyArgs &a, const Item
 // Kernel 3: the TV pass over the pair items at T > 0, two items in flight
 // per wave.
 template <typename TT, typename TD, int N, int EPV>
-__global__ void __launch_bounds__(kBlock, 4) tv_kernel(VerifyArgs a) {
+__global__ void __launch_bounds__(kBlock, kStreamWaves) tv_kernel(VerifyArgs a) {
     const int lane = lane_id();
-    const uint32_t work = (uint32_t)a.R * (uint32_t)a.UG * (uint32_t)a.C;
-    ItemCursor cur;
-    Item x0, x1;
-    uint64_t w0 = 0, w1 = 0;
-    RawChunk<TT, N, EPV> rt0, rt1;
-    RawChunk<TD, N, EPV> rd0, rd1;
-    bool h0 = cur.next(a, work, x0, true);
-    if (h0) w0 = load_tv_item(a, x0, rt0, rd0);
-    bool h1 = h0 && cur.next(a, work, x1, true);
-    if (h1) w1 = load_tv_item(a, x1, rt1, rd1);
+    extern __shared__ uint32_t lds[];
+    Walker cur = make_walker(a, lds, true);
     // kernels 1 and 2 wrote the words before this launch: a stale tag could
     // only come from an earlier call, so the wait never spins
     auto words = [&](const Item &it, uint64_t w) -> uint32_t {
@@ -1129,14 +1277,12 @@ __global__ void __launch_bounds__(kBlock, 4) tv_kernel(VerifyArgs a) {
                                        : a.nrm + (size_t)it.u * 4 + (lane & 3);
         return await_lane(p, lane < 8, a.tag, a.ctl);
     };
-    while (h0) {
-        tv_item<N>(a, x0, rt0, rd0, words(x0, w0));
-        h0 = h1 && cur.next(a, work, x0, true);
-        if (h0) w0 = load_tv_item(a, x0, rt0, rd0);
-        if (!h1) break;
-        tv_item<N>(a, x1, rt1, rd1, words(x1, w1));
-        h1 = h0 && cur.next(a, work, x1, true);
-        if (h1) w1 = load_tv_item(a, x1, rt1, rd1);
+    Item x;
+    RawChunk<TT, N, EPV> rt;
+    RawChunk<TD, N, EPV> rd;
+    while (cur.next(a, x)) {
+        const uint64_t w = load_tv_item(a, x, rt, rd);
+        tv_item<N>(a, x, rt, rd, words(x, w));
     }
 }
 
@@ -1236,22 +1382,23 @@ size_t plan_bytes(long R, long upr, long V) {
 bool dtype_ok(int d) { return d == SPEC_F32 || d == SPEC_BF16; }
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
-// Resident workgroups of a kernel on the current device (cached).
-long resident_blocks(const void *kernel) {
-    struct Entry { const void *k; int dev; long cap; };
+// Resident workgroups of a kernel with `lds` bytes of dynamic shared memory on
+// the current device (cached per kernel, device and size).
+long resident_blocks(const void *kernel, size_t lds) {
+    struct Entry { const void *k; int dev; size_t lds; long cap; };
     static std::mutex mu;
     static std::vector<Entry> cache;
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return 0;
     std::lock_guard<std::mutex> lock(mu);
     for (const Entry &e : cache)
-        if (e.k == kernel && e.dev == dev) return e.cap;
+        if (e.k == kernel && e.dev == dev && e.lds == lds) return e.cap;
     int nb = 0, ncu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kernel, kBlock, 0) != hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kernel, kBlock, lds) != hipSuccess ||
         hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         return 0;
     const long cap = (long)nb * ncu;
-    cache.push_back(Entry{kernel, dev, cap});
+    cache.push_back(Entry{kernel, dev, lds, cap});
     return cap;
 }
 
@@ -1261,32 +1408,42 @@ uint32_t next_tag() {
 }
 
 // Persistent grid of kernel k: its resident capacity, at most one wave per item.
-long persistent_grid(const void *k, long items) {
-    const long cap = resident_blocks(k);
+long persistent_grid(const void *k, size_t lds, long items) {
+    const long cap = resident_blocks(k, lds);
     const long want = (items + kWaves - 1) / kWaves;
     if (cap <= 0) return want > 0 ? want : 1;
     const long g = want < cap ? want : cap;
     return g > 0 ? g : 1;
 }
 
+// Shared memory of the unit table (0: too large, walk all candidates).
+constexpr size_t kMaxTableBytes = 32768;
+size_t table_bytes(const VerifyArgs &a) {
+    const size_t b = 4 * (3 * (size_t)a.R + (size_t)a.R * a.UG);
+    return b <= kMaxTableBytes ? (b + 255) / 256 * 256 : 0;
+}
+
 template <typename TT, typename TD, int N, int EPV>
 int launch_kernels(VerifyArgs a, hipStream_t st) {
     const void *k1 = reinterpret_cast<const void *>(&stats_kernel<TT, TD, N, EPV>);
     const void *k3 = reinterpret_cast<const void *>(&tv_kernel<TT, TD, N, EPV>);
+    const size_t lds = table_bytes(a);
+    a.compact = lds > 0;
     const long items = (long)a.R * a.UG * a.C;
     const long units = (long)a.R * a.UG;
-    const long g1 = persistent_grid(k1, items), g3 = persistent_grid(k3, items);
+    const long g1 = persistent_grid(k1, lds, items), g3 = persistent_grid(k3, lds, items);
     const long gu = (units + kWaves - 1) / kWaves;
     a.tag = next_tag();  // one tag for every launch of the call
     static bool said = false;
     if (!said && getenv("SPECVERIFY_VERBOSE")) {
         said = true;
-        fprintf(stderr, "[specverify] verify N=%d EPV=%d C=%d items=%ld grids %ld / %ld\n", N,
-                EPV, a.C, items, g1, g3);
+        fprintf(stderr, "[specverify] verify N=%d EPV=%d C=%d items=%ld grids %ld / %ld lds %zu\n",
+                N, EPV, a.C, items, g1, g3, lds);
     }
-    hipLaunchKernelGGL((stats_kernel<TT, TD, N, EPV>), dim3((unsigned)g1), dim3(kBlock), 0, st, a);
+    hipLaunchKernelGGL((stats_kernel<TT, TD, N, EPV>), dim3((unsigned)g1), dim3(kBlock), lds, st,
+                       a);
     hipLaunchKernelGGL((norm_kernel<TT, TD, N, EPV>), dim3((unsigned)gu), dim3(kBlock), 0, st, a);
-    hipLaunchKernelGGL((tv_kernel<TT, TD, N, EPV>), dim3((unsigned)g3), dim3(kBlock), 0, st, a);
+    hipLaunchKernelGGL((tv_kernel<TT, TD, N, EPV>), dim3((unsigned)g3), dim3(kBlock), lds, st, a);
     hipLaunchKernelGGL((tv_combine_kernel<TT, TD, N, EPV>), dim3((unsigned)gu), dim3(kBlock), 0,
                        st, a);
     return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_EHIP;
