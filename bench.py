@@ -3,7 +3,9 @@
 A step is one spec_verify_batch call over the batched workload (R = 64
 requests, gamma = 7, V = 151936, bf16 logits, verify lengths uniform on 0..7,
 T = 1): every row of the hot path (softmax statistics, c*, accept tests,
-prefix survival, residual / bonus draw, commit) runs in that one launch.
+prefix survival, residual / bonus draw, commit) runs in that one call, which
+launches four kernels on the current stream (chunk statistics, per-row
+combine, total-variation pass, residual draw and commit).
 
 Inputs are generated once (seeded), uploaded, and replicated into enough
 device copies that consecutive steps never find their logits in the 256 MB
@@ -13,7 +15,8 @@ traffic, so the timed region streams from HBM.
 Prints one JSON line:
   value      verified draft positions per second (sum of l_r per call / time)
   roofline   algorithmic bytes (every verified draft row and target row plus
-             the bonus row, read once) / average kernel time, against 8 TB/s
+             the bonus row, read once) / average HIP-event time of the whole
+             call (its four kernels), against 8 TB/s
   cpu_baseline  the fp64 oracle on the host (one thread) over the same batch
 
 --workload dspark measures the Markov-head draft (R = 64, gamma = 7,
@@ -41,11 +44,18 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
 def source_hash() -> str:
+    """Hash of the kernel library's code with comments and blank space removed,
+    so that counter figures stay tied to the code they were measured on."""
+    import re
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "lossless_verification_sampling_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(f.encode() + fh.read())
+        with open(os.path.join(csrc, f), encoding="utf-8") as fh:
+            code = fh.read()
+        code = re.sub(r"/\*.*?\*/", " ", code, flags=re.S)
+        code = re.sub(r"//[^\n]*", " ", code)
+        code = " ".join(code.split())
+        h.update(f.encode() + b"\0" + code.encode())
     return h.hexdigest()[:16]
 
 
@@ -165,7 +175,7 @@ def bench_verify(args):
                      "kernel_ms_mean": float(kern_ms.mean()),
                      "kernel_ms_p10": float(np.percentile(kern_ms, 10)),
                      "kernel_ms_p90": float(np.percentile(kern_ms, 90)),
-                     "kernel": "verify_kernel (bf16, bf16)"},
+                     "kernel": "spec_verify_batch call: stats_kernel + norm_kernel + tv_kernel + tv_combine_kernel (bf16, bf16)"},
         "kernel_positions_per_s": sum_l / avg_kernel_s,
     }
     if not args.no_cpu_baseline:
@@ -225,6 +235,21 @@ def bench_dspark(args):
     }
 
 
+def calibrate_copy(args):
+    """One device-to-device copy of a known size, repeated: the reference that
+    scales rocprofv3's FETCH_SIZE / WRITE_SIZE counters to bytes."""
+    import torch
+    dev = torch.device("cuda:0")
+    nbytes = 256 << 20
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(args.warmup + args.steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    return {"calibration": "device copy", "bytes_read_per_copy": nbytes,
+            "bytes_written_per_copy": nbytes, "copies": args.warmup + args.steps}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -235,13 +260,18 @@ def main():
     ap.add_argument("--workload", choices=["batched", "dspark"], default="batched")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only copy a 256 MiB buffer (reference for the HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
               "(requests shard across GPUs with no exchange; see the design notes)",
               file=sys.stderr)
         sys.exit(2)
-    res = bench_verify(args) if args.workload == "batched" else bench_dspark(args)
+    if args.calibrate_copy:
+        res = calibrate_copy(args)
+    else:
+        res = bench_verify(args) if args.workload == "batched" else bench_dspark(args)
     print(json.dumps(res))
 
 

@@ -1,5 +1,5 @@
 // verify.hip -- batched lossless speculative-sampling verification and the
-// analytic acceptance rate on gfx950, in one persistent launch per call.
+// analytic acceptance rate on gfx950: four stream-ordered launches per call.
 //
 // Method (pages cited by title and section):
 //  * DART reading note (zhongzhuzhou.org), sec. 2.3, eq. (3)-(4): a draft token
@@ -17,30 +17,32 @@
 // Design.  A "unit" is one position of one request: the (target, draft) row
 // pair of position i < l_r, or the bonus target row i = l_r.  Each unit's rows
 // are cut into C chunks of 64 N logits, and an "item" is one chunk of one
-// unit.  Two persistent launches of independent wave64s walk the items
-// round-robin (item k belongs to wave k mod W):
-//  1. stats_kernel streams every needed row exactly once from HBM with
-//     16-byte loads (two items in flight per wave).  Per item it publishes the
-//     chunk's scaled max mu and weight sum S = sum 2^(z s - mu) per row
-//     (s = log2(e) / T; the argmax at T = 0) and arrives on the unit's
-//     counter.  The wave whose arrival completes a unit ("last arriver")
-//     combines the C chunk words into the rows' normalisers, runs the
-//     position's accept test on the two gathered logits, and for the bonus
-//     unit makes the inverse-CDF draw from q; at T = 0 it settles the unit.
-//  2. tv_kernel re-reads the pair chunks at T > 0 -- kernel 1 has just
-//     streamed them, so they come from the 256 MB Infinity Cache when they
-//     fit -- rebuilds each chunk's weights exactly and publishes sum min(p, q)
-//     and the residual mass.  The unit's last TV arriver sums c* and Res and,
+// unit.  The four launches, in stream order:
+//  1. stats_kernel: persistent wave64s stream every needed row exactly once
+//     from HBM with 16-byte loads, the items balanced over the waves through a
+//     per-block unit table in LDS.  Per item it writes the chunk's scaled max
+//     mu and weight sum S = sum 2^(z s - mu) per row (s = log2(e) / T), or the
+//     chunk argmax at T = 0.  Malformed requests get their outputs here.
+//  2. norm_kernel: one wave per unit folds the C chunk words into the row
+//     normalisers (M = max mu, Z = sum S 2^(mu - M)), runs the position's
+//     accept test on the two gathered logits, and for the bonus unit makes the
+//     inverse-CDF draw from q; at T = 0 it settles the unit completely.
+//  3. tv_kernel: the pair items at T > 0 again -- launch 1 has just streamed
+//     them, so they come from the 256 MB Infinity Cache when they fit -- with
+//     each chunk's weights rebuilt exactly as launch 1 made them; per item the
+//     chunk's sum min(p, q) and residual mass.
+//  4. tv_combine_kernel: one wave per pair unit at T > 0 sums c* and Res and,
 //     if the position was rejected, makes the residual draw.
-//  3. The wave that finishes a request's last unit (in either kernel) applies
-//     prefix survival to the units' accept bits and writes the outputs.
+// Each unit's last step (launch 2 or 4) arrives on its request's counter; the
+// wave completing a request applies prefix survival to the units' accept bits
+// and writes the outputs, and returns the counter to zero.
 // Words passed between waves are 64-bit (launch tag, payload) pairs written
 // and read with agent-scope atomics, so a reader never mistakes a stale word
-// for a current one; counters return to zero when their last arriver is done.
-// A wave only ever waits for words whose stores were issued before the
-// counter arrival that made it the last arriver, so no wait depends on
-// another wave being scheduled; every wait is still bounded and raises
-// SPEC_DEV_SPIN_TIMEOUT rather than spin forever.
+// (an earlier call's) for a current one.  A wave only ever waits for words
+// whose stores were issued before it read them as needed -- by an earlier
+// launch, or by the waves whose counter arrivals made it the request's last
+// -- so no wait depends on another wave being scheduled; every wait is still
+// bounded and raises SPEC_DEV_SPIN_TIMEOUT rather than spin forever.
 #include <math.h>
 #include <stddef.h>
 #include <stdio.h>
@@ -59,8 +61,8 @@ constexpr int kLanes = 64;
 // waves per SIMD the streaming kernels are compiled for (their registers fit)
 constexpr int kStreamWaves = 5;
 
-// Per-unit record words (tagged), filled by the unit's last arrivers and read
-// by the request's finaliser.
+// Per-unit record words (tagged), filled by the unit's combines (launches 2
+// and 4) and read by the request's finaliser.
 enum : int { kRecFlags = 0, kRecLqx = 1, kRecDraw = 2, kRecLqd = 3, kRecCs = 4, kRecRs = 5,
              kRecWords = 8 };
 constexpr uint32_t kFlagValid = 1u, kFlagAccept = 2u;
@@ -882,7 +884,7 @@ __device__ __forceinline__ void unit_done(const VerifyArgs &a, const Item &x) {
 }
 
 // ---------------------------------------------------------------------------
-// unit combines (run by the wave whose arrival completed the unit)
+// unit combines (one wave per unit, in launches 2 and 4)
 // ---------------------------------------------------------------------------
 
 // All C chunk statistics of unit x are published: row normalisers (published
@@ -1115,7 +1117,7 @@ __device__ __forceinline__ void tv_combine(const VerifyArgs &a, const Item &x) {
 }
 
 // ---------------------------------------------------------------------------
-// the two persistent kernels
+// the four kernels
 // ---------------------------------------------------------------------------
 
 // Issues item x's loads: its chunk of the target row and, for a pair, of the
@@ -1174,8 +1176,9 @@ __device__ __forceinline__ bool unit_item(const VerifyArgs &a, long u, Item &x) 
     return true;
 }
 
-// Kernel 1: every needed row streamed once from HBM, two items in flight per
-// wave; per item the chunk words.  Malformed requests get their outputs here.
+// Kernel 1: every needed row streamed once from HBM, one item in flight per
+// wave (five waves per SIMD); per item the chunk words.  Malformed requests
+// get their outputs here.
 template <typename TT, typename TD, int N, int EPV>
 __global__ void __launch_bounds__(kBlock, kStreamWaves) stats_kernel(VerifyArgs a) {
     if (!a.compact) {
@@ -1262,8 +1265,8 @@ __device__ __forceinline__ uint64_t load_tv_item(const VerifyArgs &a, const Item
     return w;
 }
 
-// Kernel 3: the TV pass over the pair items at T > 0, two items in flight
-// per wave.
+// Kernel 3: the TV pass over the pair items at T > 0, one item in flight per
+// wave.
 template <typename TT, typename TD, int N, int EPV>
 __global__ void __launch_bounds__(kBlock, kStreamWaves) tv_kernel(VerifyArgs a) {
     const int lane = lane_id();
