@@ -184,6 +184,15 @@ __device__ __forceinline__ int wave_min_i(int v) {
     return min(min(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
                min(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
 }
+// Wave inclusive prefix sum (fp64) in lane order.
+__device__ __forceinline__ double wave_incl_scan(double v) {
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const double n = __shfl_up(v, o, 64);
+        if ((int)(threadIdx.x & 63) >= o) v += n;
+    }
+    return v;
+}
 // (value, index): larger value wins, equal values -> smaller index.
 __device__ __forceinline__ void argmax_combine(float &v, int &i, float v2, int i2) {
     if (v2 > v || (v2 == v && i2 < i)) {

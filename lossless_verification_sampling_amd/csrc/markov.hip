@@ -10,15 +10,20 @@
 //
 // Per step k two launches:
 //  * markov_logits_kernel: one workgroup per 128-logit tile of the vocabulary.
-//    The tile of W2 ([256][128] bf16) is staged in LDS (transposed so each
-//    lane reads 8 consecutive k of one column), the gathered rows W1[x_{k-1}]
-//    of all requests feed v_mfma_f32_16x16x32_bf16 as the A operand, and the
-//    epilogue adds U_k, stores the fp32 logits and reduces per-(request,
-//    tile) softmax statistics (max and sum of 2^((l - m) s), or the argmax at
-//    T = 0).  W2 is read once per step for all requests.
-//  * markov_sample_kernel: one workgroup per request combines the tile
-//    statistics, picks the tile holding u * total (inverse CDF in ascending
-//    token id), re-reads that tile's 128 logits and finishes the draw.
+//    The tile of W2 ([256][128] bf16) is staged in LDS transposed, w2t[n][k],
+//    by loading 8x8 blocks, transposing them in registers and writing 16-byte
+//    rows.  The product b[v][r] = sum_k W2[k][v] W1[x_r][k] runs on
+//    v_mfma_f32_16x16x32_bf16 with the W2 tile as the A operand (16 vocabulary
+//    rows per block) and the gathered rows W1[x_{k-1}] as B (16 requests per
+//    block), so that each lane ends with four consecutive vocabulary entries
+//    of one request: U is read and the fp32 logits written 8 and 16 bytes at
+//    a time, and the per-(request, tile) softmax statistics (max and sum of
+//    2^((l - m) s), or the argmax at T = 0) reduce inside the wave.  W2 is
+//    read once per step for all requests.
+//  * markov_sample_kernel: one wave per request combines the tile statistics,
+//    picks the tile holding u * total (inverse CDF in ascending token id)
+//    with a wave scan, re-reads that tile's 128 logits and finishes the draw
+//    with a second scan.
 #include <math.h>
 
 #include "common.h"
@@ -26,9 +31,10 @@
 namespace sv {
 
 constexpr int kMkRank = 256;        // rank of W1 W2 (the pages' default r)
-constexpr int kMkTile = 128;        // logits per tile
+constexpr int kMkTile = 64;         // logits per tile (one workgroup each)
 constexpr int kMkRows = 64;         // requests per MFMA row block (4 waves x 16)
 constexpr int kMkLdsStride = kMkRank + 8;  // bf16 per LDS row (padding vs bank conflicts)
+constexpr int kMkBatch = 16;        // tile statistics loaded together per lane
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
@@ -42,6 +48,8 @@ struct MarkovArgs {
     const float *ud;         // [R][gamma]
     int R, gamma, V, ntiles;
     int k;                   // current step, 1..gamma
+    int vec;                 // U rows and logit rows allow 4-wide loads and stores
+    int tile0;               // first tile of the launch
     int32_t *out_tok;        // [R][gamma]
     float *out_logits;       // [R][gamma][V]
     float2 *tstats;          // [R][ntiles]: (max, exp-sum) or (max, argmax bits)
@@ -54,228 +62,385 @@ __device__ __forceinline__ bool mk_temperature_ok(float T) {
     return T == 0.0f || T >= 1e-30f;
 }
 
-template <typename TU>
-__global__ void __launch_bounds__(kBlock) markov_logits_kernel(MarkovArgs a) {
-    __shared__ __attribute__((aligned(16))) uint16_t w2t[kMkTile * kMkLdsStride];
-    const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63;
-    const int tile = blockIdx.x;
-    const long v0 = (long)tile * kMkTile;
-    const int V = a.V;
-
-    // ---- stage W2[:, v0:v0+128] transposed: w2t[n][k] ------------------------
-    // 256 rows of 128 bf16; thread t handles column group (t % 16) * 8 of rows
-    // t / 16, t / 16 + 16, ...
-    {
-        const int cg = (tid & 15) * 8;
-        for (int kk = tid >> 4; kk < kMkRank; kk += kBlock / 16) {
-            const long base = (long)kk * V + v0 + cg;
-            uint16_t v8[8];
-            if ((V & 7) == 0 && v0 + cg + 8 <= V) {
-                uint4 w = *reinterpret_cast<const uint4 *>(a.W2 + base);
-                v8[0] = (uint16_t)w.x; v8[1] = (uint16_t)(w.x >> 16);
-                v8[2] = (uint16_t)w.y; v8[3] = (uint16_t)(w.y >> 16);
-                v8[4] = (uint16_t)w.z; v8[5] = (uint16_t)(w.z >> 16);
-                v8[6] = (uint16_t)w.w; v8[7] = (uint16_t)(w.w >> 16);
-            } else {
+// 8 x 8 block transpose of bf16 pairs: r[j] holds row j (8 values, two per
+// word); c[i] gets column i (the 8 rows' values, two per word, row order).
+__device__ __forceinline__ void transpose8x8(const uint4 (&r)[8], uint4 (&c)[8]) {
 #pragma unroll
-                for (int q = 0; q < 8; ++q) v8[q] = (v0 + cg + q < V) ? a.W2[base + q] : (uint16_t)0;
-            }
+    for (int i = 0; i < 8; ++i) {
+        uint32_t w[4];
 #pragma unroll
-            for (int q = 0; q < 8; ++q) w2t[(cg + q) * kMkLdsStride + kk] = v8[q];
+        for (int d = 0; d < 4; ++d) {
+            const uint4 &lo = r[2 * d], &hi = r[2 * d + 1];
+            const uint32_t a = (i >> 1) == 0 ? lo.x : (i >> 1) == 1 ? lo.y : (i >> 1) == 2 ? lo.z : lo.w;
+            const uint32_t b = (i >> 1) == 0 ? hi.x : (i >> 1) == 1 ? hi.y : (i >> 1) == 2 ? hi.z : hi.w;
+            w[d] = (i & 1) ? ((b & 0xffff0000u) | (a >> 16)) : ((b << 16) | (a & 0xffffu));
         }
+        c[i] = make_uint4(w[0], w[1], w[2], w[3]);
     }
-    __syncthreads();
+}
 
-    const int col_in_blk = lane & 15;     // column within a 16-wide block
-    const int kgrp = lane >> 4;           // which 8-wide k group of the 32
-    const int k = a.k;
+// Per-lane operands of one 16-request block: the request, its W1 row slices
+// (the B operand for the 8 k steps) and its U values for the tile.
+template <typename TU> struct MkLane;
+template <> struct MkLane<uint16_t> {
+    uint2 u[kMkTile / 16];  // 4 bf16 of U per vocabulary block
+};
+template <> struct MkLane<float> {
+    float4 u[kMkTile / 16];
+};
 
-    for (int rb = 0; rb * kMkRows < a.R; ++rb) {
-        // A operand rows of this wave: r = rb * 64 + wave * 16 + (lane % 16)
-        const int ra = rb * kMkRows + wave * 16 + (lane & 15);
-        int xprev = -1;
-        if (ra < a.R) xprev = (k == 1) ? a.anchor[ra] : a.out_tok[(size_t)ra * a.gamma + (k - 2)];
-        const bool xok = xprev >= 0 && xprev < V;
-        f32x4_t acc[kMkTile / 16];
+// The previous token of request r (the anchor at the first step); -1 for a
+// request outside the batch.
+__device__ __forceinline__ int mk_prev_token(const MarkovArgs &a, int r) {
+    if (r >= a.R) return -1;
+    return (a.k == 1) ? a.anchor[r] : a.out_tok[(size_t)r * a.gamma + (a.k - 2)];
+}
+
+// U values of request r for this lane's 4 vocabulary entries in each block.
+template <typename TU, bool FULL>
+__device__ __forceinline__ void mk_load_u(const MarkovArgs &a, int r, long v0, int kgrp,
+                                          MkLane<TU> &ln) {
+    const int V = a.V;
+    const TU *urow = (const TU *)a.U + ((long)(r < a.R ? r : 0) * a.gamma + (a.k - 1)) * V;
 #pragma unroll
-        for (int nb = 0; nb < kMkTile / 16; ++nb) acc[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 1
-        for (int ks = 0; ks < kMkRank / 32; ++ks) {
-            const int kk = ks * 32 + kgrp * 8;
-            uint4 araw = make_uint4(0u, 0u, 0u, 0u);
-            if (xok) araw = *reinterpret_cast<const uint4 *>(a.W1 + (long)xprev * kMkRank + kk);
-            const bf16x8_t av = __builtin_bit_cast(bf16x8_t, araw);
-#pragma unroll
-            for (int nb = 0; nb < kMkTile / 16; ++nb) {
-                const uint4 braw = *reinterpret_cast<const uint4 *>(
-                    &w2t[(nb * 16 + col_in_blk) * kMkLdsStride + kk]);
-                const bf16x8_t bv = __builtin_bit_cast(bf16x8_t, braw);
-                acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc[nb], 0, 0, 0);
-            }
-        }
-        // ---- epilogue: D lane layout row = (lane / 16) * 4 + j, col = lane % 16
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int r = rb * kMkRows + wave * 16 + kgrp * 4 + j;
-            const bool rok = r < a.R;
-            const float T = rok ? a.temp[r] : 1.0f;
-            const bool greedy = (T == 0.0f);
-            const float s = (!greedy && mk_temperature_ok(T)) ? (float)(kLog2e / (double)T) : 1.0f;
-            float lv[kMkTile / 16];
-            float m = -__builtin_inff();
-            int arg = 0x7fffffff, nanseen = 0;
-#pragma unroll
-            for (int nb = 0; nb < kMkTile / 16; ++nb) {
-                const long v = v0 + nb * 16 + col_in_blk;
-                float l = -__builtin_inff();
-                if (rok && v < V) {
-                    const TU *urow = (const TU *)a.U + ((long)r * a.gamma + (k - 1)) * V;
-                    l = load_one(urow, v) + acc[nb][j];
-                    a.out_logits[((long)r * a.gamma + (k - 1)) * V + v] = l;
-                }
-                lv[nb] = l;
-                if (l != l) nanseen = 1;
-                if (l > m) { m = l; arg = (int)v; }
-            }
-            // reduce over the 16 lanes sharing this row (lane bits 0..3)
-#pragma unroll
-            for (int o = 1; o < 16; o <<= 1) {
-                const float m2 = __shfl_xor(m, o, 64);
-                const int a2 = __shfl_xor(arg, o, 64);
-                argmax_combine(m, arg, m2, a2);
-            }
-#pragma unroll
-            for (int o = 1; o < 16; o <<= 1) nanseen |= __shfl_xor(nanseen, o, 64);
-            float out1;
-            if (greedy) {
-                if (nanseen) m = __builtin_nanf("");
-                out1 = __int_as_float(arg);
+    for (int vb = 0; vb < kMkTile / 16; ++vb) {
+        const long v = v0 + vb * 16 + kgrp * 4;
+        if constexpr (sizeof(TU) == 2) {
+            if constexpr (FULL) {
+                ln.u[vb] = *reinterpret_cast<const uint2 *>(urow + v);
             } else {
-                float e = 0.0f;
-                if (m > -__builtin_inff()) {
+                uint32_t h[4];
 #pragma unroll
-                    for (int nb = 0; nb < kMkTile / 16; ++nb)
-                        e += __builtin_amdgcn_exp2f((lv[nb] - m) * s);
-                } else {
-#pragma unroll
-                    for (int nb = 0; nb < kMkTile / 16; ++nb)
-                        if (lv[nb] != lv[nb]) e = lv[nb];
-                }
-#pragma unroll
-                for (int o = 1; o < 16; o <<= 1) e += __shfl_xor(e, o, 64);
-                out1 = e;
+                for (int j = 0; j < 4; ++j) h[j] = (v + j < V) ? (uint32_t)urow[v + j] : 0u;
+                ln.u[vb] = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
             }
-            if (rok && col_in_blk == 0) a.tstats[(size_t)r * a.ntiles + tile] = make_float2(m, out1);
+        } else {
+            if constexpr (FULL) {
+                ln.u[vb] = *reinterpret_cast<const float4 *>(urow + v);
+            } else {
+                float h[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) h[j] = (v + j < V) ? urow[v + j] : 0.0f;
+                ln.u[vb] = make_float4(h[0], h[1], h[2], h[3]);
+            }
         }
     }
 }
 
-// One workgroup per request: tile choice, then the draw inside the tile.
+// The B operand of the 8 k steps: W1[xprev][ks * 32 + kgrp * 8 .. + 8]
+// (zero for an invalid previous token).
+__device__ __forceinline__ void mk_load_w1(const MarkovArgs &a, int xprev, int kgrp,
+                                           uint4 (&b)[kMkRank / 32]) {
+    const bool xok = xprev >= 0 && xprev < a.V;
+    const uint16_t *w1 = a.W1 + (long)(xok ? xprev : 0) * kMkRank + kgrp * 8;
+#pragma unroll
+    for (int ks = 0; ks < kMkRank / 32; ++ks) {
+        b[ks] = *reinterpret_cast<const uint4 *>(w1 + ks * 32);
+        if (!xok) b[ks] = make_uint4(0u, 0u, 0u, 0u);
+    }
+}
+
+__device__ __forceinline__ void mk_unpack_u(const uint2 &w, float (&o)[4]) {
+    o[0] = bf16_lo(w.x); o[1] = bf16_hi(w.x); o[2] = bf16_lo(w.y); o[3] = bf16_hi(w.y);
+}
+__device__ __forceinline__ void mk_unpack_u(const float4 &w, float (&o)[4]) {
+    o[0] = w.x; o[1] = w.y; o[2] = w.z; o[3] = w.w;
+}
+
+// FULL: every tile of the launch lies inside the row, V is a multiple of 8
+// (16-byte aligned W2 rows) and the U and logit rows allow 4-wide accesses,
+// so every load and store is a vector; otherwise (odd V, the ragged last
+// tile, unaligned U or logits) they are guarded scalars.
+template <typename TU, bool FULL>
+__global__ void __launch_bounds__(kBlock, 4) markov_logits_kernel(MarkovArgs a) {
+    __shared__ __attribute__((aligned(16))) uint16_t w2t[kMkTile * kMkLdsStride];
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
+    const int tile = a.tile0 + (int)blockIdx.x;
+    const long v0 = (long)tile * kMkTile;
+    const int V = a.V;
+    const int col = lane & 15;   // request within the wave's 16 / vocabulary row within A
+    const int kgrp = lane >> 4;  // which 8-wide k group of the 32
+
+    // ---- issue every load of the first request block up front ---------------
+    // W2 block (k0.., n0..): 8 consecutive threads read one 128-byte row piece
+    const int k0 = (tid >> 3) * 8, n0 = (tid & 7) * 8;
+    uint4 rw[8];
+    if constexpr (FULL) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            rw[j] = *reinterpret_cast<const uint4 *>(a.W2 + (long)(k0 + j) * V + v0 + n0);
+    } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            uint32_t w[4];
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                const long c = v0 + n0 + 2 * d;
+                const uint32_t x0 = c < V ? a.W2[(long)(k0 + j) * V + c] : 0u;
+                const uint32_t x1 = c + 1 < V ? a.W2[(long)(k0 + j) * V + c + 1] : 0u;
+                w[d] = x0 | (x1 << 16);
+            }
+            rw[j] = make_uint4(w[0], w[1], w[2], w[3]);
+        }
+    }
+    int xprev = mk_prev_token(a, wave * 16 + col);
+    MkLane<TU> ln;
+    mk_load_u<TU, FULL>(a, wave * 16 + col, v0, kgrp, ln);
+    // the W1 operand too, where registers allow (the guarded variant's
+    // scalar staging needs them; it loads W1 after the barrier)
+    uint4 bop[kMkRank / 32];
+    if constexpr (FULL) mk_load_w1(a, xprev, kgrp, bop);
+
+    // ---- stage W2[:, v0:v0+64] transposed: w2t[n][k] -------------------------
+    {
+        uint4 cw[8];
+        transpose8x8(rw, cw);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            *reinterpret_cast<uint4 *>(&w2t[(n0 + i) * kMkLdsStride + k0]) = cw[i];
+    }
+    __syncthreads();
+
+    for (int rb = 0; rb * kMkRows < a.R; ++rb) {
+        const int r = rb * kMkRows + wave * 16 + col;
+        const bool rok = r < a.R;
+        // keeps the tile's LDS reads inside the loop: hoisted out of it they
+        // would hold the whole 32 KB A operand in registers
+        asm volatile("" ::: "memory");
+        if (rb > 0) {
+            xprev = mk_prev_token(a, r);
+            mk_load_u<TU, FULL>(a, r, v0, kgrp, ln);
+        }
+        if (rb > 0 || !FULL) mk_load_w1(a, xprev, kgrp, bop);
+        // b[v][r] = sum_k W2[k][v] W1[x_r][k]: A = the W2 tile (16 vocabulary
+        // rows per block), B = 16 gathered W1 rows
+        f32x4_t acc[kMkTile / 16];
+#pragma unroll
+        for (int vb = 0; vb < kMkTile / 16; ++vb) acc[vb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < kMkRank / 32; ++ks) {
+            const bf16x8_t bv = __builtin_bit_cast(bf16x8_t, bop[ks]);
+#pragma unroll
+            for (int vb = 0; vb < kMkTile / 16; ++vb) {
+                const uint4 araw = *reinterpret_cast<const uint4 *>(
+                    &w2t[(vb * 16 + col) * kMkLdsStride + ks * 32 + kgrp * 8]);
+                acc[vb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    __builtin_bit_cast(bf16x8_t, araw), bv, acc[vb], 0, 0, 0);
+            }
+        }
+        // ---- epilogue: acc[vb][j] = b[v][r], v = v0 + vb * 16 + kgrp * 4 + j
+        const float T = rok ? a.temp[r] : 1.0f;
+        const bool greedy = (T == 0.0f);
+        const float s = (!greedy && mk_temperature_ok(T)) ? (float)(kLog2e / (double)T) : 1.0f;
+        float *lrow = a.out_logits + ((long)(rok ? r : 0) * a.gamma + (a.k - 1)) * V;
+        float lv[kMkTile / 16][4];
+        float m = -__builtin_inff();
+        int arg = 0x7fffffff, nanseen = 0;
+#pragma unroll
+        for (int vb = 0; vb < kMkTile / 16; ++vb) {
+            const long v = v0 + vb * 16 + kgrp * 4;
+            float u4[4];
+            mk_unpack_u(ln.u[vb], u4);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float l = (rok && v + j < V) ? u4[j] + acc[vb][j] : -__builtin_inff();
+                lv[vb][j] = l;
+                if (l != l) nanseen = 1;
+                if (l > m) { m = l; arg = (int)(v + j); }
+            }
+            if (rok) {
+                if constexpr (FULL) {
+                    *reinterpret_cast<float4 *>(lrow + v) =
+                        make_float4(lv[vb][0], lv[vb][1], lv[vb][2], lv[vb][3]);
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        if (v + j < V) lrow[v + j] = lv[vb][j];
+                }
+            }
+        }
+        // reduce over the 4 lanes sharing this request (lane bits 4..5)
+#pragma unroll
+        for (int o = 16; o < 64; o <<= 1) {
+            const float m2 = __shfl_xor(m, o, 64);
+            const int a2 = __shfl_xor(arg, o, 64);
+            argmax_combine(m, arg, m2, a2);
+            nanseen |= __shfl_xor(nanseen, o, 64);
+        }
+        float out1;
+        if (greedy) {
+            if (nanseen) m = __builtin_nanf("");
+            out1 = __int_as_float(arg);
+        } else {
+            float e = 0.0f;
+            if (m > -__builtin_inff()) {
+#pragma unroll
+                for (int vb = 0; vb < kMkTile / 16; ++vb)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) e += __builtin_amdgcn_exp2f((lv[vb][j] - m) * s);
+            } else {
+#pragma unroll
+                for (int vb = 0; vb < kMkTile / 16; ++vb)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        if (lv[vb][j] != lv[vb][j]) e = lv[vb][j];
+            }
+#pragma unroll
+            for (int o = 16; o < 64; o <<= 1) e += __shfl_xor(e, o, 64);
+            out1 = e;
+        }
+        if (rok && kgrp == 0) a.tstats[(size_t)r * a.ntiles + tile] = make_float2(m, out1);
+    }
+}
+
+// Tile mass relative to the row maximum M: sum over the tile of 2^((l - M) s).
+__device__ __forceinline__ double mk_tile_mass(float2 st, float M, float s) {
+    return st.x > -__builtin_inff()
+               ? (double)st.y * (double)__builtin_amdgcn_exp2f((st.x - M) * s)
+               : 0.0;
+}
+
+// One workgroup per request; thread i owns the run of tiles [i tp, (i + 1) tp)
+// and keeps its statistics in registers (NB >= tp, else batches of NB).
+//  1. every load of the request is issued at once: its parameters and the
+//     statistics of every run.  The block takes the row maximum M, each
+//     thread its run's mass relative to M, and a block scan over the 256 run
+//     masses finds the run holding u * total;
+//  2. every thread walks its run in registers; the hit thread's walk gives
+//     the tile and the target left inside it;
+//  3. the first wave reads that tile's 64 logits (one per lane) and a wave
+//     scan finds the token.
+// The CDF must exceed the target strictly; a target at or past the total,
+// which only rounding can produce, takes the last token of positive mass.
+// Lane indices in the first wave come from ballots, so they are wave-uniform
+// and neighbouring prefixes are read with readlane.
+template <int NB>
 __global__ void __launch_bounds__(kBlock) markov_sample_kernel(MarkovArgs a) {
     __shared__ BlockScratch bs;
-    __shared__ int s_tok;
-    __shared__ double s_t;
-    const int tid = threadIdx.x;
+    __shared__ int s_tile;
+    __shared__ double s_tin;
+    const int tid = threadIdx.x, lane = tid & 63;
     const int r = blockIdx.x;
     const int k = a.k;
     const int V = a.V;
+    const int nt = a.ntiles;
+    const int tp = (nt + kBlock - 1) / kBlock;  // tiles per thread
+    const int nb = (tp + NB - 1) / NB;          // register batches per run
+    const int t0 = tid * tp;
+    const float2 *ts = a.tstats + (size_t)r * nt;
+    float2 st[NB];
+    auto load_batch = [&](int b) {
+#pragma unroll
+        for (int i = 0; i < NB; ++i) st[i] = ts[min(t0 + b * NB + i, nt - 1)];
+    };
+    auto valid = [&](int b, int i) { return b * NB + i < tp && t0 + b * NB + i < nt; };
     const float T = a.temp[r];
     const int32_t anc = a.anchor[r];
-    bool ok = mk_temperature_ok(T) && anc >= 0 && anc < V && a.bad[r] == 0u;
+    const uint32_t rbad = a.bad[r];
     const float u = a.ud[(size_t)r * a.gamma + (k - 1)];
+    load_batch(0);
+    bool ok = mk_temperature_ok(T) && anc >= 0 && anc < V && rbad == 0u;
     if (T != 0.0f && !(u >= 0.0f && u < 1.0f)) ok = false;
-    const float2 *ts = a.tstats + (size_t)r * a.ntiles;
+    const float s = (T > 0.0f && ok) ? (float)(kLog2e / (double)T) : 1.0f;
     int token = -1;
 
-    if (ok && T == 0.0f) {
-        float bv = -__builtin_inff();
-        int bi = 0x7fffffff, nan = 0;
-        for (int t = tid; t < a.ntiles; t += kBlock) {
-            const float2 st = ts[t];
-            if (st.x != st.x) nan = 1;
-            argmax_combine(bv, bi, st.x, __float_as_int(st.y));
+    // pass 1: run maximum, NaN flags, greedy argmax
+    float lm = -__builtin_inff();
+    int bad = 0;
+    float bv = -__builtin_inff();
+    int bi = 0x7fffffff;
+    for (int b = 0; b < nb; ++b) {
+        if (b > 0) load_batch(b);
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+            if (!valid(b, i)) continue;
+            const float2 x = st[i];
+            if (x.x != x.x || (T != 0.0f && x.y != x.y)) bad = 1;
+            if (T == 0.0f)
+                argmax_combine(bv, bi, x.x, __float_as_int(x.y));
+            else
+                lm = fmaxf(lm, x.x);
         }
+    }
+    bad = block_max_i(bad, bs);
+    if (ok && T == 0.0f) {
         float dv = -__builtin_inff();
         int di = 0;
         block_argmax2(bv, bi, dv, di, bs);
-        nan = block_max_i(nan, bs);
-        ok = !nan && bv < __builtin_inff() && bi != 0x7fffffff;
+        ok = !bad && bv < __builtin_inff() && bi != 0x7fffffff;
         token = bi;
     } else if (ok) {
-        const float s = (float)(kLog2e / (double)T);
-        float M = -__builtin_inff(), dummy = -__builtin_inff();
-        int bad = 0;
-        for (int t = tid; t < a.ntiles; t += kBlock) {
-            const float2 st = ts[t];
-            M = fmaxf(M, st.x);
-            if (st.y != st.y) bad = 1;
-        }
+        float M = lm, dummy = -__builtin_inff();
         block_max2(M, dummy, bs);
-        bad = block_max_i(bad, bs);
         ok = !bad && M > -__builtin_inff() && M < __builtin_inff();
         if (ok) {
-            // tile masses in tile order, processed 256 tiles at a time
-            double W = 0.0;
-            for (int t0 = 0; t0 < a.ntiles; t0 += kBlock) {
-                const int t = t0 + tid;
-                double w = 0.0;
-                if (t < a.ntiles) {
-                    const float2 st = ts[t];
-                    if (st.x > -__builtin_inff()) w = (double)st.y * exp2((double)(st.x - M) * (double)s);
+            // run masses relative to M, block scan, the run holding u * W
+            double lsum = 0.0;
+            int lastp = -1;
+            for (int b = 0; b < nb; ++b) {
+                if (nb > 1) load_batch(b);
+#pragma unroll
+                for (int i = 0; i < NB; ++i) {
+                    if (!valid(b, i)) continue;
+                    const double w = mk_tile_mass(st[i], M, s);
+                    lsum += w;
+                    if (w > 0.0) lastp = t0 + b * NB + i;
                 }
-                double tot;
-                (void)block_exclusive_scan(w, &tot, bs);
-                W += tot;
             }
+            double W;
+            const double excl = block_exclusive_scan(lsum, &W, bs);
             const double tt = (double)u * W;
-            double run = 0.0;
-            int tile = -1, last_pos = -1;
-            double tsel = 0.0;
-            for (int t0 = 0; t0 < a.ntiles; t0 += kBlock) {
-                const int t = t0 + tid;
-                double w = 0.0;
-                if (t < a.ntiles) {
-                    const float2 st = ts[t];
-                    if (st.x > -__builtin_inff()) w = (double)st.y * exp2((double)(st.x - M) * (double)s);
+            const int h = block_min_i((lsum > 0.0 && excl + lsum > tt) ? tid : 0x7fffffff, bs);
+            if (h == 0x7fffffff) {  // u * W at or past the total (rounding)
+                const int lt = block_max_i(lastp, bs);
+                if (tid == 0) {
+                    s_tile = lt;
+                    s_tin = INFINITY;
                 }
-                double tot;
-                const double excl = run + block_exclusive_scan(w, &tot, bs);
-                const int hit = block_min_i((t < a.ntiles && excl + w > tt) ? t : 0x7fffffff, bs);
-                last_pos = max(last_pos, block_max_i(w > 0.0 ? t : -1, bs));
-                if (hit != 0x7fffffff) {  // block-uniform
-                    if (t == hit) s_t = tt - excl;
-                    __syncthreads();
-                    tile = hit;
-                    tsel = s_t;
-                    break;
+            } else if (tid == h) {
+                // pass 2: the hit thread walks its run
+                double run = excl;
+                int tl = -1;
+                double tin = INFINITY;
+                for (int b = 0; b < nb && tl < 0; ++b) {
+                    if (nb > 1) load_batch(b);
+#pragma unroll
+                    for (int i = 0; i < NB; ++i) {
+                        if (!valid(b, i) || tl >= 0) continue;
+                        const double w = mk_tile_mass(st[i], M, s);
+                        if (w > 0.0 && run + w > tt) {
+                            tl = t0 + b * NB + i;
+                            tin = tt - run;
+                        }
+                        run += w;
+                    }
                 }
-                run += tot;
-            }
-            if (tile < 0) {  // u * W at or past the total (rounding): last positive tile
-                tile = last_pos;
-                tsel = INFINITY;
-            }
-            if (tile < 0) tile = 0;  // unreachable: the tile holding the max has mass
-            // draw inside the tile (one lane walks the 128 logits in order)
-            if (tid == 0) {
-                const float m = ts[tile].x;
-                const long v0 = (long)tile * kMkTile;
-                const float *lrow = a.out_logits + ((long)r * a.gamma + (k - 1)) * V;
-                double cum = 0.0;
-                int tok = -1, lastp = -1;
-                for (int q = 0; q < kMkTile && v0 + q < V; ++q) {
-                    const float e = (m > -__builtin_inff())
-                                        ? __builtin_amdgcn_exp2f((lrow[v0 + q] - m) * s)
-                                        : 0.0f;
-                    if (e > 0.0f) lastp = (int)(v0 + q);
-                    cum += (double)e * exp2((double)(m - M) * (double)s);
-                    if (tok < 0 && cum > tsel) tok = (int)(v0 + q);
-                }
-                s_tok = (tok >= 0) ? tok : lastp;
+                if (tl < 0) tl = lastp;  // rounding inside the run: its last tile with mass
+                s_tile = tl;
+                s_tin = tin;
             }
             __syncthreads();
-            token = s_tok;
+            int tile = s_tile;
+            const double tin = s_tin;
+            if (tile < 0) tile = 0;  // unreachable: the tile holding M has mass
+            if (tid < 64) {
+                // round 3: the tile's logits, one per lane, in id order
+                const float m = ts[tile].x;
+                const long v = (long)tile * kMkTile + lane;
+                const float *lrow = a.out_logits + ((long)r * a.gamma + (k - 1)) * V;
+                const float e = (v < V && m > -__builtin_inff())
+                                    ? __builtin_amdgcn_exp2f((lrow[min(v, (long)V - 1)] - m) * s)
+                                    : 0.0f;
+                const double w3 = (double)e * (double)__builtin_amdgcn_exp2f((m - M) * s);
+                const double inc3 = wave_incl_scan(w3);
+                const uint64_t h3 = __ballot(w3 > 0.0 && inc3 > tin);
+                const uint64_t pos3 = __ballot(w3 > 0.0);
+                if (h3)
+                    token = tile * kMkTile + __builtin_ctzll(h3);
+                else
+                    token = pos3 ? tile * kMkTile + 63 - __builtin_clzll(pos3) : -1;
+            }
             ok = token >= 0;
         }
     }
@@ -359,18 +524,41 @@ int spec_markov_draft_sample(const void *U, int u_dtype, const void *W1, const v
     a.tstats = (float2 *)(ws + p.off_stats);
     a.bad = (uint32_t *)(ws + p.off_bad);
     a.ctl = (Control *)ws;
+    const size_t ub = (u_dtype == SPEC_BF16) ? 2 : 4;
+    a.vec = (V % 4 == 0) && ((uintptr_t)U % (4 * ub) == 0) && ((uintptr_t)out_draft_logits % 16 == 0);
     note_workspace_clean(workspace, sizeof(Control));
     hipStream_t st = (hipStream_t)stream;
     hipLaunchKernelGGL(markov_clear_kernel, dim3((R + kBlock - 1) / kBlock), dim3(kBlock), 0, st,
                        a.bad, R);
+    // whole tiles in 16-byte aligned rows take the vector kernel; the ragged
+    // last tile (or every tile of an odd V or unaligned rows) the guarded one
+    const int nfull = (V % 8 == 0 && a.vec) ? V / kMkTile : 0;
+    const int tp = (p.ntiles + kBlock - 1) / kBlock;  // tiles per thread of the sampling block
     for (int k = 1; k <= gamma; ++k) {
         a.k = k;
-        if (u_dtype == SPEC_BF16)
-            hipLaunchKernelGGL(markov_logits_kernel<uint16_t>, dim3(p.ntiles), dim3(kBlock), 0, st,
-                               a);
+        const bool bf = (u_dtype == SPEC_BF16);
+        if (nfull > 0) {
+            a.tile0 = 0;
+            if (bf)
+                hipLaunchKernelGGL((markov_logits_kernel<uint16_t, true>), dim3(nfull), dim3(kBlock),
+                                   0, st, a);
+            else
+                hipLaunchKernelGGL((markov_logits_kernel<float, true>), dim3(nfull), dim3(kBlock), 0,
+                                   st, a);
+        }
+        if (nfull < p.ntiles) {
+            a.tile0 = nfull;
+            if (bf)
+                hipLaunchKernelGGL((markov_logits_kernel<uint16_t, false>), dim3(p.ntiles - nfull),
+                                   dim3(kBlock), 0, st, a);
+            else
+                hipLaunchKernelGGL((markov_logits_kernel<float, false>), dim3(p.ntiles - nfull),
+                                   dim3(kBlock), 0, st, a);
+        }
+        if (tp <= 8)
+            hipLaunchKernelGGL(markov_sample_kernel<8>, dim3(R), dim3(kBlock), 0, st, a);
         else
-            hipLaunchKernelGGL(markov_logits_kernel<float>, dim3(p.ntiles), dim3(kBlock), 0, st, a);
-        hipLaunchKernelGGL(markov_sample_kernel, dim3(R), dim3(kBlock), 0, st, a);
+            hipLaunchKernelGGL(markov_sample_kernel<16>, dim3(R), dim3(kBlock), 0, st, a);
     }
     return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_EHIP;
 }

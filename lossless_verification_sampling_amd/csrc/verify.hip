@@ -175,16 +175,6 @@ __device__ __forceinline__ uint32_t rl(uint32_t v, int l) {
 }
 __device__ __forceinline__ float rlf(float v, int l) { return readlane_f(v, l); }
 
-// Wave inclusive prefix sum (fp64) in lane order.
-__device__ __forceinline__ double wave_incl_scan(double v) {
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const double n = __shfl_up(v, o, 64);
-        if (lane_id() >= o) v += n;
-    }
-    return v;
-}
-
 // ---------------------------------------------------------------------------
 // items
 // ---------------------------------------------------------------------------

@@ -67,6 +67,7 @@ def compare_markov(mk, tok, lg, ref, rows=None):
     (70, 2, 2048, 1.0),     # two MFMA row blocks
     (4, 3, 4096, 0.0),      # greedy
     (1, 7, 129280, 1.0),
+    (2, 2, 300000, 0.8),    # more than 64 tiles per lane in the sampling scan
 ])
 def test_markov_small(sv, dev, R, gamma, V, T):
     print(f"[markov] R={R} gamma={gamma} V={V} T={T}", flush=True)
@@ -75,6 +76,29 @@ def test_markov_small(sv, dev, R, gamma, V, T):
     ref = oracle.markov_draft(mk.U, mk.W1, mk.W2, mk.anchor, mk.temperature, mk.u_draft)
     ties = compare_markov(mk, tok, lg, ref)
     print(f"[markov] near ties: {ties}", flush=True)
+
+
+@pytest.mark.parametrize("u_f32", [False, True])
+def test_markov_unaligned_rows(sv, dev, u_f32):
+    """U and the logits output one element off 16-byte alignment: every tile
+    takes the guarded (scalar) path."""
+    R, gamma, V = 5, 3, 1024
+    mk = workloads.dspark_markov(seed=11, R=R, gamma=gamma, V=V, temperature=0.9)
+    if u_f32:
+        mk.U = (mk.U.astype(np.uint32) << 16).view(np.float32)
+    u_dev = to_device(mk.U, dev)
+    u_big = torch.empty(u_dev.numel() + 1, dtype=u_dev.dtype, device=dev)
+    u_off = u_big[1:].view(R, gamma, V)
+    u_off.copy_(u_dev)
+    lg_big = torch.empty(R * gamma * V + 1, dtype=torch.float32, device=dev)
+    lg_off = lg_big[1:].view(R, gamma, V)
+    tok, lg = sv.spec_markov_draft_sample(u_off, to_device(mk.W1, dev), to_device(mk.W2, dev),
+                                          to_device(mk.anchor, dev),
+                                          to_device(mk.temperature, dev),
+                                          to_device(mk.u_draft, dev), out_logits=lg_off)
+    torch.cuda.synchronize()
+    ref = oracle.markov_draft(mk.U, mk.W1, mk.W2, mk.anchor, mk.temperature, mk.u_draft)
+    compare_markov(mk, tok.cpu().numpy(), lg.cpu().numpy(), ref)
 
 
 def test_markov_invalid(sv, dev):
