@@ -230,7 +230,8 @@ def bench_dspark(args):
         "roofline": {"bound": "hbm", "achieved": per_step_bytes / (ms.mean() / 1e3) / 1e9,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": per_step_bytes / (ms.mean() / 1e3) / 1e9 / HBM_PEAK_GBS,
-                     "traffic": None, "algorithmic_bytes_per_call": per_step_bytes,
+                     "traffic": measured_traffic("markov_dspark"),
+                     "algorithmic_bytes_per_call": per_step_bytes,
                      "mfma_tflops": flops / (ms.mean() / 1e3) / 1e12},
     }
 
@@ -250,6 +251,74 @@ def calibrate_copy(args):
             "bytes_written_per_copy": nbytes, "copies": args.warmup + args.steps}
 
 
+def counter_rows(d, counter):
+    """(kernel name, value) of every dispatch in a rocprofv3 --pmc csv output."""
+    import csv
+    import glob
+    rows = []
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            for row in csv.DictReader(fh):
+                if row.get("Counter_Name") == counter:
+                    rows.append((row.get("Kernel_Name", ""), float(row["Counter_Value"])))
+    return rows
+
+
+def write_traffic(args):
+    """Per-call HBM bytes of this library's kernels from two rocprofv3 --pmc
+    runs of a workload (FETCH_SIZE, WRITE_SIZE; KiB per dispatch), each scaled
+    by what the same counter reads for the 256 MiB device copy of
+    --calibrate-copy.  Kernels dispatched fewer times than there were calls
+    (one-time workspace set-up) are left out.  Writes the entry under --key
+    in the traffic file, stamped with the current source hash."""
+    fetch_dir, write_dir, cfetch_dir, cwrite_dir = args.traffic_from
+    calls = args.warmup + args.steps
+    copy_bytes = 256 << 20
+
+    def scale(d, counter):
+        # the copy kernel is the one dispatched once per copy (the source fill
+        # of the calibration run is a different kernel, dispatched once)
+        groups = {}
+        for name, v in counter_rows(d, counter):
+            groups.setdefault(name, []).append(v)
+        vals = [v for vs in groups.values() if len(vs) == args.copies_counted for v in vs]
+        if not vals:
+            raise SystemExit(f"no kernel with {args.copies_counted} {counter} dispatches under {d}")
+        return copy_bytes / (sum(vals) / len(vals) * 1024.0)
+
+    def per_call(d, counter, sc):
+        per_kernel = {}
+        for name, v in counter_rows(d, counter):
+            if "sv::" not in name:
+                continue
+            key = name.split("(")[0].replace("void ", "")
+            n, tot = per_kernel.get(key, (0, 0.0))
+            per_kernel[key] = (n + 1, tot + v)
+        out = {k: tot * 1024.0 * sc / calls for k, (n, tot) in per_kernel.items() if n >= calls}
+        return out
+
+    fs, ws = scale(cfetch_dir, "FETCH_SIZE"), scale(cwrite_dir, "WRITE_SIZE")
+    fk, wk = per_call(fetch_dir, "FETCH_SIZE", fs), per_call(write_dir, "WRITE_SIZE", ws)
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        t = {}
+    t[args.key] = {
+        "source_hash": source_hash(),
+        "bytes_per_launch": sum(fk.values()) + sum(wk.values()),
+        "fetch_bytes": sum(fk.values()), "write_bytes": sum(wk.values()),
+        "fetch_scale": fs, "write_scale": ws,
+        "per_kernel_fetch": fk, "per_kernel_write": wk,
+        "note": "per call, summed over the library's kernels; FETCH_SIZE then WRITE_SIZE in "
+                "separate rocprofv3 --pmc runs, scaled by a 256 MiB device copy",
+    }
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(t, f, indent=1, sort_keys=True)
+        f.write("\n")
+    return t[args.key]
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -262,7 +331,16 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only copy a 256 MiB buffer (reference for the HBM byte counters)")
+    ap.add_argument("--traffic-from", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
+                    help="rocprofv3 --pmc output folders: write the traffic entry --key from them "
+                         "(--steps/--warmup as in the counted run)")
+    ap.add_argument("--key", default="verify_batched")
+    ap.add_argument("--copies-counted", type=int, default=6,
+                    help="copies in the counted --calibrate-copy run")
     args = ap.parse_args()
+    if args.traffic_from:
+        print(json.dumps(write_traffic(args)))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
               "(requests shard across GPUs with no exchange; see the design notes)",
