@@ -24,15 +24,16 @@
 //     mu and weight sum S = sum 2^(z s - mu) per row (s = log2(e) / T), or the
 //     chunk argmax at T = 0.  Malformed requests get their outputs here.
 //  2. norm_kernel: one wave per unit folds the C chunk words into the row
-//     normalisers (M = max mu, Z = sum S 2^(mu - M)), runs the position's
-//     accept test on the two gathered logits, and for the bonus unit makes the
-//     inverse-CDF draw from q; at T = 0 it settles the unit completely.
+//     normalisers (M = max mu, Z = sum S 2^(mu - M)); at T = 0 it runs the
+//     argmax test and settles the unit completely.
 //  3. tv_kernel: the pair items at T > 0 again -- launch 1 has just streamed
 //     them, so they come from the 256 MB Infinity Cache when they fit -- with
 //     each chunk's weights rebuilt exactly as launch 1 made them; per item the
 //     chunk's sum min(p, q) and residual mass.
-//  4. tv_combine_kernel: one wave per pair unit at T > 0 sums c* and Res and,
-//     if the position was rejected, makes the residual draw.
+//  4. tv_combine_kernel: one wave per unit at T > 0.  A position runs its
+//     accept test on the two gathered logits, sums c* and Res and, if
+//     rejected, makes the residual draw; the bonus unit makes the
+//     inverse-CDF draw from q.
 // Each unit's last step (launch 2 or 4) arrives on its request's counter; the
 // wave completing a request applies prefix survival to the units' accept bits
 // and writes the outputs, and returns the counter to zero.
@@ -877,8 +878,8 @@ __device__ __forceinline__ void unit_done(const VerifyArgs &a, const Item &x) {
 // unit combines (one wave per unit, in launches 2 and 4)
 // ---------------------------------------------------------------------------
 
-// All C chunk statistics of unit x are published: row normalisers (published
-// first, for the TV items), then the unit's accept test or bonus draw.
+// All C chunk statistics of unit x are published: the row normalisers (for
+// the TV items and the last combine), or at T = 0 the unit's argmax test.
 template <typename TT, typename TD, int N, int EPV>
 __device__ __forceinline__ void stats_combine(const VerifyArgs &a, const Item &x) {
     const int lane = lane_id();
@@ -887,14 +888,9 @@ __device__ __forceinline__ void stats_combine(const VerifyArgs &a, const Item &x
     uint64_t *nrm = a.nrm + (size_t)x.u * 4;
     uint64_t *rec = a.rec + (size_t)x.u * kRecWords;
     const float nan = __builtin_nanf("");
-    // the position's draft token and uniforms, loaded early
+    // the position's draft token (greedy accept test), loaded early
     int xtok = 0;
-    float uacc = 0.0f, usm = 0.0f;
-    if (!a.tv_mode) {
-        if (pair) xtok = a.tokens[(size_t)x.r * G + x.i];
-        if (pair) uacc = a.ua[(size_t)x.r * G + x.i];
-        usm = a.us[(size_t)x.r * (G + 1) + x.i];
-    }
+    if (!a.tv_mode && pair && x.T == 0.0f) xtok = a.tokens[(size_t)x.r * G + x.i];
     uint32_t w[kCB][4];
     const bool want[4] = {true, true, pair, pair};
     load_unit_words<4>(a.st1 + (size_t)x.u * C * 4, C, want, a.tag, a.ctl, w, true);
@@ -959,55 +955,82 @@ __device__ __forceinline__ void stats_combine(const VerifyArgs &a, const Item &x
     publish_n(nrm, a.tag, 4, __float_as_uint(Mt), __float_as_uint(Zt), __float_as_uint(Md),
               __float_as_uint(Zd));
 
-    bool valid = finite_f(Mt) && Zt > 0.0f && finite_f(Zt);
-    if (pair) valid = valid && finite_f(Md) && Zd > 0.0f && finite_f(Zd);
     if (a.tv_mode) {
+        bool valid = finite_f(Mt) && Zt > 0.0f && finite_f(Zt);
+        if (pair) valid = valid && finite_f(Md) && Zd > 0.0f && finite_f(Zd);
         publish_n(rec, a.tag, 1, valid ? kFlagValid : 0u, 0u, 0u, 0u);
-        return;
     }
-    const float s = x.s;
-    const TT *trow = row_ptr<TT>(a.zt, x.r, a.tG, x.i, a.V);
-    if (pair) {
-        valid = valid && xtok >= 0 && xtok < a.V && uniform_ok(uacc) && uniform_ok(usm);
-        bool acc = false;
-        float lqx = nan;
-        if (valid) {
-            const float zx = load_one(trow, xtok);
-            const float dx = load_one(row_ptr<TD>(a.zd, x.r, a.dG, x.i, a.V), xtok);
-            const double lq2 = (double)zx * (double)s - (double)Mt;
-            const double lp2 = (double)dx * (double)s - (double)Md;
-            const double q = exp2(lq2) / (double)Zt;
-            const double p = exp2(lp2) / (double)Zd;
-            acc = q >= p || (double)uacc < q / p;
-            lqx = (float)(lq2 * kLn2 - log((double)Zt));
+    // the accept test of a position and the draw of the bonus token come in
+    // the last combine, which has the normalisers in the same batch as its
+    // TV words
+}
+
+// All C TV partials of pair unit x (T > 0) are published: c*, Res, and the
+// residual draw if the position was rejected.
+// The bonus unit at T > 0 (target row l_r): the draw from q by inverse CDF,
+// from the unit's chunk words and normalisers.
+template <typename TT, typename TD, int N, int EPV>
+__device__ __forceinline__ void bonus_draw(const VerifyArgs &a, const Item &x) {
+    const int lane = lane_id();
+    const int C = a.C, G = a.gamma;
+    const float nan = __builtin_nanf("");
+    uint64_t *rec = a.rec + (size_t)x.u * kRecWords;
+    const float usm = a.us[(size_t)x.r * (G + 1) + x.i];
+    uint32_t w[kCB][2];
+    float Mt, Zt;
+    {
+        const uint64_t *p[2 * kCB + 1];
+        bool act[2 * kCB + 1];
+        uint32_t o[2 * kCB + 1];
+#pragma unroll
+        for (int b = 0; b < kCB; ++b)
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const int c = b * 64 + lane;
+                p[b * 2 + q] = a.st1 + ((size_t)x.u * C + c) * 4 + q;
+                act[b * 2 + q] = c < C;
+            }
+        p[2 * kCB] = a.nrm + (size_t)x.u * 4 + (lane & 1);
+        act[2 * kCB] = lane < 2;
+        await_batch<2 * kCB + 1>(p, act, a.tag, a.ctl, o, true);
+#pragma unroll
+        for (int b = 0; b < kCB; ++b) {
+            w[b][0] = o[b * 2];
+            w[b][1] = o[b * 2 + 1];
         }
-        const uint32_t fl = (valid ? kFlagValid : 0u) | (acc ? kFlagAccept : 0u);
-        publish_n(rec, a.tag, 2, fl, __float_as_uint(lqx), 0u, 0u);
-        return;  // c*, Res and any residual draw come from the TV combine
+        Mt = __uint_as_float(rl(o[2 * kCB], 0));
+        Zt = __uint_as_float(rl(o[2 * kCB], 1));
     }
-    // bonus unit: the draw from q of target row l
-    valid = valid && uniform_ok(usm);
+    const bool valid = finite_f(Mt) && Zt > 0.0f && finite_f(Zt) && uniform_ok(usm);
     int tok = -1;
     float lqd = nan;
     if (valid) {
+        const float s = x.s;
         float ztok;
-        tok = draw_from_q<TT, N, EPV, 4>(a, trow, w, s, Mt, Zt, usm, &ztok);
+        tok = draw_from_q<TT, N, EPV, 2>(a, row_ptr<TT>(a.zt, x.r, a.tG, x.i, a.V), w, s, Mt, Zt,
+                                         usm, &ztok);
         lqd = (float)(((double)ztok * (double)s - (double)Mt) * kLn2 - log((double)Zt));
     }
     publish_n(rec, a.tag, 4, valid ? kFlagValid : 0u, 0u, (uint32_t)tok, __float_as_uint(lqd));
     unit_done(a, x);
 }
 
-// All C TV partials of pair unit x (T > 0) are published: c*, Res, and the
-// residual draw if the position was rejected.
 template <typename TT, typename TD, int N, int EPV>
 __device__ __forceinline__ void tv_combine(const VerifyArgs &a, const Item &x) {
     const int lane = lane_id();
     const int C = a.C, G = a.gamma;
+    const float nan = __builtin_nanf("");
     uint64_t *rec = a.rec + (size_t)x.u * kRecWords;
-    float usm = 0.0f;
-    if (!a.tv_mode) usm = a.us[(size_t)x.r * (G + 1) + x.i];
-    // the unit's TV words, its record flags and its normalisers in one batch
+    // the position's draft token and uniforms, loaded early
+    float usm = 0.0f, uacc = 0.0f;
+    int xtok = 0;
+    if (!a.tv_mode) {
+        usm = a.us[(size_t)x.r * (G + 1) + x.i];
+        xtok = a.tokens[(size_t)x.r * G + x.i];
+        uacc = a.ua[(size_t)x.r * G + x.i];
+    }
+    // the unit's TV words, its record flags (row-pair mode) and its
+    // normalisers in one batch
     uint32_t v2[kCB][2];
     {
         const uint64_t *p[2 * kCB + 2];
@@ -1022,7 +1045,7 @@ __device__ __forceinline__ void tv_combine(const VerifyArgs &a, const Item &x) {
                 act[b * 2 + q] = c < C;
             }
         p[2 * kCB] = rec + kRecFlags;
-        act[2 * kCB] = lane == 0;
+        act[2 * kCB] = a.tv_mode && lane == 0;
         p[2 * kCB + 1] = a.nrm + (size_t)x.u * 4 + (lane & 3);
         act[2 * kCB + 1] = lane < 4;
         await_batch<2 * kCB + 2>(p, act, a.tag, a.ctl, o, true);
@@ -1044,9 +1067,8 @@ __device__ __forceinline__ void tv_combine(const VerifyArgs &a, const Item &x) {
         }
         cs = wave_sum(cs);
         rs = wave_sum(rs);
-        const bool valid = fl & kFlagValid;
         if (a.tv_mode) {
-            if (!valid) {
+            if (!(fl & kFlagValid)) {
                 write_invalid(a, x.r);
             } else if (lane == 0) {
                 a.out_cs[x.r] = (float)cs;
@@ -1054,12 +1076,30 @@ __device__ __forceinline__ void tv_combine(const VerifyArgs &a, const Item &x) {
             }
             return;
         }
+        // the accept test: p and q of the draft token from the gathered logits
+        const float s = x.s;
+        const TT *trow = row_ptr<TT>(a.zt, x.r, a.tG, x.i, a.V);
+        const TD *drow = row_ptr<TD>(a.zd, x.r, a.dG, x.i, a.V);
+        const bool valid = finite_f(Mt) && Zt > 0.0f && finite_f(Zt) && finite_f(Md) &&
+                           Zd > 0.0f && finite_f(Zd) && xtok >= 0 && xtok < a.V &&
+                           uniform_ok(uacc) && uniform_ok(usm);
+        bool acc = false;
+        float lqx = nan;
+        if (valid) {
+            const float zx = load_one(trow, xtok);
+            const float dx = load_one(drow, xtok);
+            const double lq2 = (double)zx * (double)s - (double)Mt;
+            const double lp2 = (double)dx * (double)s - (double)Md;
+            const double q = exp2(lq2) / (double)Zt;
+            const double pp = exp2(lp2) / (double)Zd;
+            acc = q >= pp || (double)uacc < q / pp;
+            lqx = (float)(lq2 * kLn2 - log((double)Zt));
+        }
+        publish_n(rec, a.tag, 2, (valid ? kFlagValid : 0u) | (acc ? kFlagAccept : 0u),
+                  __float_as_uint(lqx), 0u, 0u);
         int tok = -1;
-        float lqd = __builtin_nanf("");
-        if (valid && !(fl & kFlagAccept)) {
-            const float s = x.s;
-            const TT *trow = row_ptr<TT>(a.zt, x.r, a.tG, x.i, a.V);
-            const TD *drow = row_ptr<TD>(a.zd, x.r, a.dG, x.i, a.V);
+        float lqd = nan;
+        if (valid && !acc) {
             float ztok = 0.0f;
             if (rs > 0.0) {
                 // residual [q - p]_+: chunk masses, then one chunk in id order
@@ -1189,8 +1229,8 @@ __global__ void __launch_bounds__(kBlock, kStreamWaves) stats_kernel(VerifyArgs 
     }
 }
 
-// Kernel 2: one wave per active unit combines kernel 1's chunk words
-// (normalisers, accept test, bonus draw; everything at T = 0).
+// Kernel 2: one wave per active unit combines kernel 1's chunk words into
+// the row normalisers (at T = 0: the argmax test, which settles the unit).
 template <typename TT, typename TD, int N, int EPV>
 __global__ void __launch_bounds__(kBlock) norm_kernel(VerifyArgs a) {
     Item x;
@@ -1279,13 +1319,18 @@ __global__ void __launch_bounds__(kBlock, kStreamWaves) tv_kernel(VerifyArgs a) 
     }
 }
 
-// Kernel 4: one wave per pair unit at T > 0 sums its TV words into c* and
-// Res and makes the residual draw if the position was rejected; the wave that
-// finishes a request's last unit writes the request's outputs.
+// Kernel 4: one wave per unit at T > 0.  A position runs its accept test,
+// sums its TV words into c* and Res and makes the residual draw if rejected;
+// the bonus unit draws from q.  The wave that finishes a request's last unit
+// writes the request's outputs.
 template <typename TT, typename TD, int N, int EPV>
 __global__ void __launch_bounds__(kBlock) tv_combine_kernel(VerifyArgs a) {
     Item x;
-    if (unit_item(a, wave_index(), x) && is_tv(x)) tv_combine<TT, TD, N, EPV>(a, x);
+    if (!unit_item(a, wave_index(), x) || x.T == 0.0f) return;
+    if (is_pair(x))
+        tv_combine<TT, TD, N, EPV>(a, x);
+    else
+        bonus_draw<TT, TD, N, EPV>(a, x);
 }
 
 __global__ void zero_fill_kernel(uint32_t *p, size_t n_words) {
