@@ -653,6 +653,44 @@ __device__ __forceinline__ void await_batch(const uint64_t *const (&p)[K], const
     for (int k = 0; k < K; ++k) out[k] = (uint32_t)v[k];
 }
 
+// await_batch in two halves, so that other loads can be issued in between:
+// words_issue loads every word unconditionally (an inactive one from `safe`,
+// a valid address, and then reads as current), words_settle re-polls any
+// stale active word.  Unconditional loads keep the compiler's wait counts
+// exact for loads issued after them.
+template <int K>
+__device__ __forceinline__ void words_issue(const uint64_t *const (&p)[K], const bool (&act)[K],
+                                            const uint64_t *safe, uint32_t tag,
+                                            uint64_t (&v)[K]) {
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        const uint64_t w = *(act[k] ? p[k] : safe);
+        v[k] = act[k] ? w : ((uint64_t)tag << 32);
+    }
+}
+template <int K>
+__device__ __forceinline__ void words_settle(const uint64_t *const (&p)[K], const bool (&act)[K],
+                                             uint32_t tag, Control *ctl, uint64_t (&v)[K],
+                                             uint32_t (&out)[K]) {
+    uint32_t it = 0;
+    for (;;) {
+        bool stale = false;
+#pragma unroll
+        for (int k = 0; k < K; ++k) stale = stale || (act[k] && (uint32_t)(v[k] >> 32) != tag);
+        if (!__ballot(stale)) break;
+        if ((++it & 255u) == 0u &&
+            (it > kSpinLimit || (atomic_load_u32(&ctl->status) & SPEC_DEV_SPIN_TIMEOUT))) {
+            if (stale) atomic_or_u32(&ctl->status, SPEC_DEV_SPIN_TIMEOUT);
+            break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+        for (int k = 0; k < K; ++k)
+            if (act[k] && (uint32_t)(v[k] >> 32) != tag) v[k] = ld_word(p[k]);
+    }
+#pragma unroll
+    for (int k = 0; k < K; ++k) out[k] = (uint32_t)v[k];
+}
+
 // Chunk words of a unit, for the lane's chunks c = 64 b + lane (b < kCB):
 // w[b][q] = word q of chunk c (q < Q), 0 where c >= C or !want[q].
 template <int Q>
@@ -720,25 +758,25 @@ __device__ __forceinline__ uint32_t chunk_word(const uint32_t (&w)[kCB][Q], int 
 }
 
 // Draw inside chunk c0 of a row: the first id (ascending) whose running weight
-// exceeds tin.  wfn(e, out) gives the EPV weights of ids e..e+EPV-1 (0 past
-// the row end).  Scans the chunk one vector row (64 lanes x EPV ids) at a
-// time.  Clamps to the chunk's last positive weight; if none, its first id.
-template <int N, int EPV, typename WFn>
-__device__ __forceinline__ int draw_in_chunk(long c0, double tin, WFn wfn) {
+// exceeds tin.  w[j][q] of lane l is the weight of id c0 + (64 j + l) EPV + q
+// (0 past the row end).  Scans the chunk one vector row (64 lanes x EPV ids)
+// at a time.  Clamps to the chunk's last positive weight; if none, its first
+// id.
+template <int N, int EPV>
+__device__ __forceinline__ int draw_in_chunk_w(long c0, double tin,
+                                               const float (&w)[N / EPV][EPV]) {
     const int lane = lane_id();
     double run = 0.0;
     int lastpos = -1;
-#pragma unroll 1
+#pragma unroll
     for (int j = 0; j < N / EPV; ++j) {
         const long e = c0 + ((long)j * kLanes + lane) * EPV;
-        float w[EPV];
-        wfn(e, w);
         double tot = 0.0;
         int lp = -1;
 #pragma unroll
         for (int q = 0; q < EPV; ++q) {
-            tot += (double)w[q];
-            if (w[q] > 0.0f) lp = (int)e + q;
+            tot += (double)w[j][q];
+            if (w[j][q] > 0.0f) lp = (int)e + q;
         }
         lastpos = max(lastpos, wave_max_i(lp));
         const double incl = wave_incl_scan(tot);
@@ -751,7 +789,7 @@ __device__ __forceinline__ int draw_in_chunk(long c0, double tin, WFn wfn) {
                 double cum = excl;
 #pragma unroll
                 for (int q = 0; q < EPV; ++q) {
-                    cum += (double)w[q];
+                    cum += (double)w[j][q];
                     if (tok < 0 && cum > tin) tok = (int)e + q;
                 }
                 if (tok < 0) tok = lp;  // rounding: last positive id of this lane
@@ -763,15 +801,35 @@ __device__ __forceinline__ int draw_in_chunk(long c0, double tin, WFn wfn) {
     return lastpos >= 0 ? lastpos : (int)c0;
 }
 
-// Loads EPV logits of a row at ids e.. as fp32 (-inf past the row end).
-template <typename T, int EPV>
-__device__ __forceinline__ void load_ids(const T *row, long e, int V, float (&z)[EPV]) {
-    if (e < V) {
-        VecLoad<T, EPV>::run(row, e, z);
-    } else {
+// Chunk logits in the draw's layout: z[j][q] of lane l is id c0 + (64 j + l)
+// EPV + q; past the row end -inf.  The loads are unconditional (an id past
+// the end re-reads id 0), so all of them are in flight at once.
+template <typename T, int N, int EPV>
+__device__ __forceinline__ void load_chunk_ids(const T *row, long c0, int V,
+                                               float (&z)[N / EPV][EPV]) {
+    const int lane = lane_id();
 #pragma unroll
-        for (int q = 0; q < EPV; ++q) z[q] = -kInf;
+    for (int j = 0; j < N / EPV; ++j) {
+        const long e = c0 + ((long)j * kLanes + lane) * EPV;
+        VecLoad<T, EPV>::run(row, e < V ? e : 0, z[j]);
+        if (e >= V) {
+#pragma unroll
+            for (int q = 0; q < EPV; ++q) z[j][q] = -kInf;
+        }
     }
+}
+
+// The logit of id tok (inside the chunk from c0) out of z, from its lane.
+template <int N, int EPV>
+__device__ __forceinline__ float chunk_logit(long c0, int tok, const float (&z)[N / EPV][EPV]) {
+    const int rel = tok - (int)c0;
+    const int jt = rel / (kLanes * EPV), lt = (rel / EPV) % kLanes, qt = rel % EPV;
+    float v = 0.0f;
+#pragma unroll
+    for (int j = 0; j < N / EPV; ++j)
+#pragma unroll
+        for (int q = 0; q < EPV; ++q) v = (j == jt && q == qt) ? z[j][q] : v;
+    return readlane_f(v, lt);
 }
 
 // Draw from q of a target row (T > 0), its chunk words w (mu_t, S_t in q = 0,
@@ -799,13 +857,14 @@ __device__ __forceinline__ int draw_from_q(const VerifyArgs &a, const TT *trow,
     const float ref = exp_ref(mu);
     const long c0 = (long)cs * kLanes * N;
     const double te = (al > 0.0f) ? tin / (double)al : INFINITY;
-    const int tok = draw_in_chunk<N, EPV>(c0, te, [&](long e, float (&wv)[EPV]) {
-        float z[EPV];
-        load_ids<TT, EPV>(trow, e, a.V, z);
+    float z[N / EPV][EPV], wv[N / EPV][EPV];
+    load_chunk_ids<TT, N, EPV>(trow, c0, a.V, z);
 #pragma unroll
-        for (int q = 0; q < EPV; ++q) wv[q] = ew(z[q], s, ref);
-    });
-    *ztok = load_one(trow, tok);
+    for (int j = 0; j < N / EPV; ++j)
+#pragma unroll
+        for (int q = 0; q < EPV; ++q) wv[j][q] = ew(z[j][q], s, ref);
+    const int tok = draw_in_chunk_w<N, EPV>(c0, te, wv);
+    *ztok = chunk_logit<N, EPV>(c0, tok, z);
     return tok;
 }
 
@@ -1108,29 +1167,35 @@ __device__ __forceinline__ void tv_combine(const VerifyArgs &a, const Item &x) {
                 for (int b = 0; b < kCB; ++b) m[b] = (double)__uint_as_float(v2[b][1]);
                 double tin;
                 const int csel = select_chunk(C, (double)usm * rs, m, &tin);
+                // the chunk's words and both rows' logits in one round of loads
+                const long c0 = (long)csel * kLanes * N;
                 const uint64_t *const sp[1] = {a.st1 + ((size_t)x.u * C + csel) * 4 + (lane & 3)};
                 const bool sa[1] = {lane < 4};
+                uint64_t sv[1];
                 uint32_t so[1];
-                await_batch<1>(sp, sa, a.tag, a.ctl, so, true);
+                words_issue<1>(sp, sa, sp[0], a.tag, sv);
+                float zt[N / EPV][EPV], zd[N / EPV][EPV];
+                load_chunk_ids<TT, N, EPV>(trow, c0, a.V, zt);
+                load_chunk_ids<TD, N, EPV>(drow, c0, a.V, zd);
+                words_settle<1>(sp, sa, a.tag, a.ctl, sv, so);
                 const uint32_t s4 = so[0];
                 const float mut = __uint_as_float(rl(s4, 0)), mud = __uint_as_float(rl(s4, 2));
                 const PairScale ps =
                     pair_scale(chunk_alpha(mut, Mt, Zt), chunk_alpha(mud, Md, Zd));
                 const float reft = exp_ref(mut), refd = exp_ref(mud);
-                const long c0 = (long)csel * kLanes * N;
                 const double te = (ps.unit > 0.0f) ? tin / (double)ps.unit : INFINITY;
-                tok = draw_in_chunk<N, EPV>(c0, te, [&](long e, float (&wv)[EPV]) {
-                    float zt[EPV], zd[EPV];
-                    load_ids<TT, EPV>(trow, e, a.V, zt);
-                    load_ids<TD, EPV>(drow, e, a.V, zd);
+                float wv[N / EPV][EPV];
+#pragma unroll
+                for (int j = 0; j < N / EPV; ++j)
 #pragma unroll
                     for (int q = 0; q < EPV; ++q) {
-                        const float et = ew(zt[q], s, reft) * ps.kt;
-                        const float mn = __builtin_elementwise_minimum(et, ew(zd[q], s, refd) * ps.kd);
-                        wv[q] = et - mn;
+                        const float et = ew(zt[j][q], s, reft) * ps.kt;
+                        const float mn =
+                            __builtin_elementwise_minimum(et, ew(zd[j][q], s, refd) * ps.kd);
+                        wv[j][q] = et - mn;
                     }
-                });
-                ztok = load_one(trow, tok);
+                tok = draw_in_chunk_w<N, EPV>(c0, te, wv);
+                ztok = chunk_logit<N, EPV>(c0, tok, zt);
             } else {
                 // no residual mass (rounding): draw from q of the same row
                 uint32_t w4[kCB][4];
