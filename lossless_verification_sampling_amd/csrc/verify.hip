@@ -1510,9 +1510,29 @@ uint32_t next_tag() {
     return (counter.fetch_add(1u) + 1u) | 0x80000000u;
 }
 
-// Persistent grid of kernel k: its resident capacity, at most one wave per item.
+// Compute units of the current device (cached per device; 0 if unknown).
+long device_cus() {
+    static std::mutex mu;
+    static std::vector<std::pair<int, int>> cache;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    std::lock_guard<std::mutex> lock(mu);
+    for (const auto &e : cache)
+        if (e.first == dev) return e.second;
+    int ncu = 0;
+    if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return 0;
+    cache.emplace_back(dev, ncu);
+    return ncu;
+}
+
+// Persistent grid of kernel k: its resident capacity, at most kStreamWaves
+// workgroups per CU (the streaming passes measure fastest there, also when
+// the registers would let more be resident), at most one wave per item.
 long persistent_grid(const void *k, size_t lds, long items) {
-    const long cap = resident_blocks(k, lds);
+    long cap = resident_blocks(k, lds);
+    const long cus = device_cus();
+    if (cap > 0 && cus > 0 && cap > cus * kStreamWaves) cap = cus * kStreamWaves;
     const long want = (items + kWaves - 1) / kWaves;
     if (cap <= 0) return want > 0 ? want : 1;
     const long g = want < cap ? want : cap;
