@@ -20,7 +20,8 @@ Prints one JSON line:
   cpu_baseline  the fp64 oracle on the host (one thread) over the same batch
 
 --workload dspark measures the Markov-head draft (R = 64, gamma = 7,
-V = 129280, rank 256) instead, as an extra line.
+V = 129280, rank 256) instead, as an extra line; --workload schedule the
+confidence-scheduled verify lengths of the same batch size (448 candidates).
 """
 from __future__ import annotations
 
@@ -236,6 +237,64 @@ def bench_dspark(args):
     }
 
 
+def bench_schedule(args):
+    """Confidence-scheduled verify lengths for the headline batch (R = 64,
+    gamma = 7) on the smooth step-rate curve: one workgroup sorts the 448
+    candidates and finds the early stop.  The oracle (plain Python) is timed
+    beside it."""
+    import torch
+    import lossless_verification_sampling_amd as sv
+    import workloads
+
+    dev = torch.device("cuda:0")
+    R, gamma = 64, 7
+    case = workloads.schedule_case(seed=args.seed + 5, R=R, gamma=gamma, curve="smooth")
+    conf = to_device(case.conf, dev)
+    sps = to_device(case.sps, dev)
+    ln = torch.empty((R,), dtype=torch.int32, device=dev)
+    th = torch.empty((1,), dtype=torch.float64, device=dev)
+    ws = sv.Workspace(dev, sv.spec_schedule_workspace_bytes())
+    for _ in range(args.warmup):
+        sv.spec_schedule_verify_len(conf, sps, out_len=ln, out_theta=th, workspace=ws)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        ev[k][0].record(stream)
+        sv.spec_schedule_verify_len(conf, sps, out_len=ln, out_theta=th, workspace=ws)
+        ev[k][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = np.array([a.elapsed_time(b) for a, b in ev])
+    res = {
+        "metric": "confidence-scheduled verify lengths: schedules/sec",
+        "value": args.steps / wall,
+        "unit": "schedules/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": wall / args.steps * 1e3,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32 products, f64 sums", "data": "synthetic",
+        "config": {"workload": "schedule", "R": R, "gamma": gamma, "candidates": R * gamma,
+                   "curve": "smooth", "admitted": int(ln.sum().item())},
+        "roofline": None,
+        "kernel_us_mean": float(ms.mean()) * 1e3,
+        "note": "one workgroup, latency-bound (a bitonic sort of 512 keys in LDS, a block "
+                "scan and a block minimum); no HBM or MFMA roofline applies",
+    }
+    if not args.no_cpu_baseline:
+        from oracle import schedule as osch
+        n, t1 = 0, time.perf_counter()
+        while time.perf_counter() - t1 < min(args.cpu_seconds, 5.0):
+            osch.schedule(case.conf, case.sps)
+            n += 1
+        el = time.perf_counter() - t1
+        res["cpu_baseline"] = {"value": n / el, "unit": "schedules/s", "cores": 1, "kind": "oracle",
+                               "sample": f"{n} schedules of the same 64 x 7 pool, plain Python"}
+    return res
+
+
 def calibrate_copy(args):
     """One device-to-device copy of a known size, repeated: the reference that
     scales rocprofv3's FETCH_SIZE / WRITE_SIZE counters to bytes."""
@@ -326,7 +385,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--seed", type=int, default=3)
     ap.add_argument("--copies", type=int, default=0, help="input copies rotated (0 = auto)")
-    ap.add_argument("--workload", choices=["batched", "dspark"], default="batched")
+    ap.add_argument("--workload", choices=["batched", "dspark", "schedule"], default="batched")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -349,7 +408,8 @@ def main():
     if args.calibrate_copy:
         res = calibrate_copy(args)
     else:
-        res = bench_verify(args) if args.workload == "batched" else bench_dspark(args)
+        res = {"batched": bench_verify, "dspark": bench_dspark,
+               "schedule": bench_schedule}[args.workload](args)
     print(json.dumps(res))
 
 

@@ -79,6 +79,9 @@ typedef enum {
  * is cut into at most 256 chunks of 1024 logits). */
 #define SPEC_MAX_VERIFY_VOCAB 262144
 
+/* Largest candidate pool (R * gamma, and R) spec_schedule_verify_len accepts. */
+#define SPEC_SCHED_MAX_POOL 8192
+
 /* Library version, major * 10000 + minor * 100 + patch. */
 int spec_version(void);
 
@@ -182,6 +185,40 @@ int spec_markov_draft_sample(const void *U, int u_dtype,
                              const float *u_draft,
                              int R, int gamma, int V, int rank,
                              int32_t *out_draft_tokens, float *out_draft_logits,
+                             void *workspace, size_t workspace_bytes, void *stream);
+
+/* Workspace bytes for spec_schedule_verify_len (the device status word). */
+size_t spec_schedule_workspace_bytes(void);
+
+/*
+ * Confidence-scheduled verify lengths (DSpark guide, "scheduler").
+ *
+ * The survival probability of draft position j of request r is the running
+ * product a[r][j] = c[r][1] * ... * c[r][j] of the confidence head's outputs
+ * (fp32, left to right).  All candidates (r, j) form one pool in descending
+ * a (ties: request, then position ascending).  Starting from l_r = 0 for
+ * every request (B = R, tau = R), candidates are admitted in pool order,
+ * each adding 1 to B and a[r][j] to tau (fp64), and
+ *   topk < 0:  the walk stops at the first admission after which
+ *              Theta = tau * sps[B] is not larger than before it (the early
+ *              stop of the pages' greedy scheduler);
+ *   topk >= 0: the first topk candidates are admitted (the asynchronous
+ *              top-K variant), with no comparison.
+ * Either walk also stops before B would pass bmax.  out_len[r] is the number
+ * of admitted positions of request r (always a prefix).
+ *   confidence  [R][gamma]  fp32 in [0, 1]      (device)
+ *   sps         [bmax + 1]  fp32 >= 0, finite   (device; steps per second at
+ *                                                batch size B, index B)
+ *   out_len     [R]         int32               (device)
+ *   out_theta   [1]         fp64, nullable      (device; Theta of the result)
+ * Sizes: R >= 0, gamma >= 0, bmax >= 0, R * gamma <= SPEC_SCHED_MAX_POOL.
+ * A confidence outside [0, 1] (or NaN) or a negative or non-finite table
+ * entry sets SPEC_DEV_BAD_REQUEST in the workspace status word and every
+ * out_len to -1.  One workgroup; the inputs, outputs and workspace belong to
+ * the caller; work is enqueued on `stream`.
+ */
+int spec_schedule_verify_len(const float *confidence, const float *sps, int R, int gamma,
+                             int bmax, int topk, int32_t *out_len, double *out_theta,
                              void *workspace, size_t workspace_bytes, void *stream);
 
 /* Synchronises `stream`, copies the workspace's device status word (the OR

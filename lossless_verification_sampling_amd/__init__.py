@@ -28,6 +28,7 @@ SPEC_DEV_BAD_REQUEST = 0x1
 SPEC_DEV_SPIN_TIMEOUT = 0x2
 SPEC_MAX_VOCAB = 2097152
 SPEC_MAX_VERIFY_VOCAB = 262144
+SPEC_SCHED_MAX_POOL = 8192
 
 EXPORTED = (
     "spec_version",
@@ -38,6 +39,8 @@ EXPORTED = (
     "spec_tv_workspace_bytes",
     "spec_tv_accept_rate",
     "spec_markov_workspace_bytes",
+    "spec_schedule_workspace_bytes",
+    "spec_schedule_verify_len",
     "spec_markov_draft_sample",
     "spec_get_device_status",
 )
@@ -73,6 +76,10 @@ def _load() -> ctypes.CDLL:
     lib.spec_tv_accept_rate.argtypes = [p, p, i, p, i, i, p, p, p, sz, p]
     lib.spec_markov_draft_sample.restype = i
     lib.spec_markov_draft_sample.argtypes = [p, i, p, p, i, p, p, p, i, i, i, i, p, p, p, sz, p]
+    lib.spec_schedule_workspace_bytes.restype = sz
+    lib.spec_schedule_workspace_bytes.argtypes = []
+    lib.spec_schedule_verify_len.restype = i
+    lib.spec_schedule_verify_len.argtypes = [p, p, i, i, i, i, p, p, p, sz, p]
     lib.spec_get_device_status.restype = i
     lib.spec_get_device_status.argtypes = [p, ctypes.POINTER(ctypes.c_uint32), i, p]
     return lib
@@ -103,6 +110,10 @@ def spec_tv_workspace_bytes(N: int, V: int) -> int:
 
 def spec_markov_workspace_bytes(R: int, gamma: int, V: int, rank: int) -> int:
     return int(_lib.spec_markov_workspace_bytes(R, gamma, V, rank))
+
+
+def spec_schedule_workspace_bytes() -> int:
+    return int(_lib.spec_schedule_workspace_bytes())
 
 
 # ---------------------------------------------------------------------------
@@ -287,6 +298,33 @@ def spec_tv_accept_rate(draft_logits: torch.Tensor, target_logits: torch.Tensor,
                                   buf.numel(), _stream_ptr(stream, dev))
     _raise(st, "spec_tv_accept_rate")
     return cs, rs
+
+
+def spec_schedule_verify_len(confidence: torch.Tensor, sps: torch.Tensor, *, topk: int = -1,
+                             out_len: Optional[torch.Tensor] = None,
+                             out_theta: Optional[torch.Tensor] = None,
+                             workspace: Optional[Workspace] = None, stream=None):
+    """Confidence-scheduled verify lengths.  confidence [R, gamma] float32 in
+    [0, 1], sps [bmax + 1] float32 (steps per second at batch size B).  topk < 0:
+    greedy admission with early stop; topk >= 0: the top-K variant.  Returns
+    (lengths [R] int32, theta [1] float64)."""
+    R, gamma = confidence.shape
+    dev = confidence.device
+    _check(confidence, "confidence", torch.float32, (R, gamma), dev)
+    _check(sps, "sps", torch.float32, None, dev)
+    if sps.dim() != 1 or sps.numel() < 1:
+        raise ValueError("sps must be a non-empty 1-D table")
+    ln = out_len if out_len is not None else torch.empty((R,), dtype=torch.int32, device=dev)
+    th = out_theta if out_theta is not None else torch.empty((1,), dtype=torch.float64, device=dev)
+    _check(ln, "out_len", torch.int32, (R,), dev)
+    _check(th, "out_theta", torch.float64, (1,), dev)
+    ws = workspace or default_workspace(dev)
+    buf = ws.ensure(spec_schedule_workspace_bytes(), stream)
+    st = _lib.spec_schedule_verify_len(_ptr(confidence), _ptr(sps), R, gamma, sps.numel() - 1,
+                                       int(topk), _ptr(ln), _ptr(th), _ptr(buf), buf.numel(),
+                                       _stream_ptr(stream, dev))
+    _raise(st, "spec_schedule_verify_len")
+    return ln, th
 
 
 def spec_markov_draft_sample(U: torch.Tensor, W1: torch.Tensor, W2: torch.Tensor,

@@ -135,6 +135,37 @@ def test_markov_and_tv_argument_validation(lib):
     assert t(fake, fake, 0, fake, 0, 100, fake, None, None, 0, None) == SPEC_OK
 
 
+def test_schedule_argument_validation(lib):
+    p = ctypes.c_void_p
+    fake = p(0x1000)
+    f = lib.spec_schedule_verify_len
+    f.restype = ctypes.c_int
+    f.argtypes = [p, p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, p, p, p,
+                  ctypes.c_size_t, p]
+    w = lib.spec_schedule_workspace_bytes
+    w.restype = ctypes.c_size_t
+    assert w() == 256
+
+    def sc(**kw):
+        a = dict(c=fake, sps=fake, R=64, gamma=7, bmax=600, topk=-1, out=fake, th=None,
+                 ws=p(0x10000), wsb=256)
+        a.update(kw)
+        return f(a["c"], a["sps"], a["R"], a["gamma"], a["bmax"], a["topk"], a["out"], a["th"],
+                 a["ws"], a["wsb"], None)
+
+    assert sc(R=-1) == SPEC_EINVAL
+    assert sc(gamma=-1) == SPEC_EINVAL
+    assert sc(bmax=-1) == SPEC_EINVAL
+    assert sc(R=2048, gamma=5) == SPEC_EUNSUPPORTED    # pool of 10240 > 8192
+    assert sc(c=None) == SPEC_EINVAL
+    assert sc(sps=None) == SPEC_EINVAL
+    assert sc(out=None) == SPEC_EINVAL
+    assert sc(ws=None) == SPEC_EWORKSPACE
+    assert sc(wsb=8) == SPEC_EWORKSPACE
+    assert sc(ws=p(0x10004)) == SPEC_EWORKSPACE        # misaligned
+    assert sc(R=0) == SPEC_OK
+
+
 def test_workspace_init_validation(lib):
     f = lib.spec_workspace_init
     f.restype = ctypes.c_int

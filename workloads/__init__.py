@@ -15,6 +15,7 @@ Random numbers come from numpy's Philox counter-based generator
   stream 5  draft-logit noise
   stream 6  per-request parameters (verify lengths, noise scales, anchors)
   stream 7  Markov tables W1, W2 and base logits U
+  stream 8  scheduler confidences and step-rate tables
 
 Uniforms are fp32 values (w >> 8) * 2**-24 of 32-bit Philox words: exact in
 fp32 and always in [0, 1).
@@ -311,6 +312,43 @@ WORKLOADS = {
     "dspark_markov": dspark_markov,
     "high_load_mixed": high_load_mixed,
 }
+
+
+@dataclasses.dataclass
+class ScheduleCase:
+    """Inputs of the confidence-scheduled verify length: per-position
+    confidences (the confidence head's outputs) and a step-rate table."""
+    conf: np.ndarray  # [R, gamma] fp32 in [0, 1]
+    sps: np.ndarray   # [bmax + 1] fp32, steps per second at batch size B
+    R: int
+    gamma: int
+
+
+def schedule_case(seed: int = 8, R: int = 64, gamma: int = 7, curve: str = "smooth",
+                  bmax: Optional[int] = None) -> ScheduleCase:
+    """Confidences with a per-request level and a decay along the block (the
+    suffix decay of acceptance), and one of three step-rate curves over batch
+    sizes 0..bmax: "smooth" (falls as 1 / (1 + B / (2 R))), "cliff" (the same
+    curve taken at B rounded up to a multiple of 128 rows: flat inside a tile,
+    a step down past each boundary, the saw-tooth of a padded engine) or
+    "flat"."""
+    gen = rng(seed, 8)
+    level = gen.uniform(0.55, 0.98, size=(R, 1))
+    decay = gen.uniform(0.0, 0.06, size=(R, 1))
+    noise = gen.normal(0.0, 0.05, size=(R, gamma))
+    conf = np.clip(level - decay * np.arange(gamma)[None, :] + noise, 0.01, 0.999)
+    conf = conf.astype(np.float32)
+    bmax = R * (gamma + 1) if bmax is None else bmax
+    B = np.arange(bmax + 1, dtype=np.float64)
+    if curve == "flat":
+        sps = np.full(bmax + 1, 50.0)
+    elif curve == "smooth":
+        sps = 1000.0 / (1.0 + B / (2.0 * max(R, 1)))
+    elif curve == "cliff":
+        sps = 1000.0 / (1.0 + np.ceil(B / 128.0) * 128.0 / (2.0 * max(R, 1)))
+    else:
+        raise ValueError(curve)
+    return ScheduleCase(conf=conf, sps=sps.astype(np.float32), R=R, gamma=gamma)
 
 
 def algorithmic_bytes(verify_len: np.ndarray, V: int, t_elt: int, d_elt: int) -> int:
