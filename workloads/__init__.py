@@ -16,6 +16,7 @@ Random numbers come from numpy's Philox counter-based generator
   stream 6  per-request parameters (verify lengths, noise scales, anchors)
   stream 7  Markov tables W1, W2 and base logits U
   stream 8  scheduler confidences and step-rate tables
+  stream 9  RNN-head backbone hidden states and gate weights
 
 Uniforms are fp32 values (w >> 8) * 2**-24 of 32-bit Philox words: exact in
 fp32 and always in [0, 1).
@@ -45,6 +46,8 @@ STREAM_TARGET = 4
 STREAM_NOISE = 5
 STREAM_PARAMS = 6
 STREAM_MARKOV = 7
+STREAM_SCHEDULE = 8
+STREAM_RNN = 9
 
 
 def rng(seed: int, stream: int) -> np.random.Generator:
@@ -315,6 +318,33 @@ WORKLOADS = {
 
 
 @dataclasses.dataclass
+class RnnCase:
+    """Inputs of one RNN-head draft call: the Markov head's U, W1, W2,
+    anchors, temperatures and uniforms, plus the backbone hidden states and
+    the gate weights."""
+    mk: MarkovCase
+    H: np.ndarray    # [R, gamma, hidden] fp32 backbone hidden states h_k
+    Wg: np.ndarray   # [2 rank + hidden, 2 rank] bf16 bits: update-gate and candidate weights
+    bg: np.ndarray   # [2 rank] fp32 biases
+
+
+def rnn_head(seed: int = 6, R: int = 64, gamma: int = 7, V: int = 129280, hidden: int = 1024,
+             temperature: float = 1.0) -> RnnCase:
+    """The Markov workload's U, W1, W2 (same recipe), hidden states
+    h_k ~ N(0, 1), gate weights ~ N(0, 1 / (2 rank + hidden)) in bf16 and
+    biases ~ N(0, 0.1^2)."""
+    mk = dspark_markov(seed=seed, R=R, gamma=gamma, V=V, temperature=temperature)
+    g = rng(seed, STREAM_RNN)
+    rank = mk.rank
+    din = 2 * rank + hidden
+    H = g.standard_normal((R, gamma, hidden), dtype=np.float32)
+    Wg = f32_to_bf16_bits(g.standard_normal((din, 2 * rank), dtype=np.float32)
+                          * np.float32(1.0 / np.sqrt(din)))
+    bg = (g.standard_normal(2 * rank, dtype=np.float32) * np.float32(0.1)).astype(np.float32)
+    return RnnCase(mk=mk, H=H, Wg=Wg, bg=bg)
+
+
+@dataclasses.dataclass
 class ScheduleCase:
     """Inputs of the confidence-scheduled verify length: per-position
     confidences (the confidence head's outputs) and a step-rate table."""
@@ -332,7 +362,7 @@ def schedule_case(seed: int = 8, R: int = 64, gamma: int = 7, curve: str = "smoo
     curve taken at B rounded up to a multiple of 128 rows: flat inside a tile,
     a step down past each boundary, the saw-tooth of a padded engine) or
     "flat"."""
-    gen = rng(seed, 8)
+    gen = rng(seed, STREAM_SCHEDULE)
     level = gen.uniform(0.55, 0.98, size=(R, 1))
     decay = gen.uniform(0.0, 0.06, size=(R, 1))
     noise = gen.normal(0.0, 0.05, size=(R, gamma))
