@@ -79,6 +79,9 @@ typedef enum {
  * is cut into at most 256 chunks of 1024 logits). */
 #define SPEC_MAX_VERIFY_VOCAB 262144
 
+/* Largest backbone hidden size spec_rnn_draft_sample accepts. */
+#define SPEC_RNN_MAX_HIDDEN 3072
+
 /* Largest candidate pool (R * gamma, and R) spec_schedule_verify_len accepts. */
 #define SPEC_SCHED_MAX_POOL 8192
 
@@ -186,6 +189,37 @@ int spec_markov_draft_sample(const void *U, int u_dtype,
                              int R, int gamma, int V, int rank,
                              int32_t *out_draft_tokens, float *out_draft_logits,
                              void *workspace, size_t workspace_bytes, void *stream);
+
+/* Workspace bytes for spec_rnn_draft_sample. */
+size_t spec_rnn_workspace_bytes(int R, int gamma, int V, int rank, int hidden);
+
+/*
+ * RNN serial head (DSpark guide, the serial-head section: the RNN variant
+ * described after the Markov head).
+ *
+ * Like spec_markov_draft_sample, with the transition bias taken from a
+ * recurrent state instead of the previous token alone: s_0 = 0 and, for
+ * k = 1..gamma, with c = [s_{k-1}; W1[x_{k-1}]; h_k] (2 rank + hidden values),
+ *   z   = sigmoid(c Wg[:, 0:rank] + bg[0:rank])
+ *   n   = tanh(c Wg[:, rank:2 rank] + bg[rank:2 rank])
+ *   s_k = (1 - z) * s_{k-1} + z * n                      (fp32)
+ *   l_k = U_k + s_k W2,  x_k ~ softmax(l_k / T)           (as the Markov head)
+ * The product s_k W2 runs on the bf16 MFMA with s_k split into three bf16
+ * parts (hi + mid + lo = s_k to fp32 precision).  The pages fix no gate
+ * form; this single update gate on the concatenation is the reading taken.
+ *   hidden_states [R][gamma][hidden]     fp32 backbone hidden states h_k
+ *   Wg            [2 rank + hidden][2 rank]  w_dtype (bf16)
+ *   bg            [2 rank]               fp32
+ *   out_state     [R][gamma][rank]       fp32 states s_k, nullable
+ * Other arguments, sizes and errors as spec_markov_draft_sample, plus
+ * 1 <= hidden <= SPEC_RNN_MAX_HIDDEN.
+ */
+int spec_rnn_draft_sample(const void *U, int u_dtype, const void *W1, const void *W2,
+                          int w_dtype, const float *hidden_states, int hidden, const void *Wg,
+                          const float *bg, const int32_t *anchor, const float *temperature,
+                          const float *u_draft, int R, int gamma, int V, int rank,
+                          int32_t *out_draft_tokens, float *out_draft_logits, float *out_state,
+                          void *workspace, size_t workspace_bytes, void *stream);
 
 /* Workspace bytes for spec_schedule_verify_len (the device status word). */
 size_t spec_schedule_workspace_bytes(void);

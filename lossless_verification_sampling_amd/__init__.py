@@ -29,6 +29,7 @@ SPEC_DEV_SPIN_TIMEOUT = 0x2
 SPEC_MAX_VOCAB = 2097152
 SPEC_MAX_VERIFY_VOCAB = 262144
 SPEC_SCHED_MAX_POOL = 8192
+SPEC_RNN_MAX_HIDDEN = 3072
 
 EXPORTED = (
     "spec_version",
@@ -39,6 +40,8 @@ EXPORTED = (
     "spec_tv_workspace_bytes",
     "spec_tv_accept_rate",
     "spec_markov_workspace_bytes",
+    "spec_rnn_workspace_bytes",
+    "spec_rnn_draft_sample",
     "spec_schedule_workspace_bytes",
     "spec_schedule_verify_len",
     "spec_markov_draft_sample",
@@ -76,6 +79,11 @@ def _load() -> ctypes.CDLL:
     lib.spec_tv_accept_rate.argtypes = [p, p, i, p, i, i, p, p, p, sz, p]
     lib.spec_markov_draft_sample.restype = i
     lib.spec_markov_draft_sample.argtypes = [p, i, p, p, i, p, p, p, i, i, i, i, p, p, p, sz, p]
+    lib.spec_rnn_workspace_bytes.restype = sz
+    lib.spec_rnn_workspace_bytes.argtypes = [i, i, i, i, i]
+    lib.spec_rnn_draft_sample.restype = i
+    lib.spec_rnn_draft_sample.argtypes = [p, i, p, p, i, p, i, p, p, p, p, p, i, i, i, i, p, p, p,
+                                          p, sz, p]
     lib.spec_schedule_workspace_bytes.restype = sz
     lib.spec_schedule_workspace_bytes.argtypes = []
     lib.spec_schedule_verify_len.restype = i
@@ -110,6 +118,10 @@ def spec_tv_workspace_bytes(N: int, V: int) -> int:
 
 def spec_markov_workspace_bytes(R: int, gamma: int, V: int, rank: int) -> int:
     return int(_lib.spec_markov_workspace_bytes(R, gamma, V, rank))
+
+
+def spec_rnn_workspace_bytes(R: int, gamma: int, V: int, rank: int, hidden: int) -> int:
+    return int(_lib.spec_rnn_workspace_bytes(R, gamma, V, rank, hidden))
 
 
 def spec_schedule_workspace_bytes() -> int:
@@ -325,6 +337,50 @@ def spec_schedule_verify_len(confidence: torch.Tensor, sps: torch.Tensor, *, top
                                        _stream_ptr(stream, dev))
     _raise(st, "spec_schedule_verify_len")
     return ln, th
+
+
+def spec_rnn_draft_sample(U: torch.Tensor, W1: torch.Tensor, W2: torch.Tensor,
+                          hidden_states: torch.Tensor, Wg: torch.Tensor, bg: torch.Tensor,
+                          anchor: torch.Tensor, temperature: torch.Tensor, u_draft: torch.Tensor,
+                          *, want_state: bool = False, out_tokens: Optional[torch.Tensor] = None,
+                          out_logits: Optional[torch.Tensor] = None,
+                          workspace: Optional[Workspace] = None, stream=None):
+    """RNN-head draft.  As spec_markov_draft_sample plus hidden_states
+    [R, gamma, hidden] float32, Wg [2 rank + hidden, 2 rank] bfloat16, bg
+    [2 rank] float32.  Returns (tokens, logits, states [R, gamma, rank] float32
+    or None)."""
+    R, gamma, V = U.shape
+    rank = W1.shape[1]
+    hidden = hidden_states.shape[2]
+    dev = U.device
+    _check(U, "U", device=dev)
+    _check(W1, "W1", torch.bfloat16, (V, rank), dev)
+    _check(W2, "W2", torch.bfloat16, (rank, V), dev)
+    _check(hidden_states, "hidden_states", torch.float32, (R, gamma, hidden), dev)
+    _check(Wg, "Wg", torch.bfloat16, (2 * rank + hidden, 2 * rank), dev)
+    _check(bg, "bg", torch.float32, (2 * rank,), dev)
+    _check(anchor, "anchor", torch.int32, (R,), dev)
+    _check(temperature, "temperature", torch.float32, (R,), dev)
+    _check(u_draft, "u_draft", torch.float32, (R, gamma), dev)
+    tok = out_tokens if out_tokens is not None else torch.empty((R, gamma), dtype=torch.int32,
+                                                                 device=dev)
+    lg = out_logits if out_logits is not None else torch.empty((R, gamma, V),
+                                                                dtype=torch.float32, device=dev)
+    stt = torch.empty((R, gamma, rank), dtype=torch.float32, device=dev) if want_state else None
+    _check(tok, "out_tokens", torch.int32, (R, gamma), dev)
+    _check(lg, "out_logits", torch.float32, (R, gamma, V), dev)
+    ws = workspace or default_workspace(dev)
+    need = spec_rnn_workspace_bytes(R, gamma, V, rank, hidden)
+    if need == 0:
+        raise SpecError(-5, "spec_rnn_workspace_bytes")
+    buf = ws.ensure(need, stream)
+    st = _lib.spec_rnn_draft_sample(_ptr(U), _dtype(U), _ptr(W1), _ptr(W2), SPEC_BF16,
+                                    _ptr(hidden_states), hidden, _ptr(Wg), _ptr(bg), _ptr(anchor),
+                                    _ptr(temperature), _ptr(u_draft), R, gamma, V, rank, _ptr(tok),
+                                    _ptr(lg), _ptr(stt), _ptr(buf), buf.numel(),
+                                    _stream_ptr(stream, dev))
+    _raise(st, "spec_rnn_draft_sample")
+    return tok, lg, stt
 
 
 def spec_markov_draft_sample(U: torch.Tensor, W1: torch.Tensor, W2: torch.Tensor,

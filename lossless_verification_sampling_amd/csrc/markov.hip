@@ -49,6 +49,7 @@ struct MarkovArgs {
     int R, gamma, V, ntiles;
     int k;                   // current step, 1..gamma
     int vec;                 // U rows and logit rows allow 4-wide loads and stores
+    const uint16_t *bsplit;  // RNN head: [3][R][rank] bf16 parts of the state (B rows)
     int tile0;               // first tile of the launch
     int32_t *out_tok;        // [R][gamma]
     float *out_logits;       // [R][gamma][V]
@@ -140,6 +141,26 @@ __device__ __forceinline__ void mk_load_w1(const MarkovArgs &a, int xprev, int k
     }
 }
 
+// The B operand of the 8 k steps for request r: the gathered row W1[xprev]
+// (Markov head, NSPLIT = 1), or bf16 part sp of the request's state (RNN
+// head, NSPLIT = 3; the fp32 state is the sum of its three parts).
+template <int NSPLIT>
+__device__ __forceinline__ void mk_load_b(const MarkovArgs &a, int xprev, int r, int sp, int kgrp,
+                                          uint4 (&b)[kMkRank / 32]) {
+    if constexpr (NSPLIT == 1) {
+        mk_load_w1(a, xprev, kgrp, b);
+    } else {
+        const bool rok = r < a.R;
+        const uint16_t *row = a.bsplit + ((size_t)sp * a.R + (rok ? r : 0)) * kMkRank + kgrp * 8;
+        const uint32_t keep = rok ? ~0u : 0u;
+#pragma unroll
+        for (int ks = 0; ks < kMkRank / 32; ++ks) {
+            const uint4 w = *reinterpret_cast<const uint4 *>(row + ks * 32);
+            b[ks] = make_uint4(w.x & keep, w.y & keep, w.z & keep, w.w & keep);
+        }
+    }
+}
+
 __device__ __forceinline__ void mk_unpack_u(const uint2 &w, float (&o)[4]) {
     o[0] = bf16_lo(w.x); o[1] = bf16_hi(w.x); o[2] = bf16_lo(w.y); o[3] = bf16_hi(w.y);
 }
@@ -151,7 +172,7 @@ __device__ __forceinline__ void mk_unpack_u(const float4 &w, float (&o)[4]) {
 // (16-byte aligned W2 rows) and the U and logit rows allow 4-wide accesses,
 // so every load and store is a vector; otherwise (odd V, the ragged last
 // tile, unaligned U or logits) they are guarded scalars.
-template <typename TU, bool FULL>
+template <typename TU, bool FULL, int NSPLIT>
 __global__ void __launch_bounds__(kBlock, 4) markov_logits_kernel(MarkovArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t w2t[kMkTile * kMkLdsStride];
     const int tid = threadIdx.x;
@@ -190,7 +211,7 @@ __global__ void __launch_bounds__(kBlock, 4) markov_logits_kernel(MarkovArgs a) 
     // the W1 operand too, where registers allow (the guarded variant's
     // scalar staging needs them; it loads W1 after the barrier)
     uint4 bop[kMkRank / 32];
-    if constexpr (FULL) mk_load_w1(a, xprev, kgrp, bop);
+    if constexpr (FULL) mk_load_b<NSPLIT>(a, xprev, wave * 16 + col, 0, kgrp, bop);
 
     // ---- stage W2[:, v0:v0+64] transposed: w2t[n][k] -------------------------
     {
@@ -212,21 +233,28 @@ __global__ void __launch_bounds__(kBlock, 4) markov_logits_kernel(MarkovArgs a) 
             xprev = mk_prev_token(a, r);
             mk_load_u<TU, FULL>(a, r, v0, kgrp, ln);
         }
-        if (rb > 0 || !FULL) mk_load_w1(a, xprev, kgrp, bop);
-        // b[v][r] = sum_k W2[k][v] W1[x_r][k]: A = the W2 tile (16 vocabulary
-        // rows per block), B = 16 gathered W1 rows
+        if (rb > 0 || !FULL) mk_load_b<NSPLIT>(a, xprev, r, 0, kgrp, bop);
+        // b[v][r] = sum_k W2[k][v] B_r[k]: A = the W2 tile (16 vocabulary rows
+        // per block), B = 16 gathered W1 rows (Markov head) or the bf16 parts
+        // of 16 states, one after the other (RNN head)
         f32x4_t acc[kMkTile / 16];
 #pragma unroll
         for (int vb = 0; vb < kMkTile / 16; ++vb) acc[vb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int sp = 0; sp < NSPLIT; ++sp) {
+            if (sp > 0) {
+                asm volatile("" ::: "memory");
+                mk_load_b<NSPLIT>(a, xprev, r, sp, kgrp, bop);
+            }
 #pragma unroll
-        for (int ks = 0; ks < kMkRank / 32; ++ks) {
-            const bf16x8_t bv = __builtin_bit_cast(bf16x8_t, bop[ks]);
+            for (int ks = 0; ks < kMkRank / 32; ++ks) {
+                const bf16x8_t bv = __builtin_bit_cast(bf16x8_t, bop[ks]);
 #pragma unroll
-            for (int vb = 0; vb < kMkTile / 16; ++vb) {
-                const uint4 araw = *reinterpret_cast<const uint4 *>(
-                    &w2t[(vb * 16 + col) * kMkLdsStride + ks * 32 + kgrp * 8]);
-                acc[vb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                    __builtin_bit_cast(bf16x8_t, araw), bv, acc[vb], 0, 0, 0);
+                for (int vb = 0; vb < kMkTile / 16; ++vb) {
+                    const uint4 araw = *reinterpret_cast<const uint4 *>(
+                        &w2t[(vb * 16 + col) * kMkLdsStride + ks * 32 + kgrp * 8]);
+                    acc[vb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf16x8_t, araw), bv, acc[vb], 0, 0, 0);
+                }
             }
         }
         // ---- epilogue: acc[vb][j] = b[v][r], v = v0 + vb * 16 + kgrp * 4 + j
@@ -454,6 +482,92 @@ __global__ void __launch_bounds__(kBlock) markov_sample_kernel(MarkovArgs a) {
     }
 }
 
+// fp32 value of x rounded to bf16 (nearest, ties to even; finite x).
+__device__ __forceinline__ float bf16_round(float x) {
+    const uint32_t b = __float_as_uint(x);
+    return __uint_as_float((b + 0x7fffu + ((b >> 16) & 1u)) & 0xffff0000u);
+}
+
+// ---------------------------------------------------------------------------
+// RNN serial head: the gated state update of step k
+// ---------------------------------------------------------------------------
+
+constexpr int kRnnReq = 4;      // requests per workgroup (one wave each)
+constexpr int kRnnUnits = 32;   // state units per workgroup (two gate columns each)
+constexpr int kRnnMaxHidden = SPEC_RNN_MAX_HIDDEN;  // keeps the LDS of a workgroup under 64 KB
+
+struct RnnArgs {
+    const uint16_t *W1;     // [V][rank] bf16 embedding
+    const float *H;         // [R][gamma][hidden] backbone hidden states
+    const uint16_t *Wg;     // [2 rank + hidden][2 rank] bf16: update-gate | candidate columns
+    const float *bg;        // [2 rank]
+    const int32_t *anchor;  // [R]
+    const int32_t *tok;     // [R][gamma] drafted tokens (the previous step's)
+    const float *s_prev;    // [R][rank]
+    float *s_next;          // [R][rank]
+    uint16_t *bsplit;       // [3][R][rank] bf16 parts of s_next
+    float *out_state;       // [R][gamma][rank] or null
+    int R, gamma, V, hidden, k;
+};
+
+// Workgroup (request block q0, unit block u0): wave w is request q0 + w, lane
+// l computes gate column (l / 32) * rank + u0 + l % 32 over the concatenation
+// c = [s_{k-1}; W1[x_{k-1}]; h_k] (fp32 sums of bf16 weights), then the first
+// 32 lanes make the update s_k = (1 - z) s_{k-1} + z tanh(n) and write s_k and
+// its three bf16 parts (hi = bf16(s), mid = bf16(s - hi), lo = bf16(s - hi -
+// mid); both differences are exact in fp32).
+__global__ void __launch_bounds__(kBlock) rnn_gate_kernel(RnnArgs a) {
+    extern __shared__ float cvec[];  // [kRnnReq][2 rank + hidden], then gates [kRnnReq][64]
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int dc = 2 * kMkRank + a.hidden;
+    const int q0 = blockIdx.x * kRnnReq, u0 = blockIdx.y * kRnnUnits;
+    for (int i = tid; i < kRnnReq * dc; i += kBlock) {
+        const int q = i / dc, e = i - q * dc;
+        const int r = q0 + q;
+        float v = 0.0f;
+        if (r < a.R) {
+            if (e < kMkRank) {
+                v = a.k > 1 ? a.s_prev[(size_t)r * kMkRank + e] : 0.0f;
+            } else if (e < 2 * kMkRank) {
+                const int x = a.k == 1 ? a.anchor[r] : a.tok[(size_t)r * a.gamma + (a.k - 2)];
+                if (x >= 0 && x < a.V)
+                    v = __uint_as_float((uint32_t)a.W1[(size_t)x * kMkRank + (e - kMkRank)] << 16);
+            } else {
+                v = a.H[((size_t)r * a.gamma + (a.k - 1)) * a.hidden + (e - 2 * kMkRank)];
+            }
+        }
+        cvec[i] = v;
+    }
+    __syncthreads();
+    const int unit = u0 + (lane & 31);
+    const int colg = (lane >> 5) * kMkRank + unit;  // column of Wg
+    const float *c = cvec + wave * dc;
+    float acc = a.bg[colg];
+#pragma unroll 8
+    for (int i = 0; i < dc; ++i)
+        acc = fmaf(c[i], __uint_as_float((uint32_t)a.Wg[(size_t)i * 2 * kMkRank + colg] << 16), acc);
+    float *gates = cvec + kRnnReq * dc;
+    gates[wave * 64 + lane] = acc;
+    __syncthreads();
+    const int r = q0 + wave;
+    if (lane < 32 && r < a.R) {
+        const float gz = gates[wave * 64 + lane], gn = gates[wave * 64 + 32 + lane];
+        const float z = 1.0f / (1.0f + expf(-gz));
+        const float n = tanhf(gn);
+        const float sp = c[unit];
+        const float sn = (1.0f - z) * sp + z * n;
+        a.s_next[(size_t)r * kMkRank + unit] = sn;
+        if (a.out_state) a.out_state[((size_t)r * a.gamma + (a.k - 1)) * kMkRank + unit] = sn;
+        const float hi = bf16_round(sn);
+        const float mid = bf16_round(sn - hi);
+        const float lo = bf16_round(sn - hi - mid);
+        const size_t o = (size_t)r * kMkRank + unit, plane = (size_t)a.R * kMkRank;
+        a.bsplit[o] = (uint16_t)(__float_as_uint(hi) >> 16);
+        a.bsplit[plane + o] = (uint16_t)(__float_as_uint(mid) >> 16);
+        a.bsplit[2 * plane + o] = (uint16_t)(__float_as_uint(lo) >> 16);
+    }
+}
+
 __global__ void markov_clear_kernel(uint32_t *bad, int R) {
     for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < R; i += gridDim.x * blockDim.x)
         bad[i] = 0u;
@@ -474,6 +588,83 @@ bool mk_plan(long R, long V, MkPlan &p) {
     p.off_bad = mk_round_up(p.off_stats + sizeof(float2) * (size_t)R * p.ntiles, 256);
     p.bytes = mk_round_up(p.off_bad + sizeof(uint32_t) * (size_t)R, 256);
     return true;
+}
+
+// Step k's logits (U_k + B W2 with the B rows of NSPLIT) and draw.
+template <int NSPLIT>
+void mk_launch_step(MarkovArgs a, const MkPlan &p, bool bf, hipStream_t st) {
+    const int R = a.R, V = a.V;
+    // whole tiles in 16-byte aligned rows take the vector kernel; the ragged
+    // last tile (or every tile of an odd V or unaligned rows) the guarded one
+    const int nfull = (V % 8 == 0 && a.vec) ? V / kMkTile : 0;
+    const int tp = (p.ntiles + kBlock - 1) / kBlock;  // tiles per thread of the sampling block
+    if (nfull > 0) {
+        a.tile0 = 0;
+        if (bf)
+            hipLaunchKernelGGL((markov_logits_kernel<uint16_t, true, NSPLIT>), dim3(nfull),
+                               dim3(kBlock), 0, st, a);
+        else
+            hipLaunchKernelGGL((markov_logits_kernel<float, true, NSPLIT>), dim3(nfull),
+                               dim3(kBlock), 0, st, a);
+    }
+    if (nfull < p.ntiles) {
+        a.tile0 = nfull;
+        if (bf)
+            hipLaunchKernelGGL((markov_logits_kernel<uint16_t, false, NSPLIT>),
+                               dim3(p.ntiles - nfull), dim3(kBlock), 0, st, a);
+        else
+            hipLaunchKernelGGL((markov_logits_kernel<float, false, NSPLIT>),
+                               dim3(p.ntiles - nfull), dim3(kBlock), 0, st, a);
+    }
+    if (tp <= 8)
+        hipLaunchKernelGGL(markov_sample_kernel<8>, dim3(R), dim3(kBlock), 0, st, a);
+    else
+        hipLaunchKernelGGL(markov_sample_kernel<16>, dim3(R), dim3(kBlock), 0, st, a);
+}
+
+// Workspace of the RNN head: the Markov head's, then two fp32 states and the
+// three bf16 parts of the current one.
+struct RnnPlan {
+    MkPlan mk;
+    size_t off_s0, off_s1, off_split, bytes;
+};
+
+bool rnn_plan(long R, long V, RnnPlan &p) {
+    mk_plan(R, V, p.mk);
+    const size_t sb = sizeof(float) * (size_t)R * kMkRank;
+    p.off_s0 = p.mk.bytes;
+    p.off_s1 = mk_round_up(p.off_s0 + sb, 256);
+    p.off_split = mk_round_up(p.off_s1 + sb, 256);
+    p.bytes = mk_round_up(p.off_split + 3 * sizeof(uint16_t) * (size_t)R * kMkRank, 256);
+    return true;
+}
+
+// Shared argument set-up of the two draft heads.
+int mk_setup(const void *U, int u_dtype, const void *W1, const void *W2, int w_dtype,
+             const int32_t *anchor, const float *temperature, const float *u_draft, int R,
+             int gamma, int V, int rank, int32_t *out_tok, float *out_logits, void *workspace,
+             const MkPlan &p, MarkovArgs &a) {
+    char *ws = (char *)workspace;
+    a = MarkovArgs{};
+    a.U = U;
+    a.W1 = (const uint16_t *)W1;
+    a.W2 = (const uint16_t *)W2;
+    a.anchor = anchor;
+    a.temp = temperature;
+    a.ud = u_draft;
+    a.R = R;
+    a.gamma = gamma;
+    a.V = V;
+    a.ntiles = p.ntiles;
+    a.out_tok = out_tok;
+    a.out_logits = out_logits;
+    a.tstats = (float2 *)(ws + p.off_stats);
+    a.bad = (uint32_t *)(ws + p.off_bad);
+    a.ctl = (Control *)ws;
+    const size_t ub = (u_dtype == SPEC_BF16) ? 2 : 4;
+    a.vec = (V % 4 == 0) && ((uintptr_t)U % (4 * ub) == 0) && ((uintptr_t)out_logits % 16 == 0);
+    (void)W2; (void)w_dtype; (void)rank; (void)anchor; (void)temperature; (void)u_draft;
+    return SPEC_OK;
 }
 
 }  // namespace
@@ -507,58 +698,79 @@ int spec_markov_draft_sample(const void *U, int u_dtype, const void *W1, const v
     mk_plan(R, V, p);
     if (!workspace || ((uintptr_t)workspace & 255u) || workspace_bytes < p.bytes)
         return SPEC_EWORKSPACE;
-    char *ws = (char *)workspace;
-    MarkovArgs a{};
-    a.U = U;
-    a.W1 = (const uint16_t *)W1;
-    a.W2 = (const uint16_t *)W2;
-    a.anchor = anchor;
-    a.temp = temperature;
-    a.ud = u_draft;
-    a.R = R;
-    a.gamma = gamma;
-    a.V = V;
-    a.ntiles = p.ntiles;
-    a.out_tok = out_draft_tokens;
-    a.out_logits = out_draft_logits;
-    a.tstats = (float2 *)(ws + p.off_stats);
-    a.bad = (uint32_t *)(ws + p.off_bad);
-    a.ctl = (Control *)ws;
-    const size_t ub = (u_dtype == SPEC_BF16) ? 2 : 4;
-    a.vec = (V % 4 == 0) && ((uintptr_t)U % (4 * ub) == 0) && ((uintptr_t)out_draft_logits % 16 == 0);
+    MarkovArgs a;
+    mk_setup(U, u_dtype, W1, W2, w_dtype, anchor, temperature, u_draft, R, gamma, V, rank,
+             out_draft_tokens, out_draft_logits, workspace, p, a);
     note_workspace_clean(workspace, sizeof(Control));
     hipStream_t st = (hipStream_t)stream;
     hipLaunchKernelGGL(markov_clear_kernel, dim3((R + kBlock - 1) / kBlock), dim3(kBlock), 0, st,
                        a.bad, R);
-    // whole tiles in 16-byte aligned rows take the vector kernel; the ragged
-    // last tile (or every tile of an odd V or unaligned rows) the guarded one
-    const int nfull = (V % 8 == 0 && a.vec) ? V / kMkTile : 0;
-    const int tp = (p.ntiles + kBlock - 1) / kBlock;  // tiles per thread of the sampling block
     for (int k = 1; k <= gamma; ++k) {
         a.k = k;
-        const bool bf = (u_dtype == SPEC_BF16);
-        if (nfull > 0) {
-            a.tile0 = 0;
-            if (bf)
-                hipLaunchKernelGGL((markov_logits_kernel<uint16_t, true>), dim3(nfull), dim3(kBlock),
-                                   0, st, a);
-            else
-                hipLaunchKernelGGL((markov_logits_kernel<float, true>), dim3(nfull), dim3(kBlock), 0,
-                                   st, a);
-        }
-        if (nfull < p.ntiles) {
-            a.tile0 = nfull;
-            if (bf)
-                hipLaunchKernelGGL((markov_logits_kernel<uint16_t, false>), dim3(p.ntiles - nfull),
-                                   dim3(kBlock), 0, st, a);
-            else
-                hipLaunchKernelGGL((markov_logits_kernel<float, false>), dim3(p.ntiles - nfull),
-                                   dim3(kBlock), 0, st, a);
-        }
-        if (tp <= 8)
-            hipLaunchKernelGGL(markov_sample_kernel<8>, dim3(R), dim3(kBlock), 0, st, a);
-        else
-            hipLaunchKernelGGL(markov_sample_kernel<16>, dim3(R), dim3(kBlock), 0, st, a);
+        mk_launch_step<1>(a, p, u_dtype == SPEC_BF16, st);
+    }
+    return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_EHIP;
+}
+
+size_t spec_rnn_workspace_bytes(int R, int gamma, int V, int rank, int hidden) {
+    if (R < 0 || gamma < 0 || V < 1 || V > SPEC_MAX_VOCAB || rank != kMkRank || hidden < 1 ||
+        hidden > kRnnMaxHidden)
+        return 0;
+    RnnPlan p;
+    rnn_plan(R > 0 ? R : 1, V, p);
+    return p.bytes;
+}
+
+int spec_rnn_draft_sample(const void *U, int u_dtype, const void *W1, const void *W2, int w_dtype,
+                          const float *hidden_states, int hidden, const void *Wg, const float *bg,
+                          const int32_t *anchor, const float *temperature, const float *u_draft,
+                          int R, int gamma, int V, int rank, int32_t *out_draft_tokens,
+                          float *out_draft_logits, float *out_state, void *workspace,
+                          size_t workspace_bytes, void *stream) {
+    if (R < 0 || gamma < 0 || V < 1 || hidden < 1) return SPEC_EINVAL;
+    if ((u_dtype != SPEC_F32 && u_dtype != SPEC_BF16) || w_dtype != SPEC_BF16) return SPEC_EDTYPE;
+    if (rank != kMkRank || V > SPEC_MAX_VOCAB || hidden > kRnnMaxHidden) return SPEC_EUNSUPPORTED;
+    if (R == 0 || gamma == 0) return SPEC_OK;
+    if (!U || !W1 || !W2 || !hidden_states || !Wg || !bg || !anchor || !temperature || !u_draft ||
+        !out_draft_tokens || !out_draft_logits)
+        return SPEC_EINVAL;
+    if (((uintptr_t)W1 & 15u) || ((uintptr_t)W2 & 15u)) return SPEC_EINVAL;
+    RnnPlan p;
+    rnn_plan(R, V, p);
+    if (!workspace || ((uintptr_t)workspace & 255u) || workspace_bytes < p.bytes)
+        return SPEC_EWORKSPACE;
+    char *ws = (char *)workspace;
+    MarkovArgs a;
+    mk_setup(U, u_dtype, W1, W2, w_dtype, anchor, temperature, u_draft, R, gamma, V, rank,
+             out_draft_tokens, out_draft_logits, workspace, p.mk, a);
+    a.bsplit = (const uint16_t *)(ws + p.off_split);
+    RnnArgs g{};
+    g.W1 = (const uint16_t *)W1;
+    g.H = hidden_states;
+    g.Wg = (const uint16_t *)Wg;
+    g.bg = bg;
+    g.anchor = anchor;
+    g.tok = out_draft_tokens;
+    g.bsplit = (uint16_t *)(ws + p.off_split);
+    g.out_state = out_state;
+    g.R = R;
+    g.gamma = gamma;
+    g.V = V;
+    g.hidden = hidden;
+    float *s0 = (float *)(ws + p.off_s0), *s1 = (float *)(ws + p.off_s1);
+    const size_t lds = sizeof(float) * (size_t)kRnnReq * (2 * kMkRank + hidden + 64);
+    note_workspace_clean(workspace, sizeof(Control));
+    hipStream_t st = (hipStream_t)stream;
+    hipLaunchKernelGGL(markov_clear_kernel, dim3((R + kBlock - 1) / kBlock), dim3(kBlock), 0, st,
+                       a.bad, R);
+    const dim3 ggrid((R + kRnnReq - 1) / kRnnReq, kMkRank / kRnnUnits);
+    for (int k = 1; k <= gamma; ++k) {
+        g.k = k;
+        g.s_prev = (k & 1) ? s0 : s1;  // unread at k = 1 (s_0 = 0)
+        g.s_next = (k & 1) ? s1 : s0;
+        hipLaunchKernelGGL(rnn_gate_kernel, ggrid, dim3(kBlock), lds, st, g);
+        a.k = k;
+        mk_launch_step<3>(a, p.mk, u_dtype == SPEC_BF16, st);
     }
     return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_EHIP;
 }

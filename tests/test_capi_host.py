@@ -135,6 +135,39 @@ def test_markov_and_tv_argument_validation(lib):
     assert t(fake, fake, 0, fake, 0, 100, fake, None, None, 0, None) == SPEC_OK
 
 
+def test_rnn_argument_validation(lib):
+    p = ctypes.c_void_p
+    fake = p(0x1000)
+    f = lib.spec_rnn_draft_sample
+    f.restype = ctypes.c_int
+    i = ctypes.c_int
+    f.argtypes = [p, i, p, p, i, p, i, p, p, p, p, p, i, i, i, i, p, p, p, p, ctypes.c_size_t, p]
+
+    def rn(**kw):
+        a = dict(U=fake, ud=1, W1=fake, W2=fake, wd=1, H=fake, hid=64, Wg=fake, bg=fake,
+                 anchor=fake, temp=fake, u=fake, R=2, gamma=3, V=100, rank=256, tok=fake, lg=fake,
+                 st=None, ws=p(0x10000), wsb=1 << 30)
+        a.update(kw)
+        return f(a["U"], a["ud"], a["W1"], a["W2"], a["wd"], a["H"], a["hid"], a["Wg"], a["bg"],
+                 a["anchor"], a["temp"], a["u"], a["R"], a["gamma"], a["V"], a["rank"], a["tok"],
+                 a["lg"], a["st"], a["ws"], a["wsb"], None)
+
+    assert rn(rank=128) == SPEC_EUNSUPPORTED
+    assert rn(hid=3073) == SPEC_EUNSUPPORTED
+    assert rn(hid=0) == SPEC_EINVAL
+    assert rn(wd=0) == SPEC_EDTYPE
+    assert rn(H=None) == SPEC_EINVAL
+    assert rn(Wg=None) == SPEC_EINVAL
+    assert rn(bg=None) == SPEC_EINVAL
+    assert rn(W2=p(0x1008)) == SPEC_EINVAL
+    assert rn(ws=None) == SPEC_EWORKSPACE
+    assert rn(wsb=100) == SPEC_EWORKSPACE
+    assert rn(R=0) == SPEC_OK and rn(gamma=0) == SPEC_OK
+    w = lib.spec_rnn_workspace_bytes
+    w.restype = ctypes.c_size_t
+    assert w(64, 7, 129280, 256, 1024) > 0 and w(64, 7, 129280, 256, 4000) == 0
+
+
 def test_schedule_argument_validation(lib):
     p = ctypes.c_void_p
     fake = p(0x1000)
