@@ -21,7 +21,8 @@ Prints one JSON line:
 
 --workload dspark measures the Markov-head draft (R = 64, gamma = 7,
 V = 129280, rank 256) instead, as an extra line; --workload schedule the
-confidence-scheduled verify lengths of the same batch size (448 candidates).
+confidence-scheduled verify lengths of the same batch size (448 candidates);
+--workload rnn the RNN serial head at the Markov workload's size.
 """
 from __future__ import annotations
 
@@ -237,6 +238,57 @@ def bench_dspark(args):
     }
 
 
+def bench_rnn(args):
+    """RNN serial head at the Markov workload's size (R = 64, gamma = 7,
+    V = 129280, rank 256) with backbone hidden states of 1024."""
+    import torch
+    import lossless_verification_sampling_amd as sv
+    import workloads
+
+    dev = torch.device("cuda:0")
+    c = workloads.rnn_head(seed=args.seed + 3, hidden=1024)
+    mk = c.mk
+    R, gamma, V, rank, hidden = mk.R, mk.gamma, mk.V, mk.rank, c.H.shape[2]
+    ins = [to_device(x, dev) for x in (mk.U, mk.W1, mk.W2, c.H, c.Wg, c.bg, mk.anchor,
+                                       mk.temperature, mk.u_draft)]
+    tok = torch.empty((R, gamma), dtype=torch.int32, device=dev)
+    lg = torch.empty((R, gamma, V), dtype=torch.float32, device=dev)
+    ws = sv.Workspace(dev, sv.spec_rnn_workspace_bytes(R, gamma, V, rank, hidden))
+    for _ in range(args.warmup):
+        sv.spec_rnn_draft_sample(*ins, out_tokens=tok, out_logits=lg, workspace=ws)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        ev[k][0].record(stream)
+        sv.spec_rnn_draft_sample(*ins, out_tokens=tok, out_logits=lg, workspace=ws)
+        ev[k][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = np.array([a.elapsed_time(b) for a, b in ev])
+    din = 2 * rank + hidden
+    per_call = (R * V * 2 + rank * V * 2 + R * V * 4 + din * 2 * rank * 2 + R * hidden * 4) * gamma
+    flops = (3 * 2.0 * R * rank * V + 2.0 * R * din * 2 * rank) * gamma
+    return {
+        "metric": "RNN-head draft: drafted tokens/sec",
+        "value": R * gamma / (wall / args.steps),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": wall / args.steps * 1e3,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16-mfma (state in three bf16 parts)/f32", "data": "synthetic",
+        "config": {"workload": "rnn_head", "R": R, "gamma": gamma, "V": V, "rank": rank,
+                   "hidden": hidden},
+        "roofline": {"bound": "hbm", "achieved": per_call / (ms.mean() / 1e3) / 1e9,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": per_call / (ms.mean() / 1e3) / 1e9 / HBM_PEAK_GBS,
+                     "traffic": None, "algorithmic_bytes_per_call": per_call,
+                     "mfma_tflops": flops / (ms.mean() / 1e3) / 1e12},
+    }
+
+
 def bench_schedule(args):
     """Confidence-scheduled verify lengths for the headline batch (R = 64,
     gamma = 7) on the smooth step-rate curve: one workgroup sorts the 448
@@ -385,7 +437,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--seed", type=int, default=3)
     ap.add_argument("--copies", type=int, default=0, help="input copies rotated (0 = auto)")
-    ap.add_argument("--workload", choices=["batched", "dspark", "schedule"], default="batched")
+    ap.add_argument("--workload", choices=["batched", "dspark", "rnn", "schedule"],
+                    default="batched")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -408,7 +461,7 @@ def main():
     if args.calibrate_copy:
         res = calibrate_copy(args)
     else:
-        res = {"batched": bench_verify, "dspark": bench_dspark,
+        res = {"batched": bench_verify, "dspark": bench_dspark, "rnn": bench_rnn,
                "schedule": bench_schedule}[args.workload](args)
     print(json.dumps(res))
 

@@ -173,14 +173,15 @@ size_t spec_markov_workspace_bytes(int R, int gamma, int V, int rank);
  * The stored fp32 logits are the draft distribution that verification must
  * compare against (pass out_draft_logits as draft_logits, d_dtype SPEC_F32).
  *   U              [R][gamma][V]  u_dtype (fp32 or bf16)
- *   W1             [V][rank]      w_dtype (bf16)
- *   W2             [rank][V]      w_dtype (bf16)
+ *   W1             [V][rank]      w_dtype (bf16), 16-byte aligned
+ *   W2             [rank][V]      w_dtype (bf16), 16-byte aligned
  *   anchor         [R]            int32 in [0, V)
  *   temperature    [R]            fp32
  *   u_draft        [R][gamma]     fp32 in [0,1)
  *   out_draft_tokens [R][gamma]   int32 (-1 for an invalid request)
  *   out_draft_logits [R][gamma][V] fp32
  * Sizes: R >= 0, gamma >= 0, 1 <= V <= SPEC_MAX_VOCAB, rank == 256.
+ * A misaligned W1 or W2 returns SPEC_EINVAL.
  */
 int spec_markov_draft_sample(const void *U, int u_dtype,
                              const void *W1, const void *W2, int w_dtype,
@@ -208,11 +209,11 @@ size_t spec_rnn_workspace_bytes(int R, int gamma, int V, int rank, int hidden);
  * parts (hi + mid + lo = s_k to fp32 precision).  The pages fix no gate
  * form; this single update gate on the concatenation is the reading taken.
  *   hidden_states [R][gamma][hidden]     fp32 backbone hidden states h_k
- *   Wg            [2 rank + hidden][2 rank]  w_dtype (bf16)
+ *   Wg            [2 rank + hidden][2 rank]  w_dtype (bf16), 16-byte aligned
  *   bg            [2 rank]               fp32
  *   out_state     [R][gamma][rank]       fp32 states s_k, nullable
  * Other arguments, sizes and errors as spec_markov_draft_sample, plus
- * 1 <= hidden <= SPEC_RNN_MAX_HIDDEN.
+ * 1 <= hidden <= SPEC_RNN_MAX_HIDDEN; a misaligned Wg returns SPEC_EINVAL.
  */
 int spec_rnn_draft_sample(const void *U, int u_dtype, const void *W1, const void *W2,
                           int w_dtype, const float *hidden_states, int hidden, const void *Wg,

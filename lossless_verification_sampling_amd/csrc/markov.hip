@@ -492,9 +492,11 @@ __device__ __forceinline__ float bf16_round(float x) {
 // RNN serial head: the gated state update of step k
 // ---------------------------------------------------------------------------
 
-constexpr int kRnnReq = 4;      // requests per workgroup (one wave each)
-constexpr int kRnnUnits = 32;   // state units per workgroup (two gate columns each)
-constexpr int kRnnMaxHidden = SPEC_RNN_MAX_HIDDEN;  // keeps the LDS of a workgroup under 64 KB
+constexpr int kRnnReq = 4;      // requests per workgroup of the gate product
+constexpr int kRnnKS = 32;      // workgroups splitting the 2 rank + hidden rows
+constexpr int kRnnRowsPerWave = (2 * kMkRank + SPEC_RNN_MAX_HIDDEN + 4 * kRnnKS - 1) / (4 * kRnnKS);
+constexpr int kRnnMaxHidden = SPEC_RNN_MAX_HIDDEN;
+constexpr int kRnnCols = 2 * kMkRank;  // update-gate and candidate columns
 
 struct RnnArgs {
     const uint16_t *W1;     // [V][rank] bf16 embedding
@@ -505,67 +507,108 @@ struct RnnArgs {
     const int32_t *tok;     // [R][gamma] drafted tokens (the previous step's)
     const float *s_prev;    // [R][rank]
     float *s_next;          // [R][rank]
+    float *part;            // [kRnnKS][R][2 rank] partial gate sums
     uint16_t *bsplit;       // [3][R][rank] bf16 parts of s_next
     float *out_state;       // [R][gamma][rank] or null
     int R, gamma, V, hidden, k;
 };
 
-// Workgroup (request block q0, unit block u0): wave w is request q0 + w, lane
-// l computes gate column (l / 32) * rank + u0 + l % 32 over the concatenation
-// c = [s_{k-1}; W1[x_{k-1}]; h_k] (fp32 sums of bf16 weights), then the first
-// 32 lanes make the update s_k = (1 - z) s_{k-1} + z tanh(n) and write s_k and
-// its three bf16 parts (hi = bf16(s), mid = bf16(s - hi), lo = bf16(s - hi -
-// mid); both differences are exact in fp32).
+// Element e of request r's concatenation c = [s_{k-1}; W1[x_{k-1}]; h_k].
+__device__ __forceinline__ float rnn_c(const RnnArgs &a, int r, int e) {
+    if (e < kMkRank) return a.k > 1 ? a.s_prev[(size_t)r * kMkRank + e] : 0.0f;
+    if (e < 2 * kMkRank) {
+        const int x = a.k == 1 ? a.anchor[r] : a.tok[(size_t)r * a.gamma + (a.k - 2)];
+        return (x >= 0 && x < a.V)
+                   ? __uint_as_float((uint32_t)a.W1[(size_t)x * kMkRank + (e - kMkRank)] << 16)
+                   : 0.0f;
+    }
+    return a.H[((size_t)r * a.gamma + (a.k - 1)) * a.hidden + (e - 2 * kMkRank)];
+}
+
+// Partial gate products: workgroup (request block q0, row block kb) takes
+// rows [kb rpb, (kb + 1) rpb) of c Wg for 4 requests, one quarter per wave;
+// lane l keeps columns 8 l .. 8 l + 7 for the 4 requests, each Wg row read
+// as one 1 KB wave load.  The waves' sums are added in LDS in wave order and
+// written to part[kb].
 __global__ void __launch_bounds__(kBlock) rnn_gate_kernel(RnnArgs a) {
-    extern __shared__ float cvec[];  // [kRnnReq][2 rank + hidden], then gates [kRnnReq][64]
+    __shared__ float cv[kRnnReq][4 * kRnnRowsPerWave];
+    __shared__ float red[4][kRnnReq][kRnnCols];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int dc = 2 * kMkRank + a.hidden;
-    const int q0 = blockIdx.x * kRnnReq, u0 = blockIdx.y * kRnnUnits;
-    for (int i = tid; i < kRnnReq * dc; i += kBlock) {
-        const int q = i / dc, e = i - q * dc;
-        const int r = q0 + q;
-        float v = 0.0f;
-        if (r < a.R) {
-            if (e < kMkRank) {
-                v = a.k > 1 ? a.s_prev[(size_t)r * kMkRank + e] : 0.0f;
-            } else if (e < 2 * kMkRank) {
-                const int x = a.k == 1 ? a.anchor[r] : a.tok[(size_t)r * a.gamma + (a.k - 2)];
-                if (x >= 0 && x < a.V)
-                    v = __uint_as_float((uint32_t)a.W1[(size_t)x * kMkRank + (e - kMkRank)] << 16);
-            } else {
-                v = a.H[((size_t)r * a.gamma + (a.k - 1)) * a.hidden + (e - 2 * kMkRank)];
+    const int rpb = (dc + kRnnKS - 1) / kRnnKS;  // rows per workgroup (<= 4 kRnnRowsPerWave)
+    const int q0 = blockIdx.x * kRnnReq, kb = blockIdx.y;
+    const int i0 = kb * rpb;
+    for (int t = tid; t < kRnnReq * rpb; t += kBlock) {
+        const int q = t / rpb, e = i0 + (t - q * rpb);
+        cv[q][t - q * rpb] = (q0 + q < a.R && e < dc) ? rnn_c(a, q0 + q, e) : 0.0f;
+    }
+    __syncthreads();
+    const int rpw = (rpb + 3) / 4;
+    const int w0 = wave * rpw;
+    float acc[kRnnReq][8];
+#pragma unroll
+    for (int q = 0; q < kRnnReq; ++q)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[q][j] = 0.0f;
+#pragma unroll
+    for (int t = 0; t < kRnnRowsPerWave; ++t) {
+        const int ir = w0 + t;             // row within the workgroup's block
+        const int i = i0 + ir;
+        const bool in = t < rpw && ir < rpb && i < dc;
+        const uint4 wv = *reinterpret_cast<const uint4 *>(a.Wg + (size_t)(in ? i : 0) * kRnnCols +
+                                                          lane * 8);
+        const float w[8] = {bf16_lo(wv.x), bf16_hi(wv.x), bf16_lo(wv.y), bf16_hi(wv.y),
+                            bf16_lo(wv.z), bf16_hi(wv.z), bf16_lo(wv.w), bf16_hi(wv.w)};
+        if (in) {
+#pragma unroll
+            for (int q = 0; q < kRnnReq; ++q) {
+                const float cq = cv[q][ir];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) acc[q][j] = fmaf(cq, w[j], acc[q][j]);
             }
         }
-        cvec[i] = v;
     }
+#pragma unroll
+    for (int q = 0; q < kRnnReq; ++q)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) red[wave][q][lane * 8 + j] = acc[q][j];
     __syncthreads();
-    const int unit = u0 + (lane & 31);
-    const int colg = (lane >> 5) * kMkRank + unit;  // column of Wg
-    const float *c = cvec + wave * dc;
-    float acc = a.bg[colg];
-#pragma unroll 8
-    for (int i = 0; i < dc; ++i)
-        acc = fmaf(c[i], __uint_as_float((uint32_t)a.Wg[(size_t)i * 2 * kMkRank + colg] << 16), acc);
-    float *gates = cvec + kRnnReq * dc;
-    gates[wave * 64 + lane] = acc;
-    __syncthreads();
-    const int r = q0 + wave;
-    if (lane < 32 && r < a.R) {
-        const float gz = gates[wave * 64 + lane], gn = gates[wave * 64 + 32 + lane];
-        const float z = 1.0f / (1.0f + expf(-gz));
-        const float n = tanhf(gn);
-        const float sp = c[unit];
-        const float sn = (1.0f - z) * sp + z * n;
-        a.s_next[(size_t)r * kMkRank + unit] = sn;
-        if (a.out_state) a.out_state[((size_t)r * a.gamma + (a.k - 1)) * kMkRank + unit] = sn;
-        const float hi = bf16_round(sn);
-        const float mid = bf16_round(sn - hi);
-        const float lo = bf16_round(sn - hi - mid);
-        const size_t o = (size_t)r * kMkRank + unit, plane = (size_t)a.R * kMkRank;
-        a.bsplit[o] = (uint16_t)(__float_as_uint(hi) >> 16);
-        a.bsplit[plane + o] = (uint16_t)(__float_as_uint(mid) >> 16);
-        a.bsplit[2 * plane + o] = (uint16_t)(__float_as_uint(lo) >> 16);
+    for (int t = tid; t < kRnnReq * kRnnCols; t += kBlock) {
+        const int q = t / kRnnCols, col = t - q * kRnnCols;
+        if (q0 + q < a.R) {
+            const float v = ((red[0][q][col] + red[1][q][col]) + red[2][q][col]) + red[3][q][col];
+            a.part[((size_t)kb * a.R + q0 + q) * kRnnCols + col] = v;
+        }
     }
+}
+
+// The update of unit u of request r: the partial sums added in row-block
+// order, z = sigmoid, n = tanh, s_k = (1 - z) s_{k-1} + z n, and its three bf16
+// parts (hi = bf16(s), mid = bf16(s - hi), lo = bf16(s - hi - mid); both
+// differences are exact in fp32).
+__global__ void __launch_bounds__(kBlock) rnn_state_kernel(RnnArgs a) {
+    const int t = blockIdx.x * kBlock + threadIdx.x;
+    if (t >= a.R * kMkRank) return;
+    const int r = t / kMkRank, u = t - r * kMkRank;
+    float gz = a.bg[u], gn = a.bg[kMkRank + u];
+    for (int kb = 0; kb < kRnnKS; ++kb) {
+        const float *pp = a.part + ((size_t)kb * a.R + r) * kRnnCols;
+        gz += pp[u];
+        gn += pp[kMkRank + u];
+    }
+    const float z = 1.0f / (1.0f + expf(-gz));
+    const float n = tanhf(gn);
+    const float sp = a.k > 1 ? a.s_prev[t] : 0.0f;
+    const float sn = (1.0f - z) * sp + z * n;
+    a.s_next[t] = sn;
+    if (a.out_state) a.out_state[((size_t)r * a.gamma + (a.k - 1)) * kMkRank + u] = sn;
+    const float hi = bf16_round(sn);
+    const float mid = bf16_round(sn - hi);
+    const float lo = bf16_round(sn - hi - mid);
+    const size_t plane = (size_t)a.R * kMkRank;
+    a.bsplit[t] = (uint16_t)(__float_as_uint(hi) >> 16);
+    a.bsplit[plane + t] = (uint16_t)(__float_as_uint(mid) >> 16);
+    a.bsplit[2 * plane + t] = (uint16_t)(__float_as_uint(lo) >> 16);
 }
 
 __global__ void markov_clear_kernel(uint32_t *bad, int R) {
@@ -626,7 +669,7 @@ void mk_launch_step(MarkovArgs a, const MkPlan &p, bool bf, hipStream_t st) {
 // three bf16 parts of the current one.
 struct RnnPlan {
     MkPlan mk;
-    size_t off_s0, off_s1, off_split, bytes;
+    size_t off_s0, off_s1, off_split, off_part, bytes;
 };
 
 bool rnn_plan(long R, long V, RnnPlan &p) {
@@ -635,7 +678,8 @@ bool rnn_plan(long R, long V, RnnPlan &p) {
     p.off_s0 = p.mk.bytes;
     p.off_s1 = mk_round_up(p.off_s0 + sb, 256);
     p.off_split = mk_round_up(p.off_s1 + sb, 256);
-    p.bytes = mk_round_up(p.off_split + 3 * sizeof(uint16_t) * (size_t)R * kMkRank, 256);
+    p.off_part = mk_round_up(p.off_split + 3 * sizeof(uint16_t) * (size_t)R * kMkRank, 256);
+    p.bytes = mk_round_up(p.off_part + sizeof(float) * kRnnKS * (size_t)R * kRnnCols, 256);
     return true;
 }
 
@@ -734,7 +778,7 @@ int spec_rnn_draft_sample(const void *U, int u_dtype, const void *W1, const void
     if (!U || !W1 || !W2 || !hidden_states || !Wg || !bg || !anchor || !temperature || !u_draft ||
         !out_draft_tokens || !out_draft_logits)
         return SPEC_EINVAL;
-    if (((uintptr_t)W1 & 15u) || ((uintptr_t)W2 & 15u)) return SPEC_EINVAL;
+    if (((uintptr_t)W1 & 15u) || ((uintptr_t)W2 & 15u) || ((uintptr_t)Wg & 15u)) return SPEC_EINVAL;
     RnnPlan p;
     rnn_plan(R, V, p);
     if (!workspace || ((uintptr_t)workspace & 255u) || workspace_bytes < p.bytes)
@@ -752,23 +796,25 @@ int spec_rnn_draft_sample(const void *U, int u_dtype, const void *W1, const void
     g.anchor = anchor;
     g.tok = out_draft_tokens;
     g.bsplit = (uint16_t *)(ws + p.off_split);
+    g.part = (float *)(ws + p.off_part);
     g.out_state = out_state;
     g.R = R;
     g.gamma = gamma;
     g.V = V;
     g.hidden = hidden;
     float *s0 = (float *)(ws + p.off_s0), *s1 = (float *)(ws + p.off_s1);
-    const size_t lds = sizeof(float) * (size_t)kRnnReq * (2 * kMkRank + hidden + 64);
     note_workspace_clean(workspace, sizeof(Control));
     hipStream_t st = (hipStream_t)stream;
     hipLaunchKernelGGL(markov_clear_kernel, dim3((R + kBlock - 1) / kBlock), dim3(kBlock), 0, st,
                        a.bad, R);
-    const dim3 ggrid((R + kRnnReq - 1) / kRnnReq, kMkRank / kRnnUnits);
+    const dim3 ggrid((R + kRnnReq - 1) / kRnnReq, kRnnKS);
+    const dim3 sgrid((R * kMkRank + kBlock - 1) / kBlock);
     for (int k = 1; k <= gamma; ++k) {
         g.k = k;
         g.s_prev = (k & 1) ? s0 : s1;  // unread at k = 1 (s_0 = 0)
         g.s_next = (k & 1) ? s1 : s0;
-        hipLaunchKernelGGL(rnn_gate_kernel, ggrid, dim3(kBlock), lds, st, g);
+        hipLaunchKernelGGL(rnn_gate_kernel, ggrid, dim3(kBlock), 0, st, g);
+        hipLaunchKernelGGL(rnn_state_kernel, sgrid, dim3(kBlock), 0, st, g);
         a.k = k;
         mk_launch_step<3>(a, p.mk, u_dtype == SPEC_BF16, st);
     }
