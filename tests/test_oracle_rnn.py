@@ -2,7 +2,10 @@
 with the update gate shut it is sampling from U alone (the C Markov oracle
 with a zero embedding), with the gate open and the candidate reading only the
 embedding it is a Markov head with embedding tanh(W1) (the C Markov oracle on
-fp32 tables), and its state stays inside (-1, 1)."""
+fp32 tables), and its state stays inside (-1, 1).  Gate weights made of
+identity blocks reduce the update to scalar recurrences per state unit that
+are written out here: the candidate reading the hidden state alone, the
+previous state plus the hidden state, and the gate held at one half."""
 import numpy as np
 import pytest
 
@@ -81,3 +84,59 @@ def test_invalid_requests(lib):
     out = rnn.rnn_draft(mk.U, mk.W1, mk.W2, c.H, c.Wg, c.bg, anchor, T, mk.u_draft, lib=lib)
     assert (out["tokens"][1] == -1).all() and (out["tokens"][2] == -1).all()
     assert (out["tokens"][0] >= 0).all()
+
+
+def _identity_gate(rank, hidden, cand_from_state, cand_from_hidden, z_bias):
+    """Wg with Wz = 0 (z = sigmoid(z_bias)) and the candidate's pre-activation
+    the chosen sum of the state slot and the first rank hidden values."""
+    wg = np.zeros((2 * rank + hidden, 2 * rank), np.float32)
+    eye = np.eye(rank, dtype=np.float32)
+    if cand_from_state:
+        wg[0:rank, rank:2 * rank] = eye
+    if cand_from_hidden:
+        wg[2 * rank:3 * rank, rank:2 * rank] = eye
+    bg = np.zeros(2 * rank, np.float32)
+    bg[:rank] = z_bias
+    return wg, bg
+
+
+def _check_recurrence(c, wg, bg, step, lib):
+    """States against s_k = step(s_{k-1}, h_k[:rank]) with s_0 = 0, and the
+    logits against U_k + s_k W2, while the tokens follow the oracle's draws."""
+    mk = c.mk
+    r = mk.rank
+    out = rnn.rnn_draft(mk.U, mk.W1, mk.W2, c.H, wg, bg, mk.anchor, mk.temperature,
+                        mk.u_draft, lib=lib)
+    w2 = workloads.bf16_bits_to_f32(mk.W2).astype(np.float64)
+    u = workloads.bf16_bits_to_f32(mk.U).astype(np.float64) if mk.U.dtype == np.uint16 \
+        else mk.U.astype(np.float64)
+    for i in range(mk.R):
+        s = np.zeros(r)
+        for k in range(mk.gamma):
+            s = step(s, c.H[i, k, :r].astype(np.float64))
+            np.testing.assert_allclose(out["states"][i, k], s, rtol=0, atol=1e-12)
+            want = (u[i, k] + s @ w2).astype(np.float32)
+            np.testing.assert_allclose(out["logits"][i, k], want, rtol=0, atol=2e-6)
+    assert np.all(out["tokens"] >= 0)
+    return out
+
+
+def test_candidate_reads_the_hidden_state(lib):
+    # z = 1, n = tanh(h_k): s_k = tanh(h_k), no dependence on the tokens
+    c = small(5, R=3, gamma=4, V=300, hidden=300)
+    wg, bg = _identity_gate(c.mk.rank, 300, False, True, 1e4)
+    _check_recurrence(c, wg, bg, lambda s, h: np.tanh(h), lib)
+
+
+def test_candidate_reads_state_and_hidden(lib):
+    # z = 1, n = tanh(s_{k-1} + h_k): s_k = tanh(s_{k-1} + h_k)
+    c = small(6, R=2, gamma=5, V=300, hidden=256)
+    wg, bg = _identity_gate(c.mk.rank, 256, True, True, 1e4)
+    _check_recurrence(c, wg, bg, lambda s, h: np.tanh(s + h), lib)
+
+
+def test_half_open_gate_averages(lib):
+    # z = sigmoid(0) = 1/2: s_k = (s_{k-1} + tanh(h_k)) / 2
+    c = small(7, R=2, gamma=6, V=300, hidden=256, T=0.0)
+    wg, bg = _identity_gate(c.mk.rank, 256, False, True, 0.0)
+    _check_recurrence(c, wg, bg, lambda s, h: 0.5 * s + 0.5 * np.tanh(h), lib)
