@@ -1,5 +1,5 @@
-"""Plants plausible mistakes in copies of the Python oracles (the RNN head
-and the verify-length scheduler) and checks that at least one of their pins
+"""Plants plausible mistakes in copies of the Python oracles (the RNN head,
+the verify-length scheduler and the STS calibration) and checks that at least one of their pins
 rejects each copy.  The copy is executed as a module of the oracle package
 and swapped in for the pin module's reference while its tests run (CPU)."""
 import importlib
@@ -47,6 +47,19 @@ MUTANTS = [
      "if B + 1 > bmax:", "if B + 2 > bmax:"),
     ("schedule", "test_oracle_schedule", "topk_one_extra",
      "if topk >= 0 and admitted >= topk:", "if topk >= 0 and admitted > topk:"),
+    ("sts", "test_oracle_sts", "temperature_multiplies",
+     "a = a_prev * sigmoid(z[:, k] / grid[g])", "a = a_prev * sigmoid(z[:, k] * grid[g])"),
+    ("sts", "test_oracle_sts", "earlier_positions_raw",
+     "a_prev = a_prev * sigmoid(z[:, k] / temps[k])", "a_prev = a_prev * sigmoid(z[:, k])"),
+    ("sts", "test_oracle_sts", "top_bin_unclamped",
+     "return np.minimum(np.floor(a * bins).astype(np.int64), bins - 1)",
+     "return np.floor(a * bins).astype(np.int64) % bins"),
+    ("sts", "test_oracle_sts", "signed_bin_gaps",
+     "return float(np.abs(gap).sum() / len(a))", "return float(abs(gap.sum()) / len(a))"),
+    ("sts", "test_oracle_sts", "ties_to_last",
+     "best = int(np.argmin(curves[k]))", "best = int(len(grid) - 1 - np.argmin(curves[k][::-1]))"),
+    ("sts", "test_oracle_sts", "label_off_by_one",
+     "y = (A >= k + 1).astype(np.float64)", "y = (A > k + 1).astype(np.float64)"),
 ]
 
 
@@ -79,7 +92,7 @@ def _calls(fn, lib):
 def test_python_oracle_mutant_is_caught(mutant, monkeypatch):
     mod_name, pins_name, _, old, new = mutant
     pins = importlib.import_module(pins_name)
-    ref_attr = {"rnn": "rnn", "schedule": "sch"}[mod_name]
+    ref_attr = {"rnn": "rnn", "schedule": "sch", "sts": "sts"}[mod_name]
     assert getattr(pins, ref_attr) is importlib.import_module(f"oracle.{mod_name}")
     monkeypatch.setattr(pins, ref_attr, _mutant_module(mod_name, old, new))
     oracle.build(force=False)

@@ -48,6 +48,7 @@ STREAM_PARAMS = 6
 STREAM_MARKOV = 7
 STREAM_SCHEDULE = 8
 STREAM_RNN = 9
+STREAM_STS = 10
 
 
 def rng(seed: int, stream: int) -> np.random.Generator:
@@ -387,3 +388,35 @@ def algorithmic_bytes(verify_len: np.ndarray, V: int, t_elt: int, d_elt: int) ->
     vl = np.asarray(verify_len, dtype=np.int64)
     vl = vl[(vl >= 0)]
     return int(((vl * (t_elt + d_elt)).sum() + vl.size * t_elt) * V)
+
+
+@dataclasses.dataclass
+class StsCase:
+    """A held-out set for confidence calibration: the confidence head's raw
+    logits per draft position and each block's accepted prefix length."""
+    z: np.ndarray       # [N, gamma] fp32 raw confidence logits
+    accepted: np.ndarray  # [N] int32 leading accepted positions, 0..gamma
+    grid: np.ndarray    # [G] fp64 candidate temperatures, ascending
+    N: int
+    gamma: int
+
+
+def sts_case(seed: int = 10, N: int = 4096, gamma: int = 7, G: int = 64,
+             kappa: float = 1.2) -> StsCase:
+    """Per block a difficulty u ~ N(1, 1) and per position a suffix decay of
+    0.15; the true conditional acceptance is pi = sigmoid(u - 0.15 (k - 1) +
+    N(0, 0.5^2)), acceptance of each position is drawn from pi and the block
+    keeps its leading accepts.  The head is overconfident: its raw logit is
+    (kappa + 0.1 k) logit(pi) + N(0, 0.3^2).  Candidate temperatures: G values
+    spaced evenly in log between 0.25 and 8."""
+    g = rng(seed, STREAM_STS)
+    u = g.normal(1.0, 1.0, size=(N, 1))
+    k = np.arange(1, gamma + 1)[None, :]
+    lg = u - 0.15 * (k - 1) + g.normal(0.0, 0.5, size=(N, gamma))
+    pi = 1.0 / (1.0 + np.exp(-lg))
+    acc = g.random(size=(N, gamma)) < pi
+    rej = ~acc
+    first_rej = np.where(rej.any(axis=1), rej.argmax(axis=1), gamma)
+    z = ((kappa + 0.1 * k) * lg + g.normal(0.0, 0.3, size=(N, gamma))).astype(np.float32)
+    grid = np.exp(np.linspace(np.log(0.25), np.log(8.0), G))
+    return StsCase(z=z, accepted=first_rej.astype(np.int32), grid=grid, N=N, gamma=gamma)
