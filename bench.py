@@ -22,7 +22,8 @@ Prints one JSON line:
 --workload dspark measures the Markov-head draft (R = 64, gamma = 7,
 V = 129280, rank 256) instead, as an extra line; --workload schedule the
 confidence-scheduled verify lengths of the same batch size (448 candidates);
---workload rnn the RNN serial head at the Markov workload's size.
+--workload rnn the RNN serial head at the Markov workload's size; --workload
+sts the confidence head's sequential temperature scaling on a held-out set.
 """
 from __future__ import annotations
 
@@ -347,6 +348,75 @@ def bench_schedule(args):
     return res
 
 
+# fp64 VALU instructions the histogram loop issues per (block, temperature)
+# score (the sigmoid's exp polynomial and two divides, the bin index, the
+# running product), counted in the kernel's gfx950 assembly; the peak is
+# 256 CUs x 64 fp64 lanes per clock x 2.4 GHz.
+STS_OPS_PER_SCORE = 50
+STS_PEAK_TOPS = 256 * 64 * 2.4e9 / 1e12
+
+
+def bench_sts(args):
+    """Sequential temperature scaling of the confidence head on a held-out set
+    of 262144 draft blocks (gamma = 7), 64 candidate temperatures, 15 bins:
+    every (block, temperature, position) score is evaluated once in fp64.
+    The oracle (numpy, fp64) is timed beside it on the first 16384 blocks."""
+    import torch
+    import lossless_verification_sampling_amd as sv
+    import workloads
+
+    dev = torch.device("cuda:0")
+    N, gamma, G, bins = 262144, 7, 64, 15
+    c = workloads.sts_case(seed=args.seed + 7, N=N, gamma=gamma, G=G)
+    z, A, grid = to_device(c.z, dev), to_device(c.accepted, dev), to_device(c.grid, dev)
+    ws = sv.Workspace(dev, sv.spec_sts_workspace_bytes(N, gamma, G, bins))
+    for _ in range(args.warmup):
+        sv.spec_sts_calibrate(z, A, grid, bins=bins, workspace=ws)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        ev[k][0].record(stream)
+        t, e, _ = sv.spec_sts_calibrate(z, A, grid, bins=bins, workspace=ws)
+        ev[k][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = np.array([a.elapsed_time(b) for a, b in ev])
+    evals = N * G * gamma
+    achieved = STS_OPS_PER_SCORE * evals / (ms.mean() / 1e3) / 1e12
+    res = {
+        "metric": "STS calibration: scored (block, temperature, position) triples/sec",
+        "value": evals / (wall / args.steps),
+        "unit": "scores/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": wall / args.steps * 1e3,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f64", "data": "synthetic",
+        "config": {"workload": "sts", "N": N, "gamma": gamma, "grid": G, "bins": bins,
+                   "temperatures": [round(float(x), 4) for x in t.cpu().numpy()],
+                   "ece": [round(float(x), 5) for x in e.cpu().numpy()]},
+        "roofline": {"bound": "alu", "achieved": achieved, "peak": STS_PEAK_TOPS,
+                     "unit": "T fp64 lane-instructions/s", "frac": achieved / STS_PEAK_TOPS,
+                     "traffic": None,
+                     "ops_per_score": STS_OPS_PER_SCORE,
+                     "kernel": "spec_sts_calibrate call (sts_hist_kernel dominates)"},
+        "kernel_ms_mean": float(ms.mean()),
+    }
+    if not args.no_cpu_baseline:
+        from oracle import sts as osts
+        n_cpu = 16384
+        t1 = time.perf_counter()
+        osts.sts_calibrate(c.z[:n_cpu], c.accepted[:n_cpu], c.grid, bins=bins)
+        el = time.perf_counter() - t1
+        res["cpu_baseline"] = {"value": n_cpu * G * gamma / el, "unit": "scores/s", "cores": 1,
+                               "kind": "oracle",
+                               "sample": f"the first {n_cpu} blocks, all {G} temperatures and "
+                                         f"{gamma} positions, numpy fp64"}
+    return res
+
+
 def calibrate_copy(args):
     """One device-to-device copy of a known size, repeated: the reference that
     scales rocprofv3's FETCH_SIZE / WRITE_SIZE counters to bytes."""
@@ -437,7 +507,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--seed", type=int, default=3)
     ap.add_argument("--copies", type=int, default=0, help="input copies rotated (0 = auto)")
-    ap.add_argument("--workload", choices=["batched", "dspark", "rnn", "schedule"],
+    ap.add_argument("--workload", choices=["batched", "dspark", "rnn", "schedule", "sts"],
                     default="batched")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -462,7 +532,7 @@ def main():
         res = calibrate_copy(args)
     else:
         res = {"batched": bench_verify, "dspark": bench_dspark, "rnn": bench_rnn,
-               "schedule": bench_schedule}[args.workload](args)
+               "schedule": bench_schedule, "sts": bench_sts}[args.workload](args)
     print(json.dumps(res))
 
 

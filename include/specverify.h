@@ -85,6 +85,11 @@ typedef enum {
 /* Largest candidate pool (R * gamma, and R) spec_schedule_verify_len accepts. */
 #define SPEC_SCHED_MAX_POOL 8192
 
+/* Limits of spec_sts_calibrate: bins, grid points, held-out blocks. */
+#define SPEC_STS_MAX_BINS 24
+#define SPEC_STS_MAX_GRID 1024
+#define SPEC_STS_MAX_BLOCKS (1 << 24)
+
 /* Library version, major * 10000 + minor * 100 + patch. */
 int spec_version(void);
 
@@ -255,6 +260,41 @@ size_t spec_schedule_workspace_bytes(void);
 int spec_schedule_verify_len(const float *confidence, const float *sps, int R, int gamma,
                              int bmax, int topk, int32_t *out_len, double *out_theta,
                              void *workspace, size_t workspace_bytes, void *stream);
+
+/* Workspace bytes for spec_sts_calibrate (0 for sizes it does not accept). */
+size_t spec_sts_workspace_bytes(int N, int gamma, int G, int bins);
+
+/*
+ * Sequential temperature scaling of the confidence head (DSpark guide, the
+ * confidence-head section, "STS"), on a held-out set of N draft blocks.
+ *
+ * Position k's score of block n is c = sigmoid(z[n][k] / t_k); the
+ * cumulative probability a_k = c_1 ... c_k is labelled by
+ * y_k = [accepted_len[n] >= k] (positions 1..k all accepted).  Left to right,
+ * t_k is the grid temperature minimising
+ *   ECE_k(t) = sum_m |sum_{n in bin m} (a_{n,k}(t) - y_{n,k})| / N
+ * over `bins` equal-width bins of [0, 1] (a value of 1 in the last bin), with
+ * t_1..t_{k-1} fixed; ties go to the first grid point.  All arithmetic is
+ * fp64 in a fixed order.  The pages give the search, not these details: the
+ * sigmoid form, the prefix label, the bin layout and the tie rule are the
+ * readings taken.  A grid of the single value 1 reports the raw scores' ECE.
+ *   conf_logits     [N][gamma]  fp32 raw head logits, finite  (device)
+ *   accepted_len    [N]         int32 in [0, gamma]           (device)
+ *   grid            [G]         fp64 temperatures > 0         (device)
+ *   out_temperature [gamma]     fp64                          (device)
+ *   out_ece         [gamma]     fp64, ECE at the chosen t     (device)
+ *   out_curve       [gamma][G]  fp64 ECE at every grid point, nullable
+ * Sizes: N >= 0, gamma >= 0, 1 <= G <= SPEC_STS_MAX_GRID,
+ * 1 <= bins <= SPEC_STS_MAX_BINS, N <= SPEC_STS_MAX_BLOCKS.  A non-finite
+ * logit, an accepted length outside [0, gamma] or a grid value that is not a
+ * positive finite number sets SPEC_DEV_BAD_REQUEST and makes every output
+ * NaN.  The inputs, outputs and workspace belong to the caller; work is
+ * enqueued on `stream`.
+ */
+int spec_sts_calibrate(const float *conf_logits, const int32_t *accepted_len, const double *grid,
+                       int N, int gamma, int G, int bins, double *out_temperature,
+                       double *out_ece, double *out_curve, void *workspace,
+                       size_t workspace_bytes, void *stream);
 
 /* Synchronises `stream`, copies the workspace's device status word (the OR
  * of SPEC_DEV_* bits raised since the last clear) to *host_bits, and clears

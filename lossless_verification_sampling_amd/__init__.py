@@ -30,6 +30,9 @@ SPEC_MAX_VOCAB = 2097152
 SPEC_MAX_VERIFY_VOCAB = 262144
 SPEC_SCHED_MAX_POOL = 8192
 SPEC_RNN_MAX_HIDDEN = 3072
+SPEC_STS_MAX_BINS = 24
+SPEC_STS_MAX_GRID = 1024
+SPEC_STS_MAX_BLOCKS = 1 << 24
 
 EXPORTED = (
     "spec_version",
@@ -44,6 +47,8 @@ EXPORTED = (
     "spec_rnn_draft_sample",
     "spec_schedule_workspace_bytes",
     "spec_schedule_verify_len",
+    "spec_sts_workspace_bytes",
+    "spec_sts_calibrate",
     "spec_markov_draft_sample",
     "spec_get_device_status",
 )
@@ -88,6 +93,10 @@ def _load() -> ctypes.CDLL:
     lib.spec_schedule_workspace_bytes.argtypes = []
     lib.spec_schedule_verify_len.restype = i
     lib.spec_schedule_verify_len.argtypes = [p, p, i, i, i, i, p, p, p, sz, p]
+    lib.spec_sts_workspace_bytes.restype = sz
+    lib.spec_sts_workspace_bytes.argtypes = [i, i, i, i]
+    lib.spec_sts_calibrate.restype = i
+    lib.spec_sts_calibrate.argtypes = [p, p, p, i, i, i, i, p, p, p, p, sz, p]
     lib.spec_get_device_status.restype = i
     lib.spec_get_device_status.argtypes = [p, ctypes.POINTER(ctypes.c_uint32), i, p]
     return lib
@@ -126,6 +135,10 @@ def spec_rnn_workspace_bytes(R: int, gamma: int, V: int, rank: int, hidden: int)
 
 def spec_schedule_workspace_bytes() -> int:
     return int(_lib.spec_schedule_workspace_bytes())
+
+
+def spec_sts_workspace_bytes(N: int, gamma: int, G: int, bins: int) -> int:
+    return int(_lib.spec_sts_workspace_bytes(N, gamma, G, bins))
 
 
 # ---------------------------------------------------------------------------
@@ -337,6 +350,36 @@ def spec_schedule_verify_len(confidence: torch.Tensor, sps: torch.Tensor, *, top
                                        _stream_ptr(stream, dev))
     _raise(st, "spec_schedule_verify_len")
     return ln, th
+
+
+def spec_sts_calibrate(conf_logits: torch.Tensor, accepted_len: torch.Tensor, grid: torch.Tensor,
+                       *, bins: int = 15, want_curve: bool = False,
+                       workspace: Optional[Workspace] = None, stream=None):
+    """Sequential temperature scaling of the confidence head on a held-out
+    set.  conf_logits [N, gamma] float32 raw logits, accepted_len [N] int32
+    (accepted prefix length per block), grid [G] float64 candidate
+    temperatures.  Returns (temperatures [gamma] float64, ece [gamma] float64,
+    curves [gamma, G] float64 or None)."""
+    N, gamma = conf_logits.shape
+    G = grid.numel()
+    dev = conf_logits.device
+    _check(conf_logits, "conf_logits", torch.float32, (N, gamma), dev)
+    _check(accepted_len, "accepted_len", torch.int32, (N,), dev)
+    _check(grid, "grid", torch.float64, (G,), dev)
+    temps = torch.empty((gamma,), dtype=torch.float64, device=dev)
+    ece = torch.empty((gamma,), dtype=torch.float64, device=dev)
+    curve = torch.empty((gamma, G), dtype=torch.float64, device=dev) if want_curve else None
+    need = spec_sts_workspace_bytes(max(N, 1), gamma, G, bins)
+    if need == 0:
+        raise ValueError(f"spec_sts_calibrate: unsupported sizes N={N} G={G} bins={bins}")
+    ws = workspace or default_workspace(dev)
+    buf = ws.ensure(need, stream)
+    st = _lib.spec_sts_calibrate(_ptr(conf_logits), _ptr(accepted_len), _ptr(grid), N, gamma, G,
+                                 int(bins), _ptr(temps), _ptr(ece),
+                                 _ptr(curve) if curve is not None else None, _ptr(buf),
+                                 buf.numel(), _stream_ptr(stream, dev))
+    _raise(st, "spec_sts_calibrate")
+    return temps, ece, curve
 
 
 def spec_rnn_draft_sample(U: torch.Tensor, W1: torch.Tensor, W2: torch.Tensor,

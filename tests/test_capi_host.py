@@ -199,6 +199,46 @@ def test_schedule_argument_validation(lib):
     assert sc(R=0) == SPEC_OK
 
 
+def test_sts_argument_validation(lib):
+    p = ctypes.c_void_p
+    fake = p(0x1000)
+    i = ctypes.c_int
+    w = lib.spec_sts_workspace_bytes
+    w.restype = ctypes.c_size_t
+    w.argtypes = [i, i, i, i]
+    f = lib.spec_sts_calibrate
+    f.restype = i
+    f.argtypes = [p, p, p, i, i, i, i, p, p, p, p, ctypes.c_size_t, p]
+    need = w(4096, 7, 64, 15)
+    # a_prev (8 N) + tile sums (8 G bins tiles) + sums (8 G bins) + control
+    assert need >= 8 * 4096 + 8 * 64 * 15 * 8 + 8 * 64 * 15 + 256
+    assert w(4096, 7, 64, 25) == 0 and w(4096, 7, 1025, 15) == 0 and w(0, 7, 64, 15) == 0
+    assert w((1 << 24) + 1, 7, 64, 15) == 0
+
+    def sc(**kw):
+        a = dict(z=fake, A=fake, g=fake, N=4096, gamma=7, G=64, bins=15, t=fake, e=fake,
+                 curve=None, ws=p(0x10000), wsb=need)
+        a.update(kw)
+        return f(a["z"], a["A"], a["g"], a["N"], a["gamma"], a["G"], a["bins"], a["t"], a["e"],
+                 a["curve"], a["ws"], a["wsb"], None)
+
+    assert sc(N=-1) == SPEC_EINVAL
+    assert sc(gamma=-1) == SPEC_EINVAL
+    assert sc(G=0) == SPEC_EINVAL
+    assert sc(bins=0) == SPEC_EINVAL
+    assert sc(G=1025) == SPEC_EUNSUPPORTED
+    assert sc(bins=25) == SPEC_EUNSUPPORTED
+    assert sc(N=0) == SPEC_OK and sc(gamma=0) == SPEC_OK
+    assert sc(z=None) == SPEC_EINVAL
+    assert sc(A=None) == SPEC_EINVAL
+    assert sc(g=None) == SPEC_EINVAL
+    assert sc(t=None) == SPEC_EINVAL
+    assert sc(e=None) == SPEC_EINVAL
+    assert sc(ws=None) == SPEC_EWORKSPACE
+    assert sc(ws=p(0x10008)) == SPEC_EWORKSPACE
+    assert sc(wsb=need - 1) == SPEC_EWORKSPACE
+
+
 def test_workspace_init_validation(lib):
     f = lib.spec_workspace_init
     f.restype = ctypes.c_int

@@ -1,0 +1,106 @@
+"""GPU parity of spec_sts_calibrate against the STS oracle (fp64 both
+sides): temperatures exact and ECE values to 1e-12 (fixed-order fp64 sums of
+N terms, against numpy's order), on ragged tiles, grids that are not a
+multiple of 64, one and 24 bins, and the full held-out size; repeated calls
+bit-identical; invalid inputs flagged.  A position whose best and runner-up
+grid points lie within 1e-9 of each other, or where some cumulative value
+sits within 1e-12 of a bin edge (where exp's last bit could move a block to
+the next bin), is not graded on the temperature."""
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from gpu_util import to_device
+from oracle import sts as osts
+
+pytestmark = pytest.mark.gpu
+
+ECE_TOL = 1e-12
+
+
+@pytest.fixture(scope="module")
+def sv():
+    import lossless_verification_sampling_amd as m
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return m
+
+
+@pytest.fixture(scope="module")
+def dev(sv):
+    return torch.device("cuda:0")
+
+
+def run(sv, dev, z, A, grid, bins, ws=None):
+    t, e, c = sv.spec_sts_calibrate(to_device(z, dev), to_device(A, dev),
+                                    to_device(np.asarray(grid, np.float64), dev), bins=bins,
+                                    want_curve=True, workspace=ws)
+    torch.cuda.synchronize()
+    return t.cpu().numpy(), e.cpu().numpy(), c.cpu().numpy()
+
+
+def check(out, ref):
+    t, e, c = out
+    np.testing.assert_allclose(c, ref["curves"], rtol=0, atol=ECE_TOL)
+    np.testing.assert_allclose(e, ref["ece"], rtol=0, atol=ECE_TOL)
+    graded = (ref["tie_gap"] > 1e-9) & (ref["edge"] > 1e-12)
+    np.testing.assert_array_equal(t[graded], ref["temperatures"][graded])
+    return int(graded.sum())
+
+
+@pytest.mark.parametrize("N,gamma,G,bins", [
+    (700, 3, 37, 15),        # a ragged second tile, a partial grid block
+    (4096, 7, 64, 15),       # eight full tiles, one grid block
+    (1500, 4, 130, 10),      # three grid blocks
+    (513, 2, 5, 1),          # one bin, one block past a tile
+    (2000, 5, 64, 24),       # the largest bin count
+])
+def test_sts_matches_oracle(sv, dev, N, gamma, G, bins):
+    print(f"[sts] N={N} gamma={gamma} G={G} bins={bins}", flush=True)
+    c = workloads.sts_case(seed=N + G, N=N, gamma=gamma, G=G)
+    ref = osts.sts_calibrate(c.z, c.accepted, c.grid, bins=bins)
+    graded = check(run(sv, dev, c.z, c.accepted, c.grid, bins), ref)
+    assert graded >= gamma - 1
+
+
+def test_sts_full_held_out_set(sv, dev):
+    # the benchmark's held-out set: 262144 blocks, gamma 7, 64 temperatures
+    print("[sts] N=262144 gamma=7 G=64 bins=15", flush=True)
+    c = workloads.sts_case(seed=10, N=262144, gamma=7, G=64)
+    ref = osts.sts_calibrate(c.z, c.accepted, c.grid, bins=15)
+    check(run(sv, dev, c.z, c.accepted, c.grid, 15), ref)
+
+
+def test_raw_ece_with_unit_grid_and_repeatability(sv, dev):
+    c = workloads.sts_case(seed=4, N=3000, gamma=6, G=48)
+    ref = osts.sts_calibrate(c.z, c.accepted, np.array([1.0]), bins=15)
+    raw = run(sv, dev, c.z, c.accepted, [1.0], 15)
+    np.testing.assert_array_equal(raw[0], np.ones(6))
+    np.testing.assert_allclose(raw[1], ref["ece"], rtol=0, atol=ECE_TOL)
+    ws = sv.Workspace(dev, sv.spec_sts_workspace_bytes(3000, 6, 48, 15))
+    a = run(sv, dev, c.z, c.accepted, c.grid, 15, ws)
+    b = run(sv, dev, c.z, c.accepted, c.grid, 15, ws)
+    for x, y in zip(a, b):
+        np.testing.assert_array_equal(x, y)
+    assert np.all(a[1] < raw[1])
+
+
+@pytest.mark.parametrize("fault", ["nan_logit", "length_high", "length_negative", "grid_zero"])
+def test_sts_invalid_inputs(sv, dev, fault):
+    c = workloads.sts_case(seed=5, N=900, gamma=3, G=16)
+    z, A, grid = c.z.copy(), c.accepted.copy(), c.grid.copy()
+    if fault == "nan_logit":
+        z[17, 2] = np.nan
+    elif fault == "length_high":
+        A[5] = 4
+    elif fault == "length_negative":
+        A[800] = -1
+    else:
+        grid[3] = 0.0
+    ws = sv.Workspace(dev, sv.spec_sts_workspace_bytes(900, 3, 16, 15))
+    t, e, cv = run(sv, dev, z, A, grid, 15, ws)
+    assert np.all(np.isnan(t)) and np.all(np.isnan(e)) and np.all(np.isnan(cv))
+    assert sv.spec_get_device_status(ws, clear=True) & sv.SPEC_DEV_BAD_REQUEST
+    # the same workspace then serves a valid call
+    good = run(sv, dev, c.z, c.accepted, c.grid, 15, ws)
+    assert np.all(np.isfinite(good[0]))
