@@ -1,5 +1,6 @@
 """Plants plausible mistakes in copies of the Python oracles (the RNN head,
-the verify-length scheduler and the STS calibration) and checks that at least one of their pins
+the verify-length scheduler, the STS calibration and greedy tree
+verification) and checks that at least one of their pins
 rejects each copy.  The copy is executed as a module of the oracle package
 and swapped in for the pin module's reference while its tests run (CPU)."""
 import importlib
@@ -60,6 +61,18 @@ MUTANTS = [
      "best = int(np.argmin(curves[k]))", "best = int(len(grid) - 1 - np.argmin(curves[k][::-1]))"),
     ("sts", "test_oracle_sts", "label_off_by_one",
      "y = (A >= k + 1).astype(np.float64)", "y = (A > k + 1).astype(np.float64)"),
+    ("tree", "test_oracle_tree", "always_root_row", "g = _row_argmax(L[r, cur])",
+     "g = _row_argmax(L[r, 0])"),
+    ("tree", "test_oracle_tree", "any_node_not_children", "if P[r, v] == cur and X[r, v] == g:",
+     "if X[r, v] == g:"),
+    ("tree", "test_oracle_tree", "bonus_dropped", "                toks.append(g)\n",
+     "                toks.append(-1)\n"),
+    ("tree", "test_oracle_tree", "argmax_ties_last", "return int(np.argmax(r))",
+     "return int(len(r) - 1 - np.argmax(r[::-1]))"),
+    ("tree", "test_oracle_tree", "last_equal_sibling",
+     "                    nxt = v\n                    break\n", "                    nxt = v\n"),
+    ("tree", "test_oracle_tree", "parent_may_be_self", "ok = ok and 0 <= P[r, v] < v and",
+     "ok = ok and 0 <= P[r, v] <= v and"),
 ]
 
 
@@ -92,7 +105,7 @@ def _calls(fn, lib):
 def test_python_oracle_mutant_is_caught(mutant, monkeypatch):
     mod_name, pins_name, _, old, new = mutant
     pins = importlib.import_module(pins_name)
-    ref_attr = {"rnn": "rnn", "schedule": "sch", "sts": "sts"}[mod_name]
+    ref_attr = {"rnn": "rnn", "schedule": "sch", "sts": "sts", "tree": "otree"}[mod_name]
     assert getattr(pins, ref_attr) is importlib.import_module(f"oracle.{mod_name}")
     monkeypatch.setattr(pins, ref_attr, _mutant_module(mod_name, old, new))
     oracle.build(force=False)

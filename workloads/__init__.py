@@ -49,6 +49,7 @@ STREAM_MARKOV = 7
 STREAM_SCHEDULE = 8
 STREAM_RNN = 9
 STREAM_STS = 10
+STREAM_TREE = 11
 
 
 def rng(seed: int, stream: int) -> np.random.Generator:
@@ -420,3 +421,61 @@ def sts_case(seed: int = 10, N: int = 4096, gamma: int = 7, G: int = 64,
     z = ((kappa + 0.1 * k) * lg + g.normal(0.0, 0.3, size=(N, gamma))).astype(np.float32)
     grid = np.exp(np.linspace(np.log(0.25), np.log(8.0), G))
     return StsCase(z=z, accepted=first_rej.astype(np.int32), grid=grid, N=N, gamma=gamma)
+
+
+@dataclasses.dataclass
+class TreeCase:
+    """A draft tree per request (topological order, node 0 the root) and the
+    target's logits at every node."""
+    logits: np.ndarray   # [R, M, V] bf16 bits (uint16) or fp32
+    parent: np.ndarray   # [R, M] int32, -1 for the root and unused slots
+    tokens: np.ndarray   # [R, M] int32 draft token of each node (root: -1)
+    n_nodes: np.ndarray  # [R] int32
+    R: int
+    M: int
+    V: int
+    max_depth: int
+
+
+def tree_case(seed: int = 12, R: int = 64, M: int = 32, V: int = 151936, dtype: str = "bf16",
+              widths=(4, 3, 2, 2, 1, 1, 1, 1), p_hit: float = 0.7,
+              n_nodes: Optional[np.ndarray] = None) -> TreeCase:
+    """Trees grown breadth first with at most widths[d] children per node at
+    depth d (distinct sibling tokens) until M nodes; target rows ~ N(0, 3^2)
+    with, for each node, probability p_hit that one of its children's tokens
+    is planted as the row's argmax (+12), so accepted paths run a few levels
+    deep."""
+    g = rng(seed, STREAM_TREE)
+    parent = np.full((R, M), -1, np.int32)
+    tokens = np.full((R, M), -1, np.int32)
+    nn = np.full(R, M, np.int32) if n_nodes is None else np.asarray(n_nodes, np.int32)
+    depth_max = 0
+    for r in range(R):
+        depth = [0]
+        n = 1
+        frontier = [0]
+        while frontier and n < nn[r]:
+            nxt = []
+            for u in frontier:
+                w = widths[depth[u]] if depth[u] < len(widths) else 0
+                ids = g.choice(V, size=w, replace=False) if w else []
+                for t in ids:
+                    if n >= nn[r]:
+                        break
+                    parent[r, n] = u
+                    tokens[r, n] = int(t)
+                    depth.append(depth[u] + 1)
+                    nxt.append(n)
+                    n += 1
+            frontier = nxt
+        nn[r] = n
+        depth_max = max(depth_max, max(depth))
+    z = (g.standard_normal((R, M, V), dtype=np.float32) * np.float32(3.0))
+    for r in range(R):
+        for u in range(nn[r]):
+            kids = [v for v in range(u + 1, nn[r]) if parent[r, v] == u]
+            if kids and g.random() < p_hit:
+                z[r, u, tokens[r, g.choice(kids)]] += np.float32(12.0)
+    logits = f32_to_bf16_bits(z) if dtype == "bf16" else z
+    return TreeCase(logits=logits, parent=parent, tokens=tokens, n_nodes=nn, R=R, M=M, V=V,
+                    max_depth=depth_max)
