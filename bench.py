@@ -23,7 +23,8 @@ Prints one JSON line:
 V = 129280, rank 256) instead, as an extra line; --workload schedule the
 confidence-scheduled verify lengths of the same batch size (448 candidates);
 --workload rnn the RNN serial head at the Markov workload's size; --workload
-sts the confidence head's sequential temperature scaling on a held-out set.
+sts the confidence head's sequential temperature scaling on a held-out set;
+--workload tree greedy verification of draft trees.
 """
 from __future__ import annotations
 
@@ -417,6 +418,70 @@ def bench_sts(args):
     return res
 
 
+def bench_tree(args):
+    """Greedy (T = 0) tree verification of 64 draft trees of 48 nodes (up to
+    3 / 2 / 2 / 1 children per node by depth) over V = 151936 bf16 rows: one
+    level launch per depth, each reading the current node's row of every
+    unfinished request.  The oracle is timed beside it."""
+    import torch
+    import lossless_verification_sampling_amd as sv
+    import workloads
+
+    dev = torch.device("cuda:0")
+    R, M, V = 64, 48, 151936
+    c = workloads.tree_case(seed=args.seed + 9, R=R, M=M, V=V, dtype="bf16",
+                            widths=(3, 2, 2, 1, 1, 1, 1, 1))
+    L = to_device(c.logits, dev)
+    P, X = to_device(c.parent, dev), to_device(c.tokens, dev)
+    n = to_device(c.n_nodes, dev)
+    ws = sv.Workspace(dev, sv.spec_tree_workspace_bytes(R, M, V))
+    for _ in range(args.warmup):
+        sv.spec_tree_verify(L, P, X, n, c.max_depth, workspace=ws)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        ev[k][0].record(stream)
+        acc, _, _ = sv.spec_tree_verify(L, P, X, n, c.max_depth, workspace=ws)
+        ev[k][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = np.array([a.elapsed_time(b) for a, b in ev])
+    a = acc.cpu().numpy()
+    committed = int((a + 1).sum())
+    per_call = committed * V * 2          # the rows the walk reads
+    res = {
+        "metric": "greedy tree verification: committed tokens/sec",
+        "value": committed / (wall / args.steps),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": wall / args.steps * 1e3,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16 logits, f32 compare", "data": "synthetic",
+        "config": {"workload": "tree", "R": R, "nodes": M, "V": V, "max_depth": c.max_depth,
+                   "accepted_mean": float(a.mean()), "levels": c.max_depth + 1},
+        "roofline": {"bound": "hbm", "achieved": per_call / (ms.mean() / 1e3) / 1e9,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": per_call / (ms.mean() / 1e3) / 1e9 / HBM_PEAK_GBS, "traffic": None,
+                     "algorithmic_bytes_per_call": per_call,
+                     "kernel": "spec_tree_verify call (tree_level_kernel per level)"},
+        "kernel_ms_mean": float(ms.mean()),
+    }
+    if not args.no_cpu_baseline:
+        from oracle import tree as otree
+        nrep, t1 = 0, time.perf_counter()
+        while time.perf_counter() - t1 < min(args.cpu_seconds, 5.0):
+            otree.tree_verify(c.logits, c.parent, c.tokens, c.n_nodes)
+            nrep += 1
+        el = time.perf_counter() - t1
+        res["cpu_baseline"] = {"value": committed * nrep / el, "unit": "tokens/s", "cores": 1,
+                               "kind": "oracle",
+                               "sample": f"{nrep} full calls (64 trees), numpy"}
+    return res
+
+
 def calibrate_copy(args):
     """One device-to-device copy of a known size, repeated: the reference that
     scales rocprofv3's FETCH_SIZE / WRITE_SIZE counters to bytes."""
@@ -507,7 +572,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--seed", type=int, default=3)
     ap.add_argument("--copies", type=int, default=0, help="input copies rotated (0 = auto)")
-    ap.add_argument("--workload", choices=["batched", "dspark", "rnn", "schedule", "sts"],
+    ap.add_argument("--workload", choices=["batched", "dspark", "rnn", "schedule", "sts", "tree"],
                     default="batched")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -532,7 +597,7 @@ def main():
         res = calibrate_copy(args)
     else:
         res = {"batched": bench_verify, "dspark": bench_dspark, "rnn": bench_rnn,
-               "schedule": bench_schedule, "sts": bench_sts}[args.workload](args)
+               "schedule": bench_schedule, "sts": bench_sts, "tree": bench_tree}[args.workload](args)
     print(json.dumps(res))
 
 

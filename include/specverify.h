@@ -90,6 +90,9 @@ typedef enum {
 #define SPEC_STS_MAX_GRID 1024
 #define SPEC_STS_MAX_BLOCKS (1 << 24)
 
+/* Largest tree (nodes per request) spec_tree_verify accepts. */
+#define SPEC_TREE_MAX_NODES 1024
+
 /* Library version, major * 10000 + minor * 100 + patch. */
 int spec_version(void);
 
@@ -295,6 +298,44 @@ int spec_sts_calibrate(const float *conf_logits, const int32_t *accepted_len, co
                        int N, int gamma, int G, int bins, double *out_temperature,
                        double *out_ece, double *out_curve, void *workspace,
                        size_t workspace_bytes, void *stream);
+
+/* Workspace bytes for spec_tree_verify (0 for sizes it does not accept). */
+size_t spec_tree_workspace_bytes(int R, int M, int V);
+
+/*
+ * Greedy (T = 0) verification of draft trees (speculative-decoding survey,
+ * sec. 2.3, tree drafting; DART reading note, sec. 2.3: at temperature zero
+ * the target argmax is followed along the candidate paths -- the pages give
+ * no rule for T > 0, and none is offered).
+ *
+ * Request r's tree has n_nodes[r] nodes in topological order: node 0 is the
+ * root (the last committed token), node v >= 1 has parent[r][v] in [0, v)
+ * and draft token tokens[r][v]; logits[r][v] is the target's next-token row
+ * after the path root .. v.  From the root, the walk moves to the child whose
+ * token equals the argmax of the current row (lowest id on ties; the
+ * lowest-index child among equal siblings) and stops at a node with no such
+ * child; that row's argmax is the bonus or correction token.  Only the rows
+ * on the accepted path are read, one launch per level (max_depth + 2).
+ *   logits       [R][M][V]  dtype (SPEC_F32 / SPEC_BF16)    (device)
+ *   parent       [R][M]     int32 (root and slots >= n_nodes ignored)
+ *   tokens       [R][M]     int32 in [0, V)
+ *   n_nodes      [R]        int32 in [1, M]
+ *   max_depth    a bound on every tree's depth, 0 <= max_depth < M (a deeper
+ *                tree is rejected as malformed)
+ *   out_accepted [R]        int32 accepted draft nodes A_r
+ *   out_path     [R][M]     int32 the accepted nodes in order, -1 padded
+ *   out_tokens   [R][M]     int32 the A_r path tokens, then the bonus, -1 padded
+ * Sizes: R >= 0, 1 <= M <= SPEC_TREE_MAX_NODES, 1 <= V <= SPEC_MAX_VERIFY_VOCAB.
+ * A malformed tree (a parent outside [0, v), a token outside [0, V), n_nodes
+ * outside [1, M], depth beyond max_depth) or a row on the walk holding a NaN
+ * or +-inf logit sets SPEC_DEV_BAD_REQUEST and gives that request
+ * out_accepted -1 and all-(-1) paths and tokens.  The inputs, outputs and
+ * workspace belong to the caller; work is enqueued on `stream`.
+ */
+int spec_tree_verify(const void *logits, int dtype, const int32_t *parent, const int32_t *tokens,
+                     const int32_t *n_nodes, int R, int M, int V, int max_depth,
+                     int32_t *out_accepted, int32_t *out_path, int32_t *out_tokens,
+                     void *workspace, size_t workspace_bytes, void *stream);
 
 /* Synchronises `stream`, copies the workspace's device status word (the OR
  * of SPEC_DEV_* bits raised since the last clear) to *host_bits, and clears

@@ -33,6 +33,7 @@ SPEC_RNN_MAX_HIDDEN = 3072
 SPEC_STS_MAX_BINS = 24
 SPEC_STS_MAX_GRID = 1024
 SPEC_STS_MAX_BLOCKS = 1 << 24
+SPEC_TREE_MAX_NODES = 1024
 
 EXPORTED = (
     "spec_version",
@@ -49,6 +50,8 @@ EXPORTED = (
     "spec_schedule_verify_len",
     "spec_sts_workspace_bytes",
     "spec_sts_calibrate",
+    "spec_tree_workspace_bytes",
+    "spec_tree_verify",
     "spec_markov_draft_sample",
     "spec_get_device_status",
 )
@@ -97,6 +100,10 @@ def _load() -> ctypes.CDLL:
     lib.spec_sts_workspace_bytes.argtypes = [i, i, i, i]
     lib.spec_sts_calibrate.restype = i
     lib.spec_sts_calibrate.argtypes = [p, p, p, i, i, i, i, p, p, p, p, sz, p]
+    lib.spec_tree_workspace_bytes.restype = sz
+    lib.spec_tree_workspace_bytes.argtypes = [i, i, i]
+    lib.spec_tree_verify.restype = i
+    lib.spec_tree_verify.argtypes = [p, i, p, p, p, i, i, i, i, p, p, p, p, sz, p]
     lib.spec_get_device_status.restype = i
     lib.spec_get_device_status.argtypes = [p, ctypes.POINTER(ctypes.c_uint32), i, p]
     return lib
@@ -139,6 +146,10 @@ def spec_schedule_workspace_bytes() -> int:
 
 def spec_sts_workspace_bytes(N: int, gamma: int, G: int, bins: int) -> int:
     return int(_lib.spec_sts_workspace_bytes(N, gamma, G, bins))
+
+
+def spec_tree_workspace_bytes(R: int, M: int, V: int) -> int:
+    return int(_lib.spec_tree_workspace_bytes(R, M, V))
 
 
 # ---------------------------------------------------------------------------
@@ -380,6 +391,35 @@ def spec_sts_calibrate(conf_logits: torch.Tensor, accepted_len: torch.Tensor, gr
                                  buf.numel(), _stream_ptr(stream, dev))
     _raise(st, "spec_sts_calibrate")
     return temps, ece, curve
+
+
+def spec_tree_verify(logits: torch.Tensor, parent: torch.Tensor, tokens: torch.Tensor,
+                     n_nodes: torch.Tensor, max_depth: int, *,
+                     workspace: Optional[Workspace] = None, stream=None):
+    """Greedy (T = 0) tree verification.  logits [R, M, V] float32 or
+    bfloat16 (row v: the target's next-token logits after the path to node v),
+    parent / tokens [R, M] int32, n_nodes [R] int32, max_depth a bound on every
+    tree's depth (deeper trees are rejected).  Returns (accepted [R], path [R, M], committed tokens [R, M])
+    as int32."""
+    R, M, V = logits.shape
+    dev = logits.device
+    _check(logits, "logits", logits.dtype, (R, M, V), dev)
+    for t, nm in ((parent, "parent"), (tokens, "tokens")):
+        _check(t, nm, torch.int32, (R, M), dev)
+    _check(n_nodes, "n_nodes", torch.int32, (R,), dev)
+    acc = torch.empty((R,), dtype=torch.int32, device=dev)
+    path = torch.empty((R, M), dtype=torch.int32, device=dev)
+    tok = torch.empty((R, M), dtype=torch.int32, device=dev)
+    need = spec_tree_workspace_bytes(max(R, 1), M, V)
+    if need == 0:
+        raise ValueError(f"spec_tree_verify: unsupported sizes M={M} V={V}")
+    ws = workspace or default_workspace(dev)
+    buf = ws.ensure(need, stream)
+    st = _lib.spec_tree_verify(_ptr(logits), _dtype(logits), _ptr(parent), _ptr(tokens),
+                               _ptr(n_nodes), R, M, V, int(max_depth), _ptr(acc), _ptr(path),
+                               _ptr(tok), _ptr(buf), buf.numel(), _stream_ptr(stream, dev))
+    _raise(st, "spec_tree_verify")
+    return acc, path, tok
 
 
 def spec_rnn_draft_sample(U: torch.Tensor, W1: torch.Tensor, W2: torch.Tensor,

@@ -239,6 +239,45 @@ def test_sts_argument_validation(lib):
     assert sc(wsb=need - 1) == SPEC_EWORKSPACE
 
 
+def test_tree_argument_validation(lib):
+    p = ctypes.c_void_p
+    fake = p(0x1000)
+    i = ctypes.c_int
+    w = lib.spec_tree_workspace_bytes
+    w.restype = ctypes.c_size_t
+    w.argtypes = [i, i, i]
+    f = lib.spec_tree_verify
+    f.restype = i
+    f.argtypes = [p, i, p, p, p, i, i, i, i, p, p, p, p, ctypes.c_size_t, p]
+    need = w(64, 32, 151936)
+    # status word, then per request and level: node, argmax word, fault flag
+    assert need >= 256 + 64 * 32 * (4 + 8 + 4)
+    assert w(64, 1025, 1000) == 0 and w(64, 32, 262145) == 0 and w(0, 32, 1000) == 0
+
+    def tv(**kw):
+        a = dict(L=fake, dt=1, P=fake, X=fake, n=fake, R=64, M=32, V=151936, D=6, acc=fake,
+                 path=fake, tok=fake, ws=p(0x10000), wsb=need)
+        a.update(kw)
+        return f(a["L"], a["dt"], a["P"], a["X"], a["n"], a["R"], a["M"], a["V"], a["D"],
+                 a["acc"], a["path"], a["tok"], a["ws"], a["wsb"], None)
+
+    assert tv(R=-1) == SPEC_EINVAL
+    assert tv(M=0) == SPEC_EINVAL
+    assert tv(V=0) == SPEC_EINVAL
+    assert tv(D=-1) == SPEC_EINVAL
+    assert tv(dt=7) == SPEC_EDTYPE
+    assert tv(M=1025) == SPEC_EUNSUPPORTED
+    assert tv(V=262145) == SPEC_EUNSUPPORTED
+    assert tv(D=32) == SPEC_EUNSUPPORTED          # a depth of M is impossible
+    assert tv(R=0) == SPEC_OK
+    for k in ("L", "P", "X", "n", "acc", "path", "tok"):
+        assert tv(**{k: None}) == SPEC_EINVAL, k
+    assert tv(ws=None) == SPEC_EWORKSPACE
+    assert tv(ws=p(0x10010)) == SPEC_EWORKSPACE
+    # max_depth 6 needs 7 levels: 256 + 64 * 7 * 16 + 256 bytes
+    assert tv(wsb=256 + 64 * 7 * 16 + 255) == SPEC_EWORKSPACE
+
+
 def test_workspace_init_validation(lib):
     f = lib.spec_workspace_init
     f.restype = ctypes.c_int

@@ -443,8 +443,8 @@ def tree_case(seed: int = 12, R: int = 64, M: int = 32, V: int = 151936, dtype: 
     """Trees grown breadth first with at most widths[d] children per node at
     depth d (distinct sibling tokens) until M nodes; target rows ~ N(0, 3^2)
     with, for each node, probability p_hit that one of its children's tokens
-    is planted as the row's argmax (+12), so accepted paths run a few levels
-    deep."""
+    is planted as the row's argmax (+24, eight standard deviations: above the
+    largest of 151936 draws), so accepted paths run a few levels deep."""
     g = rng(seed, STREAM_TREE)
     parent = np.full((R, M), -1, np.int32)
     tokens = np.full((R, M), -1, np.int32)
@@ -475,7 +475,7 @@ def tree_case(seed: int = 12, R: int = 64, M: int = 32, V: int = 151936, dtype: 
         for u in range(nn[r]):
             kids = [v for v in range(u + 1, nn[r]) if parent[r, v] == u]
             if kids and g.random() < p_hit:
-                z[r, u, tokens[r, g.choice(kids)]] += np.float32(12.0)
+                z[r, u, tokens[r, g.choice(kids)]] += np.float32(24.0)
     logits = f32_to_bf16_bits(z) if dtype == "bf16" else z
     return TreeCase(logits=logits, parent=parent, tokens=tokens, n_nodes=nn, R=R, M=M, V=V,
                     max_depth=depth_max)
