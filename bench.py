@@ -47,13 +47,21 @@ MALL_BYTES = 256 << 20
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
-def source_hash() -> str:
-    """Hash of the kernel library's code with comments and blank space removed,
-    so that counter figures stay tied to the code they were measured on."""
+# The sources each counter entry's kernels are built from.
+TRAFFIC_SOURCES = {
+    "verify_batched": ("common.h", "verify.hip"),
+    "markov_dspark": ("common.h", "markov.hip"),
+}
+
+
+def source_hash(key: str) -> str:
+    """Hash of the code of entry `key`'s kernel sources with comments and blank
+    space removed, so that counter figures stay tied to the code they were
+    measured on."""
     import re
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "lossless_verification_sampling_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    for f in TRAFFIC_SOURCES[key]:
         with open(os.path.join(csrc, f), encoding="utf-8") as fh:
             code = fh.read()
         code = re.sub(r"/\*.*?\*/", " ", code, flags=re.S)
@@ -72,7 +80,7 @@ def measured_traffic(kernel_key: str):
     except (OSError, ValueError):
         return None
     e = t.get(kernel_key)
-    if not e or e.get("source_hash") != source_hash():
+    if not e or e.get("source_hash") != source_hash(kernel_key):
         return None
     return e.get("bytes_per_launch")
 
@@ -551,7 +559,7 @@ def write_traffic(args):
     except (OSError, ValueError):
         t = {}
     t[args.key] = {
-        "source_hash": source_hash(),
+        "source_hash": source_hash(args.key),
         "bytes_per_launch": sum(fk.values()) + sum(wk.values()),
         "fetch_bytes": sum(fk.values()), "write_bytes": sum(wk.values()),
         "fetch_scale": fs, "write_scale": ws,
