@@ -358,10 +358,10 @@ def bench_schedule(args):
 
 
 # fp64 VALU instructions the histogram loop issues per (block, temperature)
-# score (the sigmoid's exp polynomial and two divides, the bin index, the
-# running product), counted in the kernel's gfx950 assembly; the peak is
-# 256 CUs x 64 fp64 lanes per clock x 2.4 GHz.
-STS_OPS_PER_SCORE = 50
+# score (the sigmoid's exp polynomial, a reciprocal with two Newton steps, the
+# bin index, the running product), counted in the kernel's gfx950 assembly;
+# the peak is 256 CUs x 64 fp64 lanes per clock x 2.4 GHz.
+STS_OPS_PER_SCORE = 35
 STS_PEAK_TOPS = 256 * 64 * 2.4e9 / 1e12
 
 
