@@ -57,6 +57,16 @@ def test_tree_matches_oracle(sv, dev, R, M, V, dtype):
     assert ref["accepted"].max() >= 1
 
 
+def test_tree_benchmark_workload(sv, dev):
+    # the benchmark's trees: 64 of 48 nodes, widths 3 / 2 / 2 / 1, V = 151936 bf16
+    print("[tree] R=64 M=48 V=151936 bf16 (benchmark)", flush=True)
+    c = workloads.tree_case(seed=12, R=64, M=48, V=151936, dtype="bf16",
+                            widths=(3, 2, 2, 1, 1, 1, 1, 1))
+    ref = otree.tree_verify(c.logits, c.parent, c.tokens, c.n_nodes)
+    check(run(sv, dev, c.logits, c.parent, c.tokens, c.n_nodes, c.max_depth), ref)
+    assert ref["accepted"].max() >= 4
+
+
 def test_chain_deep_and_single_node_trees(sv, dev):
     V, M = 5000, 40
     c = workloads.tree_case(seed=2, R=4, M=M, V=V, dtype="bf16", widths=(1,) * 39, p_hit=0.95)
