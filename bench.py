@@ -230,7 +230,7 @@ def bench_dspark(args):
     ms = np.array([a.elapsed_time(b) for a, b in ev])
     flops = 2.0 * R * rank * V * gamma
     per_step_bytes = (R * V * 2 + rank * V * 2 + R * V * 4) * gamma
-    return {
+    res = {
         "metric": "Markov-head draft: drafted tokens/sec",
         "value": R * gamma / (wall / args.steps),
         "unit": "tokens/s",
@@ -246,6 +246,18 @@ def bench_dspark(args):
                      "algorithmic_bytes_per_call": per_step_bytes,
                      "mfma_tflops": flops / (ms.mean() / 1e3) / 1e12},
     }
+    if not args.no_cpu_baseline:
+        import oracle
+        n_cpu = 4
+        t1 = time.perf_counter()
+        oracle.markov_draft(mk.U[:n_cpu], mk.W1, mk.W2, mk.anchor[:n_cpu],
+                            mk.temperature[:n_cpu], mk.u_draft[:n_cpu])
+        el = time.perf_counter() - t1
+        res["cpu_baseline"] = {"value": n_cpu * gamma / el, "unit": "tokens/s", "cores": 1,
+                               "kind": "oracle",
+                               "sample": f"the first {n_cpu} of the {R} requests, all {gamma} "
+                                         "steps, the C oracle (fp64)"}
+    return res
 
 
 def bench_rnn(args):
@@ -281,7 +293,7 @@ def bench_rnn(args):
     din = 2 * rank + hidden
     per_call = (R * V * 2 + rank * V * 2 + R * V * 4 + din * 2 * rank * 2 + R * hidden * 4) * gamma
     flops = (3 * 2.0 * R * rank * V + 2.0 * R * din * 2 * rank) * gamma
-    return {
+    res = {
         "metric": "RNN-head draft: drafted tokens/sec",
         "value": R * gamma / (wall / args.steps),
         "unit": "tokens/s",
@@ -297,6 +309,18 @@ def bench_rnn(args):
                      "traffic": None, "algorithmic_bytes_per_call": per_call,
                      "mfma_tflops": flops / (ms.mean() / 1e3) / 1e12},
     }
+    if not args.no_cpu_baseline:
+        from oracle import rnn as ornn
+        n_cpu = 4
+        t1 = time.perf_counter()
+        ornn.rnn_draft(mk.U[:n_cpu], mk.W1, mk.W2, c.H[:n_cpu], c.Wg, c.bg, mk.anchor[:n_cpu],
+                       mk.temperature[:n_cpu], mk.u_draft[:n_cpu])
+        el = time.perf_counter() - t1
+        res["cpu_baseline"] = {"value": n_cpu * gamma / el, "unit": "tokens/s", "cores": 1,
+                               "kind": "oracle",
+                               "sample": f"the first {n_cpu} of the {R} requests, all {gamma} "
+                                         "steps, numpy fp64"}
+    return res
 
 
 def bench_schedule(args):
