@@ -46,6 +46,12 @@
  *    The library keeps it consistent afterwards.  Calls that share a
  *    workspace must be ordered (same stream, or synchronised); calls with
  *    distinct workspaces may run concurrently.
+ *  - Graph capture: spec_verify_batch and spec_tv_accept_rate return
+ *    SPEC_EUNSUPPORTED on a stream that is capturing (their cross-workgroup
+ *    words carry a tag drawn on the host at each call, which a replayed graph
+ *    would repeat).  The Markov and RNN drafts, the scheduler, STS and tree
+ *    verification clear their device state with kernels (no memset nodes)
+ *    and may be captured and replayed.
  */
 #ifndef SPECVERIFY_H
 #define SPECVERIFY_H

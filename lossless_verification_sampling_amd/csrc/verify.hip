@@ -1483,6 +1483,15 @@ size_t plan_bytes(long R, long upr, long V) {
 }
 
 bool dtype_ok(int d) { return d == SPEC_F32 || d == SPEC_BF16; }
+
+// The launch tag is drawn on the host at each call; a captured graph would
+// replay one tag, and a wave waiting for a word written in the same launch
+// could then take the previous replay's word for the current one.
+bool capturing(void *stream) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    return hipStreamIsCapturing((hipStream_t)stream, &cs) == hipSuccess &&
+           cs != hipStreamCaptureStatusNone;
+}
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
 // Resident workgroups of a kernel with `lds` bytes of dynamic shared memory on
@@ -1688,6 +1697,7 @@ int spec_verify_batch(const void *target_logits, int t_dtype, const void *draft_
         !out_num_accepted)
         return SPEC_EINVAL;
     if (gamma > 0 && (!draft_logits || !draft_tokens || !u_accept)) return SPEC_EINVAL;
+    if (capturing(stream)) return SPEC_EUNSUPPORTED;
     Plan p;
     if (!make_plan(R, gamma + 1, V, p)) return SPEC_EUNSUPPORTED;
     if (!workspace || ((uintptr_t)workspace & 255u) || workspace_bytes < p.bytes)
@@ -1730,6 +1740,7 @@ int spec_tv_accept_rate(const void *draft_logits, const void *target_logits, int
     if (V > SPEC_MAX_VERIFY_VOCAB) return SPEC_EUNSUPPORTED;
     if (N == 0) return SPEC_OK;
     if (!draft_logits || !target_logits || !temperature || !out_cstar) return SPEC_EINVAL;
+    if (capturing(stream)) return SPEC_EUNSUPPORTED;
     Plan p;
     if (!make_plan(N, 1, V, p)) return SPEC_EUNSUPPORTED;
     if (!workspace || ((uintptr_t)workspace & 255u) || workspace_bytes < p.bytes)
