@@ -46,12 +46,10 @@
  *    The library keeps it consistent afterwards.  Calls that share a
  *    workspace must be ordered (same stream, or synchronised); calls with
  *    distinct workspaces may run concurrently.
- *  - Graph capture: spec_verify_batch and spec_tv_accept_rate return
- *    SPEC_EUNSUPPORTED on a stream that is capturing (their cross-workgroup
- *    words carry a tag drawn on the host at each call, which a replayed graph
- *    would repeat).  The Markov and RNN drafts, the scheduler, STS and tree
- *    verification clear their device state with kernels (no memset nodes)
- *    and may be captured and replayed.
+ *  - Graph capture: every compute entry point may be captured into a HIP
+ *    graph and replayed (device state is cleared with kernels, not memset
+ *    nodes, and the verification calls draw their launch tag on the device).
+ *    A workspace's status word is cleared only by spec_get_device_status.
  */
 #ifndef SPECVERIFY_H
 #define SPECVERIFY_H

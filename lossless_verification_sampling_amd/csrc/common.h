@@ -18,9 +18,10 @@ constexpr double kLn2 = 0.6931471805599453;
 
 // Workspace control block (offset 0, 256 bytes).
 struct Control {
-    uint32_t reserved;
+    uint32_t tag_next;   // the next verification call's launch tag (0 after init)
     uint32_t status;     // SPEC_DEV_* bits
-    uint32_t pad[62];
+    uint32_t tag_call;   // the running verification call's launch tag
+    uint32_t pad[61];
 };
 static_assert(sizeof(Control) == 256, "control block size");
 

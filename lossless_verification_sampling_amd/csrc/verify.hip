@@ -39,7 +39,11 @@
 // and writes the outputs, and returns the counter to zero.
 // Words passed between waves are 64-bit (launch tag, payload) pairs written
 // and read with agent-scope atomics, so a reader never mistakes a stale word
-// (an earlier call's) for a current one.  A wave only ever waits for words
+// (an earlier call's) for a current one.  The tag is kept on the device, so
+// that a captured graph gets a new one at every replay: launch 1 reads the
+// workspace's next tag and copies it to the call's slot, launches 2-4 read
+// that slot, and launch 4 stores the tag after it as the next (nothing of
+// the call reads the next-tag slot after launch 1).  A wave only ever waits for words
 // whose stores were issued before it read them as needed -- by an earlier
 // launch, or by the waves whose counter arrivals made it the request's last
 // -- so no wait depends on another wave being scheduled; every wait is still
@@ -81,7 +85,7 @@ struct VerifyArgs {
     int UG;                  // units per request (gamma + 1, or 1 for row pairs)
     int tG, dG;              // rows per request in the target / draft tensors
     int tv_mode;             // 1: independent row pairs, c* and Res only
-    uint32_t tag;            // this launch's tag (nonzero, top bit set)
+    uint32_t tag;            // the call's tag (nonzero, top bit set), read on the device
     int compact;             // streaming kernels walk a unit table in LDS (else all candidates)
     int32_t *out_tok;
     int32_t *out_n;
@@ -169,6 +173,20 @@ __device__ __forceinline__ void publish_n(uint64_t *p, uint32_t tag, int n, uint
         const uint32_t w = lane == 0 ? w0 : lane == 1 ? w1 : lane == 2 ? w2 : w3;
         st_word(p + lane, tag, w);
     }
+}
+
+// The call's tag: launch 1 takes the workspace's next tag (0 after
+// initialisation) and records it for the later launches.  Both slots are
+// written by one thread of one workgroup and read with plain loads in later
+// launches (a kernel boundary orders them): stores from every workgroup to
+// one address would hold up each wave's first loads.
+__device__ __forceinline__ uint32_t first_launch_tag(Control *ctl) {
+    const uint32_t t = __builtin_amdgcn_readfirstlane(ctl->tag_next) | 0x80000000u;
+    if (blockIdx.x == 0 && threadIdx.x == 0) ctl->tag_call = t;
+    return t;
+}
+__device__ __forceinline__ uint32_t call_tag(const Control *ctl) {
+    return __builtin_amdgcn_readfirstlane(ctl->tag_call);
 }
 
 __device__ __forceinline__ uint32_t rl(uint32_t v, int l) {
@@ -1276,6 +1294,7 @@ __device__ __forceinline__ bool unit_item(const VerifyArgs &a, long u, Item &x) 
 // get their outputs here.
 template <typename TT, typename TD, int N, int EPV>
 __global__ void __launch_bounds__(kBlock, kStreamWaves) stats_kernel(VerifyArgs a) {
+    a.tag = first_launch_tag(a.ctl);
     if (!a.compact) {
         for (long r = wave_index(); r < a.R; r += wave_count()) {
             float T;
@@ -1298,6 +1317,7 @@ __global__ void __launch_bounds__(kBlock, kStreamWaves) stats_kernel(VerifyArgs 
 // the row normalisers (at T = 0: the argmax test, which settles the unit).
 template <typename TT, typename TD, int N, int EPV>
 __global__ void __launch_bounds__(kBlock) norm_kernel(VerifyArgs a) {
+    a.tag = call_tag(a.ctl);
     Item x;
     if (unit_item(a, wave_index(), x)) stats_combine<TT, TD, N, EPV>(a, x);
 }
@@ -1364,6 +1384,7 @@ __device__ __forceinline__ uint64_t load_tv_item(const VerifyArgs &a, const Item
 // wave.
 template <typename TT, typename TD, int N, int EPV>
 __global__ void __launch_bounds__(kBlock, kStreamWaves) tv_kernel(VerifyArgs a) {
+    a.tag = call_tag(a.ctl);
     const int lane = lane_id();
     extern __shared__ uint32_t lds[];
     Walker cur = make_walker(a, lds, true);
@@ -1390,6 +1411,8 @@ __global__ void __launch_bounds__(kBlock, kStreamWaves) tv_kernel(VerifyArgs a) 
 // writes the request's outputs.
 template <typename TT, typename TD, int N, int EPV>
 __global__ void __launch_bounds__(kBlock) tv_combine_kernel(VerifyArgs a) {
+    a.tag = call_tag(a.ctl);
+    if (blockIdx.x == 0 && threadIdx.x == 0) a.ctl->tag_next = (a.tag + 1u) | 0x80000000u;
     Item x;
     if (!unit_item(a, wave_index(), x) || x.T == 0.0f) return;
     if (is_pair(x))
@@ -1484,14 +1507,6 @@ size_t plan_bytes(long R, long upr, long V) {
 
 bool dtype_ok(int d) { return d == SPEC_F32 || d == SPEC_BF16; }
 
-// The launch tag is drawn on the host at each call; a captured graph would
-// replay one tag, and a wave waiting for a word written in the same launch
-// could then take the previous replay's word for the current one.
-bool capturing(void *stream) {
-    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-    return hipStreamIsCapturing((hipStream_t)stream, &cs) == hipSuccess &&
-           cs != hipStreamCaptureStatusNone;
-}
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
 // Resident workgroups of a kernel with `lds` bytes of dynamic shared memory on
@@ -1514,10 +1529,6 @@ long resident_blocks(const void *kernel, size_t lds) {
     return cap;
 }
 
-uint32_t next_tag() {
-    static std::atomic<uint32_t> counter{0};
-    return (counter.fetch_add(1u) + 1u) | 0x80000000u;
-}
 
 // Compute units of the current device (cached per device; 0 if unknown).
 long device_cus() {
@@ -1565,7 +1576,7 @@ int launch_kernels(VerifyArgs a, hipStream_t st) {
     const long units = (long)a.R * a.UG;
     const long g1 = persistent_grid(k1, lds, items), g3 = persistent_grid(k3, lds, items);
     const long gu = (units + kWaves - 1) / kWaves;
-    a.tag = next_tag();  // one tag for every launch of the call
+    a.tag = 0;  // read on the device by every launch
     static bool said = false;
     if (!said && getenv("SPECVERIFY_VERBOSE")) {
         said = true;
@@ -1697,7 +1708,6 @@ int spec_verify_batch(const void *target_logits, int t_dtype, const void *draft_
         !out_num_accepted)
         return SPEC_EINVAL;
     if (gamma > 0 && (!draft_logits || !draft_tokens || !u_accept)) return SPEC_EINVAL;
-    if (capturing(stream)) return SPEC_EUNSUPPORTED;
     Plan p;
     if (!make_plan(R, gamma + 1, V, p)) return SPEC_EUNSUPPORTED;
     if (!workspace || ((uintptr_t)workspace & 255u) || workspace_bytes < p.bytes)
@@ -1740,7 +1750,6 @@ int spec_tv_accept_rate(const void *draft_logits, const void *target_logits, int
     if (V > SPEC_MAX_VERIFY_VOCAB) return SPEC_EUNSUPPORTED;
     if (N == 0) return SPEC_OK;
     if (!draft_logits || !target_logits || !temperature || !out_cstar) return SPEC_EINVAL;
-    if (capturing(stream)) return SPEC_EUNSUPPORTED;
     Plan p;
     if (!make_plan(N, 1, V, p)) return SPEC_EUNSUPPORTED;
     if (!workspace || ((uintptr_t)workspace & 255u) || workspace_bytes < p.bytes)
