@@ -34,7 +34,6 @@ constexpr int kMkRank = 256;        // rank of W1 W2 (the pages' default r)
 constexpr int kMkTile = 64;         // logits per tile (one workgroup each)
 constexpr int kMkRows = 64;         // requests per MFMA row block (4 waves x 16)
 constexpr int kMkLdsStride = kMkRank + 8;  // bf16 per LDS row (padding vs bank conflicts)
-constexpr int kMkBatch = 16;        // tile statistics loaded together per lane
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
