@@ -17,37 +17,39 @@
 // Design.  A "unit" is one position of one request: the (target, draft) row
 // pair of position i < l_r, or the bonus target row i = l_r.  Each unit's rows
 // are cut into C chunks of 64 N logits, and an "item" is one chunk of one
-// unit.  The four launches, in stream order:
+// unit.  The three launches, in stream order:
 //  1. stats_kernel: persistent wave64s stream every needed row exactly once
 //     from HBM with 16-byte loads, the items balanced over the waves through a
 //     per-block unit table in LDS.  Per item it writes the chunk's scaled max
 //     mu and weight sum S = sum 2^(z s - mu) per row (s = log2(e) / T), or the
 //     chunk argmax at T = 0.  Malformed requests get their outputs here.
-//  2. norm_kernel: one wave per unit folds the C chunk words into the row
-//     normalisers (M = max mu, Z = sum S 2^(mu - M)); at T = 0 it runs the
-//     argmax test and settles the unit completely.
-//  3. tv_kernel: the pair items at T > 0 again -- launch 1 has just streamed
-//     them, so they come from the 256 MB Infinity Cache when they fit -- with
-//     each chunk's weights rebuilt exactly as launch 1 made them; per item the
-//     chunk's sum min(p, q) and residual mass.
-//  4. tv_combine_kernel: one wave per unit at T > 0.  A position runs its
+//  2. tv_kernel: first, wave w folds units w, w + W, ... at T > 0 into their
+//     row normalisers (M = max mu, Z = sum S 2^(mu - M)); then the pair items
+//     at T > 0 again -- launch 1 has just streamed them, so they come from
+//     the 256 MB Infinity Cache when they fit -- with each chunk's weights
+//     rebuilt exactly as launch 1 made them; per item the chunk's
+//     sum min(p, q) and residual mass.  An item whose unit is still being
+//     folded waits for its normalisers.
+//  3. tv_combine_kernel: one wave per unit.  At T > 0 a position runs its
 //     accept test on the two gathered logits, sums c* and Res and, if
 //     rejected, makes the residual draw; the bonus unit makes the
-//     inverse-CDF draw from q.
-// Each unit's last step (launch 2 or 4) arrives on its request's counter; the
-// wave completing a request applies prefix survival to the units' accept bits
-// and writes the outputs, and returns the counter to zero.
+//     inverse-CDF draw from q.  At T = 0 the unit's argmax test settles it.
+// Each unit's last step arrives on its request's counter; the wave completing
+// a request applies prefix survival to the units' accept bits and writes the
+// outputs, and returns the counter to zero.
 // Words passed between waves are 64-bit (launch tag, payload) pairs written
 // and read with agent-scope atomics, so a reader never mistakes a stale word
 // (an earlier call's) for a current one.  The tag is kept on the device, so
 // that a captured graph gets a new one at every replay: launch 1 reads the
-// workspace's next tag and copies it to the call's slot, launches 2-4 read
-// that slot, and launch 4 stores the tag after it as the next (nothing of
-// the call reads the next-tag slot after launch 1).  A wave only ever waits for words
-// whose stores were issued before it read them as needed -- by an earlier
-// launch, or by the waves whose counter arrivals made it the request's last
-// -- so no wait depends on another wave being scheduled; every wait is still
-// bounded and raises SPEC_DEV_SPIN_TIMEOUT rather than spin forever.
+// workspace's next tag and copies it to the call's slot, launches 2 and 3
+// read that slot, and launch 3 stores the tag after it as the next (nothing
+// of the call reads the next-tag slot after launch 1).  A wave only waits for
+// words whose writers cannot be waiting on it: the statistics words of an
+// earlier launch, the normalisers of launch 2's folds (which read only launch
+// 1's words and run before their waves take any item, on a grid that never
+// exceeds the kernel's resident capacity), and the records of the waves
+// whose counter arrivals made it the request's last.  Every wait is bounded
+// and raises SPEC_DEV_SPIN_TIMEOUT rather than spin forever.
 #include <math.h>
 #include <stddef.h>
 #include <stdio.h>
@@ -66,8 +68,8 @@ constexpr int kLanes = 64;
 // waves per SIMD the streaming kernels are compiled for (their registers fit)
 constexpr int kStreamWaves = 5;
 
-// Per-unit record words (tagged), filled by the unit's combines (launches 2
-// and 4) and read by the request's finaliser.
+// Per-unit record words (tagged), filled by the unit's combines and read by
+// the request's finaliser.
 enum : int { kRecFlags = 0, kRecLqx = 1, kRecDraw = 2, kRecLqd = 3, kRecCs = 4, kRecRs = 5,
              kRecWords = 8 };
 constexpr uint32_t kFlagValid = 1u, kFlagAccept = 2u;
@@ -709,26 +711,27 @@ __device__ __forceinline__ void words_settle(const uint64_t *const (&p)[K], cons
     for (int k = 0; k < K; ++k) out[k] = (uint32_t)v[k];
 }
 
-// Chunk words of a unit, for the lane's chunks c = 64 b + lane (b < kCB):
-// w[b][q] = word q of chunk c (q < Q), 0 where c >= C or !want[q].
-template <int Q>
+// Chunk words of a unit, for the lane's chunks c = 64 (b0 + b) + lane
+// (b < NB): w[b][q] = word q of chunk c (q < Q), 0 where c >= C or !want[q].
+template <int Q, int NB = kCB>
 __device__ __forceinline__ void load_unit_words(const uint64_t *base, int C, const bool (&want)[Q],
                                                 uint32_t tag, Control *ctl,
-                                                uint32_t (&w)[kCB][Q], bool cached = false) {
-    const uint64_t *p[kCB * Q];
-    bool act[kCB * Q];
-    uint32_t o[kCB * Q];
+                                                uint32_t (&w)[NB][Q], bool cached = false,
+                                                int b0 = 0) {
+    const uint64_t *p[NB * Q];
+    bool act[NB * Q];
+    uint32_t o[NB * Q];
 #pragma unroll
-    for (int b = 0; b < kCB; ++b)
+    for (int b = 0; b < NB; ++b)
 #pragma unroll
         for (int q = 0; q < Q; ++q) {
-            const int c = b * 64 + lane_id();
+            const int c = (b0 + b) * 64 + lane_id();
             p[b * Q + q] = base + (size_t)c * Q + q;
             act[b * Q + q] = c < C && want[q];
         }
-    await_batch<kCB * Q>(p, act, tag, ctl, o, cached);
+    await_batch<NB * Q>(p, act, tag, ctl, o, cached);
 #pragma unroll
-    for (int b = 0; b < kCB; ++b)
+    for (int b = 0; b < NB; ++b)
 #pragma unroll
         for (int q = 0; q < Q; ++q) w[b][q] = o[b * Q + q];
 }
@@ -952,94 +955,99 @@ __device__ __forceinline__ void unit_done(const VerifyArgs &a, const Item &x) {
 }
 
 // ---------------------------------------------------------------------------
-// unit combines (one wave per unit, in launches 2 and 4)
+// unit combines (one wave per unit)
 // ---------------------------------------------------------------------------
 
-// All C chunk statistics of unit x are published: the row normalisers (for
-// the TV items and the last combine), or at T = 0 the unit's argmax test.
-template <typename TT, typename TD, int N, int EPV>
-__device__ __forceinline__ void stats_combine(const VerifyArgs &a, const Item &x) {
+// The lane's chunk words of unit x (c = 64 b + lane), in rounds of two
+// blocks in increasing chunk order, each handed to fold(w, h) for block
+// b0 + h.  They come from the statistics pass (an earlier launch).
+template <typename F>
+__device__ __forceinline__ void fold_unit_words(const VerifyArgs &a, const Item &x, bool pair,
+                                                F fold) {
     const int lane = lane_id();
-    const int C = a.C, G = a.gamma;
+    const bool want[4] = {true, true, pair, pair};
+    for (int b0 = 0; b0 < kCB && b0 * 64 < a.C; b0 += 2) {
+        uint32_t w[2][4];
+        load_unit_words<4, 2>(a.st1 + (size_t)x.u * a.C * 4, a.C, want, a.tag, a.ctl, w, true,
+                              b0);
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+            if ((b0 + h) * 64 + lane < a.C) fold(w[h]);
+    }
+}
+
+// T = 0: the unit's argmax test settles it (the position's accept bit and
+// c* = [argmax q == argmax p]; the bonus unit's token).
+template <typename TT, typename TD, int N, int EPV>
+__device__ __forceinline__ void greedy_combine(const VerifyArgs &a, const Item &x) {
+    const int lane = lane_id();
+    const int G = a.gamma;
     const bool pair = is_pair(x);
-    uint64_t *nrm = a.nrm + (size_t)x.u * 4;
     uint64_t *rec = a.rec + (size_t)x.u * kRecWords;
     const float nan = __builtin_nanf("");
-    // the position's draft token (greedy accept test), loaded early
+    // the position's draft token, loaded early
     int xtok = 0;
-    if (!a.tv_mode && pair && x.T == 0.0f) xtok = a.tokens[(size_t)x.r * G + x.i];
-    uint32_t w[kCB][4];
-    const bool want[4] = {true, true, pair, pair};
-    load_unit_words<4>(a.st1 + (size_t)x.u * C * 4, C, want, a.tag, a.ctl, w, true);
-
-    if (x.T == 0.0f) {
-        float vt = -kInf, vd = -kInf;
-        int it = 0x7fffffff, id = 0x7fffffff, bad = 0;
-#pragma unroll
-        for (int b = 0; b < kCB; ++b) {
-            if (b * 64 + lane < C) {
-                if (w[b][1] == 0xffffffffu) bad = 1;
-                else argmax_combine(vt, it, __uint_as_float(w[b][0]), (int)w[b][1]);
-                if (pair) {
-                    if (w[b][3] == 0xffffffffu) bad = 1;
-                    else argmax_combine(vd, id, __uint_as_float(w[b][2]), (int)w[b][3]);
-                }
-            }
-        }
-        wave_argmax(vt, it);
-        wave_argmax(vd, id);
-        bad = wave_max_i(bad);
-        const int gt = (!bad && vt > -kInf && vt < kInf && it != 0x7fffffff) ? it : -1;
-        const int gd = pair ? ((!bad && vd > -kInf && vd < kInf && id != 0x7fffffff) ? id : -1) : 0;
-        bool valid = gt >= 0 && gd >= 0;
-        if (a.tv_mode) {
-            if (!valid) {
-                write_invalid(a, x.r);
-            } else if (lane == 0) {
-                const float cv = (gt == gd) ? 1.0f : 0.0f;
-                a.out_cs[x.r] = cv;
-                if (a.out_rs) a.out_rs[x.r] = 1.0f - cv;
-            }
-            return;
-        }
-        bool acc = false;
+    if (!a.tv_mode && pair) xtok = a.tokens[(size_t)x.r * G + x.i];
+    float vt = -kInf, vd = -kInf;
+    int it = 0x7fffffff, id = 0x7fffffff, bad = 0;
+    fold_unit_words(a, x, pair, [&](const uint32_t (&w)[4]) {
+        if (w[1] == 0xffffffffu) bad = 1;
+        else argmax_combine(vt, it, __uint_as_float(w[0]), (int)w[1]);
         if (pair) {
-            valid = valid && xtok >= 0 && xtok < a.V;
-            acc = xtok == gt;
+            if (w[3] == 0xffffffffu) bad = 1;
+            else argmax_combine(vd, id, __uint_as_float(w[2]), (int)w[3]);
         }
-        const float cv = (gt == gd) ? 1.0f : 0.0f;
-        const uint32_t fl = (valid ? kFlagValid : 0u) | (acc ? kFlagAccept : 0u);
-        publish_n(rec, a.tag, 4, fl, __float_as_uint(0.0f), (uint32_t)gt, __float_as_uint(0.0f));
-        publish_n(rec + 4, a.tag, 2, __float_as_uint(pair ? cv : nan),
-                  __float_as_uint(pair ? 1.0f - cv : nan), 0u, 0u);
-        unit_done(a, x);
+    });
+    wave_argmax(vt, it);
+    wave_argmax(vd, id);
+    bad = wave_max_i(bad);
+    const int gt = (!bad && vt > -kInf && vt < kInf && it != 0x7fffffff) ? it : -1;
+    const int gd = pair ? ((!bad && vd > -kInf && vd < kInf && id != 0x7fffffff) ? id : -1) : 0;
+    bool valid = gt >= 0 && gd >= 0;
+    if (a.tv_mode) {
+        if (!valid) {
+            write_invalid(a, x.r);
+        } else if (lane == 0) {
+            const float cv = (gt == gd) ? 1.0f : 0.0f;
+            a.out_cs[x.r] = cv;
+            if (a.out_rs) a.out_rs[x.r] = 1.0f - cv;
+        }
         return;
     }
-
-    // T > 0: per-lane online combine of (mu, S) over the lane's chunks, then
-    // across the wave: M = max mu, Z = sum S 2^(mu - M).
-    OnlineZ ot, od;
-#pragma unroll
-    for (int b = 0; b < kCB; ++b) {
-        if (b * 64 + lane < C) {
-            ot.add(__uint_as_float(w[b][0]), __uint_as_float(w[b][1]));
-            if (pair) od.add(__uint_as_float(w[b][2]), __uint_as_float(w[b][3]));
-        }
+    bool acc = false;
+    if (pair) {
+        valid = valid && xtok >= 0 && xtok < a.V;
+        acc = xtok == gt;
     }
+    const float cv = (gt == gd) ? 1.0f : 0.0f;
+    const uint32_t fl = (valid ? kFlagValid : 0u) | (acc ? kFlagAccept : 0u);
+    publish_n(rec, a.tag, 4, fl, __float_as_uint(0.0f), (uint32_t)gt, __float_as_uint(0.0f));
+    publish_n(rec + 4, a.tag, 2, __float_as_uint(pair ? cv : nan),
+              __float_as_uint(pair ? 1.0f - cv : nan), 0u, 0u);
+    unit_done(a, x);
+}
+
+// T > 0: the row normalisers M = max mu and Z = sum S 2^(mu - M) (per lane
+// over its chunks, then across the wave), published for the TV items and
+// the last combine; in row-pair mode also the unit's validity.
+template <typename TT, typename TD, int N, int EPV>
+__device__ __forceinline__ void norm_fold(const VerifyArgs &a, const Item &x) {
+    const bool pair = is_pair(x);
+    OnlineZ ot, od;
+    fold_unit_words(a, x, pair, [&](const uint32_t (&w)[4]) {
+        ot.add(__uint_as_float(w[0]), __uint_as_float(w[1]));
+        if (pair) od.add(__uint_as_float(w[2]), __uint_as_float(w[3]));
+    });
     float Mt, Zt, Md = 0.0f, Zd = 1.0f;
     ot.reduce(Mt, Zt);
     if (pair) od.reduce(Md, Zd);
-    publish_n(nrm, a.tag, 4, __float_as_uint(Mt), __float_as_uint(Zt), __float_as_uint(Md),
-              __float_as_uint(Zd));
-
+    publish_n(a.nrm + (size_t)x.u * 4, a.tag, 4, __float_as_uint(Mt), __float_as_uint(Zt),
+              __float_as_uint(Md), __float_as_uint(Zd));
     if (a.tv_mode) {
         bool valid = finite_f(Mt) && Zt > 0.0f && finite_f(Zt);
         if (pair) valid = valid && finite_f(Md) && Zd > 0.0f && finite_f(Zd);
-        publish_n(rec, a.tag, 1, valid ? kFlagValid : 0u, 0u, 0u, 0u);
+        publish_n(a.rec + (size_t)x.u * kRecWords, a.tag, 1, valid ? kFlagValid : 0u, 0u, 0u, 0u);
     }
-    // the accept test of a position and the draw of the bonus token come in
-    // the last combine, which has the normalisers in the same batch as its
-    // TV words
 }
 
 // All C TV partials of pair unit x (T > 0) are published: c*, Res, and the
@@ -1313,18 +1321,9 @@ __global__ void __launch_bounds__(kBlock, kStreamWaves) stats_kernel(VerifyArgs 
     }
 }
 
-// Kernel 2: one wave per active unit combines kernel 1's chunk words into
-// the row normalisers (at T = 0: the argmax test, which settles the unit).
-template <typename TT, typename TD, int N, int EPV>
-__global__ void __launch_bounds__(kBlock) norm_kernel(VerifyArgs a) {
-    a.tag = call_tag(a.ctl);
-    Item x;
-    if (unit_item(a, wave_index(), x)) stats_combine<TT, TD, N, EPV>(a, x);
-}
-
 // TV of pair item x at T > 0 (chunk re-read, from the Infinity Cache when the
 // rows fit there): with the chunk's words and the unit's normalisers from
-// kernel 1, the weights e = 2^(z s - mu) are rebuilt exactly as kernel 1 made
+// the statistics pass, the weights e = 2^(z s - mu) are rebuilt exactly as it made
 // them, and sum min(p, q) and the residual mass of the chunk are published.
 template <int N, typename RT, typename RD>
 __device__ __forceinline__ void tv_item(const VerifyArgs &a, const Item &x, RT &rt, RD &rd,
@@ -1340,7 +1339,7 @@ __device__ __forceinline__ void tv_item(const VerifyArgs &a, const Item &x, RT &
     const PairScale ps = pair_scale(chunk_alpha(mut, Mt, Zt), chunk_alpha(mud, Md, Zd));
     const float reft = exp_ref(mut), refd = exp_ref(mud);
     // min(p, q) in units of ps.unit, summed in the same slot order as the
-    // chunk's weight sum in kernel 1, so a chunk with q <= p everywhere has a
+    // chunk's weight sum in the statistics pass, so a chunk with q <= p everywhere has a
     // residual of exactly 0
     float acc = 0.0f, ssum;
     if (ps.kt == 1.0f) {
@@ -1374,22 +1373,31 @@ __device__ __forceinline__ uint64_t load_tv_item(const VerifyArgs &a, const Item
     const int lane = lane_id();
     const uint64_t *p = (lane < 4) ? a.st1 + ((size_t)x.u * a.C + x.c) * 4 + lane
                                    : a.nrm + (size_t)x.u * 4 + (lane & 3);
-    // written by the earlier launches of this call: a plain load sees it
+    // a plain load: the chunk words are the statistics pass's; a normaliser
+    // word that is not current yet (an older tag) is polled coherently later
     const uint64_t w = (lane < 8) ? *p : 0;
     load_item(a, x, rt, rd);
     return w;
 }
 
-// Kernel 3: the TV pass over the pair items at T > 0, one item in flight per
-// wave.
+// Kernel 2: the unit folds at T > 0, then the TV pass over the pair items at
+// T > 0, one item in flight per wave.
 template <typename TT, typename TD, int N, int EPV>
 __global__ void __launch_bounds__(kBlock, kStreamWaves) tv_kernel(VerifyArgs a) {
     a.tag = call_tag(a.ctl);
     const int lane = lane_id();
     extern __shared__ uint32_t lds[];
+    // first the folds: wave w folds units w, w + W, ... at T > 0 into their
+    // row normalisers.  They read only the statistics pass's words, so no
+    // fold waits for a TV item.
+    for (long u = wave_index(); u < (long)a.R * a.UG; u += wave_count()) {
+        Item y;
+        if (unit_item(a, u, y) && y.T != 0.0f) norm_fold<TT, TD, N, EPV>(a, y);
+    }
     Walker cur = make_walker(a, lds, true);
-    // kernels 1 and 2 wrote the words before this launch: a stale tag could
-    // only come from an earlier call, so the wait never spins
+    // the chunk words come from the statistics pass (earlier launch); a
+    // unit's normalisers may still be on their way from the wave folding it,
+    // so a stale tag is polled until it turns current (bounded)
     auto words = [&](const Item &it, uint64_t w) -> uint32_t {
         if (!__ballot(lane < 8 && (uint32_t)(w >> 32) != a.tag)) return (uint32_t)w;
         const uint64_t *p = (lane < 4) ? a.st1 + ((size_t)it.u * a.C + it.c) * 4 + lane
@@ -1405,17 +1413,19 @@ __global__ void __launch_bounds__(kBlock, kStreamWaves) tv_kernel(VerifyArgs a) 
     }
 }
 
-// Kernel 4: one wave per unit at T > 0.  A position runs its accept test,
-// sums its TV words into c* and Res and makes the residual draw if rejected;
-// the bonus unit draws from q.  The wave that finishes a request's last unit
-// writes the request's outputs.
+// Kernel 3: one wave per unit.  At T > 0 a position runs its accept test,
+// sums its TV words into c* and Res and makes the residual draw if rejected,
+// and the bonus unit draws from q; at T = 0 the argmax test settles the unit.
+// The wave that finishes a request's last unit writes the request's outputs.
 template <typename TT, typename TD, int N, int EPV>
 __global__ void __launch_bounds__(kBlock) tv_combine_kernel(VerifyArgs a) {
     a.tag = call_tag(a.ctl);
     if (blockIdx.x == 0 && threadIdx.x == 0) a.ctl->tag_next = (a.tag + 1u) | 0x80000000u;
     Item x;
-    if (!unit_item(a, wave_index(), x) || x.T == 0.0f) return;
-    if (is_pair(x))
+    if (!unit_item(a, wave_index(), x)) return;
+    if (x.T == 0.0f)
+        greedy_combine<TT, TD, N, EPV>(a, x);
+    else if (is_pair(x))
         tv_combine<TT, TD, N, EPV>(a, x);
     else
         bonus_draw<TT, TD, N, EPV>(a, x);
@@ -1585,7 +1595,6 @@ int launch_kernels(VerifyArgs a, hipStream_t st) {
     }
     hipLaunchKernelGGL((stats_kernel<TT, TD, N, EPV>), dim3((unsigned)g1), dim3(kBlock), lds, st,
                        a);
-    hipLaunchKernelGGL((norm_kernel<TT, TD, N, EPV>), dim3((unsigned)gu), dim3(kBlock), 0, st, a);
     hipLaunchKernelGGL((tv_kernel<TT, TD, N, EPV>), dim3((unsigned)g3), dim3(kBlock), lds, st, a);
     hipLaunchKernelGGL((tv_combine_kernel<TT, TD, N, EPV>), dim3((unsigned)gu), dim3(kBlock), 0,
                        st, a);
