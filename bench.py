@@ -51,6 +51,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 TRAFFIC_SOURCES = {
     "verify_batched": ("common.h", "verify.hip"),
     "markov_dspark": ("common.h", "markov.hip"),
+    "rnn_head": ("common.h", "markov.hip"),
+    "tree_greedy": ("common.h", "tree.hip"),
 }
 
 
@@ -306,7 +308,8 @@ def bench_rnn(args):
         "roofline": {"bound": "hbm", "achieved": per_call / (ms.mean() / 1e3) / 1e9,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": per_call / (ms.mean() / 1e3) / 1e9 / HBM_PEAK_GBS,
-                     "traffic": None, "algorithmic_bytes_per_call": per_call,
+                     "traffic": measured_traffic("rnn_head"),
+                     "algorithmic_bytes_per_call": per_call,
                      "mfma_tflops": flops / (ms.mean() / 1e3) / 1e12},
     }
     if not args.no_cpu_baseline:
@@ -496,7 +499,8 @@ def bench_tree(args):
                    "accepted_mean": float(a.mean()), "levels": c.max_depth + 1},
         "roofline": {"bound": "hbm", "achieved": per_call / (ms.mean() / 1e3) / 1e9,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": per_call / (ms.mean() / 1e3) / 1e9 / HBM_PEAK_GBS, "traffic": None,
+                     "frac": per_call / (ms.mean() / 1e3) / 1e9 / HBM_PEAK_GBS,
+                     "traffic": measured_traffic("tree_greedy"),
                      "algorithmic_bytes_per_call": per_call,
                      "kernel": "spec_tree_verify call (tree_level_kernel per level)"},
         "kernel_ms_mean": float(ms.mean()),
