@@ -122,6 +122,19 @@ def test_max_gamma(sv, dev):
     _check(sv, dev, case, "gamma64")
 
 
+def test_large_batch_walks_all_candidates(sv, dev):
+    # R = 160, gamma = 48: the unit table (4 (3 R + R (gamma + 1)) = 33.3 KB)
+    # exceeds the 32 KB the streaming kernels list in LDS, so they walk every
+    # candidate item instead; greedy and sampled requests mixed
+    R, G = 160, 48
+    g = np.random.default_rng(160)
+    case = workloads.make_verify_case(R, G, 1500, "bf16", seed=160, noise_std=0.3,
+                                      verify_len=g.integers(0, G + 1, size=R).tolist(),
+                                      temperature=[0.0 if r % 3 == 0 else 0.9 for r in range(R)])
+    gpu, ref, st = _check(sv, dev, case, "large_batch")
+    assert st["exact"] + st["near_ties"] == R
+
+
 def test_identical_and_disjoint_rows(sv, dev):
     case = workloads.make_verify_case(6, 4, 4096, "f32", seed=8, verify_len=4, temperature=1.0)
     case.draft[:3] = case.target[:3, :4]                 # p == q: every draft accepted
