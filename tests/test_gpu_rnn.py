@@ -50,6 +50,7 @@ def run(sv, dev, c, anchor=None, T=None):
     (70, 2, 2048, 128, 1.0),     # two MFMA request blocks, a partial gate block
     (4, 3, 4096, 256, 0.0),      # greedy
     (2, 7, 129280, 1024, 1.0),   # the DSpark vocabulary
+    (3, 2, 2000, 3072, 1.0),     # the largest hidden size
 ])
 def test_rnn_matches_oracle(sv, dev, R, gamma, V, hidden, T):
     print(f"[rnn] R={R} gamma={gamma} V={V} hidden={hidden} T={T}", flush=True)

@@ -63,6 +63,14 @@ def test_sts_matches_oracle(sv, dev, N, gamma, G, bins):
     assert graded >= gamma - 1
 
 
+def test_sts_largest_grid(sv, dev):
+    # 1024 temperatures (16 grid blocks; the select takes four per thread)
+    print("[sts] N=600 gamma=2 G=1024 bins=15", flush=True)
+    c = workloads.sts_case(seed=21, N=600, gamma=2, G=1024)
+    ref = osts.sts_calibrate(c.z, c.accepted, c.grid, bins=15)
+    check(run(sv, dev, c.z, c.accepted, c.grid, 15), ref)
+
+
 def test_sts_full_held_out_set(sv, dev):
     # the benchmark's held-out set: 262144 blocks, gamma 7, 64 temperatures
     print("[sts] N=262144 gamma=7 G=64 bins=15", flush=True)

@@ -76,6 +76,18 @@ def test_chain_deep_and_single_node_trees(sv, dev):
     assert ref["accepted"][3] == 0 and ref["accepted"].max() >= 5
 
 
+def test_largest_tree_walked_to_the_bottom(sv, dev):
+    # 1024 nodes in one chain, every edge planted: the walk accepts 1023
+    # nodes over 1025 launches (max_depth = M - 1)
+    M, V = 1024, 3000
+    print(f"[tree] chain M={M} V={V}", flush=True)
+    c = workloads.tree_case(seed=31, R=2, M=M, V=V, dtype="f32", widths=(1,) * (M - 1),
+                            p_hit=1.0)
+    ref = otree.tree_verify(c.logits, c.parent, c.tokens, c.n_nodes)
+    assert ref["accepted"][0] == M - 1
+    check(run(sv, dev, c.logits, c.parent, c.tokens, c.n_nodes, M - 1), ref)
+
+
 def test_equal_siblings_and_ties_across_slices(sv, dev):
     V, M = 20000, 6
     L = np.zeros((1, M, V), np.float32)
