@@ -135,6 +135,16 @@ def test_large_batch_walks_all_candidates(sv, dev):
     assert st["exact"] + st["near_ties"] == R
 
 
+@pytest.mark.parametrize("V,dtype", [(262144, "bf16"), (262143, "f32")])
+def test_largest_vocabulary(sv, dev, V, dtype):
+    # V = 262144: 256 chunks per row, every chunk block of the unit combines
+    # in use; V - 1 (odd) takes the scalar loads
+    case = workloads.make_verify_case(3, 3, V, dtype, seed=V % 1000, noise_std=1.0,
+                                      verify_len=[3, 2, 3], temperature=[1.0, 0.0, 0.8])
+    gpu, ref, st = _check(sv, dev, case, f"V{V}")
+    assert st["exact"] + st["near_ties"] == case.R
+
+
 def test_identical_and_disjoint_rows(sv, dev):
     case = workloads.make_verify_case(6, 4, 4096, "f32", seed=8, verify_len=4, temperature=1.0)
     case.draft[:3] = case.target[:3, :4]                 # p == q: every draft accepted
