@@ -25,12 +25,6 @@ struct Control {
 };
 static_assert(sizeof(Control) == 256, "control block size");
 
-// Host side: records that the first `bytes` of workspace `ws` read zero
-// outside the control block once the work enqueued so far has run (every
-// entry point that writes a workspace calls it; the verification counters
-// rely on it).
-void note_workspace_clean(const void *ws, size_t bytes);
-
 __device__ __forceinline__ uint32_t atomic_load_u32(const uint32_t *p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }

@@ -744,7 +744,6 @@ int spec_markov_draft_sample(const void *U, int u_dtype, const void *W1, const v
     MarkovArgs a;
     mk_setup(U, u_dtype, W1, W2, w_dtype, anchor, temperature, u_draft, R, gamma, V, rank,
              out_draft_tokens, out_draft_logits, workspace, p, a);
-    note_workspace_clean(workspace, sizeof(Control));
     hipStream_t st = (hipStream_t)stream;
     hipLaunchKernelGGL(markov_clear_kernel, dim3((R + kBlock - 1) / kBlock), dim3(kBlock), 0, st,
                        a.bad, R);
@@ -802,7 +801,6 @@ int spec_rnn_draft_sample(const void *U, int u_dtype, const void *W1, const void
     g.V = V;
     g.hidden = hidden;
     float *s0 = (float *)(ws + p.off_s0), *s1 = (float *)(ws + p.off_s1);
-    note_workspace_clean(workspace, sizeof(Control));
     hipStream_t st = (hipStream_t)stream;
     hipLaunchKernelGGL(markov_clear_kernel, dim3((R + kBlock - 1) / kBlock), dim3(kBlock), 0, st,
                        a.bad, R);

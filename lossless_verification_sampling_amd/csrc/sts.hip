@@ -271,7 +271,6 @@ int spec_sts_calibrate(const float *conf_logits, const int32_t *accepted_len, co
     a.out_ece = out_ece;
     a.out_curve = out_curve;
     a.ctl = (Control *)ws;
-    note_workspace_clean(workspace, sizeof(Control));
     hipStream_t st = (hipStream_t)stream;
     const dim3 nblk((unsigned)((N + kBlock - 1) / kBlock));
     const dim3 hgrid((unsigned)p.ntiles, (unsigned)((G + kStsGrid - 1) / kStsGrid));

@@ -260,7 +260,6 @@ int spec_tree_verify(const void *logits, int dtype, const int32_t *parent, const
     a.node = (int32_t *)(ws + sizeof(Control) + 8 * (size_t)R * L);
     a.fault = (uint32_t *)(ws + sizeof(Control) + 12 * (size_t)R * L);
     a.ctl = (Control *)ws;
-    note_workspace_clean(workspace, sizeof(Control));
     hipStream_t st = (hipStream_t)stream;
     hipLaunchKernelGGL(tree_init_kernel, dim3((unsigned)R), dim3(64), 0, st, a);
     const size_t eb = dtype == SPEC_BF16 ? 2 : 4;

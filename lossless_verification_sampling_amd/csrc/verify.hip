@@ -95,7 +95,6 @@ struct VerifyArgs {
     float *out_rs;
     float *out_lq;
     Control *ctl;
-    uint32_t *cnt_r;         // [R] finished units per request
     uint64_t *st1;           // [units][C][4] chunk stats
     uint64_t *st2;           // [units][C][2] chunk sum min(p, q), residual mass
     uint64_t *nrm;           // [units][4] unit normalisers
@@ -271,26 +270,6 @@ struct ItemCursor {
     }
 };
 
-// Invalid-request outputs of request r, written by one thread.
-__device__ __forceinline__ void write_invalid_thread(const VerifyArgs &a, int r) {
-    const float nan = __builtin_nanf("");
-    if (a.tv_mode) {
-        a.out_cs[r] = nan;
-        if (a.out_rs) a.out_rs[r] = nan;
-    } else {
-        for (int j = 0; j <= a.gamma; ++j) {
-            a.out_tok[(size_t)r * (a.gamma + 1) + j] = -1;
-            if (a.out_lq) a.out_lq[(size_t)r * (a.gamma + 1) + j] = nan;
-        }
-        for (int i = 0; i < a.gamma; ++i) {
-            if (a.out_cs) a.out_cs[(size_t)r * a.gamma + i] = nan;
-            if (a.out_rs) a.out_rs[(size_t)r * a.gamma + i] = nan;
-        }
-        a.out_n[r] = -1;
-    }
-    atomic_or_u32(&a.ctl->status, SPEC_DEV_BAD_REQUEST);
-}
-
 // Work list of the streaming kernels when the unit table fits in LDS: every
 // workgroup lists the active units (request-major) in shared memory at launch,
 // and item k (unit k / C, chunk k % C) belongs to wave k mod W.  Only active
@@ -328,9 +307,6 @@ __device__ __forceinline__ UnitTable build_unit_table(const VerifyArgs &a, uint3
         float T;
         int l;
         const bool ok = request_ok(a, r, T, l);
-        // the stats pass's first workgroup writes the outputs of malformed
-        // requests (their units are never visited)
-        if (!ok && !tv_only && blockIdx.x == 0) write_invalid_thread(a, r);
         req[3 * r + 0] = __float_as_uint(T);
         req[3 * r + 1] = __float_as_uint(ok && T != 0.0f ? exp2_scale(T) : 0.0f);
         req[3 * r + 2] = (uint32_t)l;
@@ -583,10 +559,10 @@ struct OnlineZ {
             bad = 1;
         } else if (mu > -kInf) {
             if (mu > m) {
-                z = z * (double)__builtin_amdgcn_exp2f(m - mu) + (double)S;
+                z = __builtin_fma(z, (double)__builtin_amdgcn_exp2f(m - mu), (double)S);
                 m = mu;
             } else {
-                z += (double)S * (double)__builtin_amdgcn_exp2f(mu - m);
+                z = __builtin_fma((double)S, (double)__builtin_amdgcn_exp2f(mu - m), z);
             }
         }
     }
@@ -853,6 +829,281 @@ __device__ __forceinline__ float chunk_logit(long c0, int tok, const float (&z)[
     return readlane_f(v, lt);
 }
 
+// ---------------------------------------------------------------------------
+// unit folds (launch 2) and per-request combines (launch 3)
+// ---------------------------------------------------------------------------
+
+// The lane's chunk words of unit x (c = 64 b + lane), in rounds of two
+// blocks in increasing chunk order, each handed to fold(w) for block
+// b0 + h.  They come from the statistics pass (an earlier launch).
+template <typename F>
+__device__ __forceinline__ void fold_unit_words(const VerifyArgs &a, const Item &x, bool pair,
+                                                F fold) {
+    const int lane = lane_id();
+    const bool want[4] = {true, true, pair, pair};
+    for (int b0 = 0; b0 < kCB && b0 * 64 < a.C; b0 += 2) {
+        uint32_t w[2][4];
+        load_unit_words<4, 2>(a.st1 + (size_t)x.u * a.C * 4, a.C, want, a.tag, a.ctl, w, true,
+                              b0);
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+            if ((b0 + h) * 64 + lane < a.C) fold(w[h]);
+    }
+}
+
+__device__ __forceinline__ bool norms_ok(float M, float Z) {
+    return finite_f(M) && Z > 0.0f && finite_f(Z);
+}
+
+// Row normalisers of unit x at T > 0 from the statistics pass's chunk words:
+// M = max mu and Z = sum S 2^(mu - M), per lane over its chunks in
+// increasing order, then across the wave in a fixed order, so that every wave
+// folding the same unit gets the same bits.  A bonus row gives (Md, Zd) =
+// (0, 1).
+__device__ __forceinline__ void unit_norms(const VerifyArgs &a, const Item &x, float &Mt, float &Zt,
+                                        float &Md, float &Zd) {
+    const bool pair = is_pair(x);
+    OnlineZ ot, od;
+    fold_unit_words(a, x, pair, [&](const uint32_t (&w)[4]) {
+        ot.add(__uint_as_float(w[0]), __uint_as_float(w[1]));
+        if (pair) od.add(__uint_as_float(w[2]), __uint_as_float(w[3]));
+    });
+    ot.reduce(Mt, Zt);
+    Md = 0.0f;
+    Zd = 1.0f;
+    if (pair) od.reduce(Md, Zd);
+}
+
+// Launch 2's fold of unit x at T > 0: publishes the row normalisers for the
+// TV items and the combine.  For a draft position it then runs the accept
+// test on the draft token x_{i+1}: accept <=> q(x) >= p(x) or u < q(x)/p(x)
+// (DART note eq. (3)), in fp64 from the two gathered logits, and publishes
+// the record (flags, log q(x)).  The uniform's range is checked by the
+// combine.
+template <typename TT, typename TD>
+__device__ __forceinline__ void norm_fold(const VerifyArgs &a, const Item &x) {
+    const bool pos = !a.tv_mode && is_pair(x);
+    int xtok = -1;
+    float uacc = 0.0f;
+    if (pos) {
+        xtok = a.tokens[(size_t)x.r * a.gamma + x.i];
+        uacc = a.ua[(size_t)x.r * a.gamma + x.i];
+    }
+    float Mt, Zt, Md, Zd;
+    unit_norms(a, x, Mt, Zt, Md, Zd);
+    publish_n(a.nrm + (size_t)x.u * 4, a.tag, 4, __float_as_uint(Mt), __float_as_uint(Zt),
+              __float_as_uint(Md), __float_as_uint(Zd));
+    if (!pos) return;
+    const bool valid = norms_ok(Mt, Zt) && norms_ok(Md, Zd) && xtok >= 0 && xtok < a.V;
+    bool acc = false;
+    float lqx = __builtin_nanf("");
+    if (valid) {
+        const float s = x.s;
+        const float zx = load_one(row_ptr<TT>(a.zt, x.r, a.tG, x.i, a.V), xtok);
+        const float dx = load_one(row_ptr<TD>(a.zd, x.r, a.dG, x.i, a.V), xtok);
+        const double lq2 = (double)zx * (double)s - (double)Mt;
+        const double lp2 = (double)dx * (double)s - (double)Md;
+        const double q = exp2(lq2) / (double)Zt;
+        const double pp = exp2(lp2) / (double)Zd;
+        acc = q >= pp || (double)uacc < q / pp;
+        lqx = (float)(lq2 * kLn2 - log((double)Zt));
+    }
+    publish_n(a.rec + (size_t)x.u * kRecWords, a.tag, 2,
+              (valid ? kFlagValid : 0u) | (acc ? kFlagAccept : 0u), __float_as_uint(lqx), 0u, 0u);
+}
+
+// Per-unit summary of a request in launch 3 (shared memory), written by
+// lane 0 of the unit's wave.
+struct UnitSum {
+    uint32_t flags;          // kFlagValid, kFlagAccept
+    float lqx;               // log q of the position's draft token (0 at T = 0)
+    float cs, rs;            // c*, Res of a position
+    int sel;                 // T = 0: the row's target argmax; T > 0: chunk of the
+                             // inverse-CDF draw at this row (-1: no residual mass)
+    float Mt, Zt, Md, Zd;    // row normalisers (T > 0)
+    double tin;              // the draw's target minus the mass of chunks before sel
+};
+
+constexpr int kReqWaves = 8;
+constexpr int kReqBlock = kReqWaves * 64;
+
+// T = 0 unit (DART note sec. 2.3; survey sec. 1.3): the argmaxes of its rows
+// (lowest id on ties); a position is accepted iff its draft token is the
+// target argmax, and c* = [argmax p == argmax q].
+__device__ __forceinline__ void greedy_unit(const VerifyArgs &a, const Item &x, UnitSum *s) {
+    const bool pair = is_pair(x);
+    int xtok = 0;
+    if (!a.tv_mode && pair) xtok = a.tokens[(size_t)x.r * a.gamma + x.i];
+    float vt = -kInf, vd = -kInf;
+    int it = 0x7fffffff, id = 0x7fffffff, bad = 0;
+    fold_unit_words(a, x, pair, [&](const uint32_t (&w)[4]) {
+        if (w[1] == 0xffffffffu) bad = 1;
+        else argmax_combine(vt, it, __uint_as_float(w[0]), (int)w[1]);
+        if (pair) {
+            if (w[3] == 0xffffffffu) bad = 1;
+            else argmax_combine(vd, id, __uint_as_float(w[2]), (int)w[3]);
+        }
+    });
+    wave_argmax(vt, it);
+    wave_argmax(vd, id);
+    bad = wave_max_i(bad);
+    const int gt = (!bad && vt > -kInf && vt < kInf && it != 0x7fffffff) ? it : -1;
+    const int gd = pair ? ((!bad && vd > -kInf && vd < kInf && id != 0x7fffffff) ? id : -1) : 0;
+    bool valid = gt >= 0 && gd >= 0;
+    bool acc = false;
+    if (!a.tv_mode && pair) {
+        valid = valid && xtok >= 0 && xtok < a.V;
+        acc = xtok == gt;
+    }
+    if (lane_id() == 0) {
+        const float cv = (gt == gd) ? 1.0f : 0.0f;
+        s->flags = (valid ? kFlagValid : 0u) | (acc ? kFlagAccept : 0u);
+        s->lqx = 0.0f;
+        s->cs = pair ? cv : __builtin_nanf("");
+        s->rs = pair ? 1.0f - cv : __builtin_nanf("");
+        s->sel = gt;
+    }
+}
+
+// T > 0 draft position: c* and Res from the TV pass's chunk words, the accept
+// record of the fold, and the chunk of the residual draw [q - p]_+ should
+// this row be the request's first rejection (DART note eq. (3)-(4)).
+__device__ __forceinline__ void tv_unit(const VerifyArgs &a, const Item &x, UnitSum *s) {
+    const int lane = lane_id();
+    const int C = a.C, G = a.gamma;
+    float usm = 0.0f, uacc = 0.0f;
+    if (!a.tv_mode) {
+        usm = a.us[(size_t)x.r * (G + 1) + x.i];
+        uacc = a.ua[(size_t)x.r * G + x.i];
+    }
+    const uint64_t *p[2 * kCB + 1];
+    bool act[2 * kCB + 1];
+    uint32_t o[2 * kCB + 1];
+#pragma unroll
+    for (int b = 0; b < kCB; ++b)
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const int c = b * 64 + lane;
+            p[b * 2 + q] = a.st2 + ((size_t)x.u * C + c) * 2 + q;
+            act[b * 2 + q] = c < C;
+        }
+    // lanes 0..3: normalisers; 4, 5: the fold's record (flags, log q(x))
+    p[2 * kCB] = (lane < 4) ? a.nrm + (size_t)x.u * 4 + lane
+                            : a.rec + (size_t)x.u * kRecWords + (lane & 1);
+    act[2 * kCB] = lane < 4 || (!a.tv_mode && lane < 6);
+    await_batch<2 * kCB + 1>(p, act, a.tag, a.ctl, o, true);
+    const float Mt = __uint_as_float(rl(o[2 * kCB], 0)), Zt = __uint_as_float(rl(o[2 * kCB], 1));
+    const float Md = __uint_as_float(rl(o[2 * kCB], 2)), Zd = __uint_as_float(rl(o[2 * kCB], 3));
+    double cs = 0.0, rs = 0.0, m[kCB];
+#pragma unroll
+    for (int b = 0; b < kCB; ++b) {
+        cs += (double)__uint_as_float(o[b * 2]);
+        m[b] = (double)__uint_as_float(o[b * 2 + 1]);
+        rs += m[b];
+    }
+    cs = wave_sum(cs);
+    rs = wave_sum(rs);
+    bool valid, acc = false;
+    float lqx = 0.0f;
+    if (a.tv_mode) {
+        valid = norms_ok(Mt, Zt) && norms_ok(Md, Zd);
+    } else {
+        const uint32_t fl = rl(o[2 * kCB], 4);
+        lqx = __uint_as_float(rl(o[2 * kCB], 5));
+        valid = (fl & kFlagValid) && uniform_ok(uacc) && uniform_ok(usm);
+        acc = (fl & kFlagAccept) != 0;
+    }
+    int sel = -1;
+    double tin = 0.0;
+    if (valid && !a.tv_mode && rs > 0.0) sel = select_chunk(C, (double)usm * rs, m, &tin);
+    if (lane == 0) {
+        s->flags = (valid ? kFlagValid : 0u) | (acc ? kFlagAccept : 0u);
+        s->lqx = lqx;
+        s->cs = (float)cs;
+        s->rs = (float)rs;
+        s->sel = sel;
+        s->Mt = Mt;
+        s->Zt = Zt;
+        s->Md = Md;
+        s->Zd = Zd;
+        s->tin = tin;
+    }
+}
+
+// T > 0 bonus unit (target row l_r): the chunk of the inverse-CDF draw from
+// q_l with u_sample[r][l] (DSpark guide, "basics": one bonus token).
+__device__ __forceinline__ void bonus_unit(const VerifyArgs &a, const Item &x, UnitSum *s) {
+    const int lane = lane_id();
+    const int C = a.C;
+    const float usm = a.us[(size_t)x.r * (a.gamma + 1) + x.i];
+    const uint64_t *p[2 * kCB + 1];
+    bool act[2 * kCB + 1];
+    uint32_t o[2 * kCB + 1];
+#pragma unroll
+    for (int b = 0; b < kCB; ++b)
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const int c = b * 64 + lane;
+            p[b * 2 + q] = a.st1 + ((size_t)x.u * C + c) * 4 + q;
+            act[b * 2 + q] = c < C;
+        }
+    p[2 * kCB] = a.nrm + (size_t)x.u * 4 + (lane & 1);
+    act[2 * kCB] = lane < 2;
+    await_batch<2 * kCB + 1>(p, act, a.tag, a.ctl, o, true);
+    const float Mt = __uint_as_float(rl(o[2 * kCB], 0)), Zt = __uint_as_float(rl(o[2 * kCB], 1));
+    const bool valid = norms_ok(Mt, Zt) && uniform_ok(usm);
+    int sel = -1;
+    double tin = 0.0;
+    if (valid) {
+        double m[kCB];
+        double W = 0.0;
+#pragma unroll
+        for (int b = 0; b < kCB; ++b) {
+            const int c = b * 64 + lane;
+            m[b] = (c < C) ? (double)chunk_alpha(__uint_as_float(o[b * 2]), Mt, Zt) *
+                                 (double)__uint_as_float(o[b * 2 + 1])
+                           : 0.0;
+            W += m[b];
+        }
+        W = wave_sum(W);
+        sel = select_chunk(C, (double)usm * W, m, &tin);
+    }
+    if (lane == 0) {
+        s->flags = valid ? kFlagValid : 0u;
+        s->lqx = 0.0f;
+        s->cs = __builtin_nanf("");
+        s->rs = __builtin_nanf("");
+        s->sel = sel;
+        s->Mt = Mt;
+        s->Zt = Zt;
+        s->Md = 0.0f;
+        s->Zd = 1.0f;
+        s->tin = tin;
+    }
+}
+
+// Draw inside chunk cs of target row trow from q: weights 2^(z s - mu) rebuilt
+// exactly as the statistics pass made them, and the first id whose running
+// weight exceeds tin (in probability units).  *ztok = the token's logit.
+template <typename TT, int N, int EPV>
+__device__ __forceinline__ int draw_q_chunk(const VerifyArgs &a, const TT *trow, int cs,
+                                            double tin, float s, float mu, float M, float Z,
+                                            float *ztok) {
+    const float al = chunk_alpha(mu, M, Z);
+    const float ref = exp_ref(mu);
+    const long c0 = (long)cs * kLanes * N;
+    const double te = (al > 0.0f) ? tin / (double)al : INFINITY;
+    float z[N / EPV][EPV], wv[N / EPV][EPV];
+    load_chunk_ids<TT, N, EPV>(trow, c0, a.V, z);
+#pragma unroll
+    for (int j = 0; j < N / EPV; ++j)
+#pragma unroll
+        for (int q = 0; q < EPV; ++q) wv[j][q] = ew(z[j][q], s, ref);
+    const int tok = draw_in_chunk_w<N, EPV>(c0, te, wv);
+    *ztok = chunk_logit<N, EPV>(c0, tok, z);
+    return tok;
+}
+
 // Draw from q of a target row (T > 0), its chunk words w (mu_t, S_t in q = 0,
 // 1) and normalisers (M, Z) in hand.  Returns the token; *ztok its logit.
 template <typename TT, int N, int EPV, int Q>
@@ -874,367 +1125,175 @@ __device__ __forceinline__ int draw_from_q(const VerifyArgs &a, const TT *trow,
     double tin;
     const int cs = select_chunk(C, (double)uu * W, m, &tin);
     const float mu = __uint_as_float(chunk_word<Q>(w, cs, 0));
-    const float al = chunk_alpha(mu, M, Z);
-    const float ref = exp_ref(mu);
-    const long c0 = (long)cs * kLanes * N;
-    const double te = (al > 0.0f) ? tin / (double)al : INFINITY;
-    float z[N / EPV][EPV], wv[N / EPV][EPV];
-    load_chunk_ids<TT, N, EPV>(trow, c0, a.V, z);
+    return draw_q_chunk<TT, N, EPV>(a, trow, cs, tin, s, mu, M, Z, ztok);
+}
+
+// The request's committed draw at row j (T > 0), one wave: the residual draw
+// from [q_j - p_j]_+ if j < l (DART note eq. (3)-(4); from q_j when that mass
+// is exactly 0), else the bonus draw from q_l.  Returns the token; *lqd its
+// log q.
+template <typename TT, typename TD, int N, int EPV>
+__device__ __forceinline__ int request_draw(const VerifyArgs &a, int r, int j, int l, float s,
+                                            const UnitSum &su, float *lqd) {
+    const int lane = lane_id();
+    const int C = a.C, G = a.gamma;
+    const int u = r * a.UG + j;
+    const float usm = a.us[(size_t)r * (G + 1) + j];
+    const TT *trow = row_ptr<TT>(a.zt, r, a.tG, j, a.V);
+    const float Mt = su.Mt, Zt = su.Zt;
+    float ztok = 0.0f;
+    int tok;
+    if (j == l) {
+        const uint64_t *const sp[1] = {a.st1 + ((size_t)u * C + su.sel) * 4};
+        const bool sa[1] = {lane == 0};
+        uint64_t sv[1];
+        uint32_t so[1];
+        words_issue<1>(sp, sa, sp[0], a.tag, sv);
+        words_settle<1>(sp, sa, a.tag, a.ctl, sv, so);
+        tok = draw_q_chunk<TT, N, EPV>(a, trow, su.sel, su.tin, s, __uint_as_float(rl(so[0], 0)),
+                                       Mt, Zt, &ztok);
+    } else if (su.sel >= 0) {
+        // residual [q - p]_+: the chunk's words and both rows' logits in one
+        // round of loads, then the chunk's weights in id order
+        const TD *drow = row_ptr<TD>(a.zd, r, a.dG, j, a.V);
+        const float Md = su.Md, Zd = su.Zd;
+        const long c0 = (long)su.sel * kLanes * N;
+        const uint64_t *const sp[1] = {a.st1 + ((size_t)u * C + su.sel) * 4 + (lane & 3)};
+        const bool sa[1] = {lane < 4};
+        uint64_t sv[1];
+        uint32_t so[1];
+        words_issue<1>(sp, sa, sp[0], a.tag, sv);
+        float zt[N / EPV][EPV], zd[N / EPV][EPV];
+        load_chunk_ids<TT, N, EPV>(trow, c0, a.V, zt);
+        load_chunk_ids<TD, N, EPV>(drow, c0, a.V, zd);
+        words_settle<1>(sp, sa, a.tag, a.ctl, sv, so);
+        const float mut = __uint_as_float(rl(so[0], 0)), mud = __uint_as_float(rl(so[0], 2));
+        const PairScale ps = pair_scale(chunk_alpha(mut, Mt, Zt), chunk_alpha(mud, Md, Zd));
+        const float reft = exp_ref(mut), refd = exp_ref(mud);
+        const double te = (ps.unit > 0.0f) ? su.tin / (double)ps.unit : INFINITY;
+        float wv[N / EPV][EPV];
 #pragma unroll
-    for (int j = 0; j < N / EPV; ++j)
+        for (int jj = 0; jj < N / EPV; ++jj)
 #pragma unroll
-        for (int q = 0; q < EPV; ++q) wv[j][q] = ew(z[j][q], s, ref);
-    const int tok = draw_in_chunk_w<N, EPV>(c0, te, wv);
-    *ztok = chunk_logit<N, EPV>(c0, tok, z);
+            for (int q = 0; q < EPV; ++q) {
+                const float et = ew(zt[jj][q], s, reft) * ps.kt;
+                const float mn = __builtin_elementwise_minimum(et, ew(zd[jj][q], s, refd) * ps.kd);
+                wv[jj][q] = et - mn;
+            }
+        tok = draw_in_chunk_w<N, EPV>(c0, te, wv);
+        ztok = chunk_logit<N, EPV>(c0, tok, zt);
+    } else {
+        // no residual mass (rounding): draw from q of the same row
+        uint32_t w4[kCB][4];
+        const bool want4[4] = {true, true, false, false};
+        load_unit_words<4>(a.st1 + (size_t)u * C * 4, C, want4, a.tag, a.ctl, w4, true);
+        tok = draw_from_q<TT, N, EPV, 4>(a, trow, w4, s, Mt, Zt, usm, &ztok);
+    }
+    *lqd = (float)(((double)ztok * (double)s - (double)Mt) * kLn2 - log((double)Zt));
     return tok;
 }
 
-// ---------------------------------------------------------------------------
-// request finaliser
-// ---------------------------------------------------------------------------
-
-// Prefix survival over the unit records of request r and the final outputs.
-// Run by the wave that finished the request's last unit.  Units 0..l sit on
-// lanes i = 64 b + lane, b < 2 (l <= kMaxGamma = 64).
-__device__ __forceinline__ void finalize_request(const VerifyArgs &a, int r, int l) {
-    const int lane = lane_id();
-    const int G = a.gamma;
-    const float nan = __builtin_nanf("");
-    const uint64_t *rec0 = a.rec + (size_t)r * a.UG * kRecWords;
-    constexpr int kQ = 6;  // flags, lqx, draw, lqd, c*, Res
-    const uint64_t *p[2 * kQ];
-    bool act[2 * kQ];
-    uint32_t w[2 * kQ];
-#pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-        for (int q = 0; q < kQ; ++q) {
-            const int i = b * 64 + lane;
-            p[b * kQ + q] = rec0 + (size_t)i * kRecWords + q;
-            // c* and Res exist for positions only, log q(x) is read below A only
-            act[b * kQ + q] = i <= l && ((q != kRecCs && q != kRecRs && q != kRecLqx) || i < l);
-        }
-    await_batch<2 * kQ>(p, act, a.tag, a.ctl, w);
-    const bool bad0 = lane <= l && !(w[kRecFlags] & kFlagValid);
-    const bool bad1 = 64 + lane <= l && !(w[kQ + kRecFlags] & kFlagValid);
-    if (__ballot(bad0 || bad1)) {
-        write_invalid(a, r);
-    } else {
-        const uint64_t accm = __ballot(lane < l && (w[kRecFlags] & kFlagAccept));
-        int A = (~accm == 0) ? 64 : __builtin_ctzll(~accm);
-        if (A > l) A = l;
-        const int bA = A >> 6, lA = A & 63;
-        const int draw = (int)rl(bA ? w[kQ + kRecDraw] : w[kRecDraw], lA);
-        const float lqd = __uint_as_float(rl(bA ? w[kQ + kRecLqd] : w[kRecLqd], lA));
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
-            const int k = b * 64 + lane;
-            if (k > G) continue;
-            const int32_t t = (k < A) ? a.tokens[(size_t)r * G + k] : (k == A ? draw : -1);
-            a.out_tok[(size_t)r * (G + 1) + k] = t;
-            if (a.out_lq)
-                a.out_lq[(size_t)r * (G + 1) + k] =
-                    (k < A) ? __uint_as_float(w[b * kQ + kRecLqx]) : (k == A ? lqd : nan);
-            if (k < G) {
-                if (a.out_cs)
-                    a.out_cs[(size_t)r * G + k] = (k < l) ? __uint_as_float(w[b * kQ + kRecCs]) : nan;
-                if (a.out_rs)
-                    a.out_rs[(size_t)r * G + k] = (k < l) ? __uint_as_float(w[b * kQ + kRecRs]) : nan;
-            }
-        }
-        if (lane == 0) a.out_n[r] = A;
-    }
-    if (lane == 0) atomic_store_u32(&a.cnt_r[r], 0u);
-}
-
-// Marks unit x finished; the request's last unit finalises it.
-__device__ __forceinline__ void unit_done(const VerifyArgs &a, const Item &x) {
-    uint32_t old = 0;
-    if (lane_id() == 0) old = atomic_add_u32(&a.cnt_r[x.r], 1u);
-    if (rl(old, 0) == (uint32_t)x.l) finalize_request(a, x.r, x.l);
-}
-
-// ---------------------------------------------------------------------------
-// unit combines (one wave per unit)
-// ---------------------------------------------------------------------------
-
-// The lane's chunk words of unit x (c = 64 b + lane), in rounds of two
-// blocks in increasing chunk order, each handed to fold(w, h) for block
-// b0 + h.  They come from the statistics pass (an earlier launch).
-template <typename F>
-__device__ __forceinline__ void fold_unit_words(const VerifyArgs &a, const Item &x, bool pair,
-                                                F fold) {
-    const int lane = lane_id();
-    const bool want[4] = {true, true, pair, pair};
-    for (int b0 = 0; b0 < kCB && b0 * 64 < a.C; b0 += 2) {
-        uint32_t w[2][4];
-        load_unit_words<4, 2>(a.st1 + (size_t)x.u * a.C * 4, a.C, want, a.tag, a.ctl, w, true,
-                              b0);
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-            if ((b0 + h) * 64 + lane < a.C) fold(w[h]);
-    }
-}
-
-// T = 0: the unit's argmax test settles it (the position's accept bit and
-// c* = [argmax q == argmax p]; the bonus unit's token).
+// Row-pair mode (spec_tv_accept_rate): one wave per pair writes c* and Res.
 template <typename TT, typename TD, int N, int EPV>
-__device__ __forceinline__ void greedy_combine(const VerifyArgs &a, const Item &x) {
-    const int lane = lane_id();
-    const int G = a.gamma;
-    const bool pair = is_pair(x);
-    uint64_t *rec = a.rec + (size_t)x.u * kRecWords;
-    const float nan = __builtin_nanf("");
-    // the position's draft token, loaded early
-    int xtok = 0;
-    if (!a.tv_mode && pair) xtok = a.tokens[(size_t)x.r * G + x.i];
-    float vt = -kInf, vd = -kInf;
-    int it = 0x7fffffff, id = 0x7fffffff, bad = 0;
-    fold_unit_words(a, x, pair, [&](const uint32_t (&w)[4]) {
-        if (w[1] == 0xffffffffu) bad = 1;
-        else argmax_combine(vt, it, __uint_as_float(w[0]), (int)w[1]);
-        if (pair) {
-            if (w[3] == 0xffffffffu) bad = 1;
-            else argmax_combine(vd, id, __uint_as_float(w[2]), (int)w[3]);
-        }
-    });
-    wave_argmax(vt, it);
-    wave_argmax(vd, id);
-    bad = wave_max_i(bad);
-    const int gt = (!bad && vt > -kInf && vt < kInf && it != 0x7fffffff) ? it : -1;
-    const int gd = pair ? ((!bad && vd > -kInf && vd < kInf && id != 0x7fffffff) ? id : -1) : 0;
-    bool valid = gt >= 0 && gd >= 0;
-    if (a.tv_mode) {
-        if (!valid) {
-            write_invalid(a, x.r);
-        } else if (lane == 0) {
-            const float cv = (gt == gd) ? 1.0f : 0.0f;
-            a.out_cs[x.r] = cv;
-            if (a.out_rs) a.out_rs[x.r] = 1.0f - cv;
-        }
+__device__ __forceinline__ void pair_combine(const VerifyArgs &a, int r, UnitSum *s) {
+    Item x;
+    x.u = r;
+    x.r = r;
+    x.i = 0;
+    x.c = 0;
+    x.l = 1;
+    if (!request_ok(a, r, x.T, x.l)) {
+        write_invalid(a, r);
         return;
     }
-    bool acc = false;
-    if (pair) {
-        valid = valid && xtok >= 0 && xtok < a.V;
-        acc = xtok == gt;
+    x.s = x.T != 0.0f ? exp2_scale(x.T) : 0.0f;
+    if (x.T == 0.0f) greedy_unit(a, x, s);
+    else tv_unit(a, x, s);
+    const uint32_t fl = __builtin_amdgcn_readfirstlane(s->flags);
+    if (!(fl & kFlagValid)) {
+        write_invalid(a, r);
+    } else if (lane_id() == 0) {
+        a.out_cs[r] = s->cs;
+        if (a.out_rs) a.out_rs[r] = s->rs;
     }
-    const float cv = (gt == gd) ? 1.0f : 0.0f;
-    const uint32_t fl = (valid ? kFlagValid : 0u) | (acc ? kFlagAccept : 0u);
-    publish_n(rec, a.tag, 4, fl, __float_as_uint(0.0f), (uint32_t)gt, __float_as_uint(0.0f));
-    publish_n(rec + 4, a.tag, 2, __float_as_uint(pair ? cv : nan),
-              __float_as_uint(pair ? 1.0f - cv : nan), 0u, 0u);
-    unit_done(a, x);
 }
 
-// T > 0: the row normalisers M = max mu and Z = sum S 2^(mu - M) (per lane
-// over its chunks, then across the wave), published for the TV items and
-// the last combine; in row-pair mode also the unit's validity.
+// Launch 3.  Row-pair mode: one wave per pair.  Verification: one workgroup
+// per request.  Its waves summarise units 0..l_r (accept flags, c*, Res and
+// the chunk each row would draw from); then the first wave applies strict
+// left-to-right prefix survival (DSpark guide, "basics": A_r = the number of
+// leading accepts), makes the one draw the request commits (the residual at
+// the first rejection, or the bonus from q_l; at T = 0 the target argmax of
+// row A_r) and writes the request's outputs.  No state is shared across
+// workgroups, and every word read was written by an earlier launch.
 template <typename TT, typename TD, int N, int EPV>
-__device__ __forceinline__ void norm_fold(const VerifyArgs &a, const Item &x) {
-    const bool pair = is_pair(x);
-    OnlineZ ot, od;
-    fold_unit_words(a, x, pair, [&](const uint32_t (&w)[4]) {
-        ot.add(__uint_as_float(w[0]), __uint_as_float(w[1]));
-        if (pair) od.add(__uint_as_float(w[2]), __uint_as_float(w[3]));
-    });
-    float Mt, Zt, Md = 0.0f, Zd = 1.0f;
-    ot.reduce(Mt, Zt);
-    if (pair) od.reduce(Md, Zd);
-    publish_n(a.nrm + (size_t)x.u * 4, a.tag, 4, __float_as_uint(Mt), __float_as_uint(Zt),
-              __float_as_uint(Md), __float_as_uint(Zd));
+__global__ void __launch_bounds__(kReqBlock) combine_kernel(VerifyArgs a) {
+    a.tag = call_tag(a.ctl);
+    if (blockIdx.x == 0 && threadIdx.x == 0) a.ctl->tag_next = (a.tag + 1u) | 0x80000000u;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int lane = lane_id();
+    __shared__ UnitSum sum[kMaxGamma + 1 > kReqWaves ? kMaxGamma + 1 : kReqWaves];
     if (a.tv_mode) {
-        bool valid = finite_f(Mt) && Zt > 0.0f && finite_f(Zt);
-        if (pair) valid = valid && finite_f(Md) && Zd > 0.0f && finite_f(Zd);
-        publish_n(a.rec + (size_t)x.u * kRecWords, a.tag, 1, valid ? kFlagValid : 0u, 0u, 0u, 0u);
+        const int r = (int)blockIdx.x * kReqWaves + wave;
+        if (r < a.R) pair_combine<TT, TD, N, EPV>(a, r, &sum[wave]);
+        return;
     }
-}
-
-// All C TV partials of pair unit x (T > 0) are published: c*, Res, and the
-// residual draw if the position was rejected.
-// The bonus unit at T > 0 (target row l_r): the draw from q by inverse CDF,
-// from the unit's chunk words and normalisers.
-template <typename TT, typename TD, int N, int EPV>
-__device__ __forceinline__ void bonus_draw(const VerifyArgs &a, const Item &x) {
-    const int lane = lane_id();
-    const int C = a.C, G = a.gamma;
+    const int r = blockIdx.x;
+    Item x;
+    x.r = r;
+    x.c = 0;
+    if (!request_ok(a, r, x.T, x.l)) {
+        if (wave == 0) write_invalid(a, r);
+        return;
+    }
+    const int l = x.l, G = a.gamma;
+    x.s = x.T != 0.0f ? exp2_scale(x.T) : 0.0f;
+    for (int i = wave; i <= l; i += kReqWaves) {
+        x.i = i;
+        x.u = r * a.UG + i;
+        if (x.T == 0.0f) greedy_unit(a, x, &sum[i]);
+        else if (i < l) tv_unit(a, x, &sum[i]);
+        else bonus_unit(a, x, &sum[i]);
+    }
+    __syncthreads();
+    if (wave != 0) return;
+    // prefix survival over the summaries (units 0..l sit on lanes 64 b + lane)
+    bool bad = false, rej = false;
+    int first_rej = 64 * 2;
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+        const int i = b * 64 + lane;
+        const uint32_t fl = i <= l ? sum[i].flags : kFlagValid;
+        bad = bad || !(fl & kFlagValid);
+        rej = i < l && !(fl & kFlagAccept);
+        const uint64_t m = __ballot(rej);
+        if (m && first_rej == 128) first_rej = b * 64 + __builtin_ctzll(m);
+    }
+    if (__ballot(bad)) {
+        write_invalid(a, r);
+        return;
+    }
+    const int A = first_rej < l ? first_rej : l;
+    int tok;
+    float lqd;
+    if (x.T == 0.0f) {
+        tok = sum[A].sel;
+        lqd = 0.0f;
+    } else {
+        tok = request_draw<TT, TD, N, EPV>(a, r, A, l, x.s, sum[A], &lqd);
+    }
     const float nan = __builtin_nanf("");
-    uint64_t *rec = a.rec + (size_t)x.u * kRecWords;
-    const float usm = a.us[(size_t)x.r * (G + 1) + x.i];
-    uint32_t w[kCB][2];
-    float Mt, Zt;
-    {
-        const uint64_t *p[2 * kCB + 1];
-        bool act[2 * kCB + 1];
-        uint32_t o[2 * kCB + 1];
-#pragma unroll
-        for (int b = 0; b < kCB; ++b)
-#pragma unroll
-            for (int q = 0; q < 2; ++q) {
-                const int c = b * 64 + lane;
-                p[b * 2 + q] = a.st1 + ((size_t)x.u * C + c) * 4 + q;
-                act[b * 2 + q] = c < C;
-            }
-        p[2 * kCB] = a.nrm + (size_t)x.u * 4 + (lane & 1);
-        act[2 * kCB] = lane < 2;
-        await_batch<2 * kCB + 1>(p, act, a.tag, a.ctl, o, true);
-#pragma unroll
-        for (int b = 0; b < kCB; ++b) {
-            w[b][0] = o[b * 2];
-            w[b][1] = o[b * 2 + 1];
+    for (int k = lane; k <= G; k += 64) {
+        const int32_t t = (k < A) ? a.tokens[(size_t)r * G + k] : (k == A ? tok : -1);
+        a.out_tok[(size_t)r * (G + 1) + k] = t;
+        if (a.out_lq)
+            a.out_lq[(size_t)r * (G + 1) + k] = (k < A) ? sum[k].lqx : (k == A ? lqd : nan);
+        if (k < G) {
+            if (a.out_cs) a.out_cs[(size_t)r * G + k] = (k < l) ? sum[k].cs : nan;
+            if (a.out_rs) a.out_rs[(size_t)r * G + k] = (k < l) ? sum[k].rs : nan;
         }
-        Mt = __uint_as_float(rl(o[2 * kCB], 0));
-        Zt = __uint_as_float(rl(o[2 * kCB], 1));
     }
-    const bool valid = finite_f(Mt) && Zt > 0.0f && finite_f(Zt) && uniform_ok(usm);
-    int tok = -1;
-    float lqd = nan;
-    if (valid) {
-        const float s = x.s;
-        float ztok;
-        tok = draw_from_q<TT, N, EPV, 2>(a, row_ptr<TT>(a.zt, x.r, a.tG, x.i, a.V), w, s, Mt, Zt,
-                                         usm, &ztok);
-        lqd = (float)(((double)ztok * (double)s - (double)Mt) * kLn2 - log((double)Zt));
-    }
-    publish_n(rec, a.tag, 4, valid ? kFlagValid : 0u, 0u, (uint32_t)tok, __float_as_uint(lqd));
-    unit_done(a, x);
-}
-
-template <typename TT, typename TD, int N, int EPV>
-__device__ __forceinline__ void tv_combine(const VerifyArgs &a, const Item &x) {
-    const int lane = lane_id();
-    const int C = a.C, G = a.gamma;
-    const float nan = __builtin_nanf("");
-    uint64_t *rec = a.rec + (size_t)x.u * kRecWords;
-    // the position's draft token and uniforms, loaded early
-    float usm = 0.0f, uacc = 0.0f;
-    int xtok = 0;
-    if (!a.tv_mode) {
-        usm = a.us[(size_t)x.r * (G + 1) + x.i];
-        xtok = a.tokens[(size_t)x.r * G + x.i];
-        uacc = a.ua[(size_t)x.r * G + x.i];
-    }
-    // the unit's TV words, its record flags (row-pair mode) and its
-    // normalisers in one batch
-    uint32_t v2[kCB][2];
-    {
-        const uint64_t *p[2 * kCB + 2];
-        bool act[2 * kCB + 2];
-        uint32_t o[2 * kCB + 2];
-#pragma unroll
-        for (int b = 0; b < kCB; ++b)
-#pragma unroll
-            for (int q = 0; q < 2; ++q) {
-                const int c = b * 64 + lane;
-                p[b * 2 + q] = a.st2 + ((size_t)x.u * C + c) * 2 + q;
-                act[b * 2 + q] = c < C;
-            }
-        p[2 * kCB] = rec + kRecFlags;
-        act[2 * kCB] = a.tv_mode && lane == 0;
-        p[2 * kCB + 1] = a.nrm + (size_t)x.u * 4 + (lane & 3);
-        act[2 * kCB + 1] = lane < 4;
-        await_batch<2 * kCB + 2>(p, act, a.tag, a.ctl, o, true);
-#pragma unroll
-        for (int b = 0; b < kCB; ++b) {
-            v2[b][0] = o[b * 2];
-            v2[b][1] = o[b * 2 + 1];
-        }
-        const uint32_t fl = rl(o[2 * kCB], 0);
-        const float Mt = __uint_as_float(rl(o[2 * kCB + 1], 0));
-        const float Zt = __uint_as_float(rl(o[2 * kCB + 1], 1));
-        const float Md = __uint_as_float(rl(o[2 * kCB + 1], 2));
-        const float Zd = __uint_as_float(rl(o[2 * kCB + 1], 3));
-        double cs = 0.0, rs = 0.0;
-#pragma unroll
-        for (int b = 0; b < kCB; ++b) {
-            cs += (double)__uint_as_float(v2[b][0]);
-            rs += (double)__uint_as_float(v2[b][1]);
-        }
-        cs = wave_sum(cs);
-        rs = wave_sum(rs);
-        if (a.tv_mode) {
-            if (!(fl & kFlagValid)) {
-                write_invalid(a, x.r);
-            } else if (lane == 0) {
-                a.out_cs[x.r] = (float)cs;
-                if (a.out_rs) a.out_rs[x.r] = (float)rs;
-            }
-            return;
-        }
-        // the accept test: p and q of the draft token from the gathered logits
-        const float s = x.s;
-        const TT *trow = row_ptr<TT>(a.zt, x.r, a.tG, x.i, a.V);
-        const TD *drow = row_ptr<TD>(a.zd, x.r, a.dG, x.i, a.V);
-        const bool valid = finite_f(Mt) && Zt > 0.0f && finite_f(Zt) && finite_f(Md) &&
-                           Zd > 0.0f && finite_f(Zd) && xtok >= 0 && xtok < a.V &&
-                           uniform_ok(uacc) && uniform_ok(usm);
-        bool acc = false;
-        float lqx = nan;
-        if (valid) {
-            const float zx = load_one(trow, xtok);
-            const float dx = load_one(drow, xtok);
-            const double lq2 = (double)zx * (double)s - (double)Mt;
-            const double lp2 = (double)dx * (double)s - (double)Md;
-            const double q = exp2(lq2) / (double)Zt;
-            const double pp = exp2(lp2) / (double)Zd;
-            acc = q >= pp || (double)uacc < q / pp;
-            lqx = (float)(lq2 * kLn2 - log((double)Zt));
-        }
-        publish_n(rec, a.tag, 2, (valid ? kFlagValid : 0u) | (acc ? kFlagAccept : 0u),
-                  __float_as_uint(lqx), 0u, 0u);
-        int tok = -1;
-        float lqd = nan;
-        if (valid && !acc) {
-            float ztok = 0.0f;
-            if (rs > 0.0) {
-                // residual [q - p]_+: chunk masses, then one chunk in id order
-                double m[kCB];
-#pragma unroll
-                for (int b = 0; b < kCB; ++b) m[b] = (double)__uint_as_float(v2[b][1]);
-                double tin;
-                const int csel = select_chunk(C, (double)usm * rs, m, &tin);
-                // the chunk's words and both rows' logits in one round of loads
-                const long c0 = (long)csel * kLanes * N;
-                const uint64_t *const sp[1] = {a.st1 + ((size_t)x.u * C + csel) * 4 + (lane & 3)};
-                const bool sa[1] = {lane < 4};
-                uint64_t sv[1];
-                uint32_t so[1];
-                words_issue<1>(sp, sa, sp[0], a.tag, sv);
-                float zt[N / EPV][EPV], zd[N / EPV][EPV];
-                load_chunk_ids<TT, N, EPV>(trow, c0, a.V, zt);
-                load_chunk_ids<TD, N, EPV>(drow, c0, a.V, zd);
-                words_settle<1>(sp, sa, a.tag, a.ctl, sv, so);
-                const uint32_t s4 = so[0];
-                const float mut = __uint_as_float(rl(s4, 0)), mud = __uint_as_float(rl(s4, 2));
-                const PairScale ps =
-                    pair_scale(chunk_alpha(mut, Mt, Zt), chunk_alpha(mud, Md, Zd));
-                const float reft = exp_ref(mut), refd = exp_ref(mud);
-                const double te = (ps.unit > 0.0f) ? tin / (double)ps.unit : INFINITY;
-                float wv[N / EPV][EPV];
-#pragma unroll
-                for (int j = 0; j < N / EPV; ++j)
-#pragma unroll
-                    for (int q = 0; q < EPV; ++q) {
-                        const float et = ew(zt[j][q], s, reft) * ps.kt;
-                        const float mn =
-                            __builtin_elementwise_minimum(et, ew(zd[j][q], s, refd) * ps.kd);
-                        wv[j][q] = et - mn;
-                    }
-                tok = draw_in_chunk_w<N, EPV>(c0, te, wv);
-                ztok = chunk_logit<N, EPV>(c0, tok, zt);
-            } else {
-                // no residual mass (rounding): draw from q of the same row
-                uint32_t w4[kCB][4];
-                const bool want4[4] = {true, true, false, false};
-                load_unit_words<4>(a.st1 + (size_t)x.u * C * 4, C, want4, a.tag, a.ctl, w4, true);
-                tok = draw_from_q<TT, N, EPV, 4>(a, trow, w4, s, Mt, Zt, usm, &ztok);
-            }
-            lqd = (float)(((double)ztok * (double)s - (double)Mt) * kLn2 - log((double)Zt));
-        }
-        publish_n(rec + kRecDraw, a.tag, 4, (uint32_t)tok, __float_as_uint(lqd),
-                  __float_as_uint((float)cs), __float_as_uint((float)rs));
-    }
-    unit_done(a, x);
+    if (lane == 0) a.out_n[r] = A;
 }
 
 // ---------------------------------------------------------------------------
@@ -1298,18 +1357,10 @@ __device__ __forceinline__ bool unit_item(const VerifyArgs &a, long u, Item &x) 
 }
 
 // Kernel 1: every needed row streamed once from HBM, one item in flight per
-// wave (five waves per SIMD); per item the chunk words.  Malformed requests
-// get their outputs here.
+// wave (five waves per SIMD); per item the chunk words.
 template <typename TT, typename TD, int N, int EPV>
 __global__ void __launch_bounds__(kBlock, kStreamWaves) stats_kernel(VerifyArgs a) {
     a.tag = first_launch_tag(a.ctl);
-    if (!a.compact) {
-        for (long r = wave_index(); r < a.R; r += wave_count()) {
-            float T;
-            int l;
-            if (!request_ok(a, (int)r, T, l)) write_invalid(a, (int)r);
-        }
-    }
     extern __shared__ uint32_t lds[];
     Walker cur = make_walker(a, lds, false);
     Item x;
@@ -1373,62 +1424,40 @@ __device__ __forceinline__ uint64_t load_tv_item(const VerifyArgs &a, const Item
     const int lane = lane_id();
     const uint64_t *p = (lane < 4) ? a.st1 + ((size_t)x.u * a.C + x.c) * 4 + lane
                                    : a.nrm + (size_t)x.u * 4 + (lane & 3);
-    // a plain load: the chunk words are the statistics pass's; a normaliser
-    // word that is not current yet (an older tag) is polled coherently later
+    // plain loads: both kinds of word were written by earlier launches
     const uint64_t w = (lane < 8) ? *p : 0;
     load_item(a, x, rt, rd);
     return w;
 }
 
-// Kernel 2: the unit folds at T > 0, then the TV pass over the pair items at
-// T > 0, one item in flight per wave.
+// Kernel 2: one wave per unit at T > 0 folds launch 1's chunk words into the
+// unit's row normalisers and, for a draft position, runs the accept test.
+template <typename TT, typename TD, int N, int EPV>
+__global__ void __launch_bounds__(kBlock) fold_kernel(VerifyArgs a) {
+    a.tag = call_tag(a.ctl);
+    Item y;
+    if (unit_item(a, wave_index(), y) && y.T != 0.0f) norm_fold<TT, TD>(a, y);
+}
+
+// Kernel 3: the TV pass over the pair items at T > 0, one item in flight per
+// wave.  Every word it reads is an earlier launch's, so no wave waits for
+// another.
 template <typename TT, typename TD, int N, int EPV>
 __global__ void __launch_bounds__(kBlock, kStreamWaves) tv_kernel(VerifyArgs a) {
     a.tag = call_tag(a.ctl);
     const int lane = lane_id();
     extern __shared__ uint32_t lds[];
-    // first the folds: wave w folds units w, w + W, ... at T > 0 into their
-    // row normalisers.  They read only the statistics pass's words, so no
-    // fold waits for a TV item.
-    for (long u = wave_index(); u < (long)a.R * a.UG; u += wave_count()) {
-        Item y;
-        if (unit_item(a, u, y) && y.T != 0.0f) norm_fold<TT, TD, N, EPV>(a, y);
-    }
     Walker cur = make_walker(a, lds, true);
-    // the chunk words come from the statistics pass (earlier launch); a
-    // unit's normalisers may still be on their way from the wave folding it,
-    // so a stale tag is polled until it turns current (bounded)
-    auto words = [&](const Item &it, uint64_t w) -> uint32_t {
-        if (!__ballot(lane < 8 && (uint32_t)(w >> 32) != a.tag)) return (uint32_t)w;
-        const uint64_t *p = (lane < 4) ? a.st1 + ((size_t)it.u * a.C + it.c) * 4 + lane
-                                       : a.nrm + (size_t)it.u * 4 + (lane & 3);
-        return await_lane(p, lane < 8, a.tag, a.ctl);
-    };
     Item x;
     RawChunk<TT, N, EPV> rt;
     RawChunk<TD, N, EPV> rd;
     while (cur.next(a, x)) {
         const uint64_t w = load_tv_item(a, x, rt, rd);
-        tv_item<N>(a, x, rt, rd, words(x, w));
+        // lanes 0..3: launch 1's chunk words, 4..7: launch 2's normalisers
+        if (__ballot(lane < 8 && (uint32_t)(w >> 32) != a.tag) && lane == 0)
+            atomic_or_u32(&a.ctl->status, SPEC_DEV_SPIN_TIMEOUT);
+        tv_item<N>(a, x, rt, rd, (uint32_t)w);
     }
-}
-
-// Kernel 3: one wave per unit.  At T > 0 a position runs its accept test,
-// sums its TV words into c* and Res and makes the residual draw if rejected,
-// and the bonus unit draws from q; at T = 0 the argmax test settles the unit.
-// The wave that finishes a request's last unit writes the request's outputs.
-template <typename TT, typename TD, int N, int EPV>
-__global__ void __launch_bounds__(kBlock) tv_combine_kernel(VerifyArgs a) {
-    a.tag = call_tag(a.ctl);
-    if (blockIdx.x == 0 && threadIdx.x == 0) a.ctl->tag_next = (a.tag + 1u) | 0x80000000u;
-    Item x;
-    if (!unit_item(a, wave_index(), x)) return;
-    if (x.T == 0.0f)
-        greedy_combine<TT, TD, N, EPV>(a, x);
-    else if (is_pair(x))
-        tv_combine<TT, TD, N, EPV>(a, x);
-    else
-        bonus_draw<TT, TD, N, EPV>(a, x);
 }
 
 __global__ void zero_fill_kernel(uint32_t *p, size_t n_words) {
@@ -1449,8 +1478,8 @@ struct Plan {
     int N;           // logits per lane per row
     int C;           // chunks per row
     long units;
-    // counters first (they must read zero at launch), then tagged words
-    size_t off_cr, off_data, off_st1, off_st2, off_nrm, off_rec, bytes;
+    // tagged words after the control block
+    size_t off_st1, off_st2, off_nrm, off_rec, bytes;
 };
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -1468,47 +1497,13 @@ bool make_plan(long R, long units_per_req, long V, Plan &p) {
     p.N = N;
     p.C = (int)C;
     p.units = units;
-    p.off_cr = sizeof(Control);
-    p.off_data = round_up(p.off_cr + 4 * (size_t)R, 256);
-    p.off_st1 = p.off_data;
+    p.off_st1 = round_up(sizeof(Control), 256);
     p.off_st2 = round_up(p.off_st1 + 32 * (size_t)units * C, 256);
     p.off_nrm = round_up(p.off_st2 + 16 * (size_t)units * C, 256);
     p.off_rec = round_up(p.off_nrm + 32 * (size_t)units, 256);
     p.bytes = round_up(p.off_rec + 8 * kRecWords * (size_t)units, 256);
     return true;
 }
-
-// Host-side record of how much of each workspace is known to read zero
-// outside the control block: the whole buffer after spec_workspace_init; the
-// counter area of the last call after it (its counters end at zero, the
-// tagged words after them hold data).  A call whose counters reach past that
-// prefix first clears the difference on its stream.
-struct CleanPrefix {
-    uintptr_t ws;
-    size_t bytes;
-};
-std::mutex g_clean_mu;
-std::vector<CleanPrefix> g_clean;
-
-size_t clean_prefix(const void *ws) {
-    std::lock_guard<std::mutex> lock(g_clean_mu);
-    for (const CleanPrefix &c : g_clean)
-        if (c.ws == (uintptr_t)ws) return c.bytes;
-    return sizeof(Control);
-}
-}  // namespace
-
-void note_workspace_clean(const void *ws, size_t bytes) {
-    std::lock_guard<std::mutex> lock(g_clean_mu);
-    for (CleanPrefix &c : g_clean)
-        if (c.ws == (uintptr_t)ws) {
-            c.bytes = bytes;
-            return;
-        }
-    g_clean.push_back(CleanPrefix{(uintptr_t)ws, bytes});
-}
-
-namespace {
 
 size_t plan_bytes(long R, long upr, long V) {
     Plan p;
@@ -1580,12 +1575,12 @@ template <typename TT, typename TD, int N, int EPV>
 int launch_kernels(VerifyArgs a, hipStream_t st) {
     const void *k1 = reinterpret_cast<const void *>(&stats_kernel<TT, TD, N, EPV>);
     const void *k3 = reinterpret_cast<const void *>(&tv_kernel<TT, TD, N, EPV>);
+    const long gf = ((long)a.R * a.UG + kWaves - 1) / kWaves;
     const size_t lds = table_bytes(a);
     a.compact = lds > 0;
     const long items = (long)a.R * a.UG * a.C;
-    const long units = (long)a.R * a.UG;
     const long g1 = persistent_grid(k1, lds, items), g3 = persistent_grid(k3, lds, items);
-    const long gu = (units + kWaves - 1) / kWaves;
+    const long gc = a.tv_mode ? (a.R + kReqWaves - 1) / kReqWaves : a.R;
     a.tag = 0;  // read on the device by every launch
     static bool said = false;
     if (!said && getenv("SPECVERIFY_VERBOSE")) {
@@ -1595,8 +1590,9 @@ int launch_kernels(VerifyArgs a, hipStream_t st) {
     }
     hipLaunchKernelGGL((stats_kernel<TT, TD, N, EPV>), dim3((unsigned)g1), dim3(kBlock), lds, st,
                        a);
+    hipLaunchKernelGGL((fold_kernel<TT, TD, N, EPV>), dim3((unsigned)gf), dim3(kBlock), 0, st, a);
     hipLaunchKernelGGL((tv_kernel<TT, TD, N, EPV>), dim3((unsigned)g3), dim3(kBlock), lds, st, a);
-    hipLaunchKernelGGL((tv_combine_kernel<TT, TD, N, EPV>), dim3((unsigned)gu), dim3(kBlock), 0,
+    hipLaunchKernelGGL((combine_kernel<TT, TD, N, EPV>), dim3((unsigned)gc), dim3(kReqBlock), 0,
                        st, a);
     return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_EHIP;
 }
@@ -1623,26 +1619,11 @@ int launch(const VerifyArgs &a, int tdt, int ddt, int N, bool vec, hipStream_t s
 void bind_workspace(VerifyArgs &a, void *ws, const Plan &p) {
     char *b = (char *)ws;
     a.ctl = (Control *)b;
-    a.cnt_r = (uint32_t *)(b + p.off_cr);
     a.st1 = (uint64_t *)(b + p.off_st1);
     a.st2 = (uint64_t *)(b + p.off_st2);
     a.nrm = (uint64_t *)(b + p.off_nrm);
     a.rec = (uint64_t *)(b + p.off_rec);
     a.C = p.C;
-}
-
-// Makes the plan's counters read zero at launch (see CleanPrefix).
-int prepare_counters(void *ws, const Plan &p, hipStream_t st) {
-    const size_t have = clean_prefix(ws);
-    if (have < p.off_data) {
-        const size_t words = (p.off_data - have) / 4;
-        const size_t blocks = (words + kBlock - 1) / kBlock;
-        hipLaunchKernelGGL(zero_fill_kernel, dim3((unsigned)(blocks < 4096 ? blocks : 4096)),
-                           dim3(kBlock), 0, st, (uint32_t *)((char *)ws + have), words);
-        if (hipGetLastError() != hipSuccess) return SPEC_EHIP;
-    }
-    note_workspace_clean(ws, p.off_data);
-    return SPEC_OK;
 }
 
 }  // namespace
@@ -1684,7 +1665,6 @@ int spec_workspace_init(void *workspace, size_t workspace_bytes, void *stream) {
     hipLaunchKernelGGL(zero_fill_kernel, dim3((unsigned)(blocks < 4096 ? blocks : 4096)),
                        dim3(kBlock), 0, (hipStream_t)stream, (uint32_t *)workspace, words);
     if (hipGetLastError() != hipSuccess) return SPEC_EHIP;
-    note_workspace_clean(workspace, words * 4);
     return SPEC_OK;
 }
 
@@ -1742,7 +1722,6 @@ int spec_verify_batch(const void *target_logits, int t_dtype, const void *draft_
     a.out_rs = out_resid_mass;
     a.out_lq = out_logq;
     bind_workspace(a, workspace, p);
-    if (const int rc = prepare_counters(workspace, p, (hipStream_t)stream)) return rc;
     const bool vec = (V % 8 == 0) && aligned16(target_logits) &&
                      (gamma == 0 || aligned16(draft_logits));
     // with gamma == 0 no draft row exists; the draft type only shapes the plan
@@ -1777,7 +1756,6 @@ int spec_tv_accept_rate(const void *draft_logits, const void *target_logits, int
     a.out_cs = out_cstar;
     a.out_rs = out_resid_mass;
     bind_workspace(a, workspace, p);
-    if (const int rc = prepare_counters(workspace, p, (hipStream_t)stream)) return rc;
     const bool vec = (V % 8 == 0) && aligned16(target_logits) && aligned16(draft_logits);
     return launch(a, dtype, dtype, p.N, vec, (hipStream_t)stream);
 }
