@@ -26,6 +26,15 @@ def dev(sv):
     return torch.device("cuda:0")
 
 
+@pytest.fixture(autouse=True, params=["single", "multi"])
+def verify_path(request, monkeypatch):
+    """Every test runs on both paths: the single-pass kernel (where the call
+    qualifies; chosen with SPECVERIFY_PATH=single) and the four-launch path
+    (the default)."""
+    monkeypatch.setenv("SPECVERIFY_PATH", request.param)
+    return request.param
+
+
 def _report(name, stats):
     print(f"[{name}] exact={stats['exact']} near_ties={stats['near_ties']} "
           f"(matched anyway {stats['near_ties_matched']}) invalid={stats['invalid']} "
