@@ -17,39 +17,35 @@
 // Design.  A "unit" is one position of one request: the (target, draft) row
 // pair of position i < l_r, or the bonus target row i = l_r.  Each unit's rows
 // are cut into C chunks of 64 N logits, and an "item" is one chunk of one
-// unit.  The three launches, in stream order:
+// unit.  Four launches, in stream order:
 //  1. stats_kernel: persistent wave64s stream every needed row exactly once
 //     from HBM with 16-byte loads, the items balanced over the waves through a
 //     per-block unit table in LDS.  Per item it writes the chunk's scaled max
 //     mu and weight sum S = sum 2^(z s - mu) per row (s = log2(e) / T), or the
-//     chunk argmax at T = 0.  Malformed requests get their outputs here.
-//  2. tv_kernel: first, wave w folds units w, w + W, ... at T > 0 into their
-//     row normalisers (M = max mu, Z = sum S 2^(mu - M)); then the pair items
-//     at T > 0 again -- launch 1 has just streamed them, so they come from
-//     the 256 MB Infinity Cache when they fit -- with each chunk's weights
-//     rebuilt exactly as launch 1 made them; per item the chunk's
-//     sum min(p, q) and residual mass.  An item whose unit is still being
-//     folded waits for its normalisers.
-//  3. tv_combine_kernel: one wave per unit.  At T > 0 a position runs its
-//     accept test on the two gathered logits, sums c* and Res and, if
-//     rejected, makes the residual draw; the bonus unit makes the
-//     inverse-CDF draw from q.  At T = 0 the unit's argmax test settles it.
-// Each unit's last step arrives on its request's counter; the wave completing
-// a request applies prefix survival to the units' accept bits and writes the
-// outputs, and returns the counter to zero.
-// Words passed between waves are 64-bit (launch tag, payload) pairs written
-// and read with agent-scope atomics, so a reader never mistakes a stale word
-// (an earlier call's) for a current one.  The tag is kept on the device, so
-// that a captured graph gets a new one at every replay: launch 1 reads the
-// workspace's next tag and copies it to the call's slot, launches 2 and 3
-// read that slot, and launch 3 stores the tag after it as the next (nothing
-// of the call reads the next-tag slot after launch 1).  A wave only waits for
-// words whose writers cannot be waiting on it: the statistics words of an
-// earlier launch, the normalisers of launch 2's folds (which read only launch
-// 1's words and run before their waves take any item, on a grid that never
-// exceeds the kernel's resident capacity), and the records of the waves
-// whose counter arrivals made it the request's last.  Every wait is bounded
-// and raises SPEC_DEV_SPIN_TIMEOUT rather than spin forever.
+//     chunk argmax at T = 0.
+//  2. fold_kernel: one wave per draft position at T > 0 folds the chunk words
+//     into the row normalisers (M = max mu, Z = sum S 2^(mu - M)) and runs the
+//     accept test on the two gathered logits of the draft token.
+//  3. tv_kernel: the pair items at T > 0 again -- launch 1 has just streamed
+//     them, so they come from the 256 MB Infinity Cache when they fit -- with
+//     each chunk's weights rebuilt exactly as launch 1 made them; per item
+//     the chunk's sum min(p, q) and residual mass sum [q - p]_+.
+//  4. combine_kernel: one workgroup per request.  Its waves summarise the
+//     request's units (accept flags, c*, Res, the chunk each row would draw
+//     from); prefix survival then fixes the number of accepted drafts, and
+//     the workgroup makes the one draw the request commits (the residual at
+//     the first rejection, or the bonus from q; at T = 0 the target argmax)
+//     and writes the outputs.  Row-pair mode (c* and Res only) takes one wave
+//     per pair instead.
+// No launch waits on a word of its own launch: each reads only what earlier
+// launches of the call wrote.  Those words are 64-bit (launch tag, payload)
+// pairs, so a reader never mistakes a stale word (an earlier call's, say
+// after a launch failed) for a current one.  The tag is kept on the device,
+// so that a captured graph gets a new one at every replay: launch 1 reads the
+// workspace's next tag and copies it to the call's slot, the later launches
+// read that slot, and launch 4 stores the tag after it as the next.  A word
+// that is still stale when read raises SPEC_DEV_SPIN_TIMEOUT after a bounded
+// re-poll instead of being used.
 #include <math.h>
 #include <stddef.h>
 #include <stdio.h>
@@ -74,24 +70,6 @@ constexpr int kStreamWaves = 5;
 enum : int { kRecFlags = 0, kRecLqx = 1, kRecDraw = 2, kRecLqd = 3, kRecCs = 4, kRecRs = 5,
              kRecWords = 8 };
 constexpr uint32_t kFlagValid = 1u, kFlagAccept = 2u;
-
-// Division of n < 2^31 by a fixed d (1 <= d <= 1024) by a multiply-high and
-// a shift: m = floor(2^(31 + l) / d) + 1 with l = ceil(log2 d) (the
-// round-up method for 31-bit dividends).
-struct FastDiv {
-    uint32_t d, m, l;
-};
-inline FastDiv make_fastdiv(uint32_t d) {
-    FastDiv f;
-    f.d = d;
-    f.l = 0;
-    while ((1u << f.l) < d) ++f.l;
-    f.m = d == 1 ? 0u : (uint32_t)((1ull << (31 + f.l)) / d + 1);
-    return f;
-}
-__device__ __forceinline__ uint32_t fdiv(uint32_t n, const FastDiv &f) {
-    return f.d == 1 ? n : __umulhi(n, f.m) >> (f.l - 1);
-}
 
 struct VerifyArgs {
     const void *zt;          // target logits
@@ -118,12 +96,6 @@ struct VerifyArgs {
     uint64_t *st2;           // [units][C][2] chunk sum min(p, q), residual mass
     uint64_t *nrm;           // [units][4] unit normalisers
     uint64_t *rec;           // [units][kRecWords] unit records
-    uint64_t *part;          // [units * C][4] single pass: per-tile partial normalisers
-    uint64_t *dump;          // single pass: per-wave sink of discarded stores
-    FastDiv divC, divCh;     // single pass: division by C and by ceil(C / 2)
-    uint32_t *tvbase;        // [R] single pass: TV positions of the requests before r
-    int single;              // the call takes the single pass
-    int spS;                 // single pass: stream waves per workgroup (items per tile)
 };
 
 // ---------------------------------------------------------------------------
@@ -438,20 +410,6 @@ struct RawChunk {
         for (int j = 0; j < N / EPV; ++j) {
             const uint32_t e = (j * kLanes + lane) * EPV;
             load_vec(base, (int)e < rem ? e : 0u, j);
-        }
-    }
-
-    // As load(), except that a vector past the row end reads `pad` (16 bytes
-    // of -inf logits) instead, so the words need no fix().
-    __device__ __forceinline__ void load_padded(const T *row, long c0, int V, const T *pad) {
-        const T *base = row + c0;
-        const uint32_t lane = (uint32_t)lane_id();
-        const long left = (long)V - c0;
-        rem = kLanes * N;
-#pragma unroll
-        for (int j = 0; j < N / EPV; ++j) {
-            const uint32_t e = (j * kLanes + lane) * EPV;
-            load_vec((long)e < left ? base : pad, (long)e < left ? e : 0u, j);
         }
     }
 
@@ -989,42 +947,6 @@ __device__ __forceinline__ void norm_fold(const VerifyArgs &a, const Item &x) {
     if (!a.tv_mode) accept_record<TT, TD>(a, x, Mt, Zt, Md, Zd);
 }
 
-// ---------------------------------------------------------------------------
-// normalisers from the single pass's per-tile partials
-// ---------------------------------------------------------------------------
-
-// Row normalisers of one TV unit, as the stream waves use them.
-struct SpNorm {
-    RowNorm t, d;
-};
-
-// Fold of one unit's partials, partial e in lane e (lanes with `in`), in the
-// wave's fixed reduction order, so that every workgroup gets the same bits.
-__device__ __forceinline__ SpNorm sp_fold_partials(bool in, const uint32_t (&v)[4]) {
-    OnlineZ ot, od;
-    if (in) {
-        ot.add(__uint_as_float(v[0]), __uint_as_float(v[1]));
-        od.add(__uint_as_float(v[2]), __uint_as_float(v[3]));
-    }
-    float Mt, Zt, Md, Zd;
-    ot.reduce(Mt, Zt);
-    od.reduce(Md, Zd);
-    SpNorm n;
-    n.t = row_norm(Mt, Zt);
-    n.d = row_norm(Md, Zd);
-    return n;
-}
-
-// First item of partial e of the TV unit whose first item is f: f itself, then
-// the start of every later tile (S items) the unit touches.
-__device__ __forceinline__ uint32_t sp_part_item(uint32_t f, uint32_t e, uint32_t S) {
-    return e == 0 ? f : (f / S + e) * S;
-}
-// Number of partials of the TV unit whose first item is f (C items).
-__device__ __forceinline__ uint32_t sp_nparts(uint32_t f, uint32_t C, uint32_t S) {
-    return (f + C - 1u) / S - f / S + 1u;
-}
-
 // Per-unit summary of a request in launch 3 (shared memory), written by
 // lane 0 of the unit's wave.
 struct UnitSum {
@@ -1079,27 +1001,20 @@ __device__ __forceinline__ void greedy_unit(const VerifyArgs &a, const Item &x, 
 }
 
 // T > 0 draft position: c* and Res from the TV pass's chunk words, the
-// position's row normalisers and accept test, and the chunk of the residual
-// draw [q - p]_+ should this row be the request's first rejection (DART note
-// eq. (3)-(4)).  Four-launch path: normalisers and accept record from the
-// fold launch.  Single pass: normalisers folded here from the per-tile
-// partials (the same fold as the coordinator's, so the same bits), and the
-// accept test on the gathered logits.
-template <typename TT, typename TD>
+// position's normalisers and accept record from the fold launch, and the
+// chunk of the residual draw [q - p]_+ should this row be the request's first
+// rejection (DART note eq. (3)-(4)).
 __device__ __forceinline__ void tv_unit(const VerifyArgs &a, const Item &x, UnitSum *s) {
     const int lane = lane_id();
     const int C = a.C, G = a.gamma;
     float usm = 0.0f, uacc = 0.0f;
-    int xtok = 0;
     if (!a.tv_mode) {
         usm = a.us[(size_t)x.r * (G + 1) + x.i];
         uacc = a.ua[(size_t)x.r * G + x.i];
-        xtok = a.tokens[(size_t)x.r * G + x.i];
     }
-    constexpr int K = 2 * kCB + 4;
-    const uint64_t *p[K];
-    bool act[K];
-    uint32_t o[K];
+    const uint64_t *p[2 * kCB + 1];
+    bool act[2 * kCB + 1];
+    uint32_t o[2 * kCB + 1];
 #pragma unroll
     for (int b = 0; b < kCB; ++b)
 #pragma unroll
@@ -1108,44 +1023,13 @@ __device__ __forceinline__ void tv_unit(const VerifyArgs &a, const Item &x, Unit
             p[b * 2 + q] = a.st2 + ((size_t)x.u * C + c) * 2 + q;
             act[b * 2 + q] = c < C;
         }
-    uint32_t np = 0;
-    if (a.single) {
-        // partial e of the unit in lane e
-        const uint32_t S = (uint32_t)a.spS;
-        const uint32_t f = (a.tvbase[x.r] + (uint32_t)x.i) * (uint32_t)C;
-        np = sp_nparts(f, (uint32_t)C, S);
-        const uint32_t ke = sp_part_item(f, (uint32_t)lane < np ? (uint32_t)lane : 0u, S);
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            p[2 * kCB + w] = a.part + (size_t)ke * 4 + w;
-            act[2 * kCB + w] = (uint32_t)lane < np;
-        }
-    } else {
-        // lanes 0..3: normalisers; 4, 5: the fold's record (flags, log q(x))
-        p[2 * kCB] = (lane < 4) ? a.nrm + (size_t)x.u * 4 + lane
-                                : a.rec + (size_t)x.u * kRecWords + (lane & 1);
-        act[2 * kCB] = lane < 4 || (!a.tv_mode && lane < 6);
-#pragma unroll
-        for (int w = 1; w < 4; ++w) {
-            p[2 * kCB + w] = p[2 * kCB];
-            act[2 * kCB + w] = false;
-        }
-    }
-    await_batch<K>(p, act, a.tag, a.ctl, o, true);
-    float Mt, Zt, Md, Zd;
-    if (a.single) {
-        const uint32_t vw[4] = {o[2 * kCB], o[2 * kCB + 1], o[2 * kCB + 2], o[2 * kCB + 3]};
-        const SpNorm n = sp_fold_partials((uint32_t)lane < np, vw);
-        Mt = n.t.M;
-        Zt = n.t.Z;
-        Md = n.d.M;
-        Zd = n.d.Z;
-    } else {
-        Mt = __uint_as_float(rl(o[2 * kCB], 0));
-        Zt = __uint_as_float(rl(o[2 * kCB], 1));
-        Md = __uint_as_float(rl(o[2 * kCB], 2));
-        Zd = __uint_as_float(rl(o[2 * kCB], 3));
-    }
+    // lanes 0..3: normalisers; 4, 5: the fold's record (flags, log q(x))
+    p[2 * kCB] = (lane < 4) ? a.nrm + (size_t)x.u * 4 + lane
+                            : a.rec + (size_t)x.u * kRecWords + (lane & 1);
+    act[2 * kCB] = lane < 4 || (!a.tv_mode && lane < 6);
+    await_batch<2 * kCB + 1>(p, act, a.tag, a.ctl, o, true);
+    const float Mt = __uint_as_float(rl(o[2 * kCB], 0)), Zt = __uint_as_float(rl(o[2 * kCB], 1));
+    const float Md = __uint_as_float(rl(o[2 * kCB], 2)), Zd = __uint_as_float(rl(o[2 * kCB], 3));
     double cs = 0.0, rs = 0.0, m[kCB];
 #pragma unroll
     for (int b = 0; b < kCB; ++b) {
@@ -1159,15 +1043,6 @@ __device__ __forceinline__ void tv_unit(const VerifyArgs &a, const Item &x, Unit
     float lqx = 0.0f;
     if (a.tv_mode) {
         valid = norms_ok(Mt, Zt) && norms_ok(Md, Zd);
-    } else if (a.single) {
-        valid = norms_ok(Mt, Zt) && norms_ok(Md, Zd) && xtok >= 0 && xtok < a.V &&
-                uniform_ok(uacc) && uniform_ok(usm);
-        lqx = __builtin_nanf("");
-        if (valid) {
-            const float zx = load_one(row_ptr<TT>(a.zt, x.r, a.tG, x.i, a.V), xtok);
-            const float dx = load_one(row_ptr<TD>(a.zd, x.r, a.dG, x.i, a.V), xtok);
-            acc = accept_eval(zx, dx, x.s, Mt, Zt, Md, Zd, uacc, &lqx);
-        }
     } else {
         const uint32_t fl = rl(o[2 * kCB], 4);
         lqx = __uint_as_float(rl(o[2 * kCB], 5));
@@ -1374,7 +1249,7 @@ __device__ __forceinline__ void pair_combine(const VerifyArgs &a, int r, UnitSum
     }
     x.s = x.T != 0.0f ? exp2_scale(x.T) : 0.0f;
     if (x.T == 0.0f) greedy_unit(a, x, s);
-    else tv_unit<TT, TD>(a, x, s);
+    else tv_unit(a, x, s);
     const uint32_t fl = __builtin_amdgcn_readfirstlane(s->flags);
     if (!(fl & kFlagValid)) {
         write_invalid(a, r);
@@ -1418,7 +1293,7 @@ __global__ void __launch_bounds__(kReqBlock) combine_kernel(VerifyArgs a) {
         x.i = i;
         x.u = r * a.UG + i;
         if (x.T == 0.0f) greedy_unit(a, x, &sum[i]);
-        else if (i < l) tv_unit<TT, TD>(a, x, &sum[i]);
+        else if (i < l) tv_unit(a, x, &sum[i]);
         else bonus_unit(a, x, &sum[i]);
     }
     __syncthreads();
@@ -1573,32 +1448,6 @@ __device__ __forceinline__ void tv_sums(const RT &rt, const RD &rd, float s, flo
     *cres = fmax((double)ps.unit * ((double)ssum - (double)smin), 0.0);
 }
 
-// The same TV sums from the chunk's weights e_t, e_d as the statistics made
-// them (so the same bits as tv_sums on the logits).
-template <int N>
-__device__ __forceinline__ void tv_sums_w(const float (&et)[N], const float (&ed)[N], float mut,
-                                          float St, float mud, const RowNorm &nt,
-                                          const RowNorm &nd, double *cmin, double *cres) {
-    const PairScale ps = pair_scale(mut, mud, nt, nd);
-    float acc = 0.0f, ssum;
-    if (ps.kt == 1.0f) {
-#pragma unroll
-        for (int k = 0; k < N; ++k) acc += __builtin_elementwise_minimum(et[k], ed[k] * ps.kd);
-        ssum = St;
-    } else {
-        float ek[N];
-#pragma unroll
-        for (int k = 0; k < N; ++k) {
-            ek[k] = et[k] * ps.kt;
-            acc += __builtin_elementwise_minimum(ek[k], ed[k]);
-        }
-        ssum = wave_sum_f(lane_sum<N>(ek));
-    }
-    const float smin = wave_sum_f(acc);
-    *cmin = (double)ps.unit * (double)smin;
-    *cres = fmax((double)ps.unit * ((double)ssum - (double)smin), 0.0);
-}
-
 // TV of pair item x at T > 0 (chunk re-read, from the Infinity Cache when the
 // rows fit there), with the chunk's words and the unit's normalisers from the
 // earlier launches (w8: lanes 0..3 the chunk's words, 4..7 the normalisers).
@@ -1661,629 +1510,6 @@ __global__ void __launch_bounds__(kBlock, kStreamWaves) tv_kernel(VerifyArgs a) 
     }
 }
 
-// ===========================================================================
-// single-pass path (target and draft logits of one dtype)
-// ===========================================================================
-//
-// One persistent kernel streams every needed row once.  An item is two row
-// chunks ("halves") of 64 kSpN logits:
-//   * a TV item: chunk c of the target and of the draft row of a draft
-//     position at T > 0 (these come first, position by position);
-//   * a T = 0 position's target and draft chunk c;
-//   * chunks 2m and 2m + 1 of a target row l_r (the bonus row).
-// Item k goes to stream wave k mod S of workgroup (k / S) mod G in round
-// k / (S G), so a workgroup's S items of one round are consecutive: a tile.
-// Every workgroup has S stream waves and one coordinator wave.
-//
-// A stream wave keeps its loads kSpAhead rounds ahead in a register ring.  In
-// round j it publishes the chunk words of its item (as the statistics launch
-// does), hands them to the coordinator in LDS and keeps a TV item's logits in
-// LDS; kSpLag rounds later, with the unit's row normalisers from the
-// coordinator, it publishes the TV sums of the held chunks.
-//
-// The coordinator folds, once a tile's statistics are in, each TV unit's run
-// of chunks in the tile into a partial (M, Z per row), lane by lane in item
-// order, and publishes it at the run's first item.  One round later it
-// gathers every partial of each TV unit of that tile (one per tile the unit
-// touches), folds them in item order into the unit's normalisers and hands
-// them to the stream waves; the workgroup holding the unit's first item also
-// publishes them and runs the accept test.  A partial still missing after a
-// bounded wait (its workgroup not resident) is made by the coordinator itself
-// from the logits with the same arithmetic, so no workgroup depends on
-// another being scheduled, and every fold of a unit gives the same bits.
-
-constexpr int kSpN = 16;         // logits per lane of a row chunk (chunk = 1024 logits)
-constexpr int kSpLag = 2;        // rounds from an item's statistics to its TV sums
-constexpr int kSpMaxUnits = 2048;            // unit table entries (LDS)
-constexpr uint32_t kSpHelpPolls = 64;        // polls of a missing partial before making it
-
-// Per element type: kS stream waves per workgroup and kAhead rounds of loads
-// in flight per wave, about 128 KB per compute unit.  A held TV item is its
-// fp32 chunk weights (8 KB).  bf16: 7 + 1 waves, two per SIMD (256 registers
-// each), two rounds of held items in 112 KB of LDS; fp32: 6 + 1 waves, 96 KB.
-template <typename T> struct SpCfg;
-template <> struct SpCfg<uint16_t> {
-    static constexpr int kS = 7, kAhead = 4;
-};
-template <> struct SpCfg<float> {
-    static constexpr int kS = 6, kAhead = 3;
-};
-
-enum : int { kSpTV = 0, kSpGreedy = 1, kSpRow = 2, kSpNone = 3 };
-
-// 16 bytes of -inf logits per element type: the single pass loads them for the
-// slots of a chunk past the row end.
-__device__ uint32_t kNegInfBf16[4] = {0xff80ff80u, 0xff80ff80u, 0xff80ff80u, 0xff80ff80u};
-__device__ uint32_t kNegInfF32[4] = {0xff800000u, 0xff800000u, 0xff800000u, 0xff800000u};
-template <typename T> __device__ __forceinline__ const T *neg_inf_pad();
-template <> __device__ __forceinline__ const uint16_t *neg_inf_pad<uint16_t>() {
-    return reinterpret_cast<const uint16_t *>(kNegInfBf16);
-}
-template <> __device__ __forceinline__ const float *neg_inf_pad<float>() {
-    return reinterpret_cast<const float *>(kNegInfF32);
-}
-
-// Item counts of the single pass (the same in every workgroup).
-struct SpGrid {
-    uint32_t n_tv, n_gr, n_row;   // units per group (TV positions, T = 0 positions, rows)
-    uint32_t i_tv, i_gr, items;   // item boundaries of the groups
-    uint32_t ch;                  // items per row unit: ceil(C / 2)
-    uint32_t rounds;
-};
-
-struct SpItem {
-    int kind, u, r, i, c0, c1;    // c1 < 0: the second half is unused
-    float T, s;
-};
-
-// Unit table in LDS: TV positions, then T = 0 positions, then target rows l_r,
-// each entry r << 8 | i, with the request's exp2 scale log2(e)/T (0 at T = 0)
-// in tab_s (built by every workgroup from the request arrays), so that the
-// streaming loop reads no request data from global memory.
-__device__ __forceinline__ SpGrid sp_build_table(const VerifyArgs &a, uint32_t *tab,
-                                                 float *tab_s, uint32_t (*scr)[16]) {
-    const int nt = blockDim.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int nw = nt >> 6;
-    const int K = (a.R + nt - 1) / nt;
-    const int r0 = tid * K, r1 = min(r0 + K, a.R);
-    uint32_t c[3] = {0u, 0u, 0u};
-    for (int r = r0; r < r1; ++r) {
-        float T;
-        int l;
-        if (!request_ok(a, r, T, l)) continue;
-        if (T != 0.0f) c[0] += (uint32_t)l;
-        else c[1] += (uint32_t)l;
-        if (!a.tv_mode) c[2] += 1u;
-    }
-    uint32_t incl[3], base[3], tot[3];
-#pragma unroll
-    for (int q = 0; q < 3; ++q) {
-        incl[q] = c[q];
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const uint32_t n = __shfl_up(incl[q], o, 64);
-            if (lane >= o) incl[q] += n;
-        }
-        if (lane == 63) scr[q][wave] = incl[q];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int q = 0; q < 3; ++q) {
-        base[q] = 0u;
-        tot[q] = 0u;
-        for (int w = 0; w < nw; ++w) {
-            if (w < wave) base[q] += scr[q][w];
-            tot[q] += scr[q][w];
-        }
-        base[q] += incl[q] - c[q];
-    }
-    if (blockIdx.x == 0) {
-        // TV positions of the requests before r, for the combine launch
-        uint32_t tb = base[0];
-        for (int r = r0; r < r1; ++r) {
-            float T;
-            int l;
-            a.tvbase[r] = tb;
-            if (request_ok(a, r, T, l) && T != 0.0f) tb += (uint32_t)l;
-        }
-    }
-    for (int r = r0; r < r1; ++r) {
-        float T;
-        int l;
-        if (!request_ok(a, r, T, l)) continue;
-        const uint32_t e = (uint32_t)r << 8;
-        const float s = T != 0.0f ? exp2_scale(T) : 0.0f;
-        if (T != 0.0f) {
-            for (int i = 0; i < l; ++i) {
-                tab_s[base[0]] = s;
-                tab[base[0]++] = e | (uint32_t)i;
-            }
-        } else {
-            for (int i = 0; i < l; ++i) {
-                tab_s[tot[0] + base[1]] = s;
-                tab[tot[0] + base[1]++] = e | (uint32_t)i;
-            }
-        }
-        if (!a.tv_mode) {
-            tab_s[tot[0] + tot[1] + base[2]] = s;
-            tab[tot[0] + tot[1] + base[2]++] = e | (uint32_t)l;
-        }
-    }
-    SpGrid g;
-    g.n_tv = tot[0];
-    g.n_gr = tot[1];
-    g.n_row = tot[2];
-    g.ch = ((uint32_t)a.C + 1u) / 2u;
-    g.i_tv = g.n_tv * (uint32_t)a.C;
-    g.i_gr = g.i_tv + g.n_gr * (uint32_t)a.C;
-    g.items = g.i_gr + g.n_row * g.ch;
-    return g;
-}
-
-// Item k (any k >= 0; past the end an unused item).  x.T is 0 at T = 0 and 1
-// otherwise (the statistics only ask whether T is 0); x.s = log2(e)/T.
-__device__ __forceinline__ SpItem sp_item(const VerifyArgs &a, const SpGrid &g,
-                                          const uint32_t *tab, const float *tab_s, uint32_t k) {
-    SpItem x;
-    const uint32_t C = (uint32_t)a.C;
-    uint32_t q = 0u;
-    if (k < g.i_tv) {
-        q = fdiv(k, a.divC);
-        x.kind = kSpTV;
-        x.c0 = x.c1 = (int)(k - q * C);
-    } else if (k < g.i_gr) {
-        const uint32_t k2 = k - g.i_tv, q2 = fdiv(k2, a.divC);
-        x.kind = kSpGreedy;
-        x.c0 = x.c1 = (int)(k2 - q2 * C);
-        q = g.n_tv + q2;
-    } else if (k < g.items) {
-        const uint32_t k2 = k - g.i_gr, q2 = fdiv(k2, a.divCh), m = k2 - q2 * g.ch;
-        x.kind = kSpRow;
-        x.c0 = (int)(2u * m);
-        x.c1 = (2u * m + 1u < C) ? (int)(2u * m + 1u) : -1;
-        q = g.n_tv + g.n_gr + q2;
-    } else {
-        x.kind = kSpNone;
-        x.c0 = 0;
-        x.c1 = -1;
-    }
-    const uint32_t e = __builtin_amdgcn_readfirstlane(x.kind == kSpNone ? 0u : tab[q]);
-    x.s = __uint_as_float(
-        __builtin_amdgcn_readfirstlane(x.kind == kSpNone ? 0u : __float_as_uint(tab_s[q])));
-    x.T = x.s != 0.0f ? 1.0f : 0.0f;
-    x.r = (int)(e >> 8);
-    x.i = (int)(e & 255u);
-    x.u = x.r * a.UG + x.i;
-    return x;
-}
-
-// Issues item x's loads (no branch: the slots past the row end and an unused
-// half read the -inf pad).
-template <typename T, int EPV>
-__device__ __forceinline__ void sp_issue(const VerifyArgs &a, const SpItem &x,
-                                         RawChunk<T, kSpN, EPV> &h0, RawChunk<T, kSpN, EPV> &h1) {
-    const bool none = x.kind == kSpNone;
-    const T *t0 = row_ptr<T>(a.zt, x.r, a.tG, x.i, a.V);
-    const T *t1 = (x.kind == kSpRow) ? t0 : row_ptr<T>(a.zd, x.r, a.dG, x.i, a.V);
-    const bool u1 = none || x.c1 < 0;
-    const T *pad = neg_inf_pad<T>();
-    h0.load_padded(none ? pad : t0, none ? 0 : (long)x.c0 * kLanes * kSpN, none ? 0 : a.V, pad);
-    h1.load_padded(u1 ? pad : t1, u1 ? 0 : (long)x.c1 * kLanes * kSpN, u1 ? 0 : a.V, pad);
-}
-
-// Chunk words of one half: (scaled max mu, weight sum S) at T > 0, or
-// (max value, its lowest id; 0xffffffff after a NaN) at T = 0.
-template <int N, int EPV, typename RC>
-__device__ __forceinline__ void half_words(const RC &rc, float T, float s, long c0, uint32_t &w0,
-                                           uint32_t &w1, float (&e)[N]) {
-    if (T == 0.0f) {
-        float bv;
-        int bi, bad;
-        chunk_argmax<N, EPV>(rc, c0, bv, bi, bad);
-        w0 = __float_as_uint(bv);
-        w1 = bad ? 0xffffffffu : (uint32_t)bi;
-#pragma unroll
-        for (int k = 0; k < N; ++k) e[k] = 0.0f;
-    } else {
-        float mu, S;
-        chunk_exp<N>(rc, s, e, mu, S);
-        w0 = __float_as_uint(mu);
-        w1 = __float_as_uint(S);
-    }
-}
-
-// The four chunk words of item x (loaded by sp_issue): words 0, 1 of half 0,
-// words 2, 3 of half 1, and (T > 0) the chunk weights of both halves.  Every
-// wave computing them (stream or coordinator) runs this function, so they
-// carry the same bits.
-template <typename T, int EPV>
-__device__ __forceinline__ void sp_item_words(const SpItem &x, RawChunk<T, kSpN, EPV> &h0,
-                                              RawChunk<T, kSpN, EPV> &h1, uint32_t (&w)[4],
-                                              float (&e0)[kSpN], float (&e1)[kSpN]) {
-    half_words<kSpN, EPV>(h0, x.T, x.s, (long)x.c0 * kLanes * kSpN, w[0], w[1], e0);
-    half_words<kSpN, EPV>(h1, x.T, x.s, (long)(x.c1 < 0 ? 0 : x.c1) * kLanes * kSpN, w[2], w[3],
-                          e1);
-}
-
-// The sink of a discarded store of this wave.
-__device__ __forceinline__ uint64_t *sp_dump(const VerifyArgs &a) {
-    return a.dump + ((blockIdx.x & 255u) * 16u + (threadIdx.x >> 6)) * 4u;
-}
-
-// Lane q of the result holds w[q & 3] (w wave-uniform): two selects on the
-// lane's bits, so that no lane indexes the array.
-__device__ __forceinline__ uint32_t lanes4(const uint32_t (&w)[4]) {
-    const int lane = lane_id();
-    const uint32_t lo = (lane & 1) ? w[1] : w[0];
-    const uint32_t hi = (lane & 1) ? w[3] : w[2];
-    return (lane & 2) ? hi : lo;
-}
-
-// Publishes item x's chunk words (v: lane q holds word q): a position's four
-// at its chunk, a row item's two per chunk.
-__device__ __forceinline__ void sp_publish_words(const VerifyArgs &a, const SpItem &x,
-                                                 uint32_t v) {
-    const int lane = lane_id();
-    const bool second = x.kind == kSpRow && lane >= 2;
-    const int c = second ? x.c1 : x.c0;
-    const int q = second ? lane - 2 : lane;
-    const bool dumped = x.kind == kSpNone || (second && x.c1 < 0);
-    uint64_t *p = dumped ? sp_dump(a) + (lane & 3) : a.st1 + ((size_t)x.u * a.C + c) * 4 + q;
-    if (lane < 4) st_word(p, a.tag, v);
-}
-
-// Partial normalisers of the lanes in `in` (lane w holding the words of item
-// tile * S + w): M = max mu, Z = sum S 2^(mu - M) per row, in the wave's fixed
-// reduction order.
-__device__ __forceinline__ void sp_fold_lanes(bool in, const uint32_t (&w)[4], float &Mt,
-                                              float &Zt, float &Md, float &Zd) {
-    OnlineZ ot, od;
-    if (in) {
-        ot.add(__uint_as_float(w[0]), __uint_as_float(w[1]));
-        od.add(__uint_as_float(w[2]), __uint_as_float(w[3]));
-    }
-    ot.reduce(Mt, Zt);
-    od.reduce(Md, Zd);
-}
-
-// The run of TV unit q's items in the tile holding item k0 (k0 the run's
-// first item): [k0, end).
-__device__ __forceinline__ uint32_t sp_run_end(const VerifyArgs &a, uint32_t q, uint32_t k0,
-                                               int S) {
-    const uint32_t tile_end = (k0 / (uint32_t)S + 1u) * (uint32_t)S;
-    const uint32_t unit_end = (q + 1u) * (uint32_t)a.C;
-    return tile_end < unit_end ? tile_end : unit_end;
-}
-
-// The coordinator's own statistics of TV unit q's run [k0, end), when the
-// workgroup that streams it has not published it: the run's items are loaded
-// and their words made exactly as a stream wave makes them, each in the lane
-// of its place in the tile, and folded as the tile's coordinator folds them.
-template <typename T, int EPV, int S>
-__device__ __forceinline__ void sp_make_partial(const VerifyArgs &a, const SpGrid &g,
-                                             const uint32_t *tab, const float *tab_s,
-                                             uint32_t k0, uint32_t end, float (&P)[4]) {
-    const int lane = lane_id();
-    const uint32_t tile0 = k0 / (uint32_t)S * (uint32_t)S;
-    uint32_t mine[4] = {0u, 0u, 0u, 0u};
-    for (uint32_t k = k0; k < end; ++k) {
-        const SpItem x = sp_item(a, g, tab, tab_s, k);
-        RawChunk<T, kSpN, EPV> h0, h1;
-        sp_issue<T, EPV>(a, x, h0, h1);
-        uint32_t w[4];
-        float e0[kSpN], e1[kSpN];
-        sp_item_words<T, EPV>(x, h0, h1, w, e0, e1);
-        if ((uint32_t)lane == k - tile0) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) mine[q] = w[q];
-        }
-    }
-    const bool in = (uint32_t)lane >= k0 - tile0 && (uint32_t)lane < end - tile0;
-    sp_fold_lanes(in, mine, P[0], P[1], P[2], P[3]);
-}
-
-// Loads of a batch of partials (units q .. qe - 1 of a tile, at most 64
-// partials, partial e of a unit in lane off_unit + e), issued ahead of their
-// use.
-struct SpFetch {
-    uint64_t v[4];
-    uint32_t ke;
-    int ui;
-    uint32_t q, qe;
-};
-
-template <int S>
-__device__ __forceinline__ SpFetch sp_fetch_issue(const VerifyArgs &a, uint32_t q, uint32_t qb) {
-    const int lane = lane_id();
-    const uint32_t C = (uint32_t)a.C;
-    SpFetch f;
-    f.q = q;
-    uint32_t qe = q, used = 0;
-    // np <= 64 for C <= 256 and S >= 6
-    while (qe <= qb && (qe == q || used + sp_nparts(qe * C, C, S) <= 64u))
-        used += sp_nparts((qe++) * C, C, S);
-    f.qe = qe;
-    f.ke = 0;
-    f.ui = -1;
-    uint32_t off = 0;
-    for (uint32_t u = q; u < qe; ++u) {
-        const uint32_t np = sp_nparts(u * C, C, S);
-        if ((uint32_t)lane >= off && (uint32_t)lane < off + np) {
-            f.ui = (int)(u - q);
-            f.ke = sp_part_item(u * C, (uint32_t)lane - off, (uint32_t)S);
-        }
-        off += np;
-    }
-    const bool act = f.ui >= 0;
-    const uint64_t *pp = a.part + (size_t)f.ke * 4;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) f.v[w] = act ? ld_word(pp + w) : ((uint64_t)a.tag << 32);
-    return f;
-}
-
-// Completes a batch: partials not current yet are polled; one still missing
-// after a bounded wait (its workgroup not resident) is made here and
-// published.  Each unit's partials are then moved to lanes 0.. and folded
-// into out[u - qa].
-template <typename T, int EPV, int S>
-__device__ __forceinline__ void sp_fetch_finish(const VerifyArgs &a, const SpGrid &g,
-                                                const uint32_t *tab, const float *tab_s,
-                                                SpFetch &f, uint32_t qa, SpNorm *out) {
-    const int lane = lane_id();
-    const uint32_t C = (uint32_t)a.C;
-    const bool act = f.ui >= 0;
-    const uint64_t *pp = a.part + (size_t)f.ke * 4;
-    for (uint32_t polls = 0;; ++polls) {
-        bool stale = false;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) stale = stale || (uint32_t)(f.v[w] >> 32) != a.tag;
-        const uint64_t sm = __ballot(stale);
-        if (!sm) break;
-        if (polls >= kSpHelpPolls) {
-            for (uint64_t m = sm; m; m &= m - 1) {
-                const int e = __builtin_ctzll(m);
-                const uint32_t k0 = rl(f.ke, e);
-                const uint32_t u = f.q + (uint32_t)__builtin_amdgcn_readlane(f.ui, e);
-                float P[4];
-                sp_make_partial<T, EPV, S>(a, g, tab, tab_s, k0, sp_run_end(a, u, k0, S), P);
-                publish_n(a.part + (size_t)k0 * 4, a.tag, 4, __float_as_uint(P[0]),
-                          __float_as_uint(P[1]), __float_as_uint(P[2]), __float_as_uint(P[3]));
-                if (lane == e) {
-#pragma unroll
-                    for (int w = 0; w < 4; ++w)
-                        f.v[w] = ((uint64_t)a.tag << 32) | __float_as_uint(P[w]);
-                }
-            }
-            break;
-        }
-        __builtin_amdgcn_s_sleep(1);
-#pragma unroll
-        for (int w = 0; w < 4; ++w)
-            if (act && (uint32_t)(f.v[w] >> 32) != a.tag) f.v[w] = ld_word(pp + w);
-    }
-    uint32_t vw[4];
-#pragma unroll
-    for (int w = 0; w < 4; ++w) vw[w] = (uint32_t)f.v[w];
-    uint32_t off = 0;
-    for (uint32_t u = f.q; u < f.qe; ++u) {
-        const uint32_t np = sp_nparts(u * C, C, S);
-        uint32_t mv[4];
-#pragma unroll
-        for (int w = 0; w < 4; ++w)
-            mv[w] = (uint32_t)__shfl((int)vw[w], (int)((uint32_t)lane + off) & 63, 64);
-        const SpNorm n = sp_fold_partials((uint32_t)lane < np, mv);
-        if (lane == 0) out[u - qa] = n;
-        off += np;
-    }
-}
-
-// LDS state of a single-pass workgroup.
-template <typename T, int EPV, int S>
-struct SpShared {
-    static constexpr int kV4 = kSpN / 4;  // 16-byte words of a half's weights per lane
-    uint4 hold[kSpLag][S][2][kV4][64];    // TV items' weights, per round slot and wave
-    uint32_t cw[kSpLag + 1][S][4];       // chunk words of each wave's item
-    SpNorm nrm[kSpLag][S];               // normalisers of the tile's TV units
-    uint32_t done[S];                    // rounds whose statistics each wave has handed over
-    uint32_t ready[kSpLag];              // round + 1 once the tile's normalisers are in
-    uint32_t scr[3][16];
-    uint32_t tab[kSpMaxUnits];
-    float tab_s[kSpMaxUnits];
-};
-
-__device__ __forceinline__ uint32_t lds_load(const uint32_t *p) {
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-}
-__device__ __forceinline__ void lds_store(uint32_t *p, uint32_t v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-}
-
-// The coordinator wave (see above).  Round j: the loads of tile j - 1's
-// partials are issued first; once the stream waves have handed over round j,
-// tile j's partials are published; then tile j - 1's normalisers are folded
-// and handed to the stream waves.
-template <typename TT, typename TD, typename T, int EPV, int S>
-__device__ __forceinline__ void sp_coordinator(const VerifyArgs &a, const SpGrid &g,
-                                               SpShared<T, EPV, S> &sh) {
-    const int lane = lane_id();
-    const uint32_t C = (uint32_t)a.C, G = gridDim.x;
-    for (uint32_t j = 0; j <= g.rounds; ++j) {
-        // tile j - 1: its TV units qa..qb, first batch of partial loads
-        const uint32_t jp = j - 1u;
-        const uint32_t kp = (jp * G + blockIdx.x) * (uint32_t)S;
-        const bool any = j >= 1 && kp < g.i_tv;
-        const uint32_t qa = any ? fdiv(kp, a.divC) : 0u;
-        const uint32_t qb = any ? fdiv(min(kp + (uint32_t)S, g.i_tv) - 1u, a.divC) : 0u;
-        SpFetch f;
-        if (any) f = sp_fetch_issue<S>(a, qa, qb);
-        if (j < g.rounds) {
-            uint32_t spins = 0;
-            while (__ballot(lane < S && lds_load(&sh.done[lane < S ? lane : 0]) < j + 1u)) {
-                __builtin_amdgcn_s_sleep(1);
-                if (++spins > kSpinLimit) {
-                    if (lane == 0) atomic_or_u32(&a.ctl->status, SPEC_DEV_SPIN_TIMEOUT);
-                    break;
-                }
-            }
-            __atomic_signal_fence(__ATOMIC_SEQ_CST);
-            const uint32_t k0 = (j * G + blockIdx.x) * (uint32_t)S;
-            if (k0 < g.i_tv) {
-                uint32_t w[4] = {0u, 0u, 0u, 0u};
-                const uint32_t k = k0 + (uint32_t)lane;
-                const bool tv = lane < S && k < g.i_tv;
-                if (lane < S) {
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) w[q] = sh.cw[j % (kSpLag + 1)][lane][q];
-                }
-                const uint32_t qk = fdiv(k, a.divC);
-                const uint32_t kl = min(k0 + (uint32_t)S, g.i_tv) - 1u;
-                for (uint32_t q = fdiv(k0, a.divC); q <= fdiv(kl, a.divC); ++q) {
-                    float P[4];
-                    sp_fold_lanes(tv && qk == q, w, P[0], P[1], P[2], P[3]);
-                    const uint32_t kf = max(q * C, k0);
-                    publish_n(a.part + (size_t)kf * 4, a.tag, 4, __float_as_uint(P[0]),
-                              __float_as_uint(P[1]), __float_as_uint(P[2]),
-                              __float_as_uint(P[3]));
-                }
-            }
-        }
-        if (j >= 1) {
-            if (any) {
-                SpNorm *out = sh.nrm[jp % kSpLag];
-                sp_fetch_finish<T, EPV, S>(a, g, sh.tab, sh.tab_s, f, qa, out);
-                for (uint32_t q = f.qe; q <= qb;) {
-                    SpFetch f2 = sp_fetch_issue<S>(a, q, qb);
-                    sp_fetch_finish<T, EPV, S>(a, g, sh.tab, sh.tab_s, f2, qa, out);
-                    q = f2.qe;
-                }
-            }
-            __atomic_signal_fence(__ATOMIC_SEQ_CST);
-            if (lane == 0) lds_store(&sh.ready[jp % kSpLag], jp + 1u);
-        }
-    }
-}
-
-// A stream wave (see above).  Iteration j: the loads of round j + kAhead,
-// the statistics of round j, then the TV sums of round j - kSpLag from the
-// weights held in LDS slot (j - kSpLag) % kSpLag, whose place round j's
-// weights then take.
-template <typename T, int EPV, int S>
-__device__ __forceinline__ void sp_stream(const VerifyArgs &a, const SpGrid &g,
-                                          SpShared<T, EPV, S> &sh, int wave) {
-    using RC = RawChunk<T, kSpN, EPV>;
-    constexpr int kV4 = SpShared<T, EPV, S>::kV4;
-    constexpr int kSpAhead = SpCfg<T>::kAhead, kSpRing = kSpAhead + 1;
-    const int lane = lane_id();
-    const uint32_t C = (uint32_t)a.C;
-    const uint32_t kb = blockIdx.x * (uint32_t)S + (uint32_t)wave;
-    const uint32_t stride = gridDim.x * (uint32_t)S;
-    auto item_of = [&](uint32_t j) -> uint32_t {
-        // past the last round the item index may not fit 32 bits: clamp
-        return j < g.rounds + kSpAhead + kSpLag ? kb + j * stride : 0xffffffffu;
-    };
-    RC h0[kSpRing], h1[kSpRing];
-#pragma unroll
-    for (int q = 0; q < kSpAhead; ++q)
-        sp_issue<T, EPV>(a, sp_item(a, g, sh.tab, sh.tab_s, item_of((uint32_t)q)), h0[q], h1[q]);
-    for (uint32_t j0 = 0;; j0 += kSpRing) {
-#pragma unroll
-        for (int t = 0; t < kSpRing; ++t) {
-            const uint32_t j = j0 + (uint32_t)t;
-            if (j >= g.rounds + kSpLag) return;
-            const uint32_t hs = j % kSpLag;  // LDS slot of round j (and of round j - kSpLag)
-            // loads of round j + kAhead
-            {
-                const int ns = (t + kSpAhead) % kSpRing;
-                sp_issue<T, EPV>(a, sp_item(a, g, sh.tab, sh.tab_s, item_of(j + kSpAhead)),
-                                 h0[ns], h1[ns]);
-            }
-            // statistics of round j (ring slot t): chunk words published and
-            // handed to the coordinator; the weights stay in registers
-            const int rs = t;
-            float e0[kSpN], e1[kSpN];
-            {
-                const SpItem x = sp_item(a, g, sh.tab, sh.tab_s, item_of(j));
-                uint32_t w[4];
-                sp_item_words<T, EPV>(x, h0[rs], h1[rs], w, e0, e1);
-                const uint32_t v = lanes4(w);
-                sp_publish_words(a, x, v);
-                if (lane < 4) sh.cw[j % (kSpLag + 1)][wave][lane] = v;
-                __atomic_signal_fence(__ATOMIC_SEQ_CST);
-                if (lane == 0) lds_store(&sh.done[wave], j + 1u);
-            }
-            // TV sums of round j - kSpLag, then round j's weights into its slot
-            {
-                const bool live = j >= (uint32_t)kSpLag;
-                const uint32_t jt = live ? j - kSpLag : 0u;
-                const uint32_t k = kb + jt * stride;
-                const SpItem x = sp_item(a, g, sh.tab, sh.tab_s, live ? k : 0xffffffffu);
-                if (live && jt < g.rounds) {
-                    uint32_t spins = 0;
-                    while (lds_load(&sh.ready[hs]) != jt + 1u) {
-                        __builtin_amdgcn_s_sleep(1);
-                        if (++spins > kSpinLimit) {
-                            if (lane == 0) atomic_or_u32(&a.ctl->status, SPEC_DEV_SPIN_TIMEOUT);
-                            break;
-                        }
-                    }
-                    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-                }
-                float et[kSpN], ed[kSpN];
-#pragma unroll
-                for (int v = 0; v < kV4; ++v) {
-                    const uint4 p0 = sh.hold[hs][wave][0][v][lane];
-                    const uint4 p1 = sh.hold[hs][wave][1][v][lane];
-                    et[v * 4 + 0] = __uint_as_float(p0.x); et[v * 4 + 1] = __uint_as_float(p0.y);
-                    et[v * 4 + 2] = __uint_as_float(p0.z); et[v * 4 + 3] = __uint_as_float(p0.w);
-                    ed[v * 4 + 0] = __uint_as_float(p1.x); ed[v * 4 + 1] = __uint_as_float(p1.y);
-                    ed[v * 4 + 2] = __uint_as_float(p1.z); ed[v * 4 + 3] = __uint_as_float(p1.w);
-                }
-                const bool tv = x.kind == kSpTV;
-                const uint32_t q = tv ? fdiv(k, a.divC) : 0u;
-                const uint32_t q0 = tv ? fdiv(k - (uint32_t)wave, a.divC) : 0u;
-                const SpNorm &nm = sh.nrm[hs][q - q0];
-                const uint32_t *cw = sh.cw[jt % (kSpLag + 1)][wave];
-                double cmin, cres;
-                tv_sums_w<kSpN>(et, ed, __uint_as_float(cw[0]), __uint_as_float(cw[1]),
-                                __uint_as_float(cw[2]), nm.t, nm.d, &cmin, &cres);
-                uint64_t *p = tv ? a.st2 + ((size_t)x.u * C + x.c0) * 2 + (lane & 1)
-                                 : sp_dump(a) + (lane & 1);
-                const float cv = (float)cmin, rv = (float)cres;
-                if (lane < 2) st_word(p, a.tag, __float_as_uint(lane == 0 ? cv : rv));
-#pragma unroll
-                for (int v = 0; v < kV4; ++v) {
-                    sh.hold[hs][wave][0][v][lane] =
-                        make_uint4(__float_as_uint(e0[v * 4]), __float_as_uint(e0[v * 4 + 1]),
-                                   __float_as_uint(e0[v * 4 + 2]), __float_as_uint(e0[v * 4 + 3]));
-                    sh.hold[hs][wave][1][v][lane] =
-                        make_uint4(__float_as_uint(e1[v * 4]), __float_as_uint(e1[v * 4 + 1]),
-                                   __float_as_uint(e1[v * 4 + 2]), __float_as_uint(e1[v * 4 + 3]));
-                }
-            }
-        }
-    }
-}
-
-// The single-pass kernel: S stream waves and one coordinator per workgroup,
-// one workgroup per compute unit.
-template <typename TT, typename TD, typename T, int EPV>
-__global__ void __launch_bounds__((SpCfg<T>::kS + 1) * 64, 1) sp_kernel(VerifyArgs a) {
-    constexpr int S = SpCfg<T>::kS;
-    __shared__ SpShared<T, EPV, S> sh;
-    a.tag = first_launch_tag(a.ctl);
-    SpGrid g = sp_build_table(a, sh.tab, sh.tab_s, sh.scr);
-    const uint32_t per_round = gridDim.x * (uint32_t)S;
-    g.rounds = (g.items + per_round - 1u) / per_round;
-    if (threadIdx.x < S) sh.done[threadIdx.x] = 0u;
-    if (threadIdx.x < kSpLag) sh.ready[threadIdx.x] = 0u;
-    __syncthreads();
-    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-    if (wave == S)
-        sp_coordinator<TT, TD, T, EPV, S>(a, g, sh);
-    else
-        sp_stream<T, EPV, S>(a, g, sh, wave);
-}
-
 __global__ void zero_fill_kernel(uint32_t *p, size_t n_words) {
     for (size_t k = (size_t)blockIdx.x * blockDim.x + threadIdx.x; k < n_words;
          k += (size_t)gridDim.x * blockDim.x)
@@ -2303,7 +1529,7 @@ struct Plan {
     int C;           // chunks per row
     long units;
     // tagged words after the control block
-    size_t off_st1, off_st2, off_nrm, off_rec, off_part, off_dump, off_tvb, bytes;
+    size_t off_st1, off_st2, off_nrm, off_rec, bytes;
 };
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -2325,10 +1551,7 @@ bool make_plan(long R, long units_per_req, long V, Plan &p) {
     p.off_st2 = round_up(p.off_st1 + 32 * (size_t)units * C, 256);
     p.off_nrm = round_up(p.off_st2 + 16 * (size_t)units * C, 256);
     p.off_rec = round_up(p.off_nrm + 32 * (size_t)units, 256);
-    p.off_part = round_up(p.off_rec + 8 * kRecWords * (size_t)units, 256);
-    p.off_dump = round_up(p.off_part + 32 * (size_t)units * C, 256);
-    p.off_tvb = round_up(p.off_dump + 32 * 256 * 16, 256);
-    p.bytes = round_up(p.off_tvb + 4 * (size_t)R, 256);
+    p.bytes = round_up(p.off_rec + 8 * kRecWords * (size_t)units, 256);
     return true;
 }
 
@@ -2398,39 +1621,8 @@ size_t table_bytes(const VerifyArgs &a) {
     return b <= kMaxTableBytes ? (b + 255) / 256 * 256 : 0;
 }
 
-// Which path a call takes: the four-launch path, or with
-// SPECVERIFY_PATH=single the single pass where it applies (one dtype for both
-// tensors, 16-byte vector loads, a unit table that fits in LDS).  The tests
-// run both.
-bool single_pass_allowed() {
-    const char *e = getenv("SPECVERIFY_PATH");
-    return e && e[0] == 's';
-}
-
-template <typename TT, typename TD, int N, int EPV>
-int launch_single(VerifyArgs a, hipStream_t st) {
-    using T = TT;
-    constexpr int S = SpCfg<T>::kS;
-    const long cus = device_cus();
-    const long grid = cus > 0 ? cus : 256;
-    const long gc = a.tv_mode ? (a.R + kReqWaves - 1) / kReqWaves : a.R;
-    a.tag = 0;  // read on the device by every launch
-    a.single = 1;
-    a.spS = S;
-    hipLaunchKernelGGL((sp_kernel<TT, TD, T, EPV>), dim3((unsigned)grid), dim3((S + 1) * 64), 0,
-                       st, a);
-    hipLaunchKernelGGL((combine_kernel<TT, TD, N, EPV>), dim3((unsigned)gc), dim3(kReqBlock), 0,
-                       st, a);
-    return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_EHIP;
-}
-
 template <typename TT, typename TD, int N, int EPV>
 int launch_kernels(VerifyArgs a, hipStream_t st) {
-    if constexpr (std::is_same<TT, TD>::value && N == kSpN && EPV == ChunkGeom<TT, TD, N>::kVec &&
-                  EPV > 1) {
-        if (single_pass_allowed() && (long)a.R * a.UG <= kSpMaxUnits)
-            return launch_single<TT, TD, N, EPV>(a, st);
-    }
     const void *k1 = reinterpret_cast<const void *>(&stats_kernel<TT, TD, N, EPV>);
     const void *k3 = reinterpret_cast<const void *>(&tv_kernel<TT, TD, N, EPV>);
     const long gf = ((long)a.R * a.UG + kWaves - 1) / kWaves;
@@ -2481,9 +1673,6 @@ void bind_workspace(VerifyArgs &a, void *ws, const Plan &p) {
     a.st2 = (uint64_t *)(b + p.off_st2);
     a.nrm = (uint64_t *)(b + p.off_nrm);
     a.rec = (uint64_t *)(b + p.off_rec);
-    a.part = (uint64_t *)(b + p.off_part);
-    a.dump = (uint64_t *)(b + p.off_dump);
-    a.tvbase = (uint32_t *)(b + p.off_tvb);
     a.C = p.C;
 }
 
@@ -2583,8 +1772,6 @@ int spec_verify_batch(const void *target_logits, int t_dtype, const void *draft_
     a.out_rs = out_resid_mass;
     a.out_lq = out_logq;
     bind_workspace(a, workspace, p);
-    a.divC = make_fastdiv((uint32_t)p.C);
-    a.divCh = make_fastdiv((uint32_t)(p.C + 1) / 2);
     const bool vec = (V % 8 == 0) && aligned16(target_logits) &&
                      (gamma == 0 || aligned16(draft_logits));
     // with gamma == 0 no draft row exists; the draft type only shapes the plan
@@ -2619,8 +1806,6 @@ int spec_tv_accept_rate(const void *draft_logits, const void *target_logits, int
     a.out_cs = out_cstar;
     a.out_rs = out_resid_mass;
     bind_workspace(a, workspace, p);
-    a.divC = make_fastdiv((uint32_t)p.C);
-    a.divCh = make_fastdiv((uint32_t)(p.C + 1) / 2);
     const bool vec = (V % 8 == 0) && aligned16(target_logits) && aligned16(draft_logits);
     return launch(a, dtype, dtype, p.N, vec, (hipStream_t)stream);
 }

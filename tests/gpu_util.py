@@ -111,3 +111,28 @@ def compare_verify(case, gpu: dict, ref: dict, rtol: float = None) -> dict:
             if ft < 0:
                 assert np.isnan(gpu["logq"][r, n_ref + 1:]).all(), tag
     return stats
+
+
+def markov_oracle_all(mk, workers: int = 16) -> dict:
+    """oracle.markov_draft over every request of a Markov case, the requests
+    split over host threads (the C oracle keeps no shared state, and ctypes
+    releases the interpreter lock during the call)."""
+    import concurrent.futures
+    import os
+    import oracle
+    R = mk.R
+    n = max(1, min(workers, os.cpu_count() or 1, R))
+    parts = [list(range(k, R, n)) for k in range(n)]
+
+    def one(rows):
+        return rows, oracle.markov_draft(mk.U[rows], mk.W1, mk.W2, mk.anchor[rows],
+                                         mk.temperature[rows], mk.u_draft[rows])
+
+    out = dict(tokens=np.empty((R, mk.gamma), np.int32),
+               logits=np.empty((R, mk.gamma, mk.V), np.float32),
+               margin_min=np.empty((R,), np.float64), first_tie=np.empty((R,), np.int32))
+    with concurrent.futures.ThreadPoolExecutor(n) as ex:
+        for rows, ref in ex.map(one, parts):
+            for k in ("tokens", "logits", "margin_min", "first_tie"):
+                out[k][rows] = ref[k]
+    return out

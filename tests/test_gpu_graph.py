@@ -161,3 +161,45 @@ def test_tv_accept_rate_graph(sv, dev):
 
     ws2 = sv.Workspace(dev, sv.spec_tv_workspace_bytes(16, 2000))
     replay_and_compare(g, out, fill, lambda: list(sv.spec_tv_accept_rate(d, t, T, workspace=ws2)))
+
+
+def test_verify_graph_shared_workspace(sv, dev):
+    """One workspace serves a captured verification, eager Markov drafts and an
+    eager verification with fewer requests between the replays: every replay
+    must still equal an eager call (no state of an earlier call is trusted)."""
+    cases = [workloads.make_verify_case(6, 5, 3000, "bf16", seed=s, noise_std=1.0,
+                                        temperature=[1.0, 0.0, 0.7, 1.0, 1.0, 0.0])
+             for s in (21, 22, 23)]
+    names = ("target", "draft", "draft_tokens", "verify_len", "temperature", "u_accept",
+             "u_sample")
+    args = [to_device(getattr(cases[0], nm), dev) for nm in names]
+    mk = workloads.dspark_markov(seed=24, R=8, gamma=4, V=3000)
+    small = workloads.make_verify_case(2, 3, 3000, "bf16", seed=25, noise_std=0.8)
+    nbytes = max(sv.spec_verify_workspace_bytes(6, 5, 3000),
+                 sv.spec_markov_workspace_bytes(8, 4, 3000, 256))
+    ws = sv.Workspace(dev, nbytes)
+
+    def outs(d):
+        return [d["tokens"], d["num_accepted"], d["cstar"], d["resid_mass"], d["logq"]]
+
+    g, out = capture(lambda: outs(sv.spec_verify_batch(*args, workspace=ws)))
+    mk_args = [to_device(x, dev) for x in (mk.U, mk.W1, mk.W2, mk.anchor, mk.temperature,
+                                          mk.u_draft)]
+    small_args = [to_device(getattr(small, nm), dev) for nm in names]
+    ws2 = sv.Workspace(dev, nbytes)
+    for k in range(3):
+        for t, nm in zip(args, names):
+            t.copy_(to_device(getattr(cases[k], nm), dev))
+        # other calls write the same workspace between the replays
+        sv.spec_markov_draft_sample(*mk_args, workspace=ws)
+        sv.spec_verify_batch(*small_args, workspace=ws)
+        torch.cuda.synchronize()
+        ref = [t.clone() for t in outs(sv.spec_verify_batch(*args, workspace=ws2))]
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(out, ref):
+            if a.is_floating_point():
+                a, b = a.view(torch.int32), b.view(torch.int32)
+            assert torch.equal(a, b), f"replay {k} differs from the eager call"
+    assert sv.spec_get_device_status(ws, clear=True) == 0

@@ -33,14 +33,28 @@ def run(sv, dev, conf, sps, topk=-1, ws=None):
     return ln.cpu().numpy(), float(th.cpu().numpy()[0])
 
 
+def walk_lengths(conf, k):
+    """The verify lengths after admitting the first k candidates of the
+    oracle's pool order."""
+    a = osch.survival(conf)
+    lens = np.zeros(conf.shape[0], np.int32)
+    for (r, j) in osch.pool_order(a)[:k]:
+        lens[r] = j
+    return lens
+
+
 def compare(conf, sps, topk, ln, th):
     ref = osch.schedule(conf, sps, topk)
     print(f"[schedule] admitted={ref['admitted']} sum_len={int(ln.sum())} "
           f"tie_margin={ref['tie_margin']:.3g}", flush=True)
     assert ln.shape == ref["len"].shape
     if ref["tie_margin"] < osch.TIE_REL:
-        assert abs(int(ln.sum()) - ref["admitted"]) <= 1
-        assert np.all(ln >= 0) and np.all(ln <= conf.shape[1])
+        # the stopping comparison is within rounding of a tie: the GPU may stop
+        # one admission earlier or later, but always on the oracle's walk
+        npool = conf.shape[0] * conf.shape[1]
+        cands = [walk_lengths(conf, k) for k in (ref["admitted"] - 1, ref["admitted"],
+                                                  ref["admitted"] + 1) if 0 <= k <= npool]
+        assert any(np.array_equal(ln, c) for c in cands), (ln, ref["len"])
         return ref
     np.testing.assert_array_equal(ln, ref["len"])
     assert th == pytest.approx(ref["theta"], rel=1e-12, abs=0.0)

@@ -26,15 +26,6 @@ def dev(sv):
     return torch.device("cuda:0")
 
 
-@pytest.fixture(autouse=True, params=["single", "multi"])
-def verify_path(request, monkeypatch):
-    """Every test runs on both paths: the single-pass kernel (where the call
-    qualifies; chosen with SPECVERIFY_PATH=single) and the four-launch path
-    (the default)."""
-    monkeypatch.setenv("SPECVERIFY_PATH", request.param)
-    return request.param
-
-
 def _report(name, stats):
     print(f"[{name}] exact={stats['exact']} near_ties={stats['near_ties']} "
           f"(matched anyway {stats['near_ties_matched']}) invalid={stats['invalid']} "
@@ -286,3 +277,30 @@ def test_tv_accept_rate(sv, dev, dtype):
     assert np.allclose(cs.cpu().numpy(), ref_c, rtol=tol, atol=1e-6)
     assert np.allclose(rs.cpu().numpy(), ref_r, rtol=tol, atol=1e-6)
     assert abs(cs[0].item() - 1.0) < 1e-6
+
+
+def test_concurrent_calls_on_two_streams(sv, dev):
+    """Two verification calls with distinct workspaces run concurrently on two
+    streams: both must match the oracle, with no device status bit (no wait
+    gave up)."""
+    cases = [workloads.make_verify_case(48, 7, 151936, "bf16", seed=s,
+                                        noise_std=[0.5, 0.8, 1.1, 1.4, 1.7, 2.0, 2.5],
+                                        verify_len=7) for s in (41, 42)]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    wss = [sv.Workspace(dev, sv.spec_verify_workspace_bytes(48, 7, 151936)) for _ in range(2)]
+    names = ("target", "draft", "draft_tokens", "verify_len", "temperature", "u_accept",
+             "u_sample")
+    args = [[to_device(getattr(c, nm), dev) for nm in names] for c in cases]
+    torch.cuda.synchronize()
+    outs = [None, None]
+    for rep in range(3):
+        for k in range(2):
+            with torch.cuda.stream(streams[k]):
+                outs[k] = sv.spec_verify_batch(*args[k], workspace=wss[k])
+        torch.cuda.synchronize()
+    for k in range(2):
+        assert sv.spec_get_device_status(wss[k], clear=True) == 0
+        gpu = {n: (v.cpu().numpy() if v is not None else None) for n, v in outs[k].items()}
+        ref = oracle.verify_case(cases[k])
+        st = compare_verify(cases[k], gpu, ref)
+        assert st["exact"] + st["near_ties"] == cases[k].R
