@@ -4,8 +4,9 @@ A step is one spec_verify_batch call over the batched workload (R = 64
 requests, gamma = 7, V = 151936, bf16 logits, verify lengths uniform on 0..7,
 T = 1): every row of the hot path (softmax statistics, c*, accept tests,
 prefix survival, residual / bonus draw, commit) runs in that one call, which
-launches four kernels on the current stream (chunk statistics, per-row
-combine, total-variation pass, residual draw and commit).
+launches four kernels on the current stream (chunk statistics, the per-row
+normaliser folds with the accept tests, the total-variation pass, and the
+per-request combine with the draw and the commit).
 
 Inputs are generated once (seeded), uploaded, and replicated into enough
 device copies that consecutive steps never find their logits in the 256 MB
@@ -17,14 +18,18 @@ Prints one JSON line:
   roofline   algorithmic bytes (every verified draft row and target row plus
              the bonus row, read once) / average HIP-event time of the whole
              call (its four kernels), against 8 TB/s
-  cpu_baseline  the fp64 oracle on the host (one thread) over the same batch
+  cpu_baseline  the fp64 oracle on the host over the same batch: all usable
+             cores (up to a one-GPU share of 16, requests split over
+             threads), with the one-thread figure beside it
 
---workload dspark measures the Markov-head draft (R = 64, gamma = 7,
-V = 129280, rank 256) instead, as an extra line; --workload schedule the
-confidence-scheduled verify lengths of the same batch size (448 candidates);
---workload rnn the RNN serial head at the Markov workload's size; --workload
-sts the confidence head's sequential temperature scaling on a held-out set;
---workload tree greedy verification of draft trees.
+The other verify workloads (--workload single_user, dspark_verify,
+high_load, tiny) give the same line for the other batch shapes; --workload
+dspark measures the Markov-head draft (R = 64, gamma = 7, V = 129280, rank
+256); --workload schedule the confidence-scheduled verify lengths of the same
+batch size (448 candidates); --workload rnn the RNN serial head at the Markov
+workload's size; --workload sts the confidence head's sequential temperature
+scaling on a held-out set; --workload tree greedy verification of draft
+trees.
 """
 from __future__ import annotations
 
@@ -95,19 +100,120 @@ def to_device(x, dev):
     return torch.from_numpy(x).to(dev)
 
 
+def host_cpu():
+    """The host's CPU model and the cores this process may run on."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    usable = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    return model, int(usable or 1), int(os.cpu_count() or 1)
+
+
+# Host threads for the all-cores oracle run: a one-GPU share of the host is
+# 16 cores, whatever the machine reports.
+CPU_SHARE = 16
+
+
 def cpu_baseline(case, min_seconds: float):
+    """The C oracle (fp64, unchanged) over the workload's whole batch, timed on
+    one host thread and then on all usable cores with the requests split over
+    threads (the oracle keeps no shared state and ctypes releases the
+    interpreter lock during the call).  Each leg repeats full passes until
+    min_seconds / 2 have passed."""
+    import concurrent.futures
     import oracle
-    passes, t0 = 0, time.perf_counter()
-    while True:
-        oracle.verify_case(case)
-        passes += 1
-        dt = time.perf_counter() - t0
-        if dt >= min_seconds:
-            break
-    positions = int(case.verify_len.sum()) * passes
-    return {"value": positions / dt, "unit": "positions/s", "cores": 1, "kind": "oracle",
-            "sample": f"the full {case.R}-request batch, {passes} pass(es), {dt:.1f} s, "
-                      f"fp64 C oracle on one host thread"}
+    model, usable, logical = host_cpu()
+    R = case.R
+    positions = int(np.clip(case.verify_len, 0, None).sum())
+
+    last = {}
+
+    def run_rows(r0, r1):
+        last[r0] = oracle.verify_batch(case.target[r0:r1], case.draft[r0:r1],
+                                       case.draft_tokens[r0:r1], case.verify_len[r0:r1],
+                                       case.temperature[r0:r1], case.u_accept[r0:r1],
+                                       case.u_sample[r0:r1])
+
+    def timed(fn):
+        passes, t0 = 0, time.perf_counter()
+        while True:
+            fn()
+            passes += 1
+            dt = time.perf_counter() - t0
+            if dt >= min_seconds / 2:
+                return passes, dt
+
+    p1, d1 = timed(lambda: run_rows(0, R))
+    n = max(1, min(usable, CPU_SHARE, R))
+    cuts = np.linspace(0, R, n + 1).astype(int)
+    with concurrent.futures.ThreadPoolExecutor(n) as ex:
+        def all_cores():
+            list(ex.map(lambda k: run_rows(cuts[k], cuts[k + 1]), range(n)))
+        pn, dn = timed(all_cores)
+    ref = {k: np.concatenate([last[c][k] for c in cuts[:-1]])
+           for k in ("tokens", "num_accepted", "first_tie", "cstar", "resid", "logq")}
+    return ref, {"value": positions * pn / dn, "unit": "positions/s", "cores": n, "kind": "oracle",
+            "single_thread_value": positions * p1 / d1,
+            "host": {"cpu_model": model, "usable_cores": usable, "logical_cpus": logical},
+            "sample": f"the full {R}-request batch: {pn} pass(es) in {dn:.1f} s on {n} threads "
+                      f"(requests split), {p1} pass(es) in {d1:.1f} s on one thread; "
+                      "fp64 C oracle"}
+
+
+# The kernels of one spec_verify_batch call, in launch order.
+VERIFY_KERNELS = "stats_kernel + fold_kernel + tv_kernel + combine_kernel"
+
+# Verify workloads: name -> description.
+VERIFY_WORKLOADS = {
+    "batched": "R=64 gamma=7 V=151936 bf16, l_r uniform on 0..7, T=1",
+    "single_user": "R=1 gamma=8 V=151936 fp32, one planted dominant id per row, l=8, T=1",
+    "dspark_verify": "R=64 gamma=7 V=129280: bf16 target, fp32 draft logits from the "
+                     "Markov-head draft (made on the GPU before timing), l=7, T=1",
+    "high_load": "R=256 gamma=7 V=129280 bf16, l_r truncated geometric(0.3), half T=0",
+    "tiny": "R=1 gamma=4 V=32 fp32, l=4, T=1",
+}
+
+
+def verify_inputs(args, dev):
+    """(case, device target, device draft) of a verify workload.  The case's
+    host arrays are the oracle's inputs; for dspark_verify its draft arrays
+    are filled from the GPU draft."""
+    import torch
+    import workloads
+    import lossless_verification_sampling_amd as sv
+    w = args.workload
+    seed = args.seed
+    if w == "batched":
+        case = workloads.batched(seed=3 if seed is None else seed)
+    elif w == "single_user":
+        case = workloads.single_user(seed=2 if seed is None else seed)
+    elif w == "high_load":
+        case = workloads.high_load_mixed(seed=5 if seed is None else seed)
+    elif w == "tiny":
+        case = workloads.tiny_chain(seed=1 if seed is None else seed)
+    else:
+        mk = workloads.dspark_markov(seed=4 if seed is None else seed)
+        R, gamma, V = mk.R, mk.gamma, mk.V
+        tok = torch.empty((R, gamma), dtype=torch.int32, device=dev)
+        lg = torch.empty((R, gamma, V), dtype=torch.float32, device=dev)
+        ws = sv.Workspace(dev, sv.spec_markov_workspace_bytes(R, gamma, V, mk.rank))
+        sv.spec_markov_draft_sample(to_device(mk.U, dev), to_device(mk.W1, dev),
+                                    to_device(mk.W2, dev), to_device(mk.anchor, dev),
+                                    to_device(mk.temperature, dev), to_device(mk.u_draft, dev),
+                                    out_tokens=tok, out_logits=lg, workspace=ws)
+        torch.cuda.synchronize()
+        case = workloads.VerifyCase(name="dspark_verify", target=mk.target,
+                                    draft=lg.cpu().numpy(), draft_tokens=tok.cpu().numpy(),
+                                    verify_len=mk.verify_len, temperature=mk.temperature,
+                                    u_accept=mk.u_accept, u_sample=mk.u_sample, seed=mk.seed)
+        return case, to_device(case.target, dev), lg
+    return case, to_device(case.target, dev), to_device(case.draft, dev)
 
 
 def bench_verify(args):
@@ -116,15 +222,14 @@ def bench_verify(args):
     import workloads
 
     dev = torch.device("cuda:0")
-    case = workloads.batched(seed=args.seed)
+    case, tgt0, drf0 = verify_inputs(args, dev)
     R, G1, V = case.target.shape
     gamma = G1 - 1
     sum_l = int(case.verify_len.sum())
-    alg_bytes = workloads.algorithmic_bytes(case.verify_len, V, 2, 2)
-    touched = alg_bytes
-    ncopy = args.copies or max(2, int(np.ceil(2 * MALL_BYTES / touched)) + 1)
-    tgt0 = to_device(case.target, dev)
-    drf0 = to_device(case.draft, dev)
+    te = 2 if case.target.dtype == np.uint16 else 4
+    de = 2 if case.draft.dtype == np.uint16 else 4
+    alg_bytes = workloads.algorithmic_bytes(case.verify_len, V, te, de)
+    ncopy = args.copies or max(2, int(np.ceil(2 * MALL_BYTES / alg_bytes)) + 1)
     tgts = [tgt0] + [tgt0.clone() for _ in range(ncopy - 1)]
     drfs = [drf0] + [drf0.clone() for _ in range(ncopy - 1)]
     tok = to_device(case.draft_tokens, dev)
@@ -166,9 +271,15 @@ def bench_verify(args):
     avg_kernel_s = float(kern_ms.mean()) / 1e3
     ms_per_step = wall / args.steps * 1e3
     achieved = alg_bytes / avg_kernel_s / 1e9
-    traffic = measured_traffic("verify_batched")
+    key = "verify_" + args.workload
+    traffic = measured_traffic(key)
+    tname = "bf16" if te == 2 else "f32"
+    dname = "bf16" if de == 2 else "f32"
+    Ts = sorted(set(float(t) for t in np.asarray(case.temperature).ravel()))
     result = {
-        "metric": METRIC,
+        "metric": METRIC if args.workload == "batched" else
+        f"verified draft positions/sec and achieved HBM GB/s (% of peak), {args.workload}: "
+        + VERIFY_WORKLOADS[args.workload],
         "value": sum_l / (ms_per_step / 1e3),
         "unit": "positions/s",
         "n_gpus": 1,
@@ -180,8 +291,9 @@ def bench_verify(args):
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": "batched", "R": R, "gamma": gamma, "V": V, "logits": "bf16",
-                   "sum_verify_len": sum_l, "temperature": 1.0, "seed": args.seed,
+        "config": {"workload": args.workload, "R": R, "gamma": gamma, "V": V,
+                   "logits": tname if tname == dname else f"target {tname}, draft {dname}",
+                   "sum_verify_len": sum_l, "temperature": Ts, "seed": case.seed,
                    "input_copies": ncopy, "parallelism": "none (one GPU)"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
@@ -189,12 +301,46 @@ def bench_verify(args):
                      "kernel_ms_mean": float(kern_ms.mean()),
                      "kernel_ms_p10": float(np.percentile(kern_ms, 10)),
                      "kernel_ms_p90": float(np.percentile(kern_ms, 90)),
-                     "kernel": "spec_verify_batch call: stats_kernel + tv_kernel (unit folds, TV pass) + tv_combine_kernel (bf16, bf16)"},
+                     "kernel": f"spec_verify_batch call: {VERIFY_KERNELS} "
+                               f"({tname}, {dname})"},
         "kernel_positions_per_s": sum_l / avg_kernel_s,
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
+        ref, result["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
+        result["parity"] = parity_summary(case, {k: v.cpu().numpy() for k, v in out.items()}, ref)
     return result
+
+
+def parity_summary(case, gpu: dict, ref: dict) -> dict:
+    """How the last timed call's outputs compare with the oracle's from the
+    baseline leg: requests graded exactly (no decision within 1e-6 of its
+    boundary), near ties, exact mismatches among the graded, and the largest
+    relative errors of c*, Res and log q (where the oracle's value exceeds
+    1e-3)."""
+    R = case.R
+    graded = mism = ties = 0
+    err = {"cstar": 0.0, "resid": 0.0, "logq": 0.0}
+    for r in range(R):
+        n = int(ref["num_accepted"][r])
+        if n < 0:
+            mism += int(gpu["num_accepted"][r] != -1)
+            continue
+        if int(ref["first_tie"][r]) >= 0:
+            ties += 1
+            continue
+        graded += 1
+        mism += int(gpu["num_accepted"][r] != n or
+                    not np.array_equal(gpu["tokens"][r], ref["tokens"][r]))
+        l = int(case.verify_len[r])
+        for k, gk, m in (("cstar", "cstar", l), ("resid", "resid_mass", l), ("logq", "logq", n + 1)):
+            o = ref[k][r, :m]
+            g = gpu[gk][r, :m].astype(np.float64)
+            big = np.abs(o) > 1e-3
+            if big.any():
+                err[k] = max(err[k], float((np.abs(g - o)[big] / np.abs(o[big])).max()))
+    return {"requests": R, "graded_exact": graded, "near_ties": ties,
+            "mismatches_among_graded": mism, "max_rel_err": err,
+            "tolerance": 1e-5 if case.target.dtype == case.draft.dtype == np.float32 else 2e-3}
 
 
 def bench_dspark(args):
@@ -606,10 +752,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--seed", type=int, default=3)
+    ap.add_argument("--seed", type=int, default=None,
+                    help="workload seed (default: the workload's own)")
     ap.add_argument("--copies", type=int, default=0, help="input copies rotated (0 = auto)")
-    ap.add_argument("--workload", choices=["batched", "dspark", "rnn", "schedule", "sts", "tree"],
-                    default="batched")
+    ap.add_argument("--workload", choices=list(VERIFY_WORKLOADS) +
+                    ["dspark", "rnn", "schedule", "sts", "tree"], default="batched")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -621,6 +768,8 @@ def main():
     ap.add_argument("--copies-counted", type=int, default=6,
                     help="copies in the counted --calibrate-copy run")
     args = ap.parse_args()
+    if args.seed is None and args.workload not in VERIFY_WORKLOADS:
+        args.seed = 3
     if args.traffic_from:
         print(json.dumps(write_traffic(args)))
         return
@@ -632,8 +781,9 @@ def main():
     if args.calibrate_copy:
         res = calibrate_copy(args)
     else:
-        res = {"batched": bench_verify, "dspark": bench_dspark, "rnn": bench_rnn,
-               "schedule": bench_schedule, "sts": bench_sts, "tree": bench_tree}[args.workload](args)
+        other = {"dspark": bench_dspark, "rnn": bench_rnn, "schedule": bench_schedule,
+                 "sts": bench_sts, "tree": bench_tree}
+        res = other.get(args.workload, bench_verify)(args)
     print(json.dumps(res))
 
 

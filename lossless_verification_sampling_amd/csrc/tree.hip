@@ -208,7 +208,10 @@ __global__ void __launch_bounds__(kBlock) tree_level_kernel(TreeArgs a) {
         if (bb) {
             atomic_or_u32(&a.fault[lb + l], 1u);
         } else {
-            const uint64_t word = ((uint64_t)tree_ord(bv) << 32) | (uint32_t)~(uint32_t)bi;
+            // -0.0 and +0.0 are one value to the greedy rule (the lowest id
+            // among equal maxima wins), so both take +0.0's word
+            const uint64_t word =
+                ((uint64_t)tree_ord(bv == 0.0f ? 0.0f : bv) << 32) | (uint32_t)~(uint32_t)bi;
             __hip_atomic_fetch_max(&a.key[lb + l], word, __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
         }

@@ -24,8 +24,10 @@
 //     mu and weight sum S = sum 2^(z s - mu) per row (s = log2(e) / T), or the
 //     chunk argmax at T = 0.
 //  2. fold_kernel: one wave per draft position at T > 0 folds the chunk words
-//     into the row normalisers (M = max mu, Z = sum S 2^(mu - M)) and runs the
-//     accept test on the two gathered logits of the draft token.
+//     into the row normalisers (M = max mu, Z = sum S 2^(mu - M)) and every
+//     chunk's pair scale (the factors that put the two rows' chunk weights on
+//     one probability scale), and runs the accept test on the two gathered
+//     logits of the draft token.
 //  3. tv_kernel: the pair items at T > 0 again -- launch 1 has just streamed
 //     them, so they come from the 256 MB Infinity Cache when they fit -- with
 //     each chunk's weights rebuilt exactly as launch 1 made them; per item
@@ -96,6 +98,7 @@ struct VerifyArgs {
     uint64_t *st2;           // [units][C][2] chunk sum min(p, q), residual mass
     uint64_t *nrm;           // [units][4] unit normalisers
     uint64_t *rec;           // [units][kRecWords] unit records
+    uint64_t *psc;           // [units * C][4] per-chunk pair scales (kt, kd, unit)
 };
 
 // ---------------------------------------------------------------------------
@@ -902,13 +905,10 @@ __device__ __forceinline__ void unit_norms(const VerifyArgs &a, const Item &x, f
     if (pair) od.reduce(Md, Zd);
 }
 
-// The accept test of draft position x (T > 0) once its row normalisers are
-// known: accept <=> q(x) >= p(x) or u < q(x)/p(x) (DART note eq. (3)), in
-// fp64 from the two gathered logits of the draft token x_{i+1}; publishes the
-// unit's record (flags, log q(x)).  The uniform's range is checked by the
-// combine.
-// The accept test on the gathered logits zx (target), dx (draft) of the draft
-// token: q(x) >= p(x) or u < q(x)/p(x), in fp64; *lqx = log q(x).
+// The accept test of a draft position (T > 0) on the gathered logits zx
+// (target), dx (draft) of its draft token x_{i+1}, once the row normalisers
+// are known: accept <=> q(x) >= p(x) or u < q(x)/p(x) (DART note eq. (3)), in
+// fp64; *lqx = log q(x).  The uniform's range is checked by the combine.
 __device__ __forceinline__ bool accept_eval(float zx, float dx, float s, float Mt, float Zt,
                                             float Md, float Zd, float uacc, float *lqx) {
     const double lq2 = (double)zx * (double)s - (double)Mt;
@@ -919,32 +919,67 @@ __device__ __forceinline__ bool accept_eval(float zx, float dx, float s, float M
     return q >= pp || (double)uacc < q / pp;
 }
 
-template <typename TT, typename TD>
-__device__ __forceinline__ void accept_record(const VerifyArgs &a, const Item &x, float Mt,
-                                              float Zt, float Md, float Zd) {
-    const int xtok = a.tokens[(size_t)x.r * a.gamma + x.i];
-    const float uacc = a.ua[(size_t)x.r * a.gamma + x.i];
-    const bool valid = norms_ok(Mt, Zt) && norms_ok(Md, Zd) && xtok >= 0 && xtok < a.V;
-    bool acc = false;
-    float lqx = __builtin_nanf("");
-    if (valid) {
-        const float zx = load_one(row_ptr<TT>(a.zt, x.r, a.tG, x.i, a.V), xtok);
-        const float dx = load_one(row_ptr<TD>(a.zd, x.r, a.dG, x.i, a.V), xtok);
-        acc = accept_eval(zx, dx, x.s, Mt, Zt, Md, Zd, uacc, &lqx);
-    }
-    publish_n(a.rec + (size_t)x.u * kRecWords, a.tag, 2,
-              (valid ? kFlagValid : 0u) | (acc ? kFlagAccept : 0u), __float_as_uint(lqx), 0u, 0u);
-}
-
 // The fold launch's work for draft position x at T > 0: its row normalisers
-// for the TV items and the combine, then the accept test.
+// (folded as unit_norms folds them: per lane over its chunks in increasing
+// order, then across the wave), each chunk's pair scale for the TV items --
+// formed once here rather than in every TV item -- and the accept test, whose
+// record (flags, log q(x)) the combine reads.  The draft token's two logits
+// are gathered while the chunk words load.  The pair scales are published
+// whatever the normalisers, so that the TV pass always finds current words;
+// an invalid unit's TV sums are not used.
 template <typename TT, typename TD>
 __device__ __forceinline__ void norm_fold(const VerifyArgs &a, const Item &x) {
+    const int lane = lane_id();
+    const int C = a.C;
+    int xtok = 0;
+    float uacc = 0.0f, zx = 0.0f, dx = 0.0f;
+    bool tok_ok = true;
+    if (!a.tv_mode) {
+        xtok = a.tokens[(size_t)x.r * a.gamma + x.i];
+        uacc = a.ua[(size_t)x.r * a.gamma + x.i];
+        tok_ok = xtok >= 0 && xtok < a.V;
+        if (tok_ok) {
+            zx = load_one(row_ptr<TT>(a.zt, x.r, a.tG, x.i, a.V), xtok);
+            dx = load_one(row_ptr<TD>(a.zd, x.r, a.dG, x.i, a.V), xtok);
+        }
+    }
+    const bool want[4] = {true, true, true, true};
+    uint32_t w[kCB][4];
+    load_unit_words<4, kCB>(a.st1 + (size_t)x.u * C * 4, C, want, a.tag, a.ctl, w, true, 0);
+    OnlineZ ot, od;
+#pragma unroll
+    for (int b = 0; b < kCB; ++b)
+        if (b * 64 + lane < C) {
+            ot.add(__uint_as_float(w[b][0]), __uint_as_float(w[b][1]));
+            od.add(__uint_as_float(w[b][2]), __uint_as_float(w[b][3]));
+        }
     float Mt, Zt, Md, Zd;
-    unit_norms(a, x, Mt, Zt, Md, Zd);
+    ot.reduce(Mt, Zt);
+    od.reduce(Md, Zd);
     publish_n(a.nrm + (size_t)x.u * 4, a.tag, 4, __float_as_uint(Mt), __float_as_uint(Zt),
               __float_as_uint(Md), __float_as_uint(Zd));
-    if (!a.tv_mode) accept_record<TT, TD>(a, x, Mt, Zt, Md, Zd);
+    const RowNorm nt = row_norm(Mt, Zt), nd = row_norm(Md, Zd);
+#pragma unroll
+    for (int b = 0; b < kCB; ++b) {
+        const int c = b * 64 + lane;
+        if (c < C) {
+            const PairScale ps =
+                pair_scale(__uint_as_float(w[b][0]), __uint_as_float(w[b][2]), nt, nd);
+            uint64_t *q = a.psc + ((size_t)x.u * C + c) * 4;
+            st_word(q + 0, a.tag, __float_as_uint(ps.kt));
+            st_word(q + 1, a.tag, __float_as_uint(ps.kd));
+            st_word(q + 2, a.tag, __float_as_uint(ps.unit));
+        }
+    }
+    if (!a.tv_mode) {
+        const bool valid = norms_ok(Mt, Zt) && norms_ok(Md, Zd) && tok_ok;
+        bool acc = false;
+        float lqx = __builtin_nanf("");
+        if (valid) acc = accept_eval(zx, dx, x.s, Mt, Zt, Md, Zd, uacc, &lqx);
+        publish_n(a.rec + (size_t)x.u * kRecWords, a.tag, 2,
+                  (valid ? kFlagValid : 0u) | (acc ? kFlagAccept : 0u), __float_as_uint(lqx),
+                  0u, 0u);
+    }
 }
 
 // Per-unit summary of a request in launch 3 (shared memory), written by
@@ -1414,15 +1449,14 @@ __global__ void __launch_bounds__(kBlock, kStreamWaves) stats_kernel(VerifyArgs 
 }
 
 // TV sums of one chunk pair at T > 0: with the chunk's words (mu_t, S_t,
-// mu_d) and the row normalisers, the weights e = 2^(z s - mu) are rebuilt
-// exactly as the statistics made them; *cmin = the chunk's sum min(p, q) and
+// mu_d) and its pair scale, the weights e = 2^(z s - mu) are rebuilt exactly
+// as the statistics made them; *cmin = the chunk's sum min(p, q) and
 // *cres its residual mass sum [q - p]_+.  The logits must be fixed (past-the-
 // row slots -inf).
 template <int N, typename RT, typename RD>
 __device__ __forceinline__ void tv_sums(const RT &rt, const RD &rd, float s, float mut, float St,
-                                        float mud, const RowNorm &nt, const RowNorm &nd,
-                                        double *cmin, double *cres) {
-    const PairScale ps = pair_scale(mut, mud, nt, nd);
+                                        float mud, const PairScale &ps, double *cmin,
+                                        double *cres) {
     const float reft = exp_ref(mut), refd = exp_ref(mud);
     // min(p, q) in units of ps.unit, summed in the same slot order as the
     // chunk's weight sum in the statistics pass, so a chunk with q <= p
@@ -1449,39 +1483,42 @@ __device__ __forceinline__ void tv_sums(const RT &rt, const RD &rd, float s, flo
 }
 
 // TV of pair item x at T > 0 (chunk re-read, from the Infinity Cache when the
-// rows fit there), with the chunk's words and the unit's normalisers from the
-// earlier launches (w8: lanes 0..3 the chunk's words, 4..7 the normalisers).
+// rows fit there), with the chunk's words and pair scale from the earlier
+// launches (w8: lanes 0..3 the chunk's words, 4..6 its pair scale).
 template <int N, typename RT, typename RD>
 __device__ __forceinline__ void tv_item(const VerifyArgs &a, const Item &x, RT &rt, RD &rd,
                                         uint32_t w8) {
     rt.fix();
     rd.fix();
     double cmin, cres;
-    const RowNorm nt = row_norm(__uint_as_float(rl(w8, 4)), __uint_as_float(rl(w8, 5)));
-    const RowNorm nd = row_norm(__uint_as_float(rl(w8, 6)), __uint_as_float(rl(w8, 7)));
+    PairScale ps;
+    ps.kt = __uint_as_float(rl(w8, 4));
+    ps.kd = __uint_as_float(rl(w8, 5));
+    ps.unit = __uint_as_float(rl(w8, 6));
     tv_sums<N>(rt, rd, x.s, __uint_as_float(rl(w8, 0)), __uint_as_float(rl(w8, 1)),
-               __uint_as_float(rl(w8, 2)), nt, nd, &cmin, &cres);
+               __uint_as_float(rl(w8, 2)), ps, &cmin, &cres);
     publish_n(a.st2 + ((size_t)x.u * a.C + x.c) * 2, a.tag, 2, __float_as_uint((float)cmin),
               __float_as_uint((float)cres), 0u, 0u);
 }
 
-// Issues the loads of pair item x: its chunk of both rows, and (lanes 0..7)
-// the chunk's words and the unit's normalisers.
+// Issues the loads of pair item x: its chunk of both rows, and (lanes 0..6)
+// the chunk's words and pair scale.
 template <typename TT, typename TD, int N, int EPV>
 __device__ __forceinline__ uint64_t load_tv_item(const VerifyArgs &a, const Item &x,
                                                  RawChunk<TT, N, EPV> &rt,
                                                  RawChunk<TD, N, EPV> &rd) {
     const int lane = lane_id();
-    const uint64_t *p = (lane < 4) ? a.st1 + ((size_t)x.u * a.C + x.c) * 4 + lane
-                                   : a.nrm + (size_t)x.u * 4 + (lane & 3);
+    const size_t ch = (size_t)x.u * a.C + x.c;
+    const uint64_t *p = (lane < 4) ? a.st1 + ch * 4 + lane : a.psc + ch * 4 + (lane & 3);
     // plain loads: both kinds of word were written by earlier launches
-    const uint64_t w = (lane < 8) ? *p : 0;
+    const uint64_t w = (lane < 7) ? *p : 0;
     load_item(a, x, rt, rd);
     return w;
 }
 
 // Kernel 2: one wave per draft position at T > 0 folds launch 1's chunk
-// words into the position's row normalisers and runs the accept test.
+// words into the position's row normalisers and each chunk's pair scale, and
+// runs the accept test.
 template <typename TT, typename TD, int N, int EPV>
 __global__ void __launch_bounds__(kBlock) fold_kernel(VerifyArgs a) {
     a.tag = call_tag(a.ctl);
@@ -1503,8 +1540,8 @@ __global__ void __launch_bounds__(kBlock, kStreamWaves) tv_kernel(VerifyArgs a) 
     RawChunk<TD, N, EPV> rd;
     while (cur.next(a, x)) {
         const uint64_t w = load_tv_item(a, x, rt, rd);
-        // lanes 0..3: launch 1's chunk words, 4..7: launch 2's normalisers
-        if (__ballot(lane < 8 && (uint32_t)(w >> 32) != a.tag) && lane == 0)
+        // lanes 0..3: launch 1's chunk words, 4..6: launch 2's pair scale
+        if (__ballot(lane < 7 && (uint32_t)(w >> 32) != a.tag) && lane == 0)
             atomic_or_u32(&a.ctl->status, SPEC_DEV_SPIN_TIMEOUT);
         tv_item<N>(a, x, rt, rd, (uint32_t)w);
     }
@@ -1529,7 +1566,7 @@ struct Plan {
     int C;           // chunks per row
     long units;
     // tagged words after the control block
-    size_t off_st1, off_st2, off_nrm, off_rec, bytes;
+    size_t off_st1, off_st2, off_nrm, off_rec, off_psc, bytes;
 };
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -1551,7 +1588,8 @@ bool make_plan(long R, long units_per_req, long V, Plan &p) {
     p.off_st2 = round_up(p.off_st1 + 32 * (size_t)units * C, 256);
     p.off_nrm = round_up(p.off_st2 + 16 * (size_t)units * C, 256);
     p.off_rec = round_up(p.off_nrm + 32 * (size_t)units, 256);
-    p.bytes = round_up(p.off_rec + 8 * kRecWords * (size_t)units, 256);
+    p.off_psc = round_up(p.off_rec + 8 * kRecWords * (size_t)units, 256);
+    p.bytes = round_up(p.off_psc + 32 * (size_t)units * C, 256);
     return true;
 }
 
@@ -1673,6 +1711,7 @@ void bind_workspace(VerifyArgs &a, void *ws, const Plan &p) {
     a.st2 = (uint64_t *)(b + p.off_st2);
     a.nrm = (uint64_t *)(b + p.off_nrm);
     a.rec = (uint64_t *)(b + p.off_rec);
+    a.psc = (uint64_t *)(b + p.off_psc);
     a.C = p.C;
 }
 

@@ -100,6 +100,26 @@ def test_equal_siblings_and_ties_across_slices(sv, dev):
     check(run(sv, dev, L, parent, tokens, [M], 2), ref)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_signed_zero_maximum_across_slices(sv, dev, dtype):
+    """A row whose maximum is zero, -0.0 at a lower id (one slice) and +0.0 at
+    a higher one (another slice): the two are equal, so the lower id is the
+    argmax, as for any tie."""
+    V, M = 20000, 3
+    L = np.full((1, M, V), -1.0, np.float32)
+    L[0, 0, 9000] = -0.0
+    L[0, 0, 17000] = 0.0
+    L[0, 1, 17000] = -0.0                                  # same again one level down,
+    L[0, 1, 9000] = 0.0                                    # with the signs swapped
+    assert np.signbit(L[0, 0, 9000]) and not np.signbit(L[0, 0, 17000])
+    parent = np.array([[-1, 0, 1]], np.int32)
+    tokens = np.array([[-1, 9000, 9000]], np.int32)
+    ref = otree.tree_verify(L, parent, tokens, np.array([M]))
+    assert ref["accepted"][0] == 2 and ref["committed"][0, 2] == int(np.argmax(L[0, 2]))
+    Ls = workloads.f32_to_bf16_bits(L) if dtype == "bf16" else L
+    check(run(sv, dev, Ls, parent, tokens, [M], 2), ref)
+
+
 @pytest.mark.parametrize("fault", ["parent_forward", "token_high", "n_zero", "too_deep",
                                    "nan_on_path", "inf_on_path"])
 def test_invalid_trees(sv, dev, fault):
