@@ -25,7 +25,8 @@
  *
  * Conventions for every entry point:
  *  - Every array pointer is a DEVICE pointer owned by the caller.  The library
- *    never allocates, frees or synchronises (except spec_get_device_status),
+ *    never allocates, frees or synchronises (except spec_get_device_status;
+ *    spec_verify_batch_noalloc uses a fixed array of its own, see there),
  *    and enqueues its work on `stream` (a hipStream_t passed as void*; NULL is
  *    the null stream).  Calls return once the work is enqueued.
  *  - Arrays are dense and row-major with the last dimension contiguous; logit
@@ -69,13 +70,17 @@ typedef enum {
     SPEC_EDTYPE = -2,        /* dtype not supported for this argument            */
     SPEC_EWORKSPACE = -3,    /* workspace null, too small or misaligned          */
     SPEC_EHIP = -4,          /* a HIP runtime call or kernel launch failed       */
-    SPEC_EUNSUPPORTED = -5   /* shape outside the supported range                */
+    SPEC_EUNSUPPORTED = -5,  /* shape outside the supported range                */
+    SPEC_ETOOLARGE = -6      /* the call needs more than the fixed scratch of
+                                spec_verify_batch_noalloc                        */
 } spec_status;
 
 /* Bits of the device status word kept in the workspace. */
 #define SPEC_DEV_BAD_REQUEST 0x1u   /* a request had invalid data (see above)      */
-#define SPEC_DEV_SPIN_TIMEOUT 0x2u  /* a cross-workgroup wait gave up; the outputs
-                                       of that call are undefined                  */
+#define SPEC_DEV_SPIN_TIMEOUT 0x2u  /* a word written by an earlier launch of the
+                                       call was still stale after a bounded re-poll
+                                       (an earlier launch failed); the outputs of
+                                       that call are undefined                     */
 
 /* Largest vocabulary the Markov-draft kernels accept. */
 #define SPEC_MAX_VOCAB 2097152
@@ -155,6 +160,36 @@ int spec_verify_batch(const void *target_logits, int t_dtype,
                       int32_t *out_tokens, int32_t *out_num_accepted,
                       float *out_cstar, float *out_resid_mass, float *out_logq,
                       void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * spec_verify_batch without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Arguments, outputs, dtypes, the order
+ * of work on `stream` and every result are those of spec_verify_batch; the
+ * workspace is instead a fixed device array inside the library, one per
+ * device, SPEC_NOALLOC_SCRATCH_BYTES long, taken at its device address on the
+ * first call on that device and held until the process ends.  The call makes
+ * no allocation (device or host).
+ * Limits: a call whose workspace (spec_verify_workspace_bytes(R, gamma, V))
+ * exceeds SPEC_NOALLOC_SCRATCH_BYTES returns SPEC_ETOOLARGE before enqueueing
+ * anything.  Every call on one device shares that device's array: calls that
+ * may overlap on one device (different streams, or different host threads
+ * without ordering) race and must not be issued; calls ordered on one stream
+ * are fine.  The array keeps the last call's contents; each call's words
+ * carry that call's tag, so nothing needs clearing between calls.  Device-side
+ * data faults still mark the faulty request's outputs (num_accepted = -1,
+ * tokens -1, NaN floats); the status bits themselves stay in the library's
+ * array and are not reported.
+ */
+#define SPEC_NOALLOC_SCRATCH_BYTES (32u << 20)
+int spec_verify_batch_noalloc(const void *target_logits, int t_dtype,
+                              const void *draft_logits, int d_dtype,
+                              const int32_t *draft_tokens, const int32_t *verify_len,
+                              const float *temperature, const float *u_accept,
+                              const float *u_sample, int R, int gamma, int V,
+                              int32_t *out_tokens, int32_t *out_num_accepted,
+                              float *out_cstar, float *out_resid_mass, float *out_logq,
+                              void *stream);
 
 /* Workspace bytes for spec_tv_accept_rate. */
 size_t spec_tv_workspace_bytes(int N, int V);

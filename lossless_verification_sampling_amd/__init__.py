@@ -24,6 +24,8 @@ LIB_PATH = os.path.join(_PKG, "libspecverify.so")
 
 SPEC_F32, SPEC_BF16 = 0, 1
 SPEC_OK = 0
+SPEC_ETOOLARGE = -6
+SPEC_NOALLOC_SCRATCH_BYTES = 32 << 20
 SPEC_DEV_BAD_REQUEST = 0x1
 SPEC_DEV_SPIN_TIMEOUT = 0x2
 SPEC_MAX_VOCAB = 2097152
@@ -41,6 +43,7 @@ EXPORTED = (
     "spec_verify_workspace_bytes",
     "spec_workspace_init",
     "spec_verify_batch",
+    "spec_verify_batch_noalloc",
     "spec_tv_workspace_bytes",
     "spec_tv_accept_rate",
     "spec_markov_workspace_bytes",
@@ -83,6 +86,9 @@ def _load() -> ctypes.CDLL:
     lib.spec_workspace_init.argtypes = [p, sz, p]
     lib.spec_verify_batch.restype = i
     lib.spec_verify_batch.argtypes = [p, i, p, i, p, p, p, p, p, i, i, i, p, p, p, p, p, p, sz, p]
+    lib.spec_verify_batch_noalloc.restype = i
+    lib.spec_verify_batch_noalloc.argtypes = [p, i, p, i, p, p, p, p, p, i, i, i, p, p, p, p, p,
+                                              p]
     lib.spec_tv_accept_rate.restype = i
     lib.spec_tv_accept_rate.argtypes = [p, p, i, p, i, i, p, p, p, sz, p]
     lib.spec_markov_draft_sample.restype = i
@@ -255,17 +261,10 @@ def spec_get_device_status(workspace: Workspace, clear: bool = True, stream=None
 # entry points
 # ---------------------------------------------------------------------------
 
-def spec_verify_batch(target_logits: torch.Tensor, draft_logits: Optional[torch.Tensor],
-                      draft_tokens: Optional[torch.Tensor], verify_len: torch.Tensor,
-                      temperature: torch.Tensor, u_accept: Optional[torch.Tensor],
-                      u_sample: torch.Tensor, *, out: Optional[dict] = None,
-                      want_cstar: bool = True, want_resid: bool = True, want_logq: bool = True,
-                      workspace: Optional[Workspace] = None, stream=None) -> dict:
-    """Batched verification.  target_logits [R, gamma+1, V], draft_logits
-    [R, gamma, V] (float32 / bfloat16), draft_tokens [R, gamma] int32,
-    verify_len [R] int32, temperature [R] float32, u_accept [R, gamma] and
-    u_sample [R, gamma+1] float32.  Returns dict(tokens, num_accepted, cstar,
-    resid_mass, logq); `out` may supply preallocated output tensors."""
+def _verify_io(target_logits, draft_logits, draft_tokens, verify_len, temperature, u_accept,
+               u_sample, out, want_cstar, want_resid, want_logq):
+    """Checks the inputs of a verification call and returns (R, gamma, V, outputs)
+    with the missing output tensors allocated."""
     R, G1, V = target_logits.shape
     gamma = G1 - 1
     dev = target_logits.device
@@ -298,6 +297,25 @@ def spec_verify_batch(target_logits: torch.Tensor, draft_logits: Optional[torch.
     _check(o_cs, "out cstar", torch.float32, (R, gamma), dev)
     _check(o_rs, "out resid_mass", torch.float32, (R, gamma), dev)
     _check(o_lq, "out logq", torch.float32, (R, G1), dev)
+    return R, gamma, V, dict(tokens=o_tok, num_accepted=o_n, cstar=o_cs, resid_mass=o_rs,
+                             logq=o_lq)
+
+
+def spec_verify_batch(target_logits: torch.Tensor, draft_logits: Optional[torch.Tensor],
+                      draft_tokens: Optional[torch.Tensor], verify_len: torch.Tensor,
+                      temperature: torch.Tensor, u_accept: Optional[torch.Tensor],
+                      u_sample: torch.Tensor, *, out: Optional[dict] = None,
+                      want_cstar: bool = True, want_resid: bool = True, want_logq: bool = True,
+                      workspace: Optional[Workspace] = None, stream=None) -> dict:
+    """Batched verification.  target_logits [R, gamma+1, V], draft_logits
+    [R, gamma, V] (float32 / bfloat16), draft_tokens [R, gamma] int32,
+    verify_len [R] int32, temperature [R] float32, u_accept [R, gamma] and
+    u_sample [R, gamma+1] float32.  Returns dict(tokens, num_accepted, cstar,
+    resid_mass, logq); `out` may supply preallocated output tensors."""
+    R, gamma, V, o = _verify_io(target_logits, draft_logits, draft_tokens, verify_len,
+                                temperature, u_accept, u_sample, out, want_cstar, want_resid,
+                                want_logq)
+    dev = target_logits.device
     ws = workspace or default_workspace(dev)
     need = spec_verify_workspace_bytes(R, gamma, V)
     if need == 0:
@@ -306,11 +324,39 @@ def spec_verify_batch(target_logits: torch.Tensor, draft_logits: Optional[torch.
     d_dtype = _dtype(draft_logits) if draft_logits is not None else SPEC_F32
     st = _lib.spec_verify_batch(_ptr(target_logits), _dtype(target_logits), _ptr(draft_logits),
                                 d_dtype, _ptr(draft_tokens), _ptr(verify_len), _ptr(temperature),
-                                _ptr(u_accept), _ptr(u_sample), R, gamma, V, _ptr(o_tok),
-                                _ptr(o_n), _ptr(o_cs), _ptr(o_rs), _ptr(o_lq), _ptr(buf),
+                                _ptr(u_accept), _ptr(u_sample), R, gamma, V, _ptr(o["tokens"]),
+                                _ptr(o["num_accepted"]), _ptr(o["cstar"]),
+                                _ptr(o["resid_mass"]), _ptr(o["logq"]), _ptr(buf),
                                 buf.numel(), _stream_ptr(stream, dev))
     _raise(st, "spec_verify_batch")
-    return dict(tokens=o_tok, num_accepted=o_n, cstar=o_cs, resid_mass=o_rs, logq=o_lq)
+    return o
+
+
+def spec_verify_batch_noalloc(target_logits: torch.Tensor, draft_logits: Optional[torch.Tensor],
+                              draft_tokens: Optional[torch.Tensor], verify_len: torch.Tensor,
+                              temperature: torch.Tensor, u_accept: Optional[torch.Tensor],
+                              u_sample: torch.Tensor, *, out: dict, stream=None) -> dict:
+    """spec_verify_batch on the library's fixed per-device scratch instead of
+    a workspace (no allocation in the library).  `out` must hold every output
+    tensor the call writes (tokens, num_accepted; cstar, resid_mass, logq or
+    None), so that the call allocates nothing here either."""
+    for k in ("tokens", "num_accepted", "cstar", "resid_mass", "logq"):
+        if k not in out:
+            raise ValueError(f"spec_verify_batch_noalloc: out[{k!r}] must be given "
+                             "(a tensor, or None for an optional output)")
+    R, gamma, V, o = _verify_io(target_logits, draft_logits, draft_tokens, verify_len,
+                                temperature, u_accept, u_sample, out, False, False, False)
+    dev = target_logits.device
+    d_dtype = _dtype(draft_logits) if draft_logits is not None else SPEC_F32
+    st = _lib.spec_verify_batch_noalloc(_ptr(target_logits), _dtype(target_logits),
+                                        _ptr(draft_logits), d_dtype, _ptr(draft_tokens),
+                                        _ptr(verify_len), _ptr(temperature), _ptr(u_accept),
+                                        _ptr(u_sample), R, gamma, V, _ptr(o["tokens"]),
+                                        _ptr(o["num_accepted"]), _ptr(o["cstar"]),
+                                        _ptr(o["resid_mass"]), _ptr(o["logq"]),
+                                        _stream_ptr(stream, dev))
+    _raise(st, "spec_verify_batch_noalloc")
+    return o
 
 
 def spec_tv_accept_rate(draft_logits: torch.Tensor, target_logits: torch.Tensor,

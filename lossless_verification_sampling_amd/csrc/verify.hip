@@ -54,9 +54,7 @@
 #include <stdlib.h>
 
 #include <atomic>
-#include <mutex>
 #include <type_traits>
-#include <vector>
 
 #include "common.h"
 
@@ -1602,40 +1600,64 @@ bool dtype_ok(int d) { return d == SPEC_F32 || d == SPEC_BF16; }
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
-// Resident workgroups of a kernel with `lds` bytes of dynamic shared memory on
-// the current device (cached per kernel, device and size).
+// Host-side caches of occupancy queries and compute-unit counts: fixed tables
+// of plain values behind a spin lock, so that no call allocates host memory
+// and nothing needs destroying when the process exits.
+constexpr int kMaxDevices = 64;
+constexpr int kOccSlots = 512;
+struct OccEntry {
+    const void *k;
+    int dev;
+    size_t lds;
+    long cap;
+};
+OccEntry g_occ[kOccSlots];
+int g_occ_n = 0;
+std::atomic_flag g_occ_lock = ATOMIC_FLAG_INIT;
+std::atomic<int> g_cus[kMaxDevices];
+
+struct SpinGuard {
+    std::atomic_flag &f;
+    explicit SpinGuard(std::atomic_flag &flag) : f(flag) {
+        while (f.test_and_set(std::memory_order_acquire)) {
+        }
+    }
+    ~SpinGuard() { f.clear(std::memory_order_release); }
+};
+
+// Resident workgroups of `kernel` (kBlock threads, `lds` bytes of dynamic
+// shared memory) on the whole current device, 0 if unknown.
 long resident_blocks(const void *kernel, size_t lds) {
-    struct Entry { const void *k; int dev; size_t lds; long cap; };
-    static std::mutex mu;
-    static std::vector<Entry> cache;
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return 0;
-    std::lock_guard<std::mutex> lock(mu);
-    for (const Entry &e : cache)
-        if (e.k == kernel && e.dev == dev && e.lds == lds) return e.cap;
+    {
+        SpinGuard g(g_occ_lock);
+        for (int e = 0; e < g_occ_n; ++e)
+            if (g_occ[e].k == kernel && g_occ[e].dev == dev && g_occ[e].lds == lds)
+                return g_occ[e].cap;
+    }
     int nb = 0, ncu = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kernel, kBlock, lds) != hipSuccess ||
         hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         return 0;
     const long cap = (long)nb * ncu;
-    cache.push_back(Entry{kernel, dev, lds, cap});
+    SpinGuard g(g_occ_lock);
+    if (g_occ_n < kOccSlots) g_occ[g_occ_n++] = OccEntry{kernel, dev, lds, cap};
     return cap;
 }
 
-
 // Compute units of the current device (cached per device; 0 if unknown).
 long device_cus() {
-    static std::mutex mu;
-    static std::vector<std::pair<int, int>> cache;
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return 0;
-    std::lock_guard<std::mutex> lock(mu);
-    for (const auto &e : cache)
-        if (e.first == dev) return e.second;
+    if (dev >= 0 && dev < kMaxDevices) {
+        const int c = g_cus[dev].load(std::memory_order_relaxed);
+        if (c > 0) return c;
+    }
     int ncu = 0;
     if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         return 0;
-    cache.emplace_back(dev, ncu);
+    if (dev >= 0 && dev < kMaxDevices) g_cus[dev].store(ncu, std::memory_order_relaxed);
     return ncu;
 }
 
@@ -1720,6 +1742,30 @@ void bind_workspace(VerifyArgs &a, void *ws, const Plan &p) {
 
 using namespace sv;
 
+// Workspace of spec_verify_batch_noalloc: one copy per device, zero-filled
+// when the code object is loaded, held until the process ends.  Host code
+// never passes this name to a kernel (on the host it only stands for the
+// symbol): it uses the device address hipGetSymbolAddress gives for it.
+static __device__ __align__(256) uint8_t scratch[SPEC_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+// Device address of `scratch` per device, taken on the first call there.
+std::atomic<void *> g_scratch_ptr[sv::kMaxDevices];
+
+int scratch_ptr(void **out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= sv::kMaxDevices) return SPEC_EHIP;
+    void *p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        // the current device is `dev`: its copy of the array
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return SPEC_EHIP;
+        g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+    *out = p;
+    return SPEC_OK;
+}
+}  // namespace
+
 extern "C" {
 
 int spec_version(void) { return 200; }
@@ -1732,6 +1778,9 @@ const char *spec_status_string(int status) {
         case SPEC_EWORKSPACE: return "SPEC_EWORKSPACE: workspace null, too small or misaligned";
         case SPEC_EHIP: return "SPEC_EHIP: HIP runtime call or kernel launch failed";
         case SPEC_EUNSUPPORTED: return "SPEC_EUNSUPPORTED: shape outside the supported range";
+        case SPEC_ETOOLARGE:
+            return "SPEC_ETOOLARGE: the call needs more workspace than the no-allocation "
+                   "entry point's fixed scratch holds";
     }
     return "unknown spec_status";
 }
@@ -1816,6 +1865,28 @@ int spec_verify_batch(const void *target_logits, int t_dtype, const void *draft_
     // with gamma == 0 no draft row exists; the draft type only shapes the plan
     const int ddt = gamma > 0 ? d_dtype : t_dtype;
     return launch(a, t_dtype, ddt, p.N, vec, (hipStream_t)stream);
+}
+
+int spec_verify_batch_noalloc(const void *target_logits, int t_dtype, const void *draft_logits,
+                              int d_dtype, const int32_t *draft_tokens,
+                              const int32_t *verify_len, const float *temperature,
+                              const float *u_accept, const float *u_sample, int R, int gamma,
+                              int V, int32_t *out_tokens, int32_t *out_num_accepted,
+                              float *out_cstar, float *out_resid_mass, float *out_logq,
+                              void *stream) {
+    if (R < 0 || gamma < 0 || V < 1) return SPEC_EINVAL;
+    if (gamma > kMaxGamma || V > SPEC_MAX_VERIFY_VOCAB) return SPEC_EUNSUPPORTED;
+    if (R == 0) return SPEC_OK;
+    const size_t need = spec_verify_workspace_bytes(R, gamma, V);
+    if (need == 0) return SPEC_EUNSUPPORTED;
+    if (need > (size_t)SPEC_NOALLOC_SCRATCH_BYTES) return SPEC_ETOOLARGE;
+    void *ws = nullptr;
+    const int st = scratch_ptr(&ws);
+    if (st != SPEC_OK) return st;
+    return spec_verify_batch(target_logits, t_dtype, draft_logits, d_dtype, draft_tokens,
+                             verify_len, temperature, u_accept, u_sample, R, gamma, V, out_tokens,
+                             out_num_accepted, out_cstar, out_resid_mass, out_logq, ws,
+                             (size_t)SPEC_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 int spec_tv_accept_rate(const void *draft_logits, const void *target_logits, int dtype,

@@ -12,6 +12,8 @@ HEADER = os.path.join(ROOT, "include", "specverify.h")
 LIB = os.path.join(ROOT, "lossless_verification_sampling_amd", "libspecverify.so")
 
 SPEC_OK, SPEC_EINVAL, SPEC_EDTYPE, SPEC_EWORKSPACE, SPEC_EHIP, SPEC_EUNSUPPORTED = 0, -1, -2, -3, -4, -5
+SPEC_ETOOLARGE = -6
+NOALLOC_SCRATCH = 32 << 20
 
 
 def declared_functions():
@@ -42,7 +44,8 @@ def test_python_binding_names_match_header():
 
 def test_status_strings_and_version(lib):
     lib.spec_status_string.restype = ctypes.c_char_p
-    for s in (SPEC_OK, SPEC_EINVAL, SPEC_EDTYPE, SPEC_EWORKSPACE, SPEC_EHIP, SPEC_EUNSUPPORTED):
+    for s in (SPEC_OK, SPEC_EINVAL, SPEC_EDTYPE, SPEC_EWORKSPACE, SPEC_EHIP, SPEC_EUNSUPPORTED,
+              SPEC_ETOOLARGE):
         assert lib.spec_status_string(s).startswith(b"SPEC_")
     assert lib.spec_version() >= 100
 
@@ -285,3 +288,32 @@ def test_workspace_init_validation(lib):
     assert f(None, 1024, None) == SPEC_EWORKSPACE
     assert f(ctypes.c_void_p(0x10010), 1024, None) == SPEC_EWORKSPACE
     assert f(ctypes.c_void_p(0x10000), 16, None) == SPEC_EWORKSPACE
+
+
+def test_noalloc_size_limits(lib):
+    """The no-allocation verify rejects, before any HIP call, sizes whose
+    workspace exceeds its fixed scratch, and invalid sizes as spec_verify_batch
+    does."""
+    p = ctypes.c_void_p
+    fake = p(0x1000)
+    f = lib.spec_verify_batch_noalloc
+    f.restype = ctypes.c_int
+    f.argtypes = [p, ctypes.c_int, p, ctypes.c_int, p, p, p, p, p, ctypes.c_int, ctypes.c_int,
+                  ctypes.c_int, p, p, p, p, p, p]
+    w = lib.spec_verify_workspace_bytes
+    w.restype = ctypes.c_size_t
+
+    def call(R, gamma, V):
+        return f(fake, 1, fake, 1, fake, fake, fake, fake, fake, R, gamma, V, fake, fake, None,
+                 None, None, None)
+
+    # the largest batched shapes of the workloads fit; twice the 256-request
+    # high-load batch at V = 151936 does not
+    assert w(256, 7, 129280) <= NOALLOC_SCRATCH and w(64, 7, 151936) <= NOALLOC_SCRATCH
+    assert w(512, 7, 151936) > NOALLOC_SCRATCH
+    assert call(512, 7, 151936) == SPEC_ETOOLARGE
+    assert call(64, 64, 262144) == SPEC_ETOOLARGE
+    assert call(-1, 7, 100) == SPEC_EINVAL
+    assert call(4, 7, 0) == SPEC_EINVAL
+    assert call(4, 65, 100) == SPEC_EUNSUPPORTED
+    assert call(0, 7, 100) == SPEC_OK
