@@ -926,15 +926,13 @@ __device__ __forceinline__ bool accept_eval(float zx, float dx, float s, float M
 // whatever the normalisers, so that the TV pass always finds current words;
 // an invalid unit's TV sums are not used.
 template <typename TT, typename TD>
-__device__ __forceinline__ void norm_fold(const VerifyArgs &a, const Item &x) {
+__device__ __forceinline__ void norm_fold(const VerifyArgs &a, const Item &x, int xtok,
+                                          float uacc) {
     const int lane = lane_id();
     const int C = a.C;
-    int xtok = 0;
-    float uacc = 0.0f, zx = 0.0f, dx = 0.0f;
+    float zx = 0.0f, dx = 0.0f;
     bool tok_ok = true;
     if (!a.tv_mode) {
-        xtok = a.tokens[(size_t)x.r * a.gamma + x.i];
-        uacc = a.ua[(size_t)x.r * a.gamma + x.i];
         tok_ok = xtok >= 0 && xtok < a.V;
         if (tok_ok) {
             zx = load_one(row_ptr<TT>(a.zt, x.r, a.tG, x.i, a.V), xtok);
@@ -990,6 +988,7 @@ struct UnitSum {
                              // inverse-CDF draw at this row (-1: no residual mass)
     float Mt, Zt, Md, Zd;    // row normalisers (T > 0)
     double tin;              // the draw's target minus the mass of chunks before sel
+    double lnZt;             // ln Zt (T > 0), for the log q of a draw at this row
 };
 
 constexpr int kReqWaves = 8;
@@ -1096,6 +1095,7 @@ __device__ __forceinline__ void tv_unit(const VerifyArgs &a, const Item &x, Unit
         s->Md = Md;
         s->Zd = Zd;
         s->tin = tin;
+        s->lnZt = log((double)Zt);
     }
 }
 
@@ -1153,6 +1153,7 @@ __device__ __forceinline__ void bonus_unit(const VerifyArgs &a, const Item &x, U
         s->Md = 0.0f;
         s->Zd = 1.0f;
         s->tin = tin;
+        s->lnZt = log((double)Zt);
     }
 }
 
@@ -1263,7 +1264,7 @@ __device__ __forceinline__ int request_draw(const VerifyArgs &a, int r, int j, i
         load_unit_words<4>(a.st1 + (size_t)u * C * 4, C, want4, a.tag, a.ctl, w4, true);
         tok = draw_from_q<TT, N, EPV, 4>(a, trow, w4, s, Mt, Zt, usm, &ztok);
     }
-    *lqd = (float)(((double)ztok * (double)s - (double)Mt) * kLn2 - log((double)Zt));
+    *lqd = (float)(((double)ztok * (double)s - (double)Mt) * kLn2 - su.lnZt);
     return tok;
 }
 
@@ -1313,6 +1314,14 @@ __global__ void __launch_bounds__(kReqBlock) combine_kernel(VerifyArgs a) {
         return;
     }
     const int r = blockIdx.x;
+    // the draft tokens the outputs copy, loaded with the request's parameters
+    // (wave 0 writes the outputs; lane k holds tokens k and 64 + k)
+    int32_t dtok[2] = {0, 0};
+    if (wave == 0) {
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+            if (b * 64 + lane < a.gamma) dtok[b] = a.tokens[(size_t)r * a.gamma + b * 64 + lane];
+    }
     Item x;
     x.r = r;
     x.c = 0;
@@ -1357,8 +1366,11 @@ __global__ void __launch_bounds__(kReqBlock) combine_kernel(VerifyArgs a) {
         tok = request_draw<TT, TD, N, EPV>(a, r, A, l, x.s, sum[A], &lqd);
     }
     const float nan = __builtin_nanf("");
-    for (int k = lane; k <= G; k += 64) {
-        const int32_t t = (k < A) ? a.tokens[(size_t)r * G + k] : (k == A ? tok : -1);
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+        const int k = b * 64 + lane;
+        if (k > G) break;
+        const int32_t t = (k < A) ? dtok[b] : (k == A ? tok : -1);
         a.out_tok[(size_t)r * (G + 1) + k] = t;
         if (a.out_lq)
             a.out_lq[(size_t)r * (G + 1) + k] = (k < A) ? sum[k].lqx : (k == A ? lqd : nan);
@@ -1415,19 +1427,6 @@ __device__ __forceinline__ void stats_item(const VerifyArgs &a, const Item &x, R
         }
     }
     publish_n(a.st1 + ((size_t)x.u * a.C + x.c) * 4, a.tag, 4, w0, w1, w2, w3);
-}
-
-// Item of unit u with chunk 0 (for the per-unit kernels); false if the unit
-// is not active (request malformed, or i > l_r).
-__device__ __forceinline__ bool unit_item(const VerifyArgs &a, long u, Item &x) {
-    if (u >= (long)a.R * a.UG) return false;
-    x.u = (int)u;
-    x.r = (int)(u / a.UG);
-    x.i = (int)(u % a.UG);
-    x.c = 0;
-    if (!request_ok(a, x.r, x.T, x.l) || x.i > x.l) return false;
-    x.s = x.T != 0.0f ? exp2_scale(x.T) : 0.0f;
-    return true;
 }
 
 // Kernel 1: every needed row streamed once from HBM, one item in flight per
@@ -1520,8 +1519,27 @@ __device__ __forceinline__ uint64_t load_tv_item(const VerifyArgs &a, const Item
 template <typename TT, typename TD, int N, int EPV>
 __global__ void __launch_bounds__(kBlock) fold_kernel(VerifyArgs a) {
     a.tag = call_tag(a.ctl);
+    const long u = wave_index();
+    if (u >= (long)a.R * a.UG) return;
     Item y;
-    if (unit_item(a, wave_index(), y) && y.T != 0.0f && is_pair(y)) norm_fold<TT, TD>(a, y);
+    y.u = (int)u;
+    y.r = (int)(u / a.UG);
+    y.i = (int)(u % a.UG);
+    y.c = 0;
+    // one round of loads: the request's parameters and the position's draft
+    // token and uniform (read before the position is known to be verified;
+    // they are in the arrays whenever i < gamma)
+    y.T = a.temp[y.r];
+    y.l = a.tv_mode ? 1 : a.vlen[y.r];
+    int xtok = 0;
+    float uacc = 0.0f;
+    if (!a.tv_mode && y.i < a.gamma) {
+        xtok = a.tokens[(size_t)y.r * a.gamma + y.i];
+        uacc = a.ua[(size_t)y.r * a.gamma + y.i];
+    }
+    if (!temperature_ok(y.T) || y.l < 0 || y.l > a.gamma || y.T == 0.0f || !is_pair(y)) return;
+    y.s = exp2_scale(y.T);
+    norm_fold<TT, TD>(a, y, xtok, uacc);
 }
 
 // Kernel 3: the TV pass over the pair items at T > 0, one item in flight per
