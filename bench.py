@@ -15,9 +15,11 @@ traffic, so the timed region streams from HBM.
 
 Prints one JSON line:
   value      verified draft positions per second (sum of l_r per call / time)
-  roofline   algorithmic bytes (every verified draft row and target row plus
-             the bonus row, read once) / average HIP-event time of the whole
-             call (its four kernels), against 8 TB/s
+  roofline   the dominant kernel, the statistics launch (it streams every
+             needed row once): algorithmic bytes (every verified draft row
+             and target row plus the bonus row, read once) / its average
+             HIP-event time inside the timed calls, against 8 TB/s;
+             call_roofline the same bytes over the whole call (four kernels)
   cpu_baseline  the fp64 oracle on the host over the same batch: all usable
              cores (up to a one-GPU share of 16, requests split over
              threads), with the one-thread figure beside it
@@ -55,6 +57,10 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 # The sources each counter entry's kernels are built from.
 TRAFFIC_SOURCES = {
     "verify_batched": ("common.h", "verify.hip"),
+    "verify_single_user": ("common.h", "verify.hip"),
+    "verify_dspark_verify": ("common.h", "verify.hip"),
+    "verify_high_load": ("common.h", "verify.hip"),
+    "verify_tiny": ("common.h", "verify.hip"),
     "markov_dspark": ("common.h", "markov.hip"),
     "rnn_head": ("common.h", "markov.hip"),
     "tree_greedy": ("common.h", "tree.hip"),
@@ -78,9 +84,10 @@ def source_hash(key: str) -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel_key: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
-    was taken on the current kernel sources; None otherwise."""
+def measured_traffic(kernel_key: str, kernel: str = None):
+    """HBM bytes per call (all of the library's kernels), or per launch of the
+    kernel whose name contains `kernel`, from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel sources; None otherwise."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
@@ -89,7 +96,46 @@ def measured_traffic(kernel_key: str):
     e = t.get(kernel_key)
     if not e or e.get("source_hash") != source_hash(kernel_key):
         return None
-    return e.get("bytes_per_launch")
+    if kernel is None:
+        return e.get("bytes_per_launch")
+    tot = [v for k, v in e.get("per_dispatch_fetch", {}).items() if kernel in k]
+    tot += [v for k, v in e.get("per_dispatch_write", {}).items() if kernel in k]
+    return sum(tot) if tot else None
+
+
+class HipEvents:
+    """hipEvent_t handles made through the HIP runtime torch has loaded, for
+    timing a launch inside a library call (torch.cuda.Event cannot be handed
+    to the library)."""
+
+    def __init__(self, n: int):
+        import ctypes
+        try:
+            self.hip = ctypes.CDLL("libamdhip64.so")
+        except OSError:
+            self.hip = ctypes.CDLL("/opt/rocm/lib/libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.events = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            if self.hip.hipEventCreate(ctypes.byref(e)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self.events.append(e.value)
+
+    def elapsed_ms(self, a: int, b: int) -> float:
+        import ctypes
+        ms = ctypes.c_float()
+        if self.hip.hipEventElapsedTime(ctypes.byref(ms), self.events[a], self.events[b]) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(ms.value)
+
+    def close(self):
+        for e in self.events:
+            self.hip.hipEventDestroy(e)
+        self.events = []
 
 
 def to_device(x, dev):
@@ -265,14 +311,27 @@ def bench_verify(args):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     kern_ms = np.array([a.elapsed_time(b) for a, b in ev])
+    # second timed pass of the same steps: the statistics launch of every call
+    # bracketed by HIP events that the library records on the call's stream
+    # (events inside a call add launch gaps, hence a pass of its own)
+    hev = HipEvents(2 * args.steps)
+    sv.spec_time_stats_launch(hev.events[:args.steps], hev.events[args.steps:])
+    for k in range(args.steps):
+        step(args.warmup + args.steps + k)
+    torch.cuda.synchronize()
+    sv.spec_time_stats_launch([], [])
+    stats_ms = np.array([hev.elapsed_ms(k, args.steps + k) for k in range(args.steps)])
+    hev.close()
     bits = sv.spec_get_device_status(ws, clear=True)
     if bits:
         raise RuntimeError(f"device status bits {bits:#x} during the timed steps")
     avg_kernel_s = float(kern_ms.mean()) / 1e3
+    avg_stats_s = float(stats_ms.mean()) / 1e3
     ms_per_step = wall / args.steps * 1e3
-    achieved = alg_bytes / avg_kernel_s / 1e9
+    achieved = alg_bytes / avg_stats_s / 1e9
+    call_achieved = alg_bytes / avg_kernel_s / 1e9
     key = "verify_" + args.workload
-    traffic = measured_traffic(key)
+    traffic = measured_traffic(key, "stats_kernel")
     tname = "bf16" if te == 2 else "f32"
     dname = "bf16" if de == 2 else "f32"
     Ts = sorted(set(float(t) for t in np.asarray(case.temperature).ravel()))
@@ -295,14 +354,24 @@ def bench_verify(args):
                    "logits": tname if tname == dname else f"target {tname}, draft {dname}",
                    "sum_verify_len": sum_l, "temperature": Ts, "seed": case.seed,
                    "input_copies": ncopy, "parallelism": "none (one GPU)"},
+        # the dominant kernel: the statistics launch streams every needed row
+        # once, so its algorithmic bytes are the call's
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "algorithmic_bytes_per_launch": alg_bytes,
-                     "kernel_ms_mean": float(kern_ms.mean()),
-                     "kernel_ms_p10": float(np.percentile(kern_ms, 10)),
-                     "kernel_ms_p90": float(np.percentile(kern_ms, 90)),
-                     "kernel": f"spec_verify_batch call: {VERIFY_KERNELS} "
-                               f"({tname}, {dname})"},
+                     "kernel_ms_mean": float(stats_ms.mean()),
+                     "kernel_ms_p10": float(np.percentile(stats_ms, 10)),
+                     "kernel_ms_p90": float(np.percentile(stats_ms, 90)),
+                     "kernel": f"stats_kernel<{tname}, {dname}> (HIP events around the launch "
+                               "inside each call of a second timed pass)"},
+        # the whole call (its four kernels) against the same bytes
+        "call_roofline": {"achieved": call_achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                          "frac": call_achieved / HBM_PEAK_GBS,
+                          "traffic": measured_traffic(key),
+                          "call_ms_mean": float(kern_ms.mean()),
+                          "call_ms_p10": float(np.percentile(kern_ms, 10)),
+                          "call_ms_p90": float(np.percentile(kern_ms, 90)),
+                          "kernels": f"spec_verify_batch: {VERIFY_KERNELS} ({tname}, {dname})"},
         "kernel_positions_per_s": sum_l / avg_kernel_s,
     }
     if not args.no_cpu_baseline:
@@ -700,7 +769,7 @@ def write_traffic(args):
     (one-time workspace set-up) are left out.  Writes the entry under --key
     in the traffic file, stamped with the current source hash."""
     fetch_dir, write_dir, cfetch_dir, cwrite_dir = args.traffic_from
-    calls = args.warmup + args.steps
+    calls = args.calls or (args.warmup + args.steps)
     copy_bytes = 256 << 20
 
     def scale(d, counter):
@@ -723,10 +792,12 @@ def write_traffic(args):
             n, tot = per_kernel.get(key, (0, 0.0))
             per_kernel[key] = (n + 1, tot + v)
         out = {k: tot * 1024.0 * sc / calls for k, (n, tot) in per_kernel.items() if n >= calls}
-        return out
+        per_dispatch = {k: tot * 1024.0 * sc / n for k, (n, tot) in per_kernel.items()
+                        if n >= calls}
+        return out, per_dispatch
 
     fs, ws = scale(cfetch_dir, "FETCH_SIZE"), scale(cwrite_dir, "WRITE_SIZE")
-    fk, wk = per_call(fetch_dir, "FETCH_SIZE", fs), per_call(write_dir, "WRITE_SIZE", ws)
+    (fk, fkd), (wk, wkd) = per_call(fetch_dir, "FETCH_SIZE", fs), per_call(write_dir, "WRITE_SIZE", ws)
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
@@ -738,6 +809,7 @@ def write_traffic(args):
         "fetch_bytes": sum(fk.values()), "write_bytes": sum(wk.values()),
         "fetch_scale": fs, "write_scale": ws,
         "per_kernel_fetch": fk, "per_kernel_write": wk,
+        "per_dispatch_fetch": fkd, "per_dispatch_write": wkd,
         "note": "per call, summed over the library's kernels; FETCH_SIZE then WRITE_SIZE in "
                 "separate rocprofv3 --pmc runs, scaled by a 256 MiB device copy",
     }
@@ -765,6 +837,9 @@ def main():
                     help="rocprofv3 --pmc output folders: write the traffic entry --key from them "
                          "(--steps/--warmup as in the counted run)")
     ap.add_argument("--key", default="verify_batched")
+    ap.add_argument("--calls", type=int, default=0,
+                    help="library calls in the counted run (default --warmup + --steps; the "
+                         "verify workloads make two timed passes: --warmup + 2 --steps)")
     ap.add_argument("--copies-counted", type=int, default=6,
                     help="copies in the counted --calibrate-copy run")
     args = ap.parse_args()

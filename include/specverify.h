@@ -191,6 +191,19 @@ int spec_verify_batch_noalloc(const void *target_logits, int t_dtype,
                               float *out_cstar, float *out_resid_mass, float *out_logq,
                               void *stream);
 
+/*
+ * Measurement hook.  For the next n verification calls (spec_verify_batch,
+ * spec_verify_batch_noalloc, spec_tv_accept_rate) made by the calling host
+ * thread, the library records the events before[i] and after[i] (hipEvent_t
+ * passed as void*, created and owned by the caller) on the call's stream
+ * immediately before and after its statistics launch -- the launch that
+ * streams every needed logit row from HBM -- so that the caller can time
+ * that kernel alone (hipEventElapsedTime).  The arrays must stay valid until
+ * those n calls have been made; n = 0 stops.  Returns SPEC_EINVAL for n < 0
+ * or missing arrays.
+ */
+int spec_time_stats_launch(void *const *before, void *const *after, int n);
+
 /* Workspace bytes for spec_tv_accept_rate. */
 size_t spec_tv_workspace_bytes(int N, int V);
 

@@ -57,6 +57,7 @@ EXPORTED = (
     "spec_tree_verify",
     "spec_markov_draft_sample",
     "spec_get_device_status",
+    "spec_time_stats_launch",
 )
 
 
@@ -86,6 +87,8 @@ def _load() -> ctypes.CDLL:
     lib.spec_workspace_init.argtypes = [p, sz, p]
     lib.spec_verify_batch.restype = i
     lib.spec_verify_batch.argtypes = [p, i, p, i, p, p, p, p, p, i, i, i, p, p, p, p, p, p, sz, p]
+    lib.spec_time_stats_launch.restype = i
+    lib.spec_time_stats_launch.argtypes = [p, p, i]
     lib.spec_verify_batch_noalloc.restype = i
     lib.spec_verify_batch_noalloc.argtypes = [p, i, p, i, p, p, p, p, p, i, i, i, p, p, p, p, p,
                                               p]
@@ -357,6 +360,24 @@ def spec_verify_batch_noalloc(target_logits: torch.Tensor, draft_logits: Optiona
                                         _stream_ptr(stream, dev))
     _raise(st, "spec_verify_batch_noalloc")
     return o
+
+
+def spec_time_stats_launch(before, after) -> None:
+    """Times the statistics launch of the calling thread's next len(before)
+    verification calls: `before` and `after` are sequences of hipEvent_t
+    handles (ints) that the library records around that launch.  The arrays
+    are kept alive here until the next call of this function."""
+    global _timing_arrays
+    n = len(before)
+    if len(after) != n:
+        raise ValueError("spec_time_stats_launch: before and after differ in length")
+    arr_t = ctypes.c_void_p * max(n, 1)
+    _timing_arrays = (arr_t(*before), arr_t(*after))
+    _raise(_lib.spec_time_stats_launch(_timing_arrays[0], _timing_arrays[1], n),
+           "spec_time_stats_launch")
+
+
+_timing_arrays = None
 
 
 def spec_tv_accept_rate(draft_logits: torch.Tensor, target_logits: torch.Tensor,

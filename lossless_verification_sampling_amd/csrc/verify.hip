@@ -1692,6 +1692,15 @@ long persistent_grid(const void *k, size_t lds, long items) {
     return g > 0 ? g : 1;
 }
 
+// Events recorded around the statistics launch of the calling thread's next
+// verification calls (spec_time_stats_launch).
+struct StatsTiming {
+    void *const *before;
+    void *const *after;
+    int n, i;
+};
+thread_local StatsTiming g_stats_timing = {nullptr, nullptr, 0, 0};
+
 // Shared memory of the unit table (0: too large, walk all candidates).
 constexpr size_t kMaxTableBytes = 32768;
 size_t table_bytes(const VerifyArgs &a) {
@@ -1716,8 +1725,12 @@ int launch_kernels(VerifyArgs a, hipStream_t st) {
         fprintf(stderr, "[specverify] verify N=%d EPV=%d C=%d items=%ld grids %ld / %ld lds %zu\n",
                 N, EPV, a.C, items, g1, g3, lds);
     }
+    StatsTiming &tm = g_stats_timing;
+    const bool timed = tm.i < tm.n;
+    if (timed) (void)hipEventRecord((hipEvent_t)tm.before[tm.i], st);
     hipLaunchKernelGGL((stats_kernel<TT, TD, N, EPV>), dim3((unsigned)g1), dim3(kBlock), lds, st,
                        a);
+    if (timed) (void)hipEventRecord((hipEvent_t)tm.after[tm.i++], st);
     hipLaunchKernelGGL((fold_kernel<TT, TD, N, EPV>), dim3((unsigned)gf), dim3(kBlock), 0, st, a);
     hipLaunchKernelGGL((tv_kernel<TT, TD, N, EPV>), dim3((unsigned)g3), dim3(kBlock), lds, st, a);
     hipLaunchKernelGGL((combine_kernel<TT, TD, N, EPV>), dim3((unsigned)gc), dim3(kReqBlock), 0,
@@ -1821,6 +1834,12 @@ int spec_workspace_init(void *workspace, size_t workspace_bytes, void *stream) {
     hipLaunchKernelGGL(zero_fill_kernel, dim3((unsigned)(blocks < 4096 ? blocks : 4096)),
                        dim3(kBlock), 0, (hipStream_t)stream, (uint32_t *)workspace, words);
     if (hipGetLastError() != hipSuccess) return SPEC_EHIP;
+    return SPEC_OK;
+}
+
+int spec_time_stats_launch(void *const *before, void *const *after, int n) {
+    if (n < 0 || (n > 0 && (!before || !after))) return SPEC_EINVAL;
+    g_stats_timing = StatsTiming{before, after, n, 0};
     return SPEC_OK;
 }
 
