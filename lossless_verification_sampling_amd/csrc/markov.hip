@@ -9,8 +9,8 @@
 // Sampling is serial over k because x_k feeds the bias of step k+1.
 //
 // Per step k two launches:
-//  * markov_logits_kernel: one workgroup per 128-logit tile of the vocabulary.
-//    The tile of W2 ([256][128] bf16) is staged in LDS transposed, w2t[n][k],
+//  * markov_logits_kernel: one workgroup per 64-logit tile of the vocabulary.
+//    The tile of W2 ([256][64] bf16) is staged in LDS transposed, w2t[n][k],
 //    by loading 8x8 blocks, transposing them in registers and writing 16-byte
 //    rows.  The product b[v][r] = sum_k W2[k][v] W1[x_r][k] runs on
 //    v_mfma_f32_16x16x32_bf16 with the W2 tile as the A operand (16 vocabulary
@@ -20,10 +20,11 @@
 //    a time, and the per-(request, tile) softmax statistics (max and sum of
 //    2^((l - m) s), or the argmax at T = 0) reduce inside the wave.  W2 is
 //    read once per step for all requests.
-//  * markov_sample_kernel: one wave per request combines the tile statistics,
-//    picks the tile holding u * total (inverse CDF in ascending token id)
-//    with a wave scan, re-reads that tile's 128 logits and finishes the draw
-//    with a second scan.
+//  * markov_sample_kernel: one workgroup per request combines the tile
+//    statistics (block maximum and a block scan over the threads' runs of
+//    tiles), picks the tile holding u * total (inverse CDF in ascending
+//    token id), and its first wave re-reads that tile's 64 logits and
+//    finishes the draw with a wave scan.
 #include <math.h>
 
 #include "common.h"
