@@ -317,3 +317,19 @@ def test_noalloc_size_limits(lib):
     assert call(4, 7, 0) == SPEC_EINVAL
     assert call(4, 65, 100) == SPEC_EUNSUPPORTED
     assert call(0, 7, 100) == SPEC_OK
+
+
+def test_timing_hook_arguments(lib):
+    """spec_time_stats_launch validates its arguments on the host; n = 0 (stop)
+    needs no arrays.  Nothing is recorded without a verification call."""
+    p = ctypes.c_void_p
+    f = lib.spec_time_stats_launch
+    f.restype = ctypes.c_int
+    f.argtypes = [p, p, ctypes.c_int]
+    arr = (p * 2)(p(0x1000), p(0x2000))
+    assert f(None, None, 0) == SPEC_OK
+    assert f(arr, arr, -1) == SPEC_EINVAL
+    assert f(None, arr, 2) == SPEC_EINVAL
+    assert f(arr, None, 2) == SPEC_EINVAL
+    assert f(arr, arr, 2) == SPEC_OK
+    assert f(None, None, 0) == SPEC_OK

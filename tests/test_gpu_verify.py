@@ -304,3 +304,37 @@ def test_concurrent_calls_on_two_streams(sv, dev):
         ref = oracle.verify_case(cases[k])
         st = compare_verify(cases[k], gpu, ref)
         assert st["exact"] + st["near_ties"] == cases[k].R
+
+
+def test_stats_launch_timing_hook(sv, dev):
+    """spec_time_stats_launch brackets the statistics launch of the next calls
+    with the caller's events: each pair spans a positive time shorter than the
+    whole call, the outputs are those of an untimed call, and calls past the
+    n requested (or after n = 0) record nothing."""
+    import bench
+    case = workloads.make_verify_case(8, 7, 151936, "bf16", seed=91,
+                                      noise_std=np.linspace(0.5, 2.5, 7),
+                                      verify_len=np.arange(8) % 8, temperature=1.0)
+    plain = run_verify(sv, case, dev)
+    hev = bench.HipEvents(4)
+    try:
+        sv.spec_time_stats_launch(hev.events[:2], hev.events[2:])
+        s0 = torch.cuda.Event(enable_timing=True)
+        s1 = torch.cuda.Event(enable_timing=True)
+        s0.record()
+        timed = [run_verify(sv, case, dev) for _ in range(2)]
+        s1.record()
+        extra = run_verify(sv, case, dev)   # past the two requested: untimed
+        torch.cuda.synchronize()
+        spans = [hev.elapsed_ms(k, 2 + k) for k in range(2)]
+        whole = s0.elapsed_time(s1)
+        print(f"[timing hook] statistics launches {spans} ms, two calls {whole:.4f} ms",
+              flush=True)
+        assert all(0.0 < t < whole for t in spans), (spans, whole)
+        for out in timed + [extra]:
+            for k in plain:
+                if plain[k] is not None:
+                    assert np.array_equal(plain[k], out[k], equal_nan=True), k
+    finally:
+        sv.spec_time_stats_launch([], [])
+        hev.close()
