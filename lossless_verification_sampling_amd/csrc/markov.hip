@@ -332,23 +332,30 @@ __device__ __forceinline__ double mk_tile_mass(float2 st, float M, float s) {
 // One workgroup per request; thread i owns the run of tiles [i tp, (i + 1) tp)
 // and keeps its statistics in registers (NB >= tp, else batches of NB).
 //  1. every load of the request is issued at once: its parameters and the
-//     statistics of every run.  The block takes the row maximum M, each
-//     thread its run's mass relative to M, and a block scan over the 256 run
-//     masses finds the run holding u * total;
-//  2. every thread walks its run in registers; the hit thread's walk gives
-//     the tile and the target left inside it;
-//  3. the first wave reads that tile's 64 logits (one per lane) and a wave
+//     statistics of every run.  Each wave reduces its threads' NaN flags and
+//     maxima (argmax at T = 0), and the four wave results meet in shared
+//     memory: the row maximum M;
+//  2. each thread's run mass relative to M, an inclusive scan per wave and
+//     the wave totals in shared memory give every thread its exclusive
+//     prefix; the first thread (in thread order) whose run holds u * total
+//     is found by a ballot per wave and the first wave with a hit;
+//  3. the hit thread walks its run in registers: the tile and the target
+//     left inside it;
+//  4. the first wave reads that tile's 64 logits (one per lane) and a wave
 //     scan finds the token.
-// The CDF must exceed the target strictly; a target at or past the total,
-// which only rounding can produce, takes the last token of positive mass.
-// Lane indices in the first wave come from ballots, so they are wave-uniform
-// and neighbouring prefixes are read with readlane.
+// Four barriers in all.  The CDF must exceed the target strictly; a target at
+// or past the total, which only rounding can produce, takes the last tile
+// and token of positive mass.  Lane indices in the first wave come from
+// ballots, so they are wave-uniform and neighbouring prefixes are read with
+// readlane.
 template <int NB>
 __global__ void __launch_bounds__(kBlock) markov_sample_kernel(MarkovArgs a) {
-    __shared__ BlockScratch bs;
+    __shared__ float s_wf[kWaves];
+    __shared__ int s_wi[kWaves], s_wb[kWaves], s_wl[kWaves], s_wh[kWaves];
+    __shared__ double s_wd[kWaves];
     __shared__ int s_tile;
     __shared__ double s_tin;
-    const int tid = threadIdx.x, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r = blockIdx.x;
     const int k = a.k;
     const int V = a.V;
@@ -365,7 +372,8 @@ __global__ void __launch_bounds__(kBlock) markov_sample_kernel(MarkovArgs a) {
     auto valid = [&](int b, int i) { return b * NB + i < tp && t0 + b * NB + i < nt; };
     const float T = a.temp[r];
     const int32_t anc = a.anchor[r];
-    const uint32_t rbad = a.bad[r];
+    // the request's flag from the earlier steps (none before step 1)
+    const uint32_t rbad = k > 1 ? a.bad[r] : 0u;
     const float u = a.ud[(size_t)r * a.gamma + (k - 1)];
     load_batch(0);
     bool ok = mk_temperature_ok(T) && anc >= 0 && anc < V && rbad == 0u;
@@ -373,10 +381,10 @@ __global__ void __launch_bounds__(kBlock) markov_sample_kernel(MarkovArgs a) {
     const float s = (T > 0.0f && ok) ? (float)(kLog2e / (double)T) : 1.0f;
     int token = -1;
 
-    // pass 1: run maximum, NaN flags, greedy argmax
+    // pass 1: run maximum, NaN flags, greedy argmax; wave results, then the
+    // block's from the four waves
     float lm = -__builtin_inff();
     int bad = 0;
-    float bv = -__builtin_inff();
     int bi = 0x7fffffff;
     for (int b = 0; b < nb; ++b) {
         if (b > 0) load_batch(b);
@@ -386,24 +394,41 @@ __global__ void __launch_bounds__(kBlock) markov_sample_kernel(MarkovArgs a) {
             const float2 x = st[i];
             if (x.x != x.x || (T != 0.0f && x.y != x.y)) bad = 1;
             if (T == 0.0f)
-                argmax_combine(bv, bi, x.x, __float_as_int(x.y));
+                argmax_combine(lm, bi, x.x, __float_as_int(x.y));
             else
                 lm = fmaxf(lm, x.x);
         }
     }
-    bad = block_max_i(bad, bs);
+    bad = wave_max_i(bad);
+    if (T == 0.0f)
+        wave_argmax(lm, bi);
+    else
+        lm = wave_max(lm);
+    if (lane == 0) {
+        s_wf[wave] = lm;
+        s_wi[wave] = bi;
+        s_wb[wave] = bad;
+    }
+    __syncthreads();
+    float M = s_wf[0];
+    int B = s_wi[0];
+    bad = s_wb[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) {
+        bad = max(bad, s_wb[w]);
+        if (T == 0.0f)
+            argmax_combine(M, B, s_wf[w], s_wi[w]);
+        else
+            M = fmaxf(M, s_wf[w]);
+    }
     if (ok && T == 0.0f) {
-        float dv = -__builtin_inff();
-        int di = 0;
-        block_argmax2(bv, bi, dv, di, bs);
-        ok = !bad && bv < __builtin_inff() && bi != 0x7fffffff;
-        token = bi;
+        ok = !bad && M < __builtin_inff() && B != 0x7fffffff;
+        token = B;
     } else if (ok) {
-        float M = lm, dummy = -__builtin_inff();
-        block_max2(M, dummy, bs);
         ok = !bad && M > -__builtin_inff() && M < __builtin_inff();
         if (ok) {
-            // run masses relative to M, block scan, the run holding u * W
+            // pass 2: run masses relative to M, the exclusive prefix of every
+            // run, the run holding u * W
             double lsum = 0.0;
             int lastp = -1;
             for (int b = 0; b < nb; ++b) {
@@ -416,18 +441,42 @@ __global__ void __launch_bounds__(kBlock) markov_sample_kernel(MarkovArgs a) {
                     if (w > 0.0) lastp = t0 + b * NB + i;
                 }
             }
-            double W;
-            const double excl = block_exclusive_scan(lsum, &W, bs);
+            double incl = lsum;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const double n = __shfl_up(incl, o, 64);
+                if (lane >= o) incl += n;
+            }
+            double excl = __shfl_up(incl, 1, 64);
+            if (lane == 0) excl = 0.0;
+            const int wlast = wave_max_i(lastp);
+            if (lane == 63) s_wd[wave] = incl;
+            if (lane == 0) s_wl[wave] = wlast;
+            __syncthreads();
+            double base = 0.0, W = 0.0;
+            int last = -1;
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) {
+                if (w < wave) base += s_wd[w];
+                W += s_wd[w];
+                last = max(last, s_wl[w]);
+            }
+            excl += base;
             const double tt = (double)u * W;
-            const int h = block_min_i((lsum > 0.0 && excl + lsum > tt) ? tid : 0x7fffffff, bs);
-            if (h == 0x7fffffff) {  // u * W at or past the total (rounding)
-                const int lt = block_max_i(lastp, bs);
+            const uint64_t hm = __ballot(lsum > 0.0 && excl + lsum > tt);
+            if (lane == 0) s_wh[wave] = hm ? __builtin_ctzll(hm) : 64;
+            __syncthreads();
+            int hw = -1;
+#pragma unroll
+            for (int w = kWaves - 1; w >= 0; --w)
+                if (s_wh[w] < 64) hw = w;
+            if (hw < 0) {  // u * W at or past the total (rounding)
                 if (tid == 0) {
-                    s_tile = lt;
+                    s_tile = last;
                     s_tin = INFINITY;
                 }
-            } else if (tid == h) {
-                // pass 2: the hit thread walks its run
+            } else if (wave == hw && lane == s_wh[hw]) {
+                // pass 3: the hit thread walks its run
                 double run = excl;
                 int tl = -1;
                 double tin = INFINITY;
@@ -453,7 +502,7 @@ __global__ void __launch_bounds__(kBlock) markov_sample_kernel(MarkovArgs a) {
             const double tin = s_tin;
             if (tile < 0) tile = 0;  // unreachable: the tile holding M has mass
             if (tid < 64) {
-                // round 3: the tile's logits, one per lane, in id order
+                // the tile's logits, one per lane, in id order
                 const float m = ts[tile].x;
                 const long v = (long)tile * kMkTile + lane;
                 const float *lrow = a.out_logits + ((long)r * a.gamma + (k - 1)) * V;
@@ -473,9 +522,10 @@ __global__ void __launch_bounds__(kBlock) markov_sample_kernel(MarkovArgs a) {
         }
     }
     if (tid == 0) {
-        if (!ok) a.bad[r] = 1u;
+        const uint32_t nbad = (rbad || !ok) ? 1u : 0u;
+        a.bad[r] = nbad;
         a.out_tok[(size_t)r * a.gamma + (k - 1)] = ok ? token : -1;
-        if (k == a.gamma && (a.bad[r] || !ok)) {
+        if (k == a.gamma && nbad) {
             for (int q = 0; q < a.gamma; ++q) a.out_tok[(size_t)r * a.gamma + q] = -1;
             atomic_or_u32(&a.ctl->status, SPEC_DEV_BAD_REQUEST);
         }
@@ -611,10 +661,6 @@ __global__ void __launch_bounds__(kBlock) rnn_state_kernel(RnnArgs a) {
     a.bsplit[2 * plane + t] = (uint16_t)(__float_as_uint(lo) >> 16);
 }
 
-__global__ void markov_clear_kernel(uint32_t *bad, int R) {
-    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < R; i += gridDim.x * blockDim.x)
-        bad[i] = 0u;
-}
 
 namespace {
 
@@ -746,8 +792,6 @@ int spec_markov_draft_sample(const void *U, int u_dtype, const void *W1, const v
     mk_setup(U, u_dtype, W1, W2, w_dtype, anchor, temperature, u_draft, R, gamma, V, rank,
              out_draft_tokens, out_draft_logits, workspace, p, a);
     hipStream_t st = (hipStream_t)stream;
-    hipLaunchKernelGGL(markov_clear_kernel, dim3((R + kBlock - 1) / kBlock), dim3(kBlock), 0, st,
-                       a.bad, R);
     for (int k = 1; k <= gamma; ++k) {
         a.k = k;
         mk_launch_step<1>(a, p, u_dtype == SPEC_BF16, st);
@@ -803,8 +847,6 @@ int spec_rnn_draft_sample(const void *U, int u_dtype, const void *W1, const void
     g.hidden = hidden;
     float *s0 = (float *)(ws + p.off_s0), *s1 = (float *)(ws + p.off_s1);
     hipStream_t st = (hipStream_t)stream;
-    hipLaunchKernelGGL(markov_clear_kernel, dim3((R + kBlock - 1) / kBlock), dim3(kBlock), 0, st,
-                       a.bad, R);
     const dim3 ggrid((R + kRnnReq - 1) / kRnnReq, kRnnKS);
     const dim3 sgrid((R * kMkRank + kBlock - 1) / kBlock);
     for (int k = 1; k <= gamma; ++k) {
