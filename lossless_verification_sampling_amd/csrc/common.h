@@ -31,9 +31,6 @@ __device__ __forceinline__ uint32_t atomic_load_u32(const uint32_t *p) {
 __device__ __forceinline__ void atomic_store_u32(uint32_t *p, uint32_t v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ uint32_t atomic_add_u32(uint32_t *p, uint32_t v) {
-    return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 __device__ __forceinline__ void atomic_or_u32(uint32_t *p, uint32_t v) {
     __hip_atomic_fetch_or(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -213,105 +210,6 @@ __device__ __forceinline__ void wave_argmax(float &v, int &i) {
         argmax_combine(bv, bi, readlane_f(v, l), __builtin_amdgcn_readlane(i, l));
     v = bv;
     i = bi;
-}
-
-struct BlockScratch {
-    float f[2][kWaves];
-    double d[2][kWaves];
-    int i[2][kWaves];
-};
-
-// Block-wide max of two values; all threads receive the results.
-__device__ inline void block_max2(float &a, float &b, BlockScratch &s) {
-    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    a = wave_max(a);
-    b = wave_max(b);
-    __syncthreads();
-    if (lane == 0) {
-        s.f[0][w] = a;
-        s.f[1][w] = b;
-    }
-    __syncthreads();
-    a = fmaxf(fmaxf(s.f[0][0], s.f[0][1]), fmaxf(s.f[0][2], s.f[0][3]));
-    b = fmaxf(fmaxf(s.f[1][0], s.f[1][1]), fmaxf(s.f[1][2], s.f[1][3]));
-}
-
-// Block-wide fp64 sum of two values; all threads receive the results.
-__device__ inline void block_sum2(double &a, double &b, BlockScratch &s) {
-    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    a = wave_sum(a);
-    b = wave_sum(b);
-    __syncthreads();
-    if (lane == 0) {
-        s.d[0][w] = a;
-        s.d[1][w] = b;
-    }
-    __syncthreads();
-    a = (s.d[0][0] + s.d[0][1]) + (s.d[0][2] + s.d[0][3]);
-    b = (s.d[1][0] + s.d[1][1]) + (s.d[1][2] + s.d[1][3]);
-}
-
-__device__ inline int block_max_i(int a, BlockScratch &s) {
-    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    a = wave_max_i(a);
-    __syncthreads();
-    if (lane == 0) s.i[0][w] = a;
-    __syncthreads();
-    return max(max(s.i[0][0], s.i[0][1]), max(s.i[0][2], s.i[0][3]));
-}
-
-__device__ inline int block_min_i(int a, BlockScratch &s) {
-    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    a = wave_min_i(a);
-    __syncthreads();
-    if (lane == 0) s.i[0][w] = a;
-    __syncthreads();
-    return min(min(s.i[0][0], s.i[0][1]), min(s.i[0][2], s.i[0][3]));
-}
-
-// Block-wide argmax of two (value, index) pairs.
-__device__ inline void block_argmax2(float &va, int &ia, float &vb, int &ib, BlockScratch &s) {
-    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    wave_argmax(va, ia);
-    wave_argmax(vb, ib);
-    __syncthreads();
-    if (lane == 0) {
-        s.f[0][w] = va; s.i[0][w] = ia;
-        s.f[1][w] = vb; s.i[1][w] = ib;
-    }
-    __syncthreads();
-    va = s.f[0][0]; ia = s.i[0][0];
-    vb = s.f[1][0]; ib = s.i[1][0];
-#pragma unroll
-    for (int k = 1; k < kWaves; ++k) {
-        argmax_combine(va, ia, s.f[0][k], s.i[0][k]);
-        argmax_combine(vb, ib, s.f[1][k], s.i[1][k]);
-    }
-}
-
-// Block-wide exclusive prefix sum (fp64) in thread order; *total gets the sum.
-// Any thread t may use excl_t + v_t as its inclusive value: callers locate a
-// target by "the first thread whose excl + v exceeds it", which is robust to
-// the last-bit differences between association orders.
-__device__ inline double block_exclusive_scan(double v, double *total, BlockScratch &s) {
-    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    double incl = v;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        double n = __shfl_up(incl, o, 64);
-        if (lane >= o) incl += n;
-    }
-    double excl = __shfl_up(incl, 1, 64);
-    if (lane == 0) excl = 0.0;
-    __syncthreads();
-    if (lane == 63) s.d[0][w] = incl;
-    __syncthreads();
-    double base = 0.0;
-    for (int k = 0; k < w; ++k) base += s.d[0][k];
-    double tot = 0.0;
-    for (int k = 0; k < kWaves; ++k) tot += s.d[0][k];
-    *total = tot;
-    return base + excl;
 }
 
 }  // namespace sv

@@ -140,30 +140,6 @@ __device__ __forceinline__ void st_word(uint64_t *p, uint32_t tag, uint32_t payl
                        __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Every lane with `act` reads the word at p until it carries `tag`, then
-// returns its payload (0 for inactive lanes).  Called by every active lane of
-// the wave.  The wait is bounded: past kSpinLimit polls, or once any wave of
-// the launch has timed out, it raises SPEC_DEV_SPIN_TIMEOUT and returns.
-__device__ __forceinline__ uint32_t await_lane(const uint64_t *p, bool act, uint32_t tag,
-                                               Control *ctl) {
-    uint64_t v = act ? ld_word(p) : 0;
-    bool stale = act && (uint32_t)(v >> 32) != tag;
-    uint32_t it = 0;
-    while (__ballot(stale)) {
-        if ((++it & 255u) == 0u &&
-            (it > kSpinLimit || (atomic_load_u32(&ctl->status) & SPEC_DEV_SPIN_TIMEOUT))) {
-            if (stale) atomic_or_u32(&ctl->status, SPEC_DEV_SPIN_TIMEOUT);
-            break;
-        }
-        __builtin_amdgcn_s_sleep(2);
-        if (stale) {
-            v = ld_word(p);
-            stale = (uint32_t)(v >> 32) != tag;
-        }
-    }
-    return (uint32_t)v;
-}
-
 // Lanes 0..n-1 store words w[lane] at p[lane] (n <= 4).
 __device__ __forceinline__ void publish_n(uint64_t *p, uint32_t tag, int n, uint32_t w0,
                                           uint32_t w1, uint32_t w2, uint32_t w3) {
@@ -202,7 +178,6 @@ struct Item {
     float T, s;   // temperature and log2(e) / T (0 at T = 0)
 };
 __device__ __forceinline__ bool is_pair(const Item &x) { return x.i < x.l; }
-__device__ __forceinline__ bool is_tv(const Item &x) { return x.i < x.l && x.T != 0.0f; }
 
 // The wave's index in the grid, made explicitly wave-uniform (the compiler
 // cannot tell that threadIdx.x / 64 is the same in every lane of a wave), so
@@ -642,7 +617,9 @@ constexpr int kCB = 4;
 
 // Lane-parallel batch: word k of this lane is p[k] if act[k].  Issues every
 // load, then re-reads only the words that do not carry `tag` yet, until all
-// do (bounded as in await_lane).  out[k] = payload (0 for inactive words).
+// do.  out[k] = payload (0 for inactive words).  The wait is bounded: past
+// kSpinLimit polls, or once any wave of the launch has timed out, it raises
+// SPEC_DEV_SPIN_TIMEOUT and returns the stale payloads.
 // `cached`: the words were written by an earlier launch, so a plain (cached)
 // load sees them; only a stale tag (not expected) falls back to the coherent
 // re-reads.
@@ -884,25 +861,6 @@ __device__ __forceinline__ bool norms_ok(float M, float Z) {
     return finite_f(M) && Z > 0.0f && finite_f(Z);
 }
 
-// Row normalisers of unit x at T > 0 from the statistics pass's chunk words:
-// M = max mu and Z = sum S 2^(mu - M), per lane over its chunks in
-// increasing order, then across the wave in a fixed order, so that every wave
-// folding the same unit gets the same bits.  A bonus row gives (Md, Zd) =
-// (0, 1).
-__device__ __forceinline__ void unit_norms(const VerifyArgs &a, const Item &x, float &Mt, float &Zt,
-                                        float &Md, float &Zd) {
-    const bool pair = is_pair(x);
-    OnlineZ ot, od;
-    fold_unit_words(a, x, pair, [&](const uint32_t (&w)[4]) {
-        ot.add(__uint_as_float(w[0]), __uint_as_float(w[1]));
-        if (pair) od.add(__uint_as_float(w[2]), __uint_as_float(w[3]));
-    });
-    ot.reduce(Mt, Zt);
-    Md = 0.0f;
-    Zd = 1.0f;
-    if (pair) od.reduce(Md, Zd);
-}
-
 // The accept test of a draft position (T > 0) on the gathered logits zx
 // (target), dx (draft) of its draft token x_{i+1}, once the row normalisers
 // are known: accept <=> q(x) >= p(x) or u < q(x)/p(x) (DART note eq. (3)), in
@@ -918,8 +876,9 @@ __device__ __forceinline__ bool accept_eval(float zx, float dx, float s, float M
 }
 
 // The fold launch's work for draft position x at T > 0: its row normalisers
-// (folded as unit_norms folds them: per lane over its chunks in increasing
-// order, then across the wave), each chunk's pair scale for the TV items --
+// M = max mu and Z = sum S 2^(mu - M) (per lane over its chunks in increasing
+// order, then across the wave in a fixed order), each chunk's pair scale for
+// the TV items --
 // formed once here rather than in every TV item -- and the accept test, whose
 // record (flags, log q(x)) the combine reads.  The draft token's two logits
 // are gathered while the chunk words load.  The pair scales are published
@@ -1100,7 +1059,8 @@ __device__ __forceinline__ void tv_unit(const VerifyArgs &a, const Item &x, Unit
 }
 
 // T > 0 bonus unit (target row l_r): the row normalisers folded from the
-// statistics words (as unit_norms folds them), and the chunk of the
+// statistics words (per lane in increasing chunk order, then across the
+// wave, as the fold launch folds a pair's), and the chunk of the
 // inverse-CDF draw from q_l with u_sample[r][l] (DSpark guide, "basics": one
 // bonus token).
 __device__ __forceinline__ void bonus_unit(const VerifyArgs &a, const Item &x, UnitSum *s) {
