@@ -1523,6 +1523,412 @@ __global__ void __launch_bounds__(kBlock, kStreamWaves) tv_kernel(VerifyArgs a) 
     }
 }
 
+// ---------------------------------------------------------------------------
+// held-pair path (bf16 rows): one launch does the statistics, the fold and
+// the TV sums of every row pair at T > 0.  Each such pair belongs to one
+// workgroup, which keeps most of its chunks on the compute unit between the
+// two passes (registers, then shared memory) and reads only the rest again;
+// the workgroups that hold no pair stream the other needed rows (bonus rows,
+// T = 0 rows) for their statistics.  The combine launch follows unchanged.
+// ---------------------------------------------------------------------------
+
+constexpr int kHoldWaves = 8;                  // waves per workgroup (one workgroup per CU)
+constexpr int kHoldBlock = kHoldWaves * 64;
+constexpr int kHoldReg = 8;                   // chunk pairs per wave kept in registers
+constexpr int kHoldFill = 8;                   // row chunks per filler batch (two in flight)
+constexpr size_t kHoldLdsBytes = 160 * 1024;   // shared memory of a compute unit
+constexpr size_t kHoldStaticLds = 1024;        // kept for the kernel's static shared memory
+
+// Work list of the held path in shared memory: req[3 R] = (T, s, l), then the
+// held pairs (r << 7 | i: positions i < l at T > 0), then the filler rows
+// ((r << 7 | i) << 1 | row, row 1 = the draft row): every other row the
+// statistics must cover (the bonus row at T > 0; every row at T = 0).
+struct HoldTable {
+    const uint32_t *req;
+    const uint32_t *units;
+    uint32_t held, filler;
+};
+
+__device__ __forceinline__ HoldTable build_hold_table(const VerifyArgs &a, uint32_t *lds) {
+    __shared__ uint32_t wsum[kHoldWaves];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    uint32_t *req = lds;
+    uint32_t *units = lds + 3 * a.R;
+    const int K = (a.R + kHoldBlock - 1) / kHoldBlock;
+    const int r0 = tid * K, r1 = min(r0 + K, a.R);
+    // per-thread counts of held pairs (low half) and filler rows (high half);
+    // both stay below 2^16 since the table fits the shared memory
+    uint32_t own = 0;
+    for (int r = r0; r < r1; ++r) {
+        float T;
+        int l;
+        const bool ok = request_ok(a, r, T, l);
+        req[3 * r + 0] = __float_as_uint(T);
+        req[3 * r + 1] = __float_as_uint(ok && T != 0.0f ? exp2_scale(T) : 0.0f);
+        req[3 * r + 2] = (uint32_t)l;
+        const int n = table_units(a, ok, T, l, false);
+        const int h = (ok && T != 0.0f) ? min(l, n) : 0;
+        // filler units h..n-1: a draft row too for the pairs among them (i < l)
+        const int fr = (n - h) + max(0, min(l, n) - h);
+        own += (uint32_t)h + ((uint32_t)fr << 16);
+    }
+    uint32_t incl = own;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t v = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += v;
+    }
+    if (lane == 63) wsum[wave] = incl;
+    __syncthreads();
+    uint32_t base = 0, total = 0;
+#pragma unroll
+    for (int w = 0; w < kHoldWaves; ++w) {
+        if (w < wave) base += wsum[w];
+        total += wsum[w];
+    }
+    const uint32_t ex = base + incl - own, held = total & 0xffffu;
+    uint32_t ph = ex & 0xffffu, pf = held + (ex >> 16);
+    for (int r = r0; r < r1; ++r) {
+        const int l = (int)req[3 * r + 2];
+        const float T = __uint_as_float(req[3 * r]);
+        const bool ok = temperature_ok(T) && l >= 0 && l <= a.gamma;
+        const int n = table_units(a, ok, T, l, false);
+        const int h = (ok && T != 0.0f) ? min(l, n) : 0;
+        for (int i = 0; i < h; ++i) units[ph++] = ((uint32_t)r << 7) | (uint32_t)i;
+        for (int i = h; i < n; ++i) {
+            const uint32_t e = (((uint32_t)r << 7) | (uint32_t)i) << 1;
+            units[pf++] = e;
+            if (i < l) units[pf++] = e | 1u;
+        }
+    }
+    __syncthreads();
+    HoldTable t;
+    t.req = req;
+    t.units = units;
+    t.held = held;
+    t.filler = total >> 16;
+    return t;
+}
+
+// Shared memory of the held path: the table, a pair's chunk statistics
+// (C x 4 floats), then kl slots of one chunk pair each (both rows' raw
+// registers, lane-major: 2 x 8 words x 64 lanes).
+__host__ __device__ constexpr size_t hold_slot_words() { return 2 * 8 * 64; }
+
+// A chunk pair kept in shared-memory slot p: written after its statistics,
+// read back for its TV sums.
+template <typename RC>
+__device__ __forceinline__ void slot_put(uint32_t *slots, int p, int row, const RC &rc) {
+    uint32_t *d = slots + (size_t)p * hold_slot_words() + row * 512 + lane_id();
+#pragma unroll
+    for (int q = 0; q < 8; ++q) d[q * 64] = rc.w[q];
+}
+template <typename RC>
+__device__ __forceinline__ void slot_get(const uint32_t *slots, int p, int row, RC &rc, long c0,
+                                         int V) {
+    const uint32_t *d = slots + (size_t)p * hold_slot_words() + row * 512 + lane_id();
+#pragma unroll
+    for (int q = 0; q < 8; ++q) rc.w[q] = d[q * 64];
+    const long left = (long)V - c0;
+    rc.rem = left < (long)kLanes * 16 ? (int)left : kLanes * 16;
+}
+
+// Statistics of chunk c of held pair x (both rows at T > 0): the chunk words
+// for the combine's draws and the table entry for the fold.
+template <int N, typename RC>
+__device__ __forceinline__ void hold_stats(const VerifyArgs &a, const Item &x, int c, RC &rt,
+                                           RC &rd, float *stt) {
+    rt.fix();
+    rd.fix();
+    float e[N], mut, St, mud, Sd;
+    chunk_exp<N>(rt, x.s, e, mut, St);
+    chunk_exp<N>(rd, x.s, e, mud, Sd);
+    if (lane_id() == 0) {
+        stt[c * 4 + 0] = mut;
+        stt[c * 4 + 1] = St;
+        stt[c * 4 + 2] = mud;
+        stt[c * 4 + 3] = Sd;
+    }
+    publish_n(a.st1 + ((size_t)x.u * a.C + c) * 4, a.tag, 4, __float_as_uint(mut),
+              __float_as_uint(St), __float_as_uint(mud), __float_as_uint(Sd));
+}
+
+// TV sums of chunk c = w + 8 m of held pair x; lane m of the wave holds that
+// chunk's words (mu_t, S_t, mu_d) and pair scale.
+template <int N, typename RC>
+__device__ __forceinline__ void hold_tv(const VerifyArgs &a, const Item &x, int c, int m,
+                                        RC &rt, RC &rd, float mut, float St, float mud,
+                                        const PairScale &ps) {
+    rt.fix();
+    rd.fix();
+    PairScale q;
+    q.kt = rlf(ps.kt, m);
+    q.kd = rlf(ps.kd, m);
+    q.unit = rlf(ps.unit, m);
+    double cmin, cres;
+    tv_sums<N>(rt, rd, x.s, rlf(mut, m), rlf(St, m), rlf(mud, m), q, &cmin, &cres);
+    publish_n(a.st2 + ((size_t)x.u * a.C + c) * 2, a.tag, 2, __float_as_uint((float)cmin),
+              __float_as_uint((float)cres), 0u, 0u);
+}
+
+// One held pair x, the whole workgroup.  Wave w owns chunks c = w + 8 m: the
+// first kHoldReg in registers, the next in shared-memory slots (while slots
+// last), the rest read again for the TV sums.
+template <int N, int EPV>
+__device__ __forceinline__ void hold_pair(const VerifyArgs &a, const Item &x, float *stt,
+                                          uint32_t *slots, int kl) {
+    using RC = RawChunk<uint16_t, N, EPV>;
+    const int lane = lane_id();
+    const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int C = a.C;
+    const int nreg = kHoldWaves * kHoldReg;   // chunks kept in registers
+    const int nlds = nreg + kl;                // ... and in shared memory
+    const uint16_t *trow = row_ptr<uint16_t>(a.zt, x.r, a.tG, x.i, a.V);
+    const uint16_t *drow = row_ptr<uint16_t>(a.zd, x.r, a.dG, x.i, a.V);
+    // the accept test's token and uniform (wave 0)
+    int xtok = 0;
+    float uacc = 0.0f;
+    if (w == 0 && !a.tv_mode) {
+        xtok = a.tokens[(size_t)x.r * a.gamma + x.i];
+        uacc = a.ua[(size_t)x.r * a.gamma + x.i];
+    }
+    // ---- pass 1: every chunk once, its statistics; most chunks kept.  A
+    // chunk past the row's chunks re-reads chunk 0 (cached) and is not used.
+    const long z0 = 0;
+    RC ht[kHoldReg], hd[kHoldReg];
+#pragma unroll
+    for (int k = 0; k < kHoldReg; ++k) {
+        const int c = w + kHoldWaves * k;
+        const long c0 = c < C ? (long)c * kLanes * N : z0;
+        ht[k].load(trow, c0, a.V);
+        hd[k].load(drow, c0, a.V);
+    }
+    // the wave's first chunk past the registers, in flight behind them
+    RC at, ad, bt, bd;
+    int c = nreg + w;
+    at.load(trow, c < C ? (long)c * kLanes * N : z0, a.V);
+    ad.load(drow, c < C ? (long)c * kLanes * N : z0, a.V);
+    float zx = 0.0f, dx = 0.0f;
+    const bool tok_ok = xtok >= 0 && xtok < a.V;
+    if (w == 0 && !a.tv_mode && tok_ok) {
+        zx = load_one(trow, xtok);
+        dx = load_one(drow, xtok);
+    }
+#pragma unroll
+    for (int k = 0; k < kHoldReg; ++k) hold_stats<N>(a, x, w + kHoldWaves * k, ht[k], hd[k], stt);
+    // the wave's chunks past the registers, two in flight
+    {
+        for (; c < C; c += 2 * kHoldWaves) {
+            const int cb = c + kHoldWaves, cn = c + 2 * kHoldWaves;
+            bt.load(trow, cb < C ? (long)cb * kLanes * N : z0, a.V);
+            bd.load(drow, cb < C ? (long)cb * kLanes * N : z0, a.V);
+            hold_stats<N>(a, x, c, at, ad, stt);
+            if (c < nlds) {
+                slot_put(slots, c - nreg, 0, at);
+                slot_put(slots, c - nreg, 1, ad);
+            }
+            if (cb >= C) break;
+            at.load(trow, cn < C ? (long)cn * kLanes * N : z0, a.V);
+            ad.load(drow, cn < C ? (long)cn * kLanes * N : z0, a.V);
+            hold_stats<N>(a, x, cb, bt, bd, stt);
+            if (cb < nlds) {
+                slot_put(slots, cb - nreg, 0, bt);
+                slot_put(slots, cb - nreg, 1, bd);
+            }
+        }
+    }
+    __syncthreads();
+    // ---- the fold, in every wave (fixed order: the same bits everywhere) ----
+    OnlineZ ot, od;
+#pragma unroll
+    for (int b = 0; b < kCB; ++b) {
+        const int c = b * 64 + lane;
+        if (c < C) {
+            ot.add(stt[c * 4 + 0], stt[c * 4 + 1]);
+            od.add(stt[c * 4 + 2], stt[c * 4 + 3]);
+        }
+    }
+    float Mt, Zt, Md, Zd;
+    ot.reduce(Mt, Zt);
+    od.reduce(Md, Zd);
+    if (w == 0) {
+        publish_n(a.nrm + (size_t)x.u * 4, a.tag, 4, __float_as_uint(Mt), __float_as_uint(Zt),
+                  __float_as_uint(Md), __float_as_uint(Zd));
+        if (!a.tv_mode) {
+            const bool valid = norms_ok(Mt, Zt) && norms_ok(Md, Zd) && tok_ok;
+            bool acc = false;
+            float lqx = __builtin_nanf("");
+            if (valid) acc = accept_eval(zx, dx, x.s, Mt, Zt, Md, Zd, uacc, &lqx);
+            publish_n(a.rec + (size_t)x.u * kRecWords, a.tag, 2,
+                      (valid ? kFlagValid : 0u) | (acc ? kFlagAccept : 0u), __float_as_uint(lqx),
+                      0u, 0u);
+        }
+    }
+    // lane m: words and pair scale of the wave's chunk w + 8 m
+    const int cm = w + kHoldWaves * lane;
+    float mut = 0.0f, St = 0.0f, mud = 0.0f;
+    PairScale ps;
+    ps.kt = ps.kd = ps.unit = 0.0f;
+    if (cm < C) {
+        mut = stt[cm * 4 + 0];
+        St = stt[cm * 4 + 1];
+        mud = stt[cm * 4 + 2];
+        ps = pair_scale(mut, mud, row_norm(Mt, Zt), row_norm(Md, Zd));
+    }
+    // ---- pass 2: TV sums; the chunks past the slots are read again first ----
+    {
+        // the wave's first chunk past the slots
+        c = nreg + w;
+        while (c < nlds) c += kHoldWaves;
+        at.load(trow, c < C ? (long)c * kLanes * N : z0, a.V);
+        ad.load(drow, c < C ? (long)c * kLanes * N : z0, a.V);
+#pragma unroll
+        for (int k = 0; k < kHoldReg; ++k)
+            hold_tv<N>(a, x, w + kHoldWaves * k, k, ht[k], hd[k], mut, St, mud, ps);
+        for (int cs = nreg + w; cs < C && cs < nlds; cs += kHoldWaves) {
+            const long c0 = (long)cs * kLanes * N;
+            RC st, sd;
+            slot_get(slots, cs - nreg, 0, st, c0, a.V);
+            slot_get(slots, cs - nreg, 1, sd, c0, a.V);
+            hold_tv<N>(a, x, cs, (cs - w) / kHoldWaves, st, sd, mut, St, mud, ps);
+        }
+        for (; c < C; c += 2 * kHoldWaves) {
+            const int cb = c + kHoldWaves, cn = c + 2 * kHoldWaves;
+            bt.load(trow, cb < C ? (long)cb * kLanes * N : z0, a.V);
+            bd.load(drow, cb < C ? (long)cb * kLanes * N : z0, a.V);
+            hold_tv<N>(a, x, c, (c - w) / kHoldWaves, at, ad, mut, St, mud, ps);
+            if (cb >= C) break;
+            at.load(trow, cn < C ? (long)cn * kLanes * N : z0, a.V);
+            ad.load(drow, cn < C ? (long)cn * kLanes * N : z0, a.V);
+            hold_tv<N>(a, x, cb, (cb - w) / kHoldWaves, bt, bd, mut, St, mud, ps);
+        }
+    }
+    __syncthreads();  // the table entries and slots are reused by the next pair
+}
+
+// Filler row item k of the table: its unit (r, i), which row, which chunk.
+struct FillItem {
+    Item x;
+    int row;
+    const uint16_t *ptr;
+    long c0;
+};
+__device__ __forceinline__ FillItem fill_item(const VerifyArgs &a, const HoldTable &t, uint32_t k,
+                                              int N) {
+    FillItem f;
+    const uint32_t U = k / (uint32_t)a.C;
+    f.x.c = (int)(k - U * (uint32_t)a.C);
+    const uint32_t e = __builtin_amdgcn_readfirstlane(t.units[t.held + U]);
+    f.row = (int)(e & 1u);
+    f.x.r = (int)(e >> 8);
+    f.x.i = (int)((e >> 1) & 127u);
+    f.x.T = __uint_as_float(__builtin_amdgcn_readfirstlane(t.req[3 * f.x.r]));
+    f.x.s = __uint_as_float(__builtin_amdgcn_readfirstlane(t.req[3 * f.x.r + 1]));
+    f.x.l = (int)__builtin_amdgcn_readfirstlane(t.req[3 * f.x.r + 2]);
+    f.x.u = f.x.r * a.UG + f.x.i;
+    f.ptr = f.row ? row_ptr<uint16_t>(a.zd, f.x.r, a.dG, f.x.i, a.V)
+                  : row_ptr<uint16_t>(a.zt, f.x.r, a.tG, f.x.i, a.V);
+    f.c0 = (long)f.x.c * kLanes * N;
+    return f;
+}
+
+// Statistics of one filler row chunk: (mu, S) at T > 0, the argmax words at
+// T = 0, as the row's half of the chunk's four words.
+template <int N, int EPV, typename RC>
+__device__ __forceinline__ void fill_stats(const VerifyArgs &a, const FillItem &f, RC &rc) {
+    rc.fix();
+    uint32_t w0, w1;
+    if (f.x.T == 0.0f) {
+        float bv;
+        int bi, bad;
+        chunk_argmax<N, EPV>(rc, f.c0, bv, bi, bad);
+        w0 = __float_as_uint(bv);
+        w1 = bad ? 0xffffffffu : (uint32_t)bi;
+    } else {
+        float e[N], mu, S;
+        chunk_exp<N>(rc, f.x.s, e, mu, S);
+        w0 = __float_as_uint(mu);
+        w1 = __float_as_uint(S);
+    }
+    publish_n(a.st1 + ((size_t)f.x.u * a.C + f.x.c) * 4 + 2 * f.row, a.tag, 2, w0, w1, 0u, 0u);
+}
+
+// The filler row items [lo, hi) of this workgroup, item lo + w + 8 j to wave
+// w, in batches of kHoldFill with the next batch in flight.  Loads past hi
+// re-read item lo's chunk (cached) and are not used.
+template <int N, int EPV>
+__device__ __forceinline__ void hold_fill(const VerifyArgs &a, const HoldTable &t, uint32_t lo,
+                                          uint32_t hi) {
+    using RC = RawChunk<uint16_t, N, EPV>;
+    const uint32_t w = (uint32_t)__builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    if (lo >= hi) return;
+    const FillItem f0 = fill_item(a, t, lo, N);
+    RC A[kHoldFill], B[kHoldFill];
+    auto issue = [&](RC (&X)[kHoldFill], uint32_t k0) {
+#pragma unroll
+        for (int j = 0; j < kHoldFill; ++j) {
+            const uint32_t k = k0 + (uint32_t)j * kHoldWaves;
+            if (k < hi) {
+                const FillItem f = fill_item(a, t, k, N);
+                X[j].load(f.ptr, f.c0, a.V);
+            } else {
+                X[j].load(f0.ptr, f0.c0, a.V);
+            }
+        }
+    };
+    auto process = [&](RC (&X)[kHoldFill], uint32_t k0) {
+#pragma unroll
+        for (int j = 0; j < kHoldFill; ++j) {
+            const uint32_t k = k0 + (uint32_t)j * kHoldWaves;
+            if (k < hi) fill_stats<N, EPV>(a, fill_item(a, t, k, N), X[j]);
+        }
+    };
+    const uint32_t step = kHoldFill * kHoldWaves;
+    uint32_t k = lo + w;
+    issue(A, k);
+    for (; k < hi; k += 2 * step) {
+        issue(B, k + step);
+        process(A, k);
+        if (k + step >= hi) break;
+        issue(A, k + 2 * step);
+        process(B, k + step);
+    }
+}
+
+// The held-path launch: workgroup g holds pairs g, g + G, ... in turn; the
+// workgroups with one pair fewer than the most loaded share the filler rows.
+template <int N, int EPV>
+__global__ void __launch_bounds__(kHoldBlock, 1) hold_kernel(VerifyArgs a, int kl) {
+    a.tag = first_launch_tag(a.ctl);
+    extern __shared__ uint32_t lds[];
+    const HoldTable t = build_hold_table(a, lds);
+    const size_t tw = 3 * (size_t)a.R + (size_t)t.held + t.filler;
+    float *stt = (float *)(lds + ((tw + 3) & ~(size_t)3));
+    uint32_t *slots = (uint32_t *)(stt + 4 * (size_t)a.C);
+    const uint32_t G = gridDim.x, g = blockIdx.x;
+    for (uint32_t k = g; k < t.held; k += G) {
+        Item x;
+        const uint32_t e = t.units[k];
+        x.r = (int)(e >> 7);
+        x.i = (int)(e & 127u);
+        x.c = 0;
+        x.T = __uint_as_float(t.req[3 * x.r]);
+        x.s = __uint_as_float(t.req[3 * x.r + 1]);
+        x.l = (int)t.req[3 * x.r + 2];
+        x.u = x.r * a.UG + x.i;
+        hold_pair<N, EPV>(a, x, stt, slots, kl);
+    }
+    // filler rows: pairs in the last round P' = held - (rounds - 1) G; the
+    // workgroups past P' (all, when P' = G) share them evenly
+    const uint32_t rounds = (t.held + G - 1) / G;
+    const uint32_t last = t.held - (rounds ? rounds - 1 : 0) * G;
+    const uint32_t L = (rounds && last < G) ? G - last : G;
+    if (rounds && last < G && g < last) return;
+    const uint32_t li = (rounds && last < G) ? g - last : g;
+    const uint64_t F = (uint64_t)t.filler * a.C;
+    hold_fill<N, EPV>(a, t, (uint32_t)(F * li / L), (uint32_t)(F * (li + 1) / L));
+}
+
 __global__ void zero_fill_kernel(uint32_t *p, size_t n_words) {
     for (size_t k = (size_t)blockIdx.x * blockDim.x + threadIdx.x; k < n_words;
          k += (size_t)gridDim.x * blockDim.x)
@@ -1668,8 +2074,67 @@ size_t table_bytes(const VerifyArgs &a) {
     return b <= kMaxTableBytes ? (b + 255) / 256 * 256 : 0;
 }
 
+// Shared memory of the held path, 0 where it does not apply: the work list,
+// one pair's chunk statistics and as many chunk-pair slots as fit (*kl).
+size_t hold_bytes(const VerifyArgs &a, int *kl) {
+    const size_t tw = 3 * (size_t)a.R + (size_t)a.R * (a.UG + a.gamma);
+    const size_t head = ((tw + 3) & ~(size_t)3) * 4 + 16 * (size_t)a.C;
+    const size_t cap = kHoldLdsBytes - kHoldStaticLds;
+    if (4 * tw > kMaxTableBytes || head > cap) return 0;
+    const long room = (long)((cap - head) / (hold_slot_words() * 4));
+    const long need = (long)a.C - kHoldWaves * kHoldReg;
+    if (need < 1) return 0;  // every register chunk exists and is whole
+    const long n = need < room ? need : room;
+    *kl = (int)n;
+    return head + (size_t)n * hold_slot_words() * 4;
+}
+
+// The held path for bf16 rows: one launch for the statistics, folds and TV
+// sums, then the combine.  Returns -1 when it does not apply (the split path
+// runs instead), else the launch status.  SPECVERIFY_SPLIT=1 in the
+// environment selects the split path (for comparisons).
+template <int N, int EPV>
+int launch_hold(VerifyArgs a, hipStream_t st) {
+    if constexpr (N != 16 || EPV != 8) {
+        return -1;
+    } else {
+        int kl = 0;
+        const size_t lds = hold_bytes(a, &kl);
+        const long G = device_cus();
+        if (lds == 0 || G <= 0) return -1;
+        // at most two rounds of pairs per workgroup even if every position
+        // is verified; larger batches stream faster through the split path
+        if ((long)a.R * (a.tv_mode ? 1 : (a.gamma > 0 ? a.gamma : 1)) > 2 * G) return -1;
+        const char *sp = getenv("SPECVERIFY_SPLIT");
+        if (sp && sp[0] == '1') return -1;
+        const void *k = reinterpret_cast<const void *>(&hold_kernel<N, EPV>);
+        static std::atomic<int> attr{0};
+        if (attr.load(std::memory_order_relaxed) == 0) {
+            if (hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                    (int)(kHoldLdsBytes - kHoldStaticLds)) != hipSuccess)
+                return -1;
+            attr.store(1, std::memory_order_relaxed);
+        }
+        const long gc = a.tv_mode ? (a.R + kReqWaves - 1) / kReqWaves : a.R;
+        a.tag = 0;
+        StatsTiming &tm = g_stats_timing;
+        const bool timed = tm.i < tm.n;
+        if (timed) (void)hipEventRecord((hipEvent_t)tm.before[tm.i], st);
+        hipLaunchKernelGGL((hold_kernel<N, EPV>), dim3((unsigned)G), dim3(kHoldBlock), lds, st, a,
+                           kl);
+        if (timed) (void)hipEventRecord((hipEvent_t)tm.after[tm.i++], st);
+        hipLaunchKernelGGL((combine_kernel<uint16_t, uint16_t, N, EPV>), dim3((unsigned)gc),
+                           dim3(kReqBlock), 0, st, a);
+        return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_EHIP;
+    }
+}
+
 template <typename TT, typename TD, int N, int EPV>
 int launch_kernels(VerifyArgs a, hipStream_t st) {
+    if constexpr (std::is_same<TT, uint16_t>::value && std::is_same<TD, uint16_t>::value) {
+        const int h = launch_hold<N, EPV>(a, st);
+        if (h >= 0) return h;
+    }
     const void *k1 = reinterpret_cast<const void *>(&stats_kernel<TT, TD, N, EPV>);
     const void *k3 = reinterpret_cast<const void *>(&tv_kernel<TT, TD, N, EPV>);
     const long gf = ((long)a.R * a.UG + kWaves - 1) / kWaves;

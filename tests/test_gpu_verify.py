@@ -279,6 +279,60 @@ def test_tv_accept_rate(sv, dev, dtype):
     assert abs(cs[0].item() - 1.0) < 1e-6
 
 
+def _same_bits(a, b, what):
+    for k, x in a.items():
+        y = b[k]
+        if x is None or y is None:
+            assert x is None and y is None, (what, k)
+            continue
+        assert x.shape == y.shape and np.array_equal(x.view(np.uint8), y.view(np.uint8)), \
+            (what, k)
+
+
+@pytest.mark.parametrize("seed", [51, 52])
+def test_held_and_split_paths_identical(sv, dev, seed, monkeypatch):
+    """bf16 rows of more than 72 chunks take the held-pair launch (one
+    workgroup keeps each row pair on chip between the two passes); the split
+    launches (SPECVERIFY_SPLIT=1) must give the same bits, and both the
+    oracle's, on a batch mixing T > 0 and T = 0 requests, every verify length
+    and an invalid request."""
+    R, g, V = 24, 7, 151936
+    T = np.array([1.0, 0.0, 0.7, 1.3] * 6, np.float32)
+    lens = (np.arange(R) % (g + 1)).astype(np.int32)
+    case = workloads.make_verify_case(R, g, V, "bf16", seed=seed,
+                                      noise_std=np.linspace(0.5, 2.5, g), verify_len=lens,
+                                      temperature=T)
+    case.verify_len[5] = g + 3   # invalid
+    held = run_verify(sv, case, dev)
+    monkeypatch.setenv("SPECVERIFY_SPLIT", "1")
+    split = run_verify(sv, case, dev)
+    monkeypatch.delenv("SPECVERIFY_SPLIT")
+    _same_bits(held, split, "verify")
+    st = compare_verify(case, held, oracle.verify_case(case))
+    assert st["invalid"] == 1 and st["exact"] + st["near_ties"] == R - 1, st
+
+
+def test_held_and_split_accept_rate_identical(sv, dev, monkeypatch):
+    """Row-pair mode on bf16 rows of V = 151936: held and split launches give
+    the same bits, within the bf16 tolerance of the oracle."""
+    N, V = 40, 151936
+    gen = np.random.default_rng(5)
+    zt = (gen.standard_normal((N, V)) * 3).astype(np.float32)
+    zd = (zt + gen.standard_normal((N, V)) * np.linspace(0.05, 3, N)[:, None]).astype(np.float32)
+    T = np.array([1.0, 0.0, 0.7, 2.0] * 10, np.float32)[:N]
+    zt, zd = workloads.f32_to_bf16_bits(zt), workloads.f32_to_bf16_bits(zd)
+    args = (to_device(zd, dev), to_device(zt, dev), to_device(T, dev))
+    held = [t.cpu().numpy() for t in sv.spec_tv_accept_rate(*args)]
+    monkeypatch.setenv("SPECVERIFY_SPLIT", "1")
+    split = [t.cpu().numpy() for t in sv.spec_tv_accept_rate(*args)]
+    monkeypatch.delenv("SPECVERIFY_SPLIT")
+    torch.cuda.synchronize()
+    _same_bits({"c": held[0], "r": held[1]}, {"c": split[0], "r": split[1]}, "accept rate")
+    ref_c, ref_r = oracle.tv_accept_rate(zd, zt, T)
+    assert np.allclose(held[0], ref_c, rtol=2e-3, atol=1e-6)
+    assert np.allclose(held[1], ref_r, rtol=2e-3, atol=1e-6)
+
+
 def test_concurrent_calls_on_two_streams(sv, dev):
     """Two verification calls with distinct workspaces run concurrently on two
     streams: both must match the oracle, with no device status bit (no wait
