@@ -3,10 +3,14 @@
 A step is one spec_verify_batch call over the batched workload (R = 64
 requests, gamma = 7, V = 151936, bf16 logits, verify lengths uniform on 0..7,
 T = 1): every row of the hot path (softmax statistics, c*, accept tests,
-prefix survival, residual / bonus draw, commit) runs in that one call, which
-launches four kernels on the current stream (chunk statistics, the per-row
-normaliser folds with the accept tests, the total-variation pass, and the
-per-request combine with the draw and the commit).
+prefix survival, residual / bonus draw, commit) runs in that one call.  For
+bf16 rows of more than 72 chunks (this workload) the call launches two
+kernels on the current stream: the held-pair kernel (one workgroup per row
+pair keeps most of the pair on its compute unit between the statistics pass
+and the total-variation pass, so the pair is read from memory about once) and
+the per-request combine with the draw and the commit.  Other shapes take the
+split path's four launches (chunk statistics, normaliser folds, the
+total-variation pass, the combine); spec_verify_path says which.
 
 Inputs are generated once (seeded), uploaded, and replicated into enough
 device copies that consecutive steps never find their logits in the 256 MB
@@ -15,11 +19,12 @@ traffic, so the timed region streams from HBM.
 
 Prints one JSON line:
   value      verified draft positions per second (sum of l_r per call / time)
-  roofline   the dominant kernel, the statistics launch (it streams every
-             needed row once): algorithmic bytes (every verified draft row
+  roofline   the dominant kernel, the call's first launch (the held-pair
+             kernel, or on the split path the statistics launch; either reads
+             every needed row): algorithmic bytes (every verified draft row
              and target row plus the bonus row, read once) / its average
              HIP-event time inside the timed calls, against 8 TB/s;
-             call_roofline the same bytes over the whole call (four kernels)
+             call_roofline the same bytes over the whole call
   cpu_baseline  the fp64 oracle on the host over the same batch: all usable
              cores (up to a one-GPU share of 16, requests split over
              threads), with the one-thread figure beside it
@@ -213,7 +218,8 @@ def cpu_baseline(case, min_seconds: float):
 
 
 # The kernels of one spec_verify_batch call, in launch order.
-VERIFY_KERNELS = "stats_kernel + fold_kernel + tv_kernel + combine_kernel"
+VERIFY_KERNELS = {0: "stats_kernel + fold_kernel + tv_kernel + combine_kernel",
+                  1: "hold_kernel + combine_kernel"}
 
 # Verify workloads: name -> description.
 VERIFY_WORKLOADS = {
@@ -311,7 +317,7 @@ def bench_verify(args):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     kern_ms = np.array([a.elapsed_time(b) for a, b in ev])
-    # second timed pass of the same steps: the statistics launch of every call
+    # second timed pass of the same steps: the first launch of every call
     # bracketed by HIP events that the library records on the call's stream
     # (events inside a call add launch gaps, hence a pass of its own)
     hev = HipEvents(2 * args.steps)
@@ -331,9 +337,12 @@ def bench_verify(args):
     achieved = alg_bytes / avg_stats_s / 1e9
     call_achieved = alg_bytes / avg_kernel_s / 1e9
     key = "verify_" + args.workload
-    traffic = measured_traffic(key, "stats_kernel")
     tname = "bf16" if te == 2 else "f32"
     dname = "bf16" if de == 2 else "f32"
+    path = sv.spec_verify_path(R, gamma, V, sv.SPEC_BF16 if te == 2 else sv.SPEC_F32,
+                               sv.SPEC_BF16 if de == 2 else sv.SPEC_F32)
+    first = "hold_kernel" if path == sv.SPEC_PATH_HELD else "stats_kernel"
+    traffic = measured_traffic(key, first)
     Ts = sorted(set(float(t) for t in np.asarray(case.temperature).ravel()))
     result = {
         "metric": METRIC if args.workload == "batched" else
@@ -354,24 +363,25 @@ def bench_verify(args):
                    "logits": tname if tname == dname else f"target {tname}, draft {dname}",
                    "sum_verify_len": sum_l, "temperature": Ts, "seed": case.seed,
                    "input_copies": ncopy, "parallelism": "none (one GPU)"},
-        # the dominant kernel: the statistics launch streams every needed row
-        # once, so its algorithmic bytes are the call's
+        # the dominant kernel, the first launch: it reads every needed row,
+        # so its algorithmic bytes are the call's
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "algorithmic_bytes_per_launch": alg_bytes,
                      "kernel_ms_mean": float(stats_ms.mean()),
                      "kernel_ms_p10": float(np.percentile(stats_ms, 10)),
                      "kernel_ms_p90": float(np.percentile(stats_ms, 90)),
-                     "kernel": f"stats_kernel<{tname}, {dname}> (HIP events around the launch "
+                     "kernel": f"{first}<{tname}, {dname}> (HIP events around the launch "
                                "inside each call of a second timed pass)"},
-        # the whole call (its four kernels) against the same bytes
+        # the whole call against the same bytes
         "call_roofline": {"achieved": call_achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                           "frac": call_achieved / HBM_PEAK_GBS,
                           "traffic": measured_traffic(key),
                           "call_ms_mean": float(kern_ms.mean()),
                           "call_ms_p10": float(np.percentile(kern_ms, 10)),
                           "call_ms_p90": float(np.percentile(kern_ms, 90)),
-                          "kernels": f"spec_verify_batch: {VERIFY_KERNELS} ({tname}, {dname})"},
+                          "kernels": f"spec_verify_batch: {VERIFY_KERNELS[path]} "
+                                     f"({tname}, {dname})"},
         "kernel_positions_per_s": sum_l / avg_kernel_s,
     }
     if not args.no_cpu_baseline:

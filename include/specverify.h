@@ -117,6 +117,24 @@ size_t spec_verify_workspace_bytes(int R, int gamma, int V);
  * buffer, or to recover a buffer after SPEC_DEV_SPIN_TIMEOUT. */
 int spec_workspace_init(void *workspace, size_t workspace_bytes, void *stream);
 
+/* Which launch sequence a spec_verify_batch call of this shape takes on the
+ * current device, for 16-byte aligned logit rows (a negative spec_status for
+ * invalid or unsupported shapes):
+ *   SPEC_PATH_SPLIT  four launches: chunk statistics, normaliser folds, the
+ *                    total-variation pass (which reads every row pair a second
+ *                    time), the per-request combine;
+ *   SPEC_PATH_HELD   two launches: one workgroup per row pair keeps most of
+ *                    the pair on the compute unit between the statistics and
+ *                    the total-variation pass (bf16 rows of more than 72
+ *                    chunks of 1024 logits, at most 2 x compute units
+ *                    candidate pairs), then the combine.
+ * Both produce the same bits.  SPECVERIFY_SPLIT=1 in the environment selects
+ * the split path for every call (for comparisons).  Host only; enqueues
+ * nothing. */
+#define SPEC_PATH_SPLIT 0
+#define SPEC_PATH_HELD 1
+int spec_verify_path(int R, int gamma, int V, int target_dtype, int draft_dtype);
+
 /*
  * Batched verification (DART note eq. (3)-(4); DSpark guide "basics",
  * "confidence head", "scheduler"; survey sec. 1.3).
@@ -196,9 +214,11 @@ int spec_verify_batch_noalloc(const void *target_logits, int t_dtype,
  * spec_verify_batch_noalloc, spec_tv_accept_rate) made by the calling host
  * thread, the library records the events before[i] and after[i] (hipEvent_t
  * passed as void*, created and owned by the caller) on the call's stream
- * immediately before and after its statistics launch -- the launch that
- * streams every needed logit row from HBM -- so that the caller can time
- * that kernel alone (hipEventElapsedTime).  The arrays must stay valid until
+ * immediately before and after its first launch -- the one that streams
+ * every needed logit row from HBM: the statistics launch on the split path,
+ * the held-pair launch on the held path (spec_verify_path) -- so that the
+ * caller can time that kernel alone (hipEventElapsedTime).  The arrays must
+ * stay valid until
  * those n calls have been made; n = 0 stops.  Returns SPEC_EINVAL for n < 0
  * or missing arrays.
  */

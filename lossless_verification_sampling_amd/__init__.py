@@ -36,11 +36,13 @@ SPEC_STS_MAX_BINS = 24
 SPEC_STS_MAX_GRID = 1024
 SPEC_STS_MAX_BLOCKS = 1 << 24
 SPEC_TREE_MAX_NODES = 1024
+SPEC_PATH_SPLIT, SPEC_PATH_HELD = 0, 1
 
 EXPORTED = (
     "spec_version",
     "spec_status_string",
     "spec_verify_workspace_bytes",
+    "spec_verify_path",
     "spec_workspace_init",
     "spec_verify_batch",
     "spec_verify_batch_noalloc",
@@ -79,6 +81,8 @@ def _load() -> ctypes.CDLL:
     lib.spec_status_string.argtypes = [i]
     lib.spec_verify_workspace_bytes.restype = sz
     lib.spec_verify_workspace_bytes.argtypes = [i, i, i]
+    lib.spec_verify_path.restype = i
+    lib.spec_verify_path.argtypes = [i, i, i, i, i]
     lib.spec_tv_workspace_bytes.restype = sz
     lib.spec_tv_workspace_bytes.argtypes = [i, i]
     lib.spec_markov_workspace_bytes.restype = sz
@@ -135,6 +139,20 @@ def spec_status_string(status: int) -> str:
 
 def spec_verify_workspace_bytes(R: int, gamma: int, V: int) -> int:
     return int(_lib.spec_verify_workspace_bytes(R, gamma, V))
+
+
+def spec_verify_path(R: int, gamma: int, V: int, target_dtype, draft_dtype) -> int:
+    """SPEC_PATH_HELD or SPEC_PATH_SPLIT: the launch sequence a
+    spec_verify_batch call of this shape takes on the current device (16-byte
+    aligned rows); dtypes as torch dtypes or SPEC_F32 / SPEC_BF16."""
+    def code(d):
+        if isinstance(d, torch.dtype):
+            return SPEC_BF16 if d == torch.bfloat16 else SPEC_F32
+        return int(d)
+    st = int(_lib.spec_verify_path(R, gamma, V, code(target_dtype), code(draft_dtype)))
+    if st < 0:
+        _raise(st, "spec_verify_path")
+    return st
 
 
 def spec_tv_workspace_bytes(N: int, V: int) -> int:

@@ -1,5 +1,6 @@
 // verify.hip -- batched lossless speculative-sampling verification and the
-// analytic acceptance rate on gfx950: four stream-ordered launches per call.
+// analytic acceptance rate on gfx950: stream-ordered launches, two or four
+// per call.
 //
 // Method (pages cited by title and section):
 //  * DART reading note (zhongzhuzhou.org), sec. 2.3, eq. (3)-(4): a draft token
@@ -17,7 +18,8 @@
 // Design.  A "unit" is one position of one request: the (target, draft) row
 // pair of position i < l_r, or the bonus target row i = l_r.  Each unit's rows
 // are cut into C chunks of 64 N logits, and an "item" is one chunk of one
-// unit.  Four launches, in stream order:
+// unit.  The split path (any dtypes and sizes) takes four launches, in
+// stream order:
 //  1. stats_kernel: persistent wave64s stream every needed row exactly once
 //     from HBM with 16-byte loads, the items balanced over the waves through a
 //     per-block unit table in LDS.  Per item it writes the chunk's scaled max
@@ -39,13 +41,23 @@
 //     the first rejection, or the bonus from q; at T = 0 the target argmax)
 //     and writes the outputs.  Row-pair mode (c* and Res only) takes one wave
 //     per pair instead.
+// The held path replaces launches 1-3 for bf16 rows of more than 72 chunks
+// (at most two pairs per compute unit): hold_kernel gives each row pair at
+// T > 0 one workgroup, which keeps 72 of its chunks in registers and as many
+// more as shared memory holds (38 at R = 64, gamma = 7, V = 151936) from the
+// statistics pass to the TV pass, folds
+// the normalisers and pair scales in every wave and reads only the rest of
+// the pair again; the workgroups without a pair stream the other rows (bonus
+// rows, T = 0 rows) for their statistics.  It writes the same words, bit for
+// bit, and the combine follows unchanged.
 // No launch waits on a word of its own launch: each reads only what earlier
 // launches of the call wrote.  Those words are 64-bit (launch tag, payload)
 // pairs, so a reader never mistakes a stale word (an earlier call's, say
 // after a launch failed) for a current one.  The tag is kept on the device,
 // so that a captured graph gets a new one at every replay: launch 1 reads the
 // workspace's next tag and copies it to the call's slot, the later launches
-// read that slot, and launch 4 stores the tag after it as the next.  A word
+// read that slot, and the combine (the last launch) stores the tag after it
+// as the next.  A word
 // that is still stale when read raises SPEC_DEV_SPIN_TIMEOUT after a bounded
 // re-poll instead of being used.
 #include <math.h>
@@ -2089,24 +2101,33 @@ size_t hold_bytes(const VerifyArgs &a, int *kl) {
     return head + (size_t)n * hold_slot_words() * 4;
 }
 
+// Whether a call of this shape takes the held path on the current device
+// (bf16 rows in 16-byte vectors assumed): its shared memory fits, every
+// register chunk is whole (more than kHoldWaves * kHoldReg chunks), and at
+// most two rounds of pairs fall to a workgroup even when every position is
+// verified (larger batches stream faster through the split path).
+// SPECVERIFY_SPLIT=1 in the environment selects the split path.
+bool hold_applies(const VerifyArgs &a, int *kl, size_t *lds, long *G) {
+    *lds = hold_bytes(a, kl);
+    *G = device_cus();
+    if (*lds == 0 || *G <= 0) return false;
+    if ((long)a.R * (a.tv_mode ? 1 : (a.gamma > 0 ? a.gamma : 1)) > 2 * *G) return false;
+    const char *sp = getenv("SPECVERIFY_SPLIT");
+    return !(sp && sp[0] == '1');
+}
+
 // The held path for bf16 rows: one launch for the statistics, folds and TV
 // sums, then the combine.  Returns -1 when it does not apply (the split path
-// runs instead), else the launch status.  SPECVERIFY_SPLIT=1 in the
-// environment selects the split path (for comparisons).
+// runs instead), else the launch status.
 template <int N, int EPV>
 int launch_hold(VerifyArgs a, hipStream_t st) {
     if constexpr (N != 16 || EPV != 8) {
         return -1;
     } else {
         int kl = 0;
-        const size_t lds = hold_bytes(a, &kl);
-        const long G = device_cus();
-        if (lds == 0 || G <= 0) return -1;
-        // at most two rounds of pairs per workgroup even if every position
-        // is verified; larger batches stream faster through the split path
-        if ((long)a.R * (a.tv_mode ? 1 : (a.gamma > 0 ? a.gamma : 1)) > 2 * G) return -1;
-        const char *sp = getenv("SPECVERIFY_SPLIT");
-        if (sp && sp[0] == '1') return -1;
+        size_t lds = 0;
+        long G = 0;
+        if (!hold_applies(a, &kl, &lds, &G)) return -1;
         const void *k = reinterpret_cast<const void *>(&hold_kernel<N, EPV>);
         static std::atomic<int> attr{0};
         if (attr.load(std::memory_order_relaxed) == 0) {
@@ -2349,6 +2370,27 @@ int spec_verify_batch_noalloc(const void *target_logits, int t_dtype, const void
                              verify_len, temperature, u_accept, u_sample, R, gamma, V, out_tokens,
                              out_num_accepted, out_cstar, out_resid_mass, out_logq, ws,
                              (size_t)SPEC_NOALLOC_SCRATCH_BYTES, stream);
+}
+
+int spec_verify_path(int R, int gamma, int V, int t_dtype, int d_dtype) {
+    if (R < 0 || gamma < 0 || V < 1) return SPEC_EINVAL;
+    if (!dtype_ok(t_dtype) || !dtype_ok(d_dtype)) return SPEC_EDTYPE;
+    if (gamma > kMaxGamma || V > SPEC_MAX_VERIFY_VOCAB) return SPEC_EUNSUPPORTED;
+    Plan p;
+    if (R > 0 && !make_plan(R, gamma + 1, V, p)) return SPEC_EUNSUPPORTED;
+    const int ddt = gamma > 0 ? d_dtype : t_dtype;
+    if (R == 0 || V % 8 != 0 || t_dtype != SPEC_BF16 || ddt != SPEC_BF16)
+        return SPEC_PATH_SPLIT;
+    VerifyArgs a{};
+    a.R = R;
+    a.gamma = gamma;
+    a.V = V;
+    a.UG = gamma + 1;
+    a.C = p.C;
+    int kl = 0;
+    size_t lds = 0;
+    long G = 0;
+    return hold_applies(a, &kl, &lds, &G) ? SPEC_PATH_HELD : SPEC_PATH_SPLIT;
 }
 
 int spec_tv_accept_rate(const void *draft_logits, const void *target_logits, int dtype,

@@ -333,3 +333,21 @@ def test_timing_hook_arguments(lib):
     assert f(arr, None, 2) == SPEC_EINVAL
     assert f(arr, arr, 2) == SPEC_OK
     assert f(None, None, 0) == SPEC_OK
+
+
+def test_verify_path_host_checks(lib):
+    """spec_verify_path: invalid shapes are refused; fp32 rows, a vocabulary
+    that is not a multiple of 8 and an empty batch take the split path (all
+    decided before any HIP call)."""
+    f = lib.spec_verify_path
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_int] * 5
+    F32, BF16 = 0, 1
+    assert f(-1, 7, 151936, BF16, BF16) == -1
+    assert f(64, 7, 0, BF16, BF16) == -1
+    assert f(64, 7, 151936, 7, BF16) == -2
+    assert f(64, 7, 262144 + 1, BF16, BF16) == -5   # past SPEC_MAX_VERIFY_VOCAB
+    assert f(64, 7, 151936, F32, F32) == 0
+    assert f(64, 7, 151936, BF16, F32) == 0
+    assert f(64, 7, 151937, BF16, BF16) == 0
+    assert f(0, 7, 151936, BF16, BF16) == 0

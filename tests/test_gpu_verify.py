@@ -289,6 +289,19 @@ def _same_bits(a, b, what):
             (what, k)
 
 
+def test_verify_path_choice(sv, dev, monkeypatch):
+    """The batched workload's shape takes the held path on this GPU, the
+    high-load batch (R = 256) and fp32 rows the split path, and the
+    environment switch forces the split path."""
+    bf = torch.bfloat16
+    assert sv.spec_verify_path(64, 7, 151936, bf, bf) == sv.SPEC_PATH_HELD
+    assert sv.spec_verify_path(256, 7, 129280, bf, bf) == sv.SPEC_PATH_SPLIT
+    assert sv.spec_verify_path(1, 8, 151936, torch.float32, torch.float32) == sv.SPEC_PATH_SPLIT
+    assert sv.spec_verify_path(64, 7, 65536, bf, bf) == sv.SPEC_PATH_SPLIT  # 64 chunks
+    monkeypatch.setenv("SPECVERIFY_SPLIT", "1")
+    assert sv.spec_verify_path(64, 7, 151936, bf, bf) == sv.SPEC_PATH_SPLIT
+
+
 @pytest.mark.parametrize("seed", [51, 52])
 def test_held_and_split_paths_identical(sv, dev, seed, monkeypatch):
     """bf16 rows of more than 72 chunks take the held-pair launch (one
