@@ -325,14 +325,41 @@ def test_held_and_split_paths_identical(sv, dev, seed, monkeypatch):
     assert st["invalid"] == 1 and st["exact"] + st["near_ties"] == R - 1, st
 
 
+@pytest.mark.parametrize("R,V,lmode", [(16, 73 * 1024 - 8, "mixed"),   # 73 chunks: one slot
+                                         (40, 129280, "mixed"),
+                                         (64, 151936, "full"),          # 448 pairs: two rounds
+                                         (72, 131072, "full")],         # 504 pairs, whole chunks
+                         ids=["V74744", "V129280", "two_rounds", "V131072_two_rounds"])
+def test_held_path_edges(sv, dev, R, V, lmode, monkeypatch):
+    """The held path at its edges: the smallest vocabulary it takes (73
+    chunks, one shared-memory slot, a ragged last chunk), V = 129280, and
+    batches with more pairs than compute units (a workgroup holds two pairs
+    in turn): the same bits as the split path and the oracle's tokens."""
+    g = 7
+    assert sv.spec_verify_path(R, g, V, torch.bfloat16, torch.bfloat16) == sv.SPEC_PATH_HELD
+    lens = np.full(R, g, np.int32) if lmode == "full" else (np.arange(R) % (g + 1)).astype(np.int32)
+    T = np.array([1.0, 0.7, 0.0, 1.5], np.float32)[np.arange(R) % 4]
+    case = workloads.make_verify_case(R, g, V, "bf16", seed=61 + R,
+                                      noise_std=np.linspace(0.5, 2.5, g), verify_len=lens,
+                                      temperature=T)
+    held = run_verify(sv, case, dev)
+    monkeypatch.setenv("SPECVERIFY_SPLIT", "1")
+    split = run_verify(sv, case, dev)
+    monkeypatch.delenv("SPECVERIFY_SPLIT")
+    _same_bits(held, split, "verify")
+    st = compare_verify(case, held, oracle.verify_case(case))
+    assert st["exact"] + st["near_ties"] == R, st
+
+
 def test_held_and_split_accept_rate_identical(sv, dev, monkeypatch):
-    """Row-pair mode on bf16 rows of V = 151936: held and split launches give
-    the same bits, within the bf16 tolerance of the oracle."""
-    N, V = 40, 151936
+    """Row-pair mode on bf16 rows of V = 151936, with more pairs than compute
+    units (two rounds per workgroup): held and split launches give the same
+    bits, within the bf16 tolerance of the oracle."""
+    N, V = 300, 151936
     gen = np.random.default_rng(5)
     zt = (gen.standard_normal((N, V)) * 3).astype(np.float32)
     zd = (zt + gen.standard_normal((N, V)) * np.linspace(0.05, 3, N)[:, None]).astype(np.float32)
-    T = np.array([1.0, 0.0, 0.7, 2.0] * 10, np.float32)[:N]
+    T = np.array([1.0, 0.0, 0.7, 2.0] * 75, np.float32)[:N]
     zt, zd = workloads.f32_to_bf16_bits(zt), workloads.f32_to_bf16_bits(zd)
     args = (to_device(zd, dev), to_device(zt, dev), to_device(T, dev))
     held = [t.cpu().numpy() for t in sv.spec_tv_accept_rate(*args)]
