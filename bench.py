@@ -4,7 +4,7 @@ A step is one spec_verify_batch call over the batched workload (R = 64
 requests, gamma = 7, V = 151936, bf16 logits, verify lengths uniform on 0..7,
 T = 1): every row of the hot path (softmax statistics, c*, accept tests,
 prefix survival, residual / bonus draw, commit) runs in that one call.  For
-bf16 rows of more than 72 chunks (this workload) the call launches two
+bf16 rows of more than 64 chunks (this workload) the call launches two
 kernels on the current stream: the held-pair kernel (one workgroup per row
 pair keeps most of the pair on its compute unit between the statistics pass
 and the total-variation pass, so the pair is read from memory about once) and
@@ -106,6 +106,30 @@ def measured_traffic(kernel_key: str, kernel: str = None):
     tot = [v for k, v in e.get("per_dispatch_fetch", {}).items() if kernel in k]
     tot += [v for k, v in e.get("per_dispatch_write", {}).items() if kernel in k]
     return sum(tot) if tot else None
+
+
+def timed_steps(call, steps: int, stream):
+    """(wall seconds, per-call GPU ms) of `steps` calls call(k).  The wall
+    time is that of the calls issued back to back with a synchronisation on
+    both sides and nothing between them; the per-call GPU times come from a
+    second pass of the same calls (k = steps .. 2 steps - 1), each bracketed
+    by HIP events (an event between two calls adds a gap of its own, hence
+    the separate pass)."""
+    import torch
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(steps):
+        call(k)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for k in range(steps):
+        ev[k][0].record(stream)
+        call(steps + k)
+        ev[k][1].record(stream)
+    torch.cuda.synchronize()
+    return wall, np.array([a.elapsed_time(b) for a, b in ev])
 
 
 class HipEvents:
@@ -305,25 +329,15 @@ def bench_verify(args):
     torch.cuda.synchronize()
     if sv.spec_get_device_status(ws, clear=True):
         raise RuntimeError("device status bits set during warm-up")
-    stream = torch.cuda.current_stream(dev)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for k in range(args.steps):
-        ev[k][0].record(stream)
-        step(args.warmup + k)
-        ev[k][1].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    kern_ms = np.array([a.elapsed_time(b) for a, b in ev])
-    # second timed pass of the same steps: the first launch of every call
-    # bracketed by HIP events that the library records on the call's stream
-    # (events inside a call add launch gaps, hence a pass of its own)
+    wall, kern_ms = timed_steps(lambda k: step(args.warmup + k), args.steps,
+                                torch.cuda.current_stream(dev))
+    # third pass of the same steps: the first launch of every call bracketed
+    # by HIP events that the library records on the call's stream (events
+    # inside a call add launch gaps, hence a pass of its own)
     hev = HipEvents(2 * args.steps)
     sv.spec_time_stats_launch(hev.events[:args.steps], hev.events[args.steps:])
     for k in range(args.steps):
-        step(args.warmup + args.steps + k)
+        step(args.warmup + 2 * args.steps + k)
     torch.cuda.synchronize()
     sv.spec_time_stats_launch([], [])
     stats_ms = np.array([hev.elapsed_ms(k, args.steps + k) for k in range(args.steps)])
@@ -372,7 +386,7 @@ def bench_verify(args):
                      "kernel_ms_p10": float(np.percentile(stats_ms, 10)),
                      "kernel_ms_p90": float(np.percentile(stats_ms, 90)),
                      "kernel": f"{first}<{tname}, {dname}> (HIP events around the launch "
-                               "inside each call of a second timed pass)"},
+                               "inside each call of a third pass)"},
         # the whole call against the same bytes
         "call_roofline": {"achieved": call_achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                           "frac": call_achieved / HBM_PEAK_GBS,
@@ -443,18 +457,12 @@ def bench_dspark(args):
         sv.spec_markov_draft_sample(U, W1, W2, anc, T, ud, out_tokens=tok, out_logits=lg,
                                     workspace=ws)
     torch.cuda.synchronize()
-    stream = torch.cuda.current_stream(dev)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
-    t0 = time.perf_counter()
-    for k in range(args.steps):
-        ev[k][0].record(stream)
+
+    def call(k):
         sv.spec_markov_draft_sample(U, W1, W2, anc, T, ud, out_tokens=tok, out_logits=lg,
                                     workspace=ws)
-        ev[k][1].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms = np.array([a.elapsed_time(b) for a, b in ev])
+
+    wall, ms = timed_steps(call, args.steps, torch.cuda.current_stream(dev))
     flops = 2.0 * R * rank * V * gamma
     per_step_bytes = (R * V * 2 + rank * V * 2 + R * V * 4) * gamma
     res = {
@@ -506,17 +514,11 @@ def bench_rnn(args):
     for _ in range(args.warmup):
         sv.spec_rnn_draft_sample(*ins, out_tokens=tok, out_logits=lg, workspace=ws)
     torch.cuda.synchronize()
-    stream = torch.cuda.current_stream(dev)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
-    t0 = time.perf_counter()
-    for k in range(args.steps):
-        ev[k][0].record(stream)
+
+    def call(k):
         sv.spec_rnn_draft_sample(*ins, out_tokens=tok, out_logits=lg, workspace=ws)
-        ev[k][1].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms = np.array([a.elapsed_time(b) for a, b in ev])
+
+    wall, ms = timed_steps(call, args.steps, torch.cuda.current_stream(dev))
     din = 2 * rank + hidden
     per_call = (R * V * 2 + rank * V * 2 + R * V * 4 + din * 2 * rank * 2 + R * hidden * 4) * gamma
     flops = (3 * 2.0 * R * rank * V + 2.0 * R * din * 2 * rank) * gamma
@@ -571,17 +573,11 @@ def bench_schedule(args):
     for _ in range(args.warmup):
         sv.spec_schedule_verify_len(conf, sps, out_len=ln, out_theta=th, workspace=ws)
     torch.cuda.synchronize()
-    stream = torch.cuda.current_stream(dev)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
-    t0 = time.perf_counter()
-    for k in range(args.steps):
-        ev[k][0].record(stream)
+
+    def call(k):
         sv.spec_schedule_verify_len(conf, sps, out_len=ln, out_theta=th, workspace=ws)
-        ev[k][1].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms = np.array([a.elapsed_time(b) for a, b in ev])
+
+    wall, ms = timed_steps(call, args.steps, torch.cuda.current_stream(dev))
     res = {
         "metric": "confidence-scheduled verify lengths: schedules/sec",
         "value": args.steps / wall,
@@ -634,17 +630,13 @@ def bench_sts(args):
     for _ in range(args.warmup):
         sv.spec_sts_calibrate(z, A, grid, bins=bins, workspace=ws)
     torch.cuda.synchronize()
-    stream = torch.cuda.current_stream(dev)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
-    t0 = time.perf_counter()
-    for k in range(args.steps):
-        ev[k][0].record(stream)
-        t, e, _ = sv.spec_sts_calibrate(z, A, grid, bins=bins, workspace=ws)
-        ev[k][1].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms = np.array([a.elapsed_time(b) for a, b in ev])
+    last = {}
+
+    def call(k):
+        last["r"] = sv.spec_sts_calibrate(z, A, grid, bins=bins, workspace=ws)
+
+    wall, ms = timed_steps(call, args.steps, torch.cuda.current_stream(dev))
+    t, e, _ = last["r"]
     evals = N * G * gamma
     achieved = STS_OPS_PER_SCORE * evals / (ms.mean() / 1e3) / 1e12
     res = {
@@ -698,17 +690,13 @@ def bench_tree(args):
     for _ in range(args.warmup):
         sv.spec_tree_verify(L, P, X, n, c.max_depth, workspace=ws)
     torch.cuda.synchronize()
-    stream = torch.cuda.current_stream(dev)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
-    t0 = time.perf_counter()
-    for k in range(args.steps):
-        ev[k][0].record(stream)
-        acc, _, _ = sv.spec_tree_verify(L, P, X, n, c.max_depth, workspace=ws)
-        ev[k][1].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms = np.array([a.elapsed_time(b) for a, b in ev])
+    last = {}
+
+    def call(k):
+        last["r"] = sv.spec_tree_verify(L, P, X, n, c.max_depth, workspace=ws)
+
+    wall, ms = timed_steps(call, args.steps, torch.cuda.current_stream(dev))
+    acc, _, _ = last["r"]
     a = acc.cpu().numpy()
     committed = int((a + 1).sum())
     per_call = committed * V * 2          # the rows the walk reads
@@ -779,7 +767,10 @@ def write_traffic(args):
     (one-time workspace set-up) are left out.  Writes the entry under --key
     in the traffic file, stamped with the current source hash."""
     fetch_dir, write_dir, cfetch_dir, cwrite_dir = args.traffic_from
-    calls = args.calls or (args.warmup + args.steps)
+    # calls of the counted run: the warm-up, then two passes of the steps
+    # (three for the verify workloads, whose last pass times the first launch)
+    passes = 3 if args.key.startswith("verify_") else 2
+    calls = args.calls or (args.warmup + passes * args.steps)
     copy_bytes = 256 << 20
 
     def scale(d, counter):
@@ -848,8 +839,8 @@ def main():
                          "(--steps/--warmup as in the counted run)")
     ap.add_argument("--key", default="verify_batched")
     ap.add_argument("--calls", type=int, default=0,
-                    help="library calls in the counted run (default --warmup + --steps; the "
-                         "verify workloads make two timed passes: --warmup + 2 --steps)")
+                    help="library calls in the counted run (default --warmup + 2 --steps; "
+                         "the verify workloads make three passes: --warmup + 3 --steps)")
     ap.add_argument("--copies-counted", type=int, default=6,
                     help="copies in the counted --calibrate-copy run")
     args = ap.parse_args()

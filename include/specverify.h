@@ -125,7 +125,7 @@ int spec_workspace_init(void *workspace, size_t workspace_bytes, void *stream);
  *                    time), the per-request combine;
  *   SPEC_PATH_HELD   two launches: one workgroup per row pair keeps most of
  *                    the pair on the compute unit between the statistics and
- *                    the total-variation pass (bf16 rows of more than 72
+ *                    the total-variation pass (bf16 rows of more than 64
  *                    chunks of 1024 logits, at most 2 x compute units
  *                    candidate pairs), then the combine.
  * Both produce the same bits.  SPECVERIFY_SPLIT=1 in the environment selects

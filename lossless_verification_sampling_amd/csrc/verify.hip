@@ -41,9 +41,9 @@
 //     the first rejection, or the bonus from q; at T = 0 the target argmax)
 //     and writes the outputs.  Row-pair mode (c* and Res only) takes one wave
 //     per pair instead.
-// The held path replaces launches 1-3 for bf16 rows of more than 72 chunks
+// The held path replaces launches 1-3 for bf16 rows of more than 64 chunks
 // (at most two pairs per compute unit): hold_kernel gives each row pair at
-// T > 0 one workgroup, which keeps 72 of its chunks in registers and as many
+// T > 0 one workgroup, which keeps 64 of its chunks in registers and as many
 // more as shared memory holds (38 at R = 64, gamma = 7, V = 151936) from the
 // statistics pass to the TV pass, folds
 // the normalisers and pair scales in every wave and reads only the rest of

@@ -304,7 +304,7 @@ def test_verify_path_choice(sv, dev, monkeypatch):
 
 @pytest.mark.parametrize("seed", [51, 52])
 def test_held_and_split_paths_identical(sv, dev, seed, monkeypatch):
-    """bf16 rows of more than 72 chunks take the held-pair launch (one
+    """bf16 rows of more than 64 chunks take the held-pair launch (one
     workgroup keeps each row pair on chip between the two passes); the split
     launches (SPECVERIFY_SPLIT=1) must give the same bits, and both the
     oracle's, on a batch mixing T > 0 and T = 0 requests, every verify length
@@ -325,13 +325,13 @@ def test_held_and_split_paths_identical(sv, dev, seed, monkeypatch):
     assert st["invalid"] == 1 and st["exact"] + st["near_ties"] == R - 1, st
 
 
-@pytest.mark.parametrize("R,V,lmode", [(16, 73 * 1024 - 8, "mixed"),   # 73 chunks: one slot
+@pytest.mark.parametrize("R,V,lmode", [(16, 65 * 1024 - 8, "mixed"),   # 65 chunks: one slot
                                          (40, 129280, "mixed"),
                                          (64, 151936, "full"),          # 448 pairs: two rounds
                                          (72, 131072, "full")],         # 504 pairs, whole chunks
-                         ids=["V74744", "V129280", "two_rounds", "V131072_two_rounds"])
+                         ids=["V66552", "V129280", "two_rounds", "V131072_two_rounds"])
 def test_held_path_edges(sv, dev, R, V, lmode, monkeypatch):
-    """The held path at its edges: the smallest vocabulary it takes (73
+    """The held path at its edges: the smallest vocabulary it takes (65
     chunks, one shared-memory slot, a ragged last chunk), V = 129280, and
     batches with more pairs than compute units (a workgroup holds two pairs
     in turn): the same bits as the split path and the oracle's tokens."""
