@@ -108,7 +108,7 @@ struct VerifyArgs {
     uint64_t *st2;           // [units][C][2] chunk sum min(p, q), residual mass
     uint64_t *nrm;           // [units][4] unit normalisers
     uint64_t *rec;           // [units][kRecWords] unit records
-    uint64_t *psc;           // [units * C][4] per-chunk pair scales (kt, kd, unit)
+    uint64_t *psc;           // [units * C][4] per-chunk pair scales (chi, clo, unit)
 };
 
 // ---------------------------------------------------------------------------
@@ -509,13 +509,18 @@ __device__ __forceinline__ void chunk_argmax(const RC &raw, long c0, float &bv, 
     bad = wave_max_i(bad);
 }
 
-// Scaling of a row pair's chunk weights for min(p, q): p_v = e_d alpha_d and
-// q_v = e_t alpha_t are compared as min(e_t kt, e_d kd) in units of `unit`
-// probability.  kt = 1 (unit alpha_t) unless the draft scale exceeds the
-// target's by more than 2^100; then kd = 1 (unit alpha_d).  Both products stay
-// finite because every e is at most 1 (up to one rounding).
+// Scaling of a row pair's chunk weights for min(p, q).  With q_v = e_t alpha_t
+// and p_v = e_d alpha_d (e = 2^(z s - ref), alpha = 2^(mu - M) / Z per row),
+// min(p, q) in units of alpha_t is 2^min(a, b): a = z_t s - ref_t is the
+// target weight's exponent and b = z_d s + c the draft weight's on the
+// target's scale, c = -ref_d + log2(alpha_d / alpha_t).  One exponential per
+// element, and where the target side is the smaller the term is the target
+// weight bit for bit, so a chunk where q <= p everywhere leaves a residual of
+// exactly 0.  c is carried as a float pair (chi + clo); both scales are at
+// least 2^-149 / V when nonzero, so |log2(alpha_d / alpha_t)| < 170.
 struct PairScale {
-    float kt, kd, unit;
+    float unit;       // alpha_t; 0 where q vanishes on the chunk (its terms are 0)
+    float chi, clo;   // c = chi + clo
 };
 
 // A row's normalisers with the reciprocal of Z taken once (fp64).
@@ -531,36 +536,29 @@ __device__ __forceinline__ RowNorm row_norm(float M, float Z) {
     return n;
 }
 
-// The pair scale of a chunk with scaled maxima mut, mud: alpha = 2^(mu - M) / Z
-// per row and kd = alpha_d / alpha_t, formed from products only (the
-// reciprocals are the rows').
+// The pair scale of a chunk with scaled maxima mut, mud.  Where q vanishes
+// on the chunk the unit is 0 (its min and residual are 0); where p does, c
+// puts every draft exponent far below the target's (min(p, q) = 0 there).
 __device__ __forceinline__ PairScale pair_scale(float mut, float mud, const RowNorm &t,
                                                 const RowNorm &d) {
     PairScale ps;
     const float et = (mut > -kInf) ? __builtin_amdgcn_exp2f(mut - t.M) : 0.0f;
     const float ed = (mud > -kInf) ? __builtin_amdgcn_exp2f(mud - d.M) : 0.0f;
     const double at = (double)et * t.rZ, ad = (double)ed * d.rZ;
-    if (!(at > 0.0)) {
-        // q vanishes on the chunk: min(p, q) = 0 and no residual
-        ps.kt = 0.0f;
-        ps.kd = 1.0f;
-        ps.unit = (float)ad;
-        return ps;
-    }
-    const double k = (ed > 0.0f) ? (double)ed * (double)__builtin_amdgcn_exp2f(t.M - mut) *
-                                       ((double)t.Z * d.rZ)
-                                 : 0.0;
-    if (k <= 0x1p100) {
-        ps.kt = 1.0f;
-        ps.kd = (float)k;
-        ps.unit = (float)at;
-    } else {
-        ps.kt = (float)((double)et * (double)__builtin_amdgcn_exp2f(d.M - mud) *
-                        ((double)d.Z * t.rZ));
-        ps.kd = 1.0f;
-        ps.unit = (float)ad;
-    }
+    ps.unit = (float)at;
+    const double lk = !(at > 0.0) ? 1024.0 : !(ad > 0.0) ? -1024.0 : log2(ad / at);
+    const double c = lk - (double)exp_ref(mud);
+    ps.chi = (float)c;
+    ps.clo = (float)(c - (double)ps.chi);
     return ps;
+}
+
+// min(p, q) of one element in units of alpha_t (see PairScale).
+__device__ __forceinline__ float min_term(float zt, float zd, float s, float reft,
+                                          const PairScale &ps) {
+    const float a = __builtin_fmaf(zt, s, -reft);
+    const float b = __builtin_fmaf(zd, s, ps.chi) + ps.clo;
+    return __builtin_amdgcn_exp2f(__builtin_elementwise_minimum(a, b));
 }
 
 // Online combine of chunk statistics (scaled max mu, weight sum S) into a
@@ -933,8 +931,8 @@ __device__ __forceinline__ void norm_fold(const VerifyArgs &a, const Item &x, in
             const PairScale ps =
                 pair_scale(__uint_as_float(w[b][0]), __uint_as_float(w[b][2]), nt, nd);
             uint64_t *q = a.psc + ((size_t)x.u * C + c) * 4;
-            st_word(q + 0, a.tag, __float_as_uint(ps.kt));
-            st_word(q + 1, a.tag, __float_as_uint(ps.kd));
+            st_word(q + 0, a.tag, __float_as_uint(ps.chi));
+            st_word(q + 1, a.tag, __float_as_uint(ps.clo));
             st_word(q + 2, a.tag, __float_as_uint(ps.unit));
         }
     }
@@ -1216,15 +1214,17 @@ __device__ __forceinline__ int request_draw(const VerifyArgs &a, int r, int j, i
         words_settle<1>(sp, sa, a.tag, a.ctl, sv, so);
         const float mut = __uint_as_float(rl(so[0], 0)), mud = __uint_as_float(rl(so[0], 2));
         const PairScale ps = pair_scale(mut, mud, row_norm(Mt, Zt), row_norm(Md, Zd));
-        const float reft = exp_ref(mut), refd = exp_ref(mud);
+        const float reft = exp_ref(mut);
         const double te = (ps.unit > 0.0f) ? su.tin / (double)ps.unit : INFINITY;
         float wv[N / EPV][EPV];
 #pragma unroll
         for (int jj = 0; jj < N / EPV; ++jj)
 #pragma unroll
             for (int q = 0; q < EPV; ++q) {
-                const float et = ew(zt[jj][q], s, reft) * ps.kt;
-                const float mn = __builtin_elementwise_minimum(et, ew(zd[jj][q], s, refd) * ps.kd);
+                // the TV pass's terms; the outer min keeps every weight >= 0
+                const float et = ew(zt[jj][q], s, reft);
+                const float mn = __builtin_elementwise_minimum(
+                    et, min_term(zt[jj][q], zd[jj][q], s, reft, ps));
                 wv[jj][q] = et - mn;
             }
         tok = draw_in_chunk_w<N, EPV>(c0, te, wv);
@@ -1424,31 +1424,17 @@ __global__ void __launch_bounds__(kBlock, kStreamWaves) stats_kernel(VerifyArgs 
 // row slots -inf).
 template <int N, typename RT, typename RD>
 __device__ __forceinline__ void tv_sums(const RT &rt, const RD &rd, float s, float mut, float St,
-                                        float mud, const PairScale &ps, double *cmin,
-                                        double *cres) {
-    const float reft = exp_ref(mut), refd = exp_ref(mud);
+                                        const PairScale &ps, double *cmin, double *cres) {
+    const float reft = exp_ref(mut);
     // min(p, q) in units of ps.unit, summed in the same slot order as the
-    // chunk's weight sum in the statistics pass, so a chunk with q <= p
+    // chunk's weight sum St in the statistics pass, so a chunk with q <= p
     // everywhere has a residual of exactly 0
-    float acc = 0.0f, ssum;
-    if (ps.kt == 1.0f) {
+    float acc = 0.0f;
 #pragma unroll
-        for (int k = 0; k < N; ++k)
-            acc += __builtin_elementwise_minimum(ew(rt.get(k), s, reft),
-                                                 ew(rd.get(k), s, refd) * ps.kd);
-        ssum = St;
-    } else {
-        float et[N];
-#pragma unroll
-        for (int k = 0; k < N; ++k) {
-            et[k] = ew(rt.get(k), s, reft) * ps.kt;
-            acc += __builtin_elementwise_minimum(et[k], ew(rd.get(k), s, refd));
-        }
-        ssum = wave_sum_f(lane_sum<N>(et));
-    }
+    for (int k = 0; k < N; ++k) acc += min_term(rt.get(k), rd.get(k), s, reft, ps);
     const float smin = wave_sum_f(acc);
     *cmin = (double)ps.unit * (double)smin;
-    *cres = fmax((double)ps.unit * ((double)ssum - (double)smin), 0.0);
+    *cres = fmax((double)ps.unit * ((double)St - (double)smin), 0.0);
 }
 
 // TV of pair item x at T > 0 (chunk re-read, from the Infinity Cache when the
@@ -1461,11 +1447,11 @@ __device__ __forceinline__ void tv_item(const VerifyArgs &a, const Item &x, RT &
     rd.fix();
     double cmin, cres;
     PairScale ps;
-    ps.kt = __uint_as_float(rl(w8, 4));
-    ps.kd = __uint_as_float(rl(w8, 5));
+    ps.chi = __uint_as_float(rl(w8, 4));
+    ps.clo = __uint_as_float(rl(w8, 5));
     ps.unit = __uint_as_float(rl(w8, 6));
-    tv_sums<N>(rt, rd, x.s, __uint_as_float(rl(w8, 0)), __uint_as_float(rl(w8, 1)),
-               __uint_as_float(rl(w8, 2)), ps, &cmin, &cres);
+    tv_sums<N>(rt, rd, x.s, __uint_as_float(rl(w8, 0)), __uint_as_float(rl(w8, 1)), ps, &cmin,
+               &cres);
     publish_n(a.st2 + ((size_t)x.u * a.C + x.c) * 2, a.tag, 2, __float_as_uint((float)cmin),
               __float_as_uint((float)cres), 0u, 0u);
 }
@@ -1666,19 +1652,19 @@ __device__ __forceinline__ void hold_stats(const VerifyArgs &a, const Item &x, i
 }
 
 // TV sums of chunk c = w + 8 m of held pair x; lane m of the wave holds that
-// chunk's words (mu_t, S_t, mu_d) and pair scale.
+// chunk's words (mu_t, S_t) and pair scale.
 template <int N, typename RC>
 __device__ __forceinline__ void hold_tv(const VerifyArgs &a, const Item &x, int c, int m,
-                                        RC &rt, RC &rd, float mut, float St, float mud,
+                                        RC &rt, RC &rd, float mut, float St,
                                         const PairScale &ps) {
     rt.fix();
     rd.fix();
     PairScale q;
-    q.kt = rlf(ps.kt, m);
-    q.kd = rlf(ps.kd, m);
+    q.chi = rlf(ps.chi, m);
+    q.clo = rlf(ps.clo, m);
     q.unit = rlf(ps.unit, m);
     double cmin, cres;
-    tv_sums<N>(rt, rd, x.s, rlf(mut, m), rlf(St, m), rlf(mud, m), q, &cmin, &cres);
+    tv_sums<N>(rt, rd, x.s, rlf(mut, m), rlf(St, m), q, &cmin, &cres);
     publish_n(a.st2 + ((size_t)x.u * a.C + c) * 2, a.tag, 2, __float_as_uint((float)cmin),
               __float_as_uint((float)cres), 0u, 0u);
 }
@@ -1778,14 +1764,13 @@ __device__ __forceinline__ void hold_pair(const VerifyArgs &a, const Item &x, fl
     }
     // lane m: words and pair scale of the wave's chunk w + 8 m
     const int cm = w + kHoldWaves * lane;
-    float mut = 0.0f, St = 0.0f, mud = 0.0f;
+    float mut = 0.0f, St = 0.0f;
     PairScale ps;
-    ps.kt = ps.kd = ps.unit = 0.0f;
+    ps.unit = ps.chi = ps.clo = 0.0f;
     if (cm < C) {
         mut = stt[cm * 4 + 0];
         St = stt[cm * 4 + 1];
-        mud = stt[cm * 4 + 2];
-        ps = pair_scale(mut, mud, row_norm(Mt, Zt), row_norm(Md, Zd));
+        ps = pair_scale(mut, stt[cm * 4 + 2], row_norm(Mt, Zt), row_norm(Md, Zd));
     }
     // ---- pass 2: TV sums; the chunks past the slots are read again first ----
     {
@@ -1796,23 +1781,23 @@ __device__ __forceinline__ void hold_pair(const VerifyArgs &a, const Item &x, fl
         ad.load(drow, c < C ? (long)c * kLanes * N : z0, a.V);
 #pragma unroll
         for (int k = 0; k < kHoldReg; ++k)
-            hold_tv<N>(a, x, w + kHoldWaves * k, k, ht[k], hd[k], mut, St, mud, ps);
+            hold_tv<N>(a, x, w + kHoldWaves * k, k, ht[k], hd[k], mut, St, ps);
         for (int cs = nreg + w; cs < C && cs < nlds; cs += kHoldWaves) {
             const long c0 = (long)cs * kLanes * N;
             RC st, sd;
             slot_get(slots, cs - nreg, 0, st, c0, a.V);
             slot_get(slots, cs - nreg, 1, sd, c0, a.V);
-            hold_tv<N>(a, x, cs, (cs - w) / kHoldWaves, st, sd, mut, St, mud, ps);
+            hold_tv<N>(a, x, cs, (cs - w) / kHoldWaves, st, sd, mut, St, ps);
         }
         for (; c < C; c += 2 * kHoldWaves) {
             const int cb = c + kHoldWaves, cn = c + 2 * kHoldWaves;
             bt.load(trow, cb < C ? (long)cb * kLanes * N : z0, a.V);
             bd.load(drow, cb < C ? (long)cb * kLanes * N : z0, a.V);
-            hold_tv<N>(a, x, c, (c - w) / kHoldWaves, at, ad, mut, St, mud, ps);
+            hold_tv<N>(a, x, c, (c - w) / kHoldWaves, at, ad, mut, St, ps);
             if (cb >= C) break;
             at.load(trow, cn < C ? (long)cn * kLanes * N : z0, a.V);
             ad.load(drow, cn < C ? (long)cn * kLanes * N : z0, a.V);
-            hold_tv<N>(a, x, cb, (cb - w) / kHoldWaves, bt, bd, mut, St, mud, ps);
+            hold_tv<N>(a, x, cb, (cb - w) / kHoldWaves, bt, bd, mut, St, ps);
         }
     }
     __syncthreads();  // the table entries and slots are reused by the next pair
