@@ -1669,12 +1669,25 @@ __device__ __forceinline__ void hold_tv(const VerifyArgs &a, const Item &x, int 
               __float_as_uint((float)cres), 0u, 0u);
 }
 
-// One held pair x, the whole workgroup.  Wave w owns chunks c = w + 8 m: the
-// first kHoldReg in registers, the next in shared-memory slots (while slots
-// last), the rest read again for the TV sums.
+// The next chunk of the pair's stream for the calling wave (a shared-memory
+// counter, one claim per wave).
+__device__ __forceinline__ int hold_claim(int *next) {
+    int v = 0;
+    if (lane_id() == 0)
+        v = __hip_atomic_fetch_add(next, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    return __builtin_amdgcn_readfirstlane(v);
+}
+
+// One held pair x, the whole workgroup.  Wave w keeps chunks c = w + 8 m,
+// m < kHoldReg, in registers; the later chunks are streamed by whichever wave
+// claims them next from *next (which holds nreg + 8 on entry: each wave's
+// first streamed chunk is nreg + w), so that every wave streams until the
+// pair's last chunk; those that fit go to the shared-memory slots (chunk
+// c to slot c - nreg), the rest are read again for the TV sums, where wave
+// w takes the slot and re-read chunks c = w + 8 m.
 template <int N, int EPV>
 __device__ __forceinline__ void hold_pair(const VerifyArgs &a, const Item &x, float *stt,
-                                          uint32_t *slots, int kl) {
+                                          uint32_t *slots, int kl, int *next) {
     using RC = RawChunk<uint16_t, N, EPV>;
     const int lane = lane_id();
     const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
@@ -1714,10 +1727,10 @@ __device__ __forceinline__ void hold_pair(const VerifyArgs &a, const Item &x, fl
     }
 #pragma unroll
     for (int k = 0; k < kHoldReg; ++k) hold_stats<N>(a, x, w + kHoldWaves * k, ht[k], hd[k], stt);
-    // the wave's chunks past the registers, two in flight
+    // the chunks past the registers, claimed one at a time, two in flight
     {
-        for (; c < C; c += 2 * kHoldWaves) {
-            const int cb = c + kHoldWaves, cn = c + 2 * kHoldWaves;
+        int cb = hold_claim(next);
+        while (c < C) {
             bt.load(trow, cb < C ? (long)cb * kLanes * N : z0, a.V);
             bd.load(drow, cb < C ? (long)cb * kLanes * N : z0, a.V);
             hold_stats<N>(a, x, c, at, ad, stt);
@@ -1726,16 +1739,19 @@ __device__ __forceinline__ void hold_pair(const VerifyArgs &a, const Item &x, fl
                 slot_put(slots, c - nreg, 1, ad);
             }
             if (cb >= C) break;
-            at.load(trow, cn < C ? (long)cn * kLanes * N : z0, a.V);
-            ad.load(drow, cn < C ? (long)cn * kLanes * N : z0, a.V);
+            c = hold_claim(next);
+            at.load(trow, c < C ? (long)c * kLanes * N : z0, a.V);
+            ad.load(drow, c < C ? (long)c * kLanes * N : z0, a.V);
             hold_stats<N>(a, x, cb, bt, bd, stt);
             if (cb < nlds) {
                 slot_put(slots, cb - nreg, 0, bt);
                 slot_put(slots, cb - nreg, 1, bd);
             }
+            cb = hold_claim(next);
         }
     }
     __syncthreads();
+    if (threadIdx.x == 0) *next = nreg + kHoldWaves;  // for the next pair's stream
     // ---- the fold, in every wave (fixed order: the same bits everywhere) ----
     OnlineZ ot, od;
 #pragma unroll
@@ -1898,6 +1914,8 @@ template <int N, int EPV>
 __global__ void __launch_bounds__(kHoldBlock, 1) hold_kernel(VerifyArgs a, int kl) {
     a.tag = first_launch_tag(a.ctl);
     extern __shared__ uint32_t lds[];
+    __shared__ int next;  // the held pairs' stream counter
+    if (threadIdx.x == 0) next = kHoldWaves * kHoldReg + kHoldWaves;
     const HoldTable t = build_hold_table(a, lds);
     const size_t tw = 3 * (size_t)a.R + (size_t)t.held + t.filler;
     float *stt = (float *)(lds + ((tw + 3) & ~(size_t)3));
@@ -1913,7 +1931,7 @@ __global__ void __launch_bounds__(kHoldBlock, 1) hold_kernel(VerifyArgs a, int k
         x.s = __uint_as_float(t.req[3 * x.r + 1]);
         x.l = (int)t.req[3 * x.r + 2];
         x.u = x.r * a.UG + x.i;
-        hold_pair<N, EPV>(a, x, stt, slots, kl);
+        hold_pair<N, EPV>(a, x, stt, slots, kl, &next);
     }
     // filler rows: pairs in the last round P' = held - (rounds - 1) G; the
     // workgroups past P' (all, when P' = G) share them evenly
