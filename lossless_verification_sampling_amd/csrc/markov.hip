@@ -27,6 +27,8 @@
 //    finishes the draw with a wave scan.
 #include <math.h>
 
+#include <atomic>
+
 #include "common.h"
 
 namespace sv {
@@ -35,6 +37,7 @@ constexpr int kMkRank = 256;        // rank of W1 W2 (the pages' default r)
 constexpr int kMkTile = 64;         // logits per tile (one workgroup each)
 constexpr int kMkRows = 64;         // requests per MFMA row block (4 waves x 16)
 constexpr int kMkLdsStride = kMkRank + 8;  // bf16 per LDS row (padding vs bank conflicts)
+constexpr int kMkPipeTiles = 8;     // tiles per workgroup of the persistent logits launch
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
@@ -51,6 +54,7 @@ struct MarkovArgs {
     int vec;                 // U rows and logit rows allow 4-wide loads and stores
     const uint16_t *bsplit;  // RNN head: [3][R][rank] bf16 parts of the state (B rows)
     int tile0;               // first tile of the launch
+    int tile1;               // end of the launch's tiles (persistent launch)
     int32_t *out_tok;        // [R][gamma]
     float *out_logits;       // [R][gamma][V]
     float2 *tstats;          // [R][ntiles]: (max, exp-sum) or (max, argmax bits)
@@ -168,6 +172,81 @@ __device__ __forceinline__ void mk_unpack_u(const float4 &w, float (&o)[4]) {
     o[0] = w.x; o[1] = w.y; o[2] = w.z; o[3] = w.w;
 }
 
+// Epilogue of one (request, tile) for the lanes of request r (temperature
+// T): acc[vb][j] = b[v][r] for v = v0 + vb * 16 + kgrp * 4 + j.  The logits
+// U + b are written out, and the tile's statistics of the request (max and
+// the sum of 2^((l - max) s), or the argmax at T = 0) reduce over the four
+// lanes that share it.  ALL: every lane's request exists (rok), and the four
+// lanes of a request all store its statistics (the same value), so that no
+// store sits behind a branch.
+template <typename TU, bool FULL, bool ALL = false>
+__device__ __forceinline__ void mk_epilogue(const MarkovArgs &a, int r, bool rok, float T,
+                                            int tile, long v0, int kgrp,
+                                            const f32x4_t (&acc)[kMkTile / 16],
+                                            const MkLane<TU> &ln) {
+    const int V = a.V;
+    const bool greedy = (T == 0.0f);
+    const float s = (!greedy && mk_temperature_ok(T)) ? (float)(kLog2e / (double)T) : 1.0f;
+    float *lrow = a.out_logits + ((long)(rok ? r : 0) * a.gamma + (a.k - 1)) * V;
+    float lv[kMkTile / 16][4];
+    float m = -__builtin_inff();
+    int arg = 0x7fffffff, nanseen = 0;
+#pragma unroll
+    for (int vb = 0; vb < kMkTile / 16; ++vb) {
+        const long v = v0 + vb * 16 + kgrp * 4;
+        float u4[4];
+        mk_unpack_u(ln.u[vb], u4);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float l = (rok && v + j < V) ? u4[j] + acc[vb][j] : -__builtin_inff();
+            lv[vb][j] = l;
+            if (l != l) nanseen = 1;
+            if (l > m) { m = l; arg = (int)(v + j); }
+        }
+        if (ALL || rok) {
+            if constexpr (FULL) {
+                *reinterpret_cast<float4 *>(lrow + v) =
+                    make_float4(lv[vb][0], lv[vb][1], lv[vb][2], lv[vb][3]);
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    if (v + j < V) lrow[v + j] = lv[vb][j];
+            }
+        }
+    }
+    // reduce over the 4 lanes sharing this request (lane bits 4..5)
+#pragma unroll
+    for (int o = 16; o < 64; o <<= 1) {
+        const float m2 = __shfl_xor(m, o, 64);
+        const int a2 = __shfl_xor(arg, o, 64);
+        argmax_combine(m, arg, m2, a2);
+        nanseen |= __shfl_xor(nanseen, o, 64);
+    }
+    float out1;
+    if (greedy) {
+        if (nanseen) m = __builtin_nanf("");
+        out1 = __int_as_float(arg);
+    } else {
+        float e = 0.0f;
+        if (m > -__builtin_inff()) {
+#pragma unroll
+            for (int vb = 0; vb < kMkTile / 16; ++vb)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) e += __builtin_amdgcn_exp2f((lv[vb][j] - m) * s);
+        } else {
+#pragma unroll
+            for (int vb = 0; vb < kMkTile / 16; ++vb)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    if (lv[vb][j] != lv[vb][j]) e = lv[vb][j];
+        }
+#pragma unroll
+        for (int o = 16; o < 64; o <<= 1) e += __shfl_xor(e, o, 64);
+        out1 = e;
+    }
+    if (ALL || (rok && kgrp == 0)) a.tstats[(size_t)r * a.ntiles + tile] = make_float2(m, out1);
+}
+
 // FULL: every tile of the launch lies inside the row, V is a multiple of 8
 // (16-byte aligned W2 rows) and the U and logit rows allow 4-wide accesses,
 // so every load and store is a vector; otherwise (odd V, the ragged last
@@ -258,67 +337,99 @@ __global__ void __launch_bounds__(kBlock, 4) markov_logits_kernel(MarkovArgs a) 
             }
         }
         // ---- epilogue: acc[vb][j] = b[v][r], v = v0 + vb * 16 + kgrp * 4 + j
-        const float T = rok ? a.temp[r] : 1.0f;
-        const bool greedy = (T == 0.0f);
-        const float s = (!greedy && mk_temperature_ok(T)) ? (float)(kLog2e / (double)T) : 1.0f;
-        float *lrow = a.out_logits + ((long)(rok ? r : 0) * a.gamma + (a.k - 1)) * V;
-        float lv[kMkTile / 16][4];
-        float m = -__builtin_inff();
-        int arg = 0x7fffffff, nanseen = 0;
+        mk_epilogue<TU, FULL>(a, r, rok, rok ? a.temp[r] : 1.0f, tile, v0, kgrp, acc, ln);
+    }
+}
+
+// The common case of markov_logits_kernel (whole tiles in 16-byte aligned
+// rows, exactly 64 requests, the Markov head) as a persistent launch:
+// workgroup g takes tiles tile0 + g, + G, ... < tile1.  The W2 loads run
+// two tiles ahead of the product and epilogue and the U loads one (two
+// register sets taken in turn), the tile's W2 block alternates between two shared-memory
+// buffers (one barrier per tile), and the gathered W1 rows are loaded once.
+// Every load and store is unconditional (a tile past the end reads the last
+// one again and is not used), so the compiler's wait counts stay exact and a
+// tile's stores never hold up the next tile's loads.  Same arithmetic, in
+// the same order, as markov_logits_kernel.
+template <typename TU>
+__global__ void __launch_bounds__(kBlock, 2) markov_logits_pipe_kernel(MarkovArgs a) {
+    __shared__ __attribute__((aligned(16))) uint16_t w2t[2][kMkTile * kMkLdsStride];
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
+    const int col = lane & 15, kgrp = lane >> 4;
+    const int k0 = (tid >> 3) * 8, n0 = (tid & 7) * 8;
+    const int r = wave * 16 + col;
+    const long V = a.V;
+    const int G = (int)gridDim.x;
+    const int tend = a.tile1;
+    int tile = a.tile0 + (int)blockIdx.x;
+    auto tile_v0 = [&](int t) { return (long)(t < tend ? t : tend - 1) * kMkTile; };
+    auto fetch_w2 = [&](int t, uint4 (&rw)[8]) {
+        const long v0 = tile_v0(t);
 #pragma unroll
-        for (int vb = 0; vb < kMkTile / 16; ++vb) {
-            const long v = v0 + vb * 16 + kgrp * 4;
-            float u4[4];
-            mk_unpack_u(ln.u[vb], u4);
+        for (int j = 0; j < 8; ++j)
+            rw[j] = *reinterpret_cast<const uint4 *>(a.W2 + (long)(k0 + j) * V + v0 + n0);
+    };
+    auto stage = [&](int buf, const uint4 (&rw)[8]) {
+        uint4 cw[8];
+        transpose8x8(rw, cw);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const float l = (rok && v + j < V) ? u4[j] + acc[vb][j] : -__builtin_inff();
-                lv[vb][j] = l;
-                if (l != l) nanseen = 1;
-                if (l > m) { m = l; arg = (int)(v + j); }
-            }
-            if (rok) {
-                if constexpr (FULL) {
-                    *reinterpret_cast<float4 *>(lrow + v) =
-                        make_float4(lv[vb][0], lv[vb][1], lv[vb][2], lv[vb][3]);
-                } else {
+        for (int i = 0; i < 8; ++i)
+            *reinterpret_cast<uint4 *>(&w2t[buf][(n0 + i) * kMkLdsStride + k0]) = cw[i];
+    };
+    // the request's operands first (their waits then leave the tile loads
+    // in flight): the gathered W1 row and the temperature
+    const int xprev = mk_prev_token(a, r);
+    const float T = a.temp[r];
+    uint4 bop[kMkRank / 32];
+    mk_load_b<1>(a, xprev, r, 0, kgrp, bop);
+    auto product = [&](int buf, int t, const MkLane<TU> &u) {
+        f32x4_t acc[kMkTile / 16];
 #pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        if (v + j < V) lrow[v + j] = lv[vb][j];
-                }
+        for (int vb = 0; vb < kMkTile / 16; ++vb) acc[vb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < kMkRank / 32; ++ks) {
+            const bf16x8_t bv = __builtin_bit_cast(bf16x8_t, bop[ks]);
+#pragma unroll
+            for (int vb = 0; vb < kMkTile / 16; ++vb) {
+                const uint4 araw = *reinterpret_cast<const uint4 *>(
+                    &w2t[buf][(vb * 16 + col) * kMkLdsStride + ks * 32 + kgrp * 8]);
+                acc[vb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    __builtin_bit_cast(bf16x8_t, araw), bv, acc[vb], 0, 0, 0);
             }
         }
-        // reduce over the 4 lanes sharing this request (lane bits 4..5)
+        mk_epilogue<TU, true, true>(a, r, true, T, t, (long)t * kMkTile, kgrp, acc, u);
+    };
+    // W2 two tiles ahead, U one tile ahead (each register set is reloaded
+    // only after its last use, so no register copies wait on loads in
+    // flight); buffer 0 holds the tiles of set a, buffer 1 those of set b,
+    // and a buffer is written again only after the barrier that follows its
+    // last reader
+    uint4 ra[8], rb[8];
+    MkLane<TU> ua, ub;
+    fetch_w2(tile, ra);
+    mk_load_u<TU, true>(a, r, tile_v0(tile), kgrp, ua);
+    fetch_w2(tile + G, rb);
+    mk_load_u<TU, true>(a, r, tile_v0(tile + G), kgrp, ub);
+    // unrolled (at most kMkPipeTiles tiles per workgroup), so that no loop
+    // header merges the wait counts of the loads in flight
 #pragma unroll
-        for (int o = 16; o < 64; o <<= 1) {
-            const float m2 = __shfl_xor(m, o, 64);
-            const int a2 = __shfl_xor(arg, o, 64);
-            argmax_combine(m, arg, m2, a2);
-            nanseen |= __shfl_xor(nanseen, o, 64);
-        }
-        float out1;
-        if (greedy) {
-            if (nanseen) m = __builtin_nanf("");
-            out1 = __int_as_float(arg);
+    for (int it = 0; it < kMkPipeTiles; ++it) {
+        if (tile >= tend) break;
+        if (it & 1) {
+            stage(1, rb);
+            __syncthreads();
+            fetch_w2(tile + 2 * G, rb);
+            product(1, tile, ub);
+            mk_load_u<TU, true>(a, r, tile_v0(tile + 2 * G), kgrp, ub);
         } else {
-            float e = 0.0f;
-            if (m > -__builtin_inff()) {
-#pragma unroll
-                for (int vb = 0; vb < kMkTile / 16; ++vb)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) e += __builtin_amdgcn_exp2f((lv[vb][j] - m) * s);
-            } else {
-#pragma unroll
-                for (int vb = 0; vb < kMkTile / 16; ++vb)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        if (lv[vb][j] != lv[vb][j]) e = lv[vb][j];
-            }
-#pragma unroll
-            for (int o = 16; o < 64; o <<= 1) e += __shfl_xor(e, o, 64);
-            out1 = e;
+            stage(0, ra);
+            __syncthreads();
+            fetch_w2(tile + 2 * G, ra);
+            product(0, tile, ua);
+            mk_load_u<TU, true>(a, r, tile_v0(tile + 2 * G), kgrp, ua);
         }
-        if (rok && kgrp == 0) a.tstats[(size_t)r * a.ntiles + tile] = make_float2(m, out1);
+        tile += G;
     }
 }
 
@@ -666,6 +777,20 @@ namespace {
 
 size_t mk_round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// Compute units of the current device, cached per device (0 if unknown).
+constexpr int kMkMaxDevices = 64;
+std::atomic<int> g_mk_cus[kMkMaxDevices];
+int mk_device_cus() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMkMaxDevices) return 0;
+    int c = g_mk_cus[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+    if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return 0;
+    g_mk_cus[dev].store(c, std::memory_order_relaxed);
+    return c;
+}
+
 struct MkPlan {
     int ntiles;
     size_t off_stats, off_bad, bytes;
@@ -687,7 +812,18 @@ void mk_launch_step(MarkovArgs a, const MkPlan &p, bool bf, hipStream_t st) {
     // last tile (or every tile of an odd V or unaligned rows) the guarded one
     const int nfull = (V % 8 == 0 && a.vec) ? V / kMkTile : 0;
     const int tp = (p.ntiles + kBlock - 1) / kBlock;  // tiles per thread of the sampling block
-    if (nfull > 0) {
+    const int cus = NSPLIT == 1 && R == kMkRows && nfull > 0 ? mk_device_cus() : 0;
+    const int g = nfull < 2 * cus ? nfull : 2 * cus;
+    if (g > 0 && (nfull + g - 1) / g <= kMkPipeTiles) {
+        // persistent: two workgroups per CU stream the whole tiles
+        a.tile0 = 0;
+        a.tile1 = nfull;
+        if (bf)
+            hipLaunchKernelGGL(markov_logits_pipe_kernel<uint16_t>, dim3(g), dim3(kBlock), 0, st,
+                               a);
+        else
+            hipLaunchKernelGGL(markov_logits_pipe_kernel<float>, dim3(g), dim3(kBlock), 0, st, a);
+    } else if (nfull > 0) {
         a.tile0 = 0;
         if (bf)
             hipLaunchKernelGGL((markov_logits_kernel<uint16_t, true, NSPLIT>), dim3(nfull),
