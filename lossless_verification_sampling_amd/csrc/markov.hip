@@ -342,33 +342,45 @@ __global__ void __launch_bounds__(kBlock, 4) markov_logits_kernel(MarkovArgs a) 
 }
 
 // The common case of markov_logits_kernel (whole tiles in 16-byte aligned
-// rows, exactly 64 requests, the Markov head) as a persistent launch:
-// workgroup g takes tiles tile0 + g, + G, ... < tile1.  The W2 loads run
-// two tiles ahead of the product and epilogue and the U loads one (two
-// register sets taken in turn), the tile's W2 block alternates between two shared-memory
-// buffers (one barrier per tile), and the gathered W1 rows are loaded once.
-// Every load and store is unconditional (a tile past the end reads the last
-// one again and is not used), so the compiler's wait counts stay exact and a
-// tile's stores never hold up the next tile's loads.  Same arithmetic, in
-// the same order, as markov_logits_kernel.
-template <typename TU>
-__global__ void __launch_bounds__(kBlock, 2) markov_logits_pipe_kernel(MarkovArgs a) {
-    __shared__ __attribute__((aligned(16))) uint16_t w2t[2][kMkTile * kMkLdsStride];
+// rows, exactly 64 requests, the Markov head) as a persistent launch over
+// wide tiles of 64 H ids (H 64-id tiles side by side, 256 H threads; wave w
+// takes requests 16 (w % 4) .. + 15 and the 64-id part w / 4): workgroup g
+// takes wide tiles tile0 + g, + G, ... < tile1 (in units of 64 H ids).  The
+// W2 loads run two tiles ahead of the product and epilogue and the U loads
+// one (two register sets taken in turn, each reloaded only after its last
+// use), the tile's W2 block alternates between two shared-memory buffers
+// (one barrier per tile), and the gathered W1 rows are loaded once.  Every
+// load and store is unconditional (a tile past the end reads the last one
+// again and is not used) and the tile loop is unrolled, so that the
+// compiler's wait counts stay exact and a tile's stores never hold up the
+// next tiles' loads.  Wider tiles read W2 and U and write the logits in
+// longer row pieces (128 H bytes of W2 and U, 256 H of logits).  Same
+// arithmetic, in the same order, as markov_logits_kernel; the statistics
+// stay per 64-id tile.
+template <typename TU, int H>
+__global__ void __launch_bounds__(kBlock * H, 2 / H) markov_logits_pipe_kernel(MarkovArgs a) {
+    extern __shared__ __attribute__((aligned(16))) uint16_t mk_dyn[];
+    constexpr int TW = kMkTile * H;  // ids per wide tile
+    uint16_t *const w2t[2] = {mk_dyn, mk_dyn + TW * kMkLdsStride};
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
     const int col = lane & 15, kgrp = lane >> 4;
-    const int k0 = (tid >> 3) * 8, n0 = (tid & 7) * 8;
-    const int r = wave * 16 + col;
+    const int part = wave >> 2;                    // 64-id part of the wide tile
+    const int k0 = (tid / (TW / 8)) * 8, n0 = (tid % (TW / 8)) * 8;
+    const int r = (wave & 3) * 16 + col;
     const long V = a.V;
     const int G = (int)gridDim.x;
     const int tend = a.tile1;
     int tile = a.tile0 + (int)blockIdx.x;
-    auto tile_v0 = [&](int t) { return (long)(t < tend ? t : tend - 1) * kMkTile; };
+    auto tile_v0 = [&](int t) { return (long)(t < tend ? t : tend - 1) * TW; };
     auto fetch_w2 = [&](int t, uint4 (&rw)[8]) {
         const long v0 = tile_v0(t);
 #pragma unroll
         for (int j = 0; j < 8; ++j)
             rw[j] = *reinterpret_cast<const uint4 *>(a.W2 + (long)(k0 + j) * V + v0 + n0);
+    };
+    auto fetch_u = [&](int t, MkLane<TU> &u) {
+        mk_load_u<TU, true>(a, r, tile_v0(t) + part * kMkTile, kgrp, u);
     };
     auto stage = [&](int buf, const uint4 (&rw)[8]) {
         uint4 cw[8];
@@ -393,26 +405,26 @@ __global__ void __launch_bounds__(kBlock, 2) markov_logits_pipe_kernel(MarkovArg
 #pragma unroll
             for (int vb = 0; vb < kMkTile / 16; ++vb) {
                 const uint4 araw = *reinterpret_cast<const uint4 *>(
-                    &w2t[buf][(vb * 16 + col) * kMkLdsStride + ks * 32 + kgrp * 8]);
+                    &w2t[buf][(part * kMkTile + vb * 16 + col) * kMkLdsStride + ks * 32 +
+                              kgrp * 8]);
                 acc[vb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                     __builtin_bit_cast(bf16x8_t, araw), bv, acc[vb], 0, 0, 0);
             }
         }
-        mk_epilogue<TU, true, true>(a, r, true, T, t, (long)t * kMkTile, kgrp, acc, u);
+        mk_epilogue<TU, true, true>(a, r, true, T, t * H + part,
+                                    (long)t * TW + part * kMkTile, kgrp, acc, u);
     };
-    // W2 two tiles ahead, U one tile ahead (each register set is reloaded
-    // only after its last use, so no register copies wait on loads in
-    // flight); buffer 0 holds the tiles of set a, buffer 1 those of set b,
-    // and a buffer is written again only after the barrier that follows its
-    // last reader
     uint4 ra[8], rb[8];
     MkLane<TU> ua, ub;
     fetch_w2(tile, ra);
-    mk_load_u<TU, true>(a, r, tile_v0(tile), kgrp, ua);
+    fetch_u(tile, ua);
+    // keeps the second tile's loads behind the first's, so that the first
+    // tile's waits leave them in flight
+    asm volatile("" ::: "memory");
     fetch_w2(tile + G, rb);
-    mk_load_u<TU, true>(a, r, tile_v0(tile + G), kgrp, ub);
-    // unrolled (at most kMkPipeTiles tiles per workgroup), so that no loop
-    // header merges the wait counts of the loads in flight
+    fetch_u(tile + G, ub);
+    // buffer 0 holds the tiles of set a, buffer 1 those of set b; a buffer
+    // is written again only after the barrier that follows its last reader
 #pragma unroll
     for (int it = 0; it < kMkPipeTiles; ++it) {
         if (tile >= tend) break;
@@ -421,13 +433,13 @@ __global__ void __launch_bounds__(kBlock, 2) markov_logits_pipe_kernel(MarkovArg
             __syncthreads();
             fetch_w2(tile + 2 * G, rb);
             product(1, tile, ub);
-            mk_load_u<TU, true>(a, r, tile_v0(tile + 2 * G), kgrp, ub);
+            fetch_u(tile + 2 * G, ub);
         } else {
             stage(0, ra);
             __syncthreads();
             fetch_w2(tile + 2 * G, ra);
             product(0, tile, ua);
-            mk_load_u<TU, true>(a, r, tile_v0(tile + 2 * G), kgrp, ua);
+            fetch_u(tile + 2 * G, ua);
         }
         tile += G;
     }
@@ -812,17 +824,48 @@ void mk_launch_step(MarkovArgs a, const MkPlan &p, bool bf, hipStream_t st) {
     // last tile (or every tile of an odd V or unaligned rows) the guarded one
     const int nfull = (V % 8 == 0 && a.vec) ? V / kMkTile : 0;
     const int tp = (p.ntiles + kBlock - 1) / kBlock;  // tiles per thread of the sampling block
-    const int cus = NSPLIT == 1 && R == kMkRows && nfull > 0 ? mk_device_cus() : 0;
-    const int g = nfull < 2 * cus ? nfull : 2 * cus;
-    if (g > 0 && (nfull + g - 1) / g <= kMkPipeTiles) {
-        // persistent: two workgroups per CU stream the whole tiles
-        a.tile0 = 0;
-        a.tile1 = nfull;
-        if (bf)
-            hipLaunchKernelGGL(markov_logits_pipe_kernel<uint16_t>, dim3(g), dim3(kBlock), 0, st,
-                               a);
-        else
-            hipLaunchKernelGGL(markov_logits_pipe_kernel<float>, dim3(g), dim3(kBlock), 0, st, a);
+    // persistent: wide tiles of 128 ids, one workgroup of 512 threads per CU
+    // (the odd 64-id tile, if any, goes to the per-tile launch below)
+    constexpr int kH = 2;
+    const int cus = NSPLIT == 1 && R == kMkRows && nfull >= kH ? mk_device_cus() : 0;
+    const int nwide = nfull / kH;
+    const int g = nwide < cus ? nwide : cus;
+    int done = 0;
+    if (g > 0 && (nwide + g - 1) / g <= kMkPipeTiles) {
+        const size_t lds = 2 * sizeof(uint16_t) * kMkTile * kH * kMkLdsStride;
+        static std::atomic<int> attr{0};
+        bool ok = attr.load(std::memory_order_relaxed) != 0;
+        if (!ok) {
+            ok = hipFuncSetAttribute(
+                     reinterpret_cast<const void *>(&markov_logits_pipe_kernel<uint16_t, kH>),
+                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) == hipSuccess &&
+                 hipFuncSetAttribute(
+                     reinterpret_cast<const void *>(&markov_logits_pipe_kernel<float, kH>),
+                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) == hipSuccess;
+            if (ok) attr.store(1, std::memory_order_relaxed);
+        }
+        if (ok) {
+            a.tile0 = 0;
+            a.tile1 = nwide;
+            if (bf)
+                hipLaunchKernelGGL((markov_logits_pipe_kernel<uint16_t, kH>), dim3(g),
+                                   dim3(kBlock * kH), lds, st, a);
+            else
+                hipLaunchKernelGGL((markov_logits_pipe_kernel<float, kH>), dim3(g),
+                                   dim3(kBlock * kH), lds, st, a);
+            done = nwide * kH;
+        }
+    }
+    if (done > 0) {
+        if (done < nfull) {
+            a.tile0 = done;
+            if (bf)
+                hipLaunchKernelGGL((markov_logits_kernel<uint16_t, true, NSPLIT>),
+                                   dim3(nfull - done), dim3(kBlock), 0, st, a);
+            else
+                hipLaunchKernelGGL((markov_logits_kernel<float, true, NSPLIT>),
+                                   dim3(nfull - done), dim3(kBlock), 0, st, a);
+        }
     } else if (nfull > 0) {
         a.tile0 = 0;
         if (bf)
