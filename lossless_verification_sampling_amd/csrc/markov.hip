@@ -26,6 +26,7 @@
 //    token id), and its first wave re-reads that tile's 64 logits and
 //    finishes the draw with a wave scan.
 #include <math.h>
+#include <stdlib.h>
 
 #include <atomic>
 
@@ -836,8 +837,12 @@ void mk_launch_step(MarkovArgs a, const MkPlan &p, bool bf, hipStream_t st) {
     const int tp = (p.ntiles + kBlock - 1) / kBlock;  // tiles per thread of the sampling block
     // persistent: wide tiles of 128 ids, one workgroup of 512 threads per CU
     // (the odd 64-id tile, if any, goes to the per-tile launch below)
+    // SPECMARKOV_TILES=1 in the environment keeps the per-tile launches (for
+    // comparisons)
     constexpr int kH = 2;
-    const int cus = NSPLIT == 1 && R == kMkRows && nfull >= kH ? mk_device_cus() : 0;
+    const char *pt = getenv("SPECMARKOV_TILES");
+    const bool per_tile = pt && pt[0] == '1';
+    const int cus = NSPLIT == 1 && R == kMkRows && nfull >= kH && !per_tile ? mk_device_cus() : 0;
     const int nwide = nfull / kH;
     const int g = nwide < cus ? nwide : cus;
     int done = 0;

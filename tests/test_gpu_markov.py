@@ -101,6 +101,32 @@ def test_markov_unaligned_rows(sv, dev, u_f32):
     compare_markov(mk, tok.cpu().numpy(), lg.cpu().numpy(), ref)
 
 
+@pytest.mark.parametrize("gamma,V,T", [
+    (3, 129280, 1.0),       # 1010 wide tiles: four per workgroup
+    (2, 64 * 601, 0.8),     # an odd 64-id tile left to the per-tile launch
+    (2, 64 * 601 + 24, 1.0),  # and a ragged last tile (guarded launch)
+    (2, 8192, 0.0),         # greedy; fewer wide tiles than compute units
+])
+def test_markov_persistent_and_per_tile_identical(sv, dev, gamma, V, T, monkeypatch):
+    """At 64 requests the whole tiles run in the persistent logits launch
+    (128-id tiles, loads two tiles ahead); SPECMARKOV_TILES=1 runs the
+    per-tile launches instead.  Tokens and fp32 logits must be bit-identical,
+    and match the oracle."""
+    R = 64
+    print(f"[markov persistent] R={R} gamma={gamma} V={V} T={T}", flush=True)
+    mk = workloads.dspark_markov(seed=V + gamma, R=R, gamma=gamma, V=V, temperature=T)
+    tok, lg = run_markov(sv, mk, dev)
+    monkeypatch.setenv("SPECMARKOV_TILES", "1")
+    tok1, lg1 = run_markov(sv, mk, dev)
+    monkeypatch.delenv("SPECMARKOV_TILES")
+    assert np.array_equal(tok, tok1)
+    assert np.array_equal(lg.view(np.uint32), lg1.view(np.uint32))
+    rows = list(range(0, R, 8))   # the oracle on a sample of the requests
+    ref = oracle.markov_draft(mk.U[rows], mk.W1, mk.W2, mk.anchor[rows], mk.temperature[rows],
+                              mk.u_draft[rows])
+    compare_markov(mk, tok, lg, ref, rows=rows)
+
+
 def test_markov_invalid(sv, dev):
     mk = workloads.dspark_markov(seed=3, R=4, gamma=3, V=777)
     mk.anchor[1] = 777            # out of range
