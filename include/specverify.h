@@ -262,6 +262,11 @@ size_t spec_markov_workspace_bytes(int R, int gamma, int V, int rank);
  *   out_draft_logits [R][gamma][V] fp32
  * Sizes: R >= 0, gamma >= 0, 1 <= V <= SPEC_MAX_VOCAB, rank == 256.
  * A misaligned W1 or W2 returns SPEC_EINVAL.
+ * Per step: one logits launch over 64-id tiles (a persistent launch over
+ * 128-id tiles where R == 64 and the rows allow 16-byte accesses), then one
+ * draw launch.  Both logits launches produce the same bits;
+ * SPECMARKOV_TILES=1 in the environment selects the per-tile one for every
+ * call (for comparisons).
  */
 int spec_markov_draft_sample(const void *U, int u_dtype,
                              const void *W1, const void *W2, int w_dtype,
