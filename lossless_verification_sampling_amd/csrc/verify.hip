@@ -152,6 +152,17 @@ __device__ __forceinline__ void st_word(uint64_t *p, uint32_t tag, uint32_t payl
                        __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Words w0..w(n-1) at p[0..n-1] (n <= 4) with no branch: every lane stores,
+// lanes n.. the last word again (the same value to the same address), so
+// that the compiler's count of memory operations in flight stays exact for
+// the waits on loads issued before it.
+__device__ __forceinline__ void publish_all(uint64_t *p, uint32_t tag, int n, uint32_t w0,
+                                            uint32_t w1, uint32_t w2, uint32_t w3) {
+    const int k = min(lane_id(), n - 1);
+    const uint32_t w = k == 0 ? w0 : k == 1 ? w1 : k == 2 ? w2 : w3;
+    st_word(p + k, tag, w);
+}
+
 // Lanes 0..n-1 store words w[lane] at p[lane] (n <= 4).
 __device__ __forceinline__ void publish_n(uint64_t *p, uint32_t tag, int n, uint32_t w0,
                                           uint32_t w1, uint32_t w2, uint32_t w3) {
@@ -1647,7 +1658,7 @@ __device__ __forceinline__ void hold_stats(const VerifyArgs &a, const Item &x, i
         stt[c * 4 + 2] = mud;
         stt[c * 4 + 3] = Sd;
     }
-    publish_n(a.st1 + ((size_t)x.u * a.C + c) * 4, a.tag, 4, __float_as_uint(mut),
+    publish_all(a.st1 + ((size_t)x.u * a.C + c) * 4, a.tag, 4, __float_as_uint(mut),
               __float_as_uint(St), __float_as_uint(mud), __float_as_uint(Sd));
 }
 
@@ -1665,7 +1676,7 @@ __device__ __forceinline__ void hold_tv(const VerifyArgs &a, const Item &x, int 
     q.unit = rlf(ps.unit, m);
     double cmin, cres;
     tv_sums<N>(rt, rd, x.s, rlf(mut, m), rlf(St, m), q, &cmin, &cres);
-    publish_n(a.st2 + ((size_t)x.u * a.C + c) * 2, a.tag, 2, __float_as_uint((float)cmin),
+    publish_all(a.st2 + ((size_t)x.u * a.C + c) * 2, a.tag, 2, __float_as_uint((float)cmin),
               __float_as_uint((float)cres), 0u, 0u);
 }
 
