@@ -1409,7 +1409,7 @@ __device__ __forceinline__ void stats_item(const VerifyArgs &a, const Item &x, R
             w3 = __float_as_uint(S);
         }
     }
-    publish_n(a.st1 + ((size_t)x.u * a.C + x.c) * 4, a.tag, 4, w0, w1, w2, w3);
+    publish_all(a.st1 + ((size_t)x.u * a.C + x.c) * 4, a.tag, 4, w0, w1, w2, w3);
 }
 
 // Kernel 1: every needed row streamed once from HBM, one item in flight per
@@ -1463,8 +1463,8 @@ __device__ __forceinline__ void tv_item(const VerifyArgs &a, const Item &x, RT &
     ps.unit = __uint_as_float(rl(w8, 6));
     tv_sums<N>(rt, rd, x.s, __uint_as_float(rl(w8, 0)), __uint_as_float(rl(w8, 1)), ps, &cmin,
                &cres);
-    publish_n(a.st2 + ((size_t)x.u * a.C + x.c) * 2, a.tag, 2, __float_as_uint((float)cmin),
-              __float_as_uint((float)cres), 0u, 0u);
+    publish_all(a.st2 + ((size_t)x.u * a.C + x.c) * 2, a.tag, 2, __float_as_uint((float)cmin),
+                __float_as_uint((float)cres), 0u, 0u);
 }
 
 // Issues the loads of pair item x: its chunk of both rows, and (lanes 0..6)
