@@ -44,13 +44,16 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 
 // Offset (bf16 elements) of the 16-byte piece k = 8 u .. 8 u + 7 of row n of
 // the transposed W2 tile in LDS.  The row stride of 264 elements (33 pieces)
-// spreads the consecutive rows an MFMA operand read touches over the banks;
-// the XOR of the piece index with bits 3..5 of the row does the same for the
-// staging writes, whose lanes take rows 8 apart (without it each write was
-// an 8-way bank conflict: SQ_LDS_BANK_CONFLICT fell from 4.65e6 to 1.03e6
-// per logits launch).
+// spreads the consecutive rows an MFMA operand read touches over the banks.
+// SW: the piece index is XOR-ed with bits 3..5 of the row, which does the
+// same for the persistent launch's staging writes (16 lanes per pass, rows 8
+// apart: without it each write was an 8-way bank conflict, and
+// SQ_LDS_BANK_CONFLICT fell from 4.65e6 to 1.03e6 per logits launch).  The
+// per-tile launch keeps the plain map: with it the RNN head's three-pass
+// tiles ran 459 us per call against 434.
+template <bool SW>
 __device__ __forceinline__ int w2t_off(int n, int u) {
-    return n * kMkLdsStride + 8 * (u ^ ((n >> 3) & 7));
+    return n * kMkLdsStride + 8 * (SW ? (u ^ ((n >> 3) & 7)) : u);
 }
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
@@ -310,7 +313,7 @@ __global__ void __launch_bounds__(kBlock, 4) markov_logits_kernel(MarkovArgs a) 
         transpose8x8(rw, cw);
 #pragma unroll
         for (int i = 0; i < 8; ++i)
-            *reinterpret_cast<uint4 *>(&w2t[w2t_off(n0 + i, k0 / 8)]) = cw[i];
+            *reinterpret_cast<uint4 *>(&w2t[w2t_off<false>(n0 + i, k0 / 8)]) = cw[i];
     }
     __syncthreads();
 
@@ -342,7 +345,7 @@ __global__ void __launch_bounds__(kBlock, 4) markov_logits_kernel(MarkovArgs a) 
 #pragma unroll
                 for (int vb = 0; vb < kMkTile / 16; ++vb) {
                     const uint4 araw = *reinterpret_cast<const uint4 *>(
-                        &w2t[w2t_off(vb * 16 + col, ks * 4 + kgrp)]);
+                        &w2t[w2t_off<false>(vb * 16 + col, ks * 4 + kgrp)]);
                     acc[vb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                         __builtin_bit_cast(bf16x8_t, araw), bv, acc[vb], 0, 0, 0);
                 }
@@ -399,7 +402,7 @@ __global__ void __launch_bounds__(kBlock * H, 2 / H) markov_logits_pipe_kernel(M
         transpose8x8(rw, cw);
 #pragma unroll
         for (int i = 0; i < 8; ++i)
-            *reinterpret_cast<uint4 *>(&w2t[buf][w2t_off(n0 + i, k0 / 8)]) = cw[i];
+            *reinterpret_cast<uint4 *>(&w2t[buf][w2t_off<true>(n0 + i, k0 / 8)]) = cw[i];
     };
     // the request's operands first (their waits then leave the tile loads
     // in flight): the gathered W1 row and the temperature
@@ -417,7 +420,7 @@ __global__ void __launch_bounds__(kBlock * H, 2 / H) markov_logits_pipe_kernel(M
 #pragma unroll
             for (int vb = 0; vb < kMkTile / 16; ++vb) {
                 const uint4 araw = *reinterpret_cast<const uint4 *>(
-                    &w2t[buf][w2t_off(part * kMkTile + vb * 16 + col, ks * 4 + kgrp)]);
+                    &w2t[buf][w2t_off<true>(part * kMkTile + vb * 16 + col, ks * 4 + kgrp)]);
                 acc[vb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                     __builtin_bit_cast(bf16x8_t, araw), bv, acc[vb], 0, 0, 0);
             }
