@@ -176,6 +176,47 @@ __device__ __forceinline__ int wave_min_i(int v) {
     return min(min(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
                min(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
 }
+// Wave inclusive prefix sums in lane order with DPP moves only: shifts by
+// 1, 2, 4 and 8 lanes inside each row of 16 (lanes whose source lies before
+// the row start read 0), then lane 15's sum added to rows 1 and 3 and lane
+// 31's to rows 2 and 3.  No LDS round trip per step, unlike the
+// ds_bpermute shuffles of wave_incl_scan.
+constexpr int kDppRowShr1 = 0x111, kDppRowShr2 = 0x112, kDppRowShr4 = 0x114,
+              kDppRowShr8 = 0x118;
+constexpr int kDppRowBcast15 = 0x142, kDppRowBcast31 = 0x143;
+
+// DPP move in which lanes of rows outside ROW_MASK, and lanes whose source
+// is out of range, read 0.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ int dpp0_i(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, 0xf, true);
+}
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ double dpp0_d(double v) {
+    const long long b = __double_as_longlong(v);
+    const int lo = dpp0_i<CTRL, ROW_MASK>((int)(b & 0xffffffffLL));
+    const int hi = dpp0_i<CTRL, ROW_MASK>((int)(b >> 32));
+    return __longlong_as_double(((long long)hi << 32) | (unsigned)lo);
+}
+__device__ __forceinline__ double wave_incl_scan_dpp(double v) {
+    v += dpp0_d<kDppRowShr1, 0xf>(v);
+    v += dpp0_d<kDppRowShr2, 0xf>(v);
+    v += dpp0_d<kDppRowShr4, 0xf>(v);
+    v += dpp0_d<kDppRowShr8, 0xf>(v);
+    v += dpp0_d<kDppRowBcast15, 0xa>(v);
+    v += dpp0_d<kDppRowBcast31, 0xc>(v);
+    return v;
+}
+__device__ __forceinline__ uint32_t wave_incl_scan_dpp(uint32_t v) {
+    v += (uint32_t)dpp0_i<kDppRowShr1, 0xf>((int)v);
+    v += (uint32_t)dpp0_i<kDppRowShr2, 0xf>((int)v);
+    v += (uint32_t)dpp0_i<kDppRowShr4, 0xf>((int)v);
+    v += (uint32_t)dpp0_i<kDppRowShr8, 0xf>((int)v);
+    v += (uint32_t)dpp0_i<kDppRowBcast15, 0xa>((int)v);
+    v += (uint32_t)dpp0_i<kDppRowBcast31, 0xc>((int)v);
+    return v;
+}
+
 // Wave inclusive prefix sum (fp64) in lane order.
 __device__ __forceinline__ double wave_incl_scan(double v) {
 #pragma unroll

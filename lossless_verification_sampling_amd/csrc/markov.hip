@@ -578,12 +578,7 @@ __global__ void __launch_bounds__(kBlock) markov_sample_kernel(MarkovArgs a) {
                     if (w > 0.0) lastp = t0 + b * NB + i;
                 }
             }
-            double incl = lsum;
-#pragma unroll
-            for (int o = 1; o < 64; o <<= 1) {
-                const double n = __shfl_up(incl, o, 64);
-                if (lane >= o) incl += n;
-            }
+            const double incl = wave_incl_scan_dpp(lsum);
             double excl = __shfl_up(incl, 1, 64);
             if (lane == 0) excl = 0.0;
             const int wlast = wave_max_i(lastp);
@@ -647,7 +642,7 @@ __global__ void __launch_bounds__(kBlock) markov_sample_kernel(MarkovArgs a) {
                                     ? __builtin_amdgcn_exp2f((lrow[min(v, (long)V - 1)] - m) * s)
                                     : 0.0f;
                 const double w3 = (double)e * (double)__builtin_amdgcn_exp2f((m - M) * s);
-                const double inc3 = wave_incl_scan(w3);
+                const double inc3 = wave_incl_scan_dpp(w3);
                 const uint64_t h3 = __ballot(w3 > 0.0 && inc3 > tin);
                 const uint64_t pos3 = __ballot(w3 > 0.0);
                 if (h3)

@@ -309,12 +309,7 @@ __device__ __forceinline__ UnitTable build_unit_table(const VerifyArgs &a, uint3
         own += (uint32_t)table_units(a, ok, T, l, tv_only);
     }
     // block exclusive scan of the per-thread unit counts
-    uint32_t incl = own;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t n = __shfl_up(incl, o, 64);
-        if (lane >= o) incl += n;
-    }
+    const uint32_t incl = wave_incl_scan_dpp(own);
     if (lane == 63) wsum[wave] = incl;
     __syncthreads();
     uint32_t base = 0, total = 0;
@@ -755,17 +750,17 @@ __device__ __forceinline__ int select_chunk(int C, double t, const double (&m)[k
     for (int b = 0; b < kCB; ++b) {
         const int c = b * 64 + lane;
         const double wc = (c < C) ? m[b] : 0.0;
-        const double incl = wave_incl_scan(wc);
+        const double incl = wave_incl_scan_dpp(wc);
         const double excl = run + incl - wc;
         const uint64_t hit = __ballot(c < C && excl + wc > t);
         const uint64_t pos = __ballot(c < C && wc > 0.0);
         if (pos) clast = b * 64 + 63 - __builtin_clzll(pos);
         if (hit) {
             const int k = __builtin_ctzll(hit);
-            *tin = __shfl(t - excl, k, 64);
+            *tin = readlane_d(t - excl, k);
             return b * 64 + k;
         }
-        run += __shfl(incl, 63, 64);
+        run += readlane_d(incl, 63);
     }
     *tin = INFINITY;
     return clast >= 0 ? clast : 0;
@@ -803,7 +798,7 @@ __device__ __forceinline__ int draw_in_chunk_w(long c0, double tin,
             if (w[j][q] > 0.0f) lp = (int)e + q;
         }
         lastpos = max(lastpos, wave_max_i(lp));
-        const double incl = wave_incl_scan(tot);
+        const double incl = wave_incl_scan_dpp(tot);
         const double excl = run + incl - tot;
         const uint64_t hit = __ballot(tot > 0.0 && excl + tot > tin);
         if (hit) {
@@ -820,7 +815,7 @@ __device__ __forceinline__ int draw_in_chunk_w(long c0, double tin,
             }
             return __builtin_amdgcn_readlane(tok, k);
         }
-        run += __shfl(incl, 63, 64);
+        run += readlane_d(incl, 63);
     }
     return lastpos >= 0 ? lastpos : (int)c0;
 }
@@ -1581,12 +1576,7 @@ __device__ __forceinline__ HoldTable build_hold_table(const VerifyArgs &a, uint3
         const int fr = (n - h) + max(0, min(l, n) - h);
         own += (uint32_t)h + ((uint32_t)fr << 16);
     }
-    uint32_t incl = own;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t v = __shfl_up(incl, o, 64);
-        if (lane >= o) incl += v;
-    }
+    const uint32_t incl = wave_incl_scan_dpp(own);
     if (lane == 63) wsum[wave] = incl;
     __syncthreads();
     uint32_t base = 0, total = 0;
