@@ -217,6 +217,25 @@ __device__ __forceinline__ uint32_t wave_incl_scan_dpp(uint32_t v) {
     return v;
 }
 
+// Lane l's value and that of lane l ^ P (P = 16 or 32) with the gfx950
+// permlane swaps: lo = the value of the pair's lane in the lower row (P = 16)
+// or half (P = 32), hi = that of the upper one, the same pair in both lanes,
+// so that both lanes combine the two values in the same order.  No LDS round
+// trip, unlike a ds_bpermute shuffle.
+template <int P>
+__device__ __forceinline__ void lane_pair(uint32_t v, uint32_t &lo, uint32_t &hi) {
+    static_assert(P == 16 || P == 32, "row or half partner");
+    if constexpr (P == 16) {
+        const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+        lo = r[0];
+        hi = r[1];
+    } else {
+        const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+        lo = r[0];
+        hi = r[1];
+    }
+}
+
 // Wave inclusive prefix sum (fp64) in lane order.
 __device__ __forceinline__ double wave_incl_scan(double v) {
 #pragma unroll

@@ -29,6 +29,7 @@
 #include <stdlib.h>
 
 #include <atomic>
+#include <type_traits>
 
 #include "common.h"
 
@@ -229,14 +230,21 @@ __device__ __forceinline__ void mk_epilogue(const MarkovArgs &a, int r, bool rok
             }
         }
     }
-    // reduce over the 4 lanes sharing this request (lane bits 4..5)
-#pragma unroll
-    for (int o = 16; o < 64; o <<= 1) {
-        const float m2 = __shfl_xor(m, o, 64);
-        const int a2 = __shfl_xor(arg, o, 64);
-        argmax_combine(m, arg, m2, a2);
-        nanseen |= __shfl_xor(nanseen, o, 64);
-    }
+    // reduce over the 4 lanes sharing this request (lane bits 4..5): the
+    // partner across rows, then across halves
+    auto pair_max = [&](auto tag) {
+        constexpr int P = decltype(tag)::value;
+        uint32_t m0, m1, a0, a1, n0, n1;
+        lane_pair<P>(__float_as_uint(m), m0, m1);
+        lane_pair<P>((uint32_t)arg, a0, a1);
+        lane_pair<P>((uint32_t)nanseen, n0, n1);
+        m = __uint_as_float(m0);
+        arg = (int)a0;
+        argmax_combine(m, arg, __uint_as_float(m1), (int)a1);
+        nanseen = (int)(n0 | n1);
+    };
+    pair_max(std::integral_constant<int, 16>{});
+    pair_max(std::integral_constant<int, 32>{});
     float out1;
     if (greedy) {
         if (nanseen) m = __builtin_nanf("");
@@ -255,8 +263,11 @@ __device__ __forceinline__ void mk_epilogue(const MarkovArgs &a, int r, bool rok
                 for (int j = 0; j < 4; ++j)
                     if (lv[vb][j] != lv[vb][j]) e = lv[vb][j];
         }
-#pragma unroll
-        for (int o = 16; o < 64; o <<= 1) e += __shfl_xor(e, o, 64);
+        uint32_t e0, e1;
+        lane_pair<16>(__float_as_uint(e), e0, e1);
+        e = __uint_as_float(e0) + __uint_as_float(e1);
+        lane_pair<32>(__float_as_uint(e), e0, e1);
+        e = __uint_as_float(e0) + __uint_as_float(e1);
         out1 = e;
     }
     if (ALL || (rok && kgrp == 0)) a.tstats[(size_t)r * a.ntiles + tile] = make_float2(m, out1);
